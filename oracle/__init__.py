@@ -1,0 +1,27 @@
+"""CPU oracle for the GPTQ layer quantizer (test infrastructure only).
+
+Only the test suite, the smoke check in ``__graft_entry__`` and the CPU
+baseline leg of ``bench.py`` may import this package.  The product path
+(the HIP library and its Python binding) never imports or calls it.
+"""
+from .gptq_oracle import (  # noqa: F401
+    NotPositiveDefinite,
+    hessian,
+    hessian_rows,
+    act_order_perm,
+    damp_and_permute,
+    inverse_cholesky_upper,
+    grid_params,
+    quantize_values,
+    gptq_quantize,
+    rtn_quantize,
+    unpermute_codes,
+    group_index,
+    dequantize,
+    layer_loss,
+    obs_loss,
+    pack_codes,
+    unpack_codes,
+    packed_words_per_row,
+    gptq_layer,
+)

@@ -1,0 +1,414 @@
+"""Plain CPU oracle for one-shot GPTQ quantization of a single linear layer.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously-correct
+definition that the HIP library is checked against.  It shares no code with
+the HIP path, and nothing on the product path imports it.
+
+Everything here follows the pages' statement of the method:
+
+* GPTQ knowledge note, "How It Works": for each linear layer the recorded
+  inputs X give the Hessian H = 2XX^T of the layer-output reconstruction
+  loss; after a column is quantized, inverse-Hessian information decides how
+  the still-unquantized columns are adjusted; all rows follow one column
+  order; 128-column blocks accumulate corrections before a global update; a
+  damped Cholesky formulation supplies the correction rows.
+* Wiki "GPTQ", "Technical Approach": low-bit grid (4/3/2 bits) with
+  group-wise quantization, each group having its own scaling factor.
+* Daily Papers page, GPTQ abstract: 2-bit and ternary grids.
+* Daily Papers page, abstract on GPTQ and Babai's nearest plane algorithm:
+  the rounding errors are propagated to the not-yet-processed entries
+  through a triangular feedback matrix (used by the tests as a pin).
+
+Precision: H, the damped inverse factor U and the error propagation are
+float64.  The few operations that decide a code (grid range, scale, zero
+point, the division w/s and the rounding) are specified in IEEE float32 with
+round-half-to-even, and are evaluated here with numpy float32 arithmetic, so
+that the GPU kernels can reproduce them bit for bit.  Where the pages are
+silent the reading taken is stated next to the code that implements it.
+
+Layouts: W is out x in (rows x columns, columns are the input features that
+are swept); X is tokens x in.  "Processing order" is the column order after
+the optional act-order permutation.
+
+Parity pins: every function here is pinned by tests/test_oracle_pins.py
+(closed forms, hand-worked fixtures under tests/golden/, brute force,
+Babai's nearest plane algorithm, a conditional least-squares definition that
+does not use U, and an exact loss identity).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+class NotPositiveDefinite(ValueError):
+    """The damped Hessian is not positive definite.
+
+    ``index`` is the 1-based position (in the factored matrix) of the first
+    non-positive pivot, LAPACK style.
+    """
+
+    def __init__(self, index: int):
+        super().__init__(f"damped Hessian not positive definite (pivot {index})")
+        self.index = index
+
+
+# ---------------------------------------------------------------------------
+# a1: Hessian.  GPTQ knowledge note, "How It Works": H = 2 X X^T over the
+# recorded layer inputs.  With X stored tokens x n this is H = 2 X^T X.
+# ---------------------------------------------------------------------------
+def hessian(X, alpha: float = 2.0) -> np.ndarray:
+    """H = alpha * X^T X in float64 (X is tokens x n, already dtype-rounded)."""
+    X64 = np.asarray(X, dtype=F64)
+    return alpha * (X64.T @ X64)
+
+
+def hessian_rows(X, rows, alpha: float = 2.0, chunk: int = 16384) -> np.ndarray:
+    """Rows ``rows`` of H = alpha * X^T X, float64, streaming over tokens."""
+    X = np.asarray(X)
+    rows = np.asarray(rows, dtype=np.int64)
+    out = np.zeros((rows.size, X.shape[1]), dtype=F64)
+    for t0 in range(0, X.shape[0], chunk):
+        Xc = np.asarray(X[t0:t0 + chunk], dtype=F64)
+        out += Xc[:, rows].T @ Xc
+    return alpha * out
+
+
+# ---------------------------------------------------------------------------
+# a2: act-order permutation and damping.
+# The pages give neither: columns are ordered by descending diag(H) (the
+# act-order option of the workload definitions) with ties kept in ascending
+# original index (a stable sort), and the damping constant is a parameter
+# lambda = damp_rel * mean(diag H) added after permutation (GPTQ knowledge
+# note, "How It Works", only says the Cholesky formulation is damped).
+# ---------------------------------------------------------------------------
+def act_order_perm(H) -> np.ndarray:
+    """Stable argsort of diag(H), descending; ties keep ascending index."""
+    d = np.diag(np.asarray(H, dtype=F64))
+    n = d.size
+    # Explicit ordering key: (-d, index).  lexsort sorts by the last key first.
+    return np.lexsort((np.arange(n), -d)).astype(np.int64)
+
+
+def damp_and_permute(H, perm, damp_rel: float):
+    """Return (H_d, lam) with H_d = H[perm][:, perm] + lam * I."""
+    H = np.asarray(H, dtype=F64)
+    n = H.shape[0]
+    perm = np.arange(n) if perm is None else np.asarray(perm, dtype=np.int64)
+    lam = float(damp_rel) * float(np.mean(np.diag(H)))
+    Hd = H[np.ix_(perm, perm)].copy()
+    Hd[np.diag_indices(n)] += lam
+    return Hd, lam
+
+
+# ---------------------------------------------------------------------------
+# a3: the damped inverse-Hessian factor.  U is upper triangular with positive
+# diagonal and U^T U = H_d^{-1}; row j of U divided by U_jj is the correction
+# row used when column j is quantized (GPTQ knowledge note, "How It Works":
+# "a damped Cholesky formulation supplies stable correction rows").
+# Plain definition: invert H_d (via its Cholesky factor), then take the upper
+# Cholesky factor of the inverse.
+# ---------------------------------------------------------------------------
+def _cholesky_lower(A) -> np.ndarray:
+    try:
+        return np.linalg.cholesky(A)
+    except np.linalg.LinAlgError:
+        # Locate the first non-positive pivot for the error report.
+        n = A.shape[0]
+        for k in range(1, n + 1):
+            try:
+                np.linalg.cholesky(A[:k, :k])
+            except np.linalg.LinAlgError:
+                raise NotPositiveDefinite(k) from None
+        raise NotPositiveDefinite(n) from None
+
+
+def inverse_cholesky_upper(Hd) -> np.ndarray:
+    """U upper, U^T U = Hd^{-1}.  Raises NotPositiveDefinite."""
+    Hd = np.asarray(Hd, dtype=F64)
+    n = Hd.shape[0]
+    if n == 0:
+        return np.zeros((0, 0), dtype=F64)
+    if not np.all(np.isfinite(Hd)):
+        raise NotPositiveDefinite(1)
+    L = _cholesky_lower(Hd)
+    Linv = np.linalg.solve(L, np.eye(n))
+    Hinv = Linv.T @ Linv
+    Hinv = 0.5 * (Hinv + Hinv.T)
+    return np.linalg.cholesky(Hinv).T
+
+
+# ---------------------------------------------------------------------------
+# a4: grid parameters.  Wiki "GPTQ", "Technical Approach": group-wise
+# quantization, each group with its own scaling factor, on a uniform low-bit
+# grid (GPTQ knowledge note, "Common Confusions": a fixed low-bit grid shared
+# with round-to-nearest).  Readings taken (the pages are silent):
+#   * asymmetric min-max grid with an integer zero point;
+#   * the range always contains 0: xmin = min(0, min w), xmax = max(0, max w);
+#   * an all-zero group uses the range [-1, 1];
+#   * float32 arithmetic, IEEE division, round half to even:
+#       s = fl32(fl32(xmax - xmin) / maxq),  z = clamp(rint(fl32(-xmin / s)), 0, maxq).
+# ---------------------------------------------------------------------------
+def grid_params(vals, maxq: int):
+    """Per-row (scale, zero) of the rows of ``vals`` (rows x group), float32."""
+    v = np.asarray(vals, dtype=F32)
+    if v.ndim == 1:
+        v = v[None, :]
+    xmin = np.minimum(v.min(axis=1), F32(0))
+    xmax = np.maximum(v.max(axis=1), F32(0))
+    degenerate = xmax == xmin
+    xmin = np.where(degenerate, F32(-1), xmin).astype(F32)
+    xmax = np.where(degenerate, F32(1), xmax).astype(F32)
+    s = ((xmax - xmin) / F32(maxq)).astype(F32)
+    z = np.rint((-xmin) / s).astype(F32)
+    z = np.clip(z, F32(0), F32(maxq)).astype(F32)
+    return s, z
+
+
+def quantize_values(w, s, z, maxq: int, clip: bool = True):
+    """Codes c = clamp(rint(fl32(w / s)) + z, 0, maxq), float32 arithmetic.
+
+    ``w`` is rounded to float32 first (the quantizer's input precision).
+    With ``clip=False`` the clamp is omitted (used only for the
+    no-clipping condition of Babai's error bound).
+    """
+    w32 = np.asarray(w, dtype=F64).astype(F32)
+    q = np.rint(w32 / np.asarray(s, dtype=F32)).astype(F32) + np.asarray(z, dtype=F32)
+    if clip:
+        q = np.clip(q, F32(0), F32(maxq))
+    return q.astype(F32)
+
+
+# ---------------------------------------------------------------------------
+# a5 + a6: the column sweep.  GPTQ knowledge note, "How It Works": after a
+# column is quantized the remaining full-precision columns are adjusted with
+# inverse-Hessian information; every row follows one column order; blocks of
+# ``block_size`` columns accumulate their corrections before one global
+# update of the columns after the block.  With block_size = 1 every update is
+# immediate (the unblocked sequential form); any block size gives the same
+# result in exact arithmetic.
+#
+# Column step j (processing order) for every row r:
+#   (group start)  (s, z) from the current values of the group's columns
+#   c   = clamp(rint(fl32(v_rj / s)) + z, 0, maxq)
+#   w^  = s * (c - z)
+#   e   = (v_rj - w^) / U_jj
+#   v_rk -= e * U_jk   for the later columns k > j   (immediately inside the
+#                      block, deferred to the block boundary outside it)
+# ---------------------------------------------------------------------------
+def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
+                  block_size: int = 128, clip: bool = True, order: str = "right",
+                  record_inputs: bool = False):
+    """Quantize W (m x n) with the inverse-Hessian factor U (processing order).
+
+    Returns a dict with (all in processing order unless noted):
+      codes   m x n float32 integer-valued codes
+      scales  m x G float32, zeros m x G float32 (G groups in processing order)
+      E       m x n float64 scaled errors e
+      row_loss m float64 = sum_j e_rj^2 / 2
+      qin     m x n float64 value each entry had when it was quantized
+              (only with record_inputs=True)
+    ``order`` selects where the deferred block update is applied:
+    "right" after each block to all later columns, "left" to each block just
+    before it is swept (identical in exact arithmetic).
+    """
+    W = np.asarray(W, dtype=F64)
+    U = np.asarray(U, dtype=F64)
+    m, n = W.shape
+    maxq = int(levels) - 1
+    if maxq < 1:
+        raise ValueError("levels must be >= 2")
+    perm = np.arange(n) if perm is None else np.asarray(perm, dtype=np.int64)
+    g = int(group_size)
+    if g < 0:
+        raise ValueError("group_size must be >= 0")
+    B = max(1, int(block_size))
+    if B > 1 and g > 0 and B % g != 0:
+        raise ValueError("blocked sweep needs block_size % group_size == 0")
+    if order not in ("right", "left"):
+        raise ValueError("order must be 'right' or 'left'")
+    G = 1 if g == 0 else -(-n // g)
+
+    V = W[:, perm].copy()
+    codes = np.zeros((m, n), dtype=F32)
+    E = np.zeros((m, n), dtype=F64)
+    scales = np.zeros((m, G), dtype=F32)
+    zeros = np.zeros((m, G), dtype=F32)
+    qin = np.zeros((m, n), dtype=F64) if record_inputs else None
+
+    if g == 0 and n > 0:
+        # Per-row grid: taken from the original row, before any update.
+        s_row, z_row = grid_params(V.astype(F32), maxq)
+        scales[:, 0], zeros[:, 0] = s_row, z_row
+    s_cur = scales[:, 0].copy()
+    z_cur = zeros[:, 0].copy()
+
+    for b0 in range(0, n, B):
+        b1 = min(n, b0 + B)
+        if order == "left" and b0 > 0:
+            V[:, b0:b1] -= E[:, :b0] @ U[:b0, b0:b1]
+        for j in range(b0, b1):
+            if g > 0 and j % g == 0:
+                gi = j // g
+                s_cur, z_cur = grid_params(V[:, j:min(n, j + g)].astype(F32), maxq)
+                scales[:, gi], zeros[:, gi] = s_cur, z_cur
+            v = V[:, j]
+            if record_inputs:
+                qin[:, j] = v
+            c = quantize_values(v, s_cur, z_cur, maxq, clip=clip)
+            what = s_cur.astype(F64) * (c.astype(F64) - z_cur.astype(F64))
+            e = (v - what) / U[j, j]
+            codes[:, j] = c
+            E[:, j] = e
+            if j + 1 < b1:
+                V[:, j + 1:b1] -= np.outer(e, U[j, j + 1:b1])
+        if order == "right" and b1 < n:
+            V[:, b1:] -= E[:, b0:b1] @ U[b0:b1, b1:]
+
+    out = dict(codes=codes, scales=scales, zeros=zeros, E=E,
+               row_loss=0.5 * np.sum(E * E, axis=1), perm=perm,
+               levels=int(levels), group_size=g)
+    if record_inputs:
+        out["qin"] = qin
+    return out
+
+
+def rtn_quantize(W, levels: int = 16, group_size: int = 0, perm=None):
+    """Round-to-nearest on the same grid rule, no error propagation.
+
+    Groups are taken in processing order (``perm``), like the GPTQ sweep.
+    Returns the same dict layout as ``gptq_quantize`` (without E/row_loss).
+    """
+    W = np.asarray(W, dtype=F64)
+    m, n = W.shape
+    maxq = int(levels) - 1
+    perm = np.arange(n) if perm is None else np.asarray(perm, dtype=np.int64)
+    V = W[:, perm]
+    g = int(group_size)
+    G = 1 if g == 0 else -(-n // g)
+    codes = np.zeros((m, n), dtype=F32)
+    scales = np.zeros((m, G), dtype=F32)
+    zeros = np.zeros((m, G), dtype=F32)
+    for gi in range(G):
+        j0, j1 = (0, n) if g == 0 else (gi * g, min(n, (gi + 1) * g))
+        s, z = grid_params(V[:, j0:j1].astype(F32), maxq)
+        scales[:, gi], zeros[:, gi] = s, z
+        for j in range(j0, j1):
+            codes[:, j] = quantize_values(V[:, j], s, z, maxq)
+    return dict(codes=codes, scales=scales, zeros=zeros, perm=perm,
+                levels=int(levels), group_size=g)
+
+
+# ---------------------------------------------------------------------------
+# a7: outputs in the original column order, packing.
+# ---------------------------------------------------------------------------
+def unpermute_codes(codes_proc, perm) -> np.ndarray:
+    """codes[:, perm[j]] = codes_proc[:, j]."""
+    codes_proc = np.asarray(codes_proc)
+    out = np.empty_like(codes_proc)
+    out[:, np.asarray(perm, dtype=np.int64)] = codes_proc
+    return out
+
+
+def group_index(perm, group_size: int) -> np.ndarray:
+    """g_idx[perm[j]] = j // group_size (0 everywhere for per-row grids)."""
+    perm = np.asarray(perm, dtype=np.int64)
+    n = perm.size
+    gidx = np.zeros(n, dtype=np.int32)
+    if group_size > 0:
+        gidx[perm] = (np.arange(n) // group_size).astype(np.int32)
+    return gidx
+
+
+def dequantize(res) -> np.ndarray:
+    """W^ in the original column order, float64: s_g * (c - z_g)."""
+    codes = res["codes"].astype(F64)
+    m, n = codes.shape
+    g = res["group_size"]
+    gi = np.zeros(n, dtype=np.int64) if g == 0 else np.arange(n) // g
+    s = res["scales"].astype(F64)[:, gi]
+    z = res["zeros"].astype(F64)[:, gi]
+    return unpermute_codes(s * (codes - z), res["perm"])
+
+
+def layer_loss(W, What, H) -> float:
+    """||(W - W^) X||_F^2 = tr(D (H/2) D^T) with H = 2 X X^T (undamped)."""
+    D = np.asarray(W, dtype=F64) - np.asarray(What, dtype=F64)
+    return float(np.sum((D @ (0.5 * np.asarray(H, dtype=F64))) * D))
+
+
+def obs_loss(W, What, Hd, perm) -> np.ndarray:
+    """Per-row 1/2 D H_d D^T in processing order (H_d is the damped, permuted H)."""
+    perm = np.asarray(perm, dtype=np.int64)
+    D = (np.asarray(W, dtype=F64) - np.asarray(What, dtype=F64))[:, perm]
+    return 0.5 * np.sum((D @ np.asarray(Hd, dtype=F64)) * D, axis=1)
+
+
+def packed_words_per_row(n: int, bits: int) -> int:
+    return -(-(int(n) * int(bits)) // 32)
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Pack b-bit codes row-wise, LSB first, into uint32 words.
+
+    Code k of a row occupies bits [k*b, (k+1)*b) of the row's little-endian
+    bit stream (the pages fix no layout; GPTQ knowledge note, "Common
+    Confusions": GPTQ is not itself a bit encoding).
+    """
+    codes = np.asarray(codes, dtype=np.int64)
+    m, n = codes.shape
+    nw = packed_words_per_row(n, bits)
+    out = np.zeros((m, nw), dtype=np.uint64)
+    for k in range(n):
+        bit = k * bits
+        w, off = divmod(bit, 32)
+        v = codes[:, k].astype(np.uint64)
+        out[:, w] |= (v << np.uint64(off)) & np.uint64(0xFFFFFFFF)
+        if off + bits > 32:
+            out[:, w + 1] |= v >> np.uint64(32 - off)
+    return out.astype(np.uint32)
+
+
+def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint64)
+    m = packed.shape[0]
+    out = np.zeros((m, n), dtype=np.int64)
+    mask = np.uint64((1 << bits) - 1)
+    for k in range(n):
+        bit = k * bits
+        w, off = divmod(bit, 32)
+        v = packed[:, w] >> np.uint64(off)
+        if off + bits > 32:
+            v |= packed[:, w + 1] << np.uint64(32 - off)
+        out[:, k] = (v & mask).astype(np.int64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# End to end for one layer.
+# ---------------------------------------------------------------------------
+def gptq_layer(W, X=None, H=None, levels: int = 16, group_size: int = 0,
+               block_size: int = 128, damp_rel: float = 0.01,
+               act_order: bool = False, alpha: float = 2.0):
+    """Quantize one linear layer: H, damp/permute, U, sweep, outputs.
+
+    Pass either calibration inputs X (tokens x n) or a precomputed H.
+    """
+    W = np.asarray(W, dtype=F64)
+    if H is None:
+        H = hessian(X, alpha)
+    H = np.asarray(H, dtype=F64)
+    perm = act_order_perm(H) if act_order else np.arange(W.shape[1])
+    Hd, lam = damp_and_permute(H, perm, damp_rel)
+    U = inverse_cholesky_upper(Hd)
+    res = gptq_quantize(W, U, perm, levels, group_size, block_size)
+    What = dequantize(res)
+    bits = max(1, int(np.ceil(np.log2(levels))))
+    codes_orig = unpermute_codes(res["codes"], perm).astype(np.int64)
+    res.update(H=H, Hd=Hd, lam=lam, U=U, What=What, codes_orig=codes_orig,
+               g_idx=group_index(perm, group_size),
+               packed=pack_codes(codes_orig, bits), bits=bits,
+               loss=layer_loss(W, What, H))
+    return res

@@ -1,0 +1,452 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+None of these compare the oracle with itself: each checks it against a
+hand-worked fixture, a closed form, a textbook algorithm implemented here
+independently (Babai's nearest plane algorithm, conditional least squares,
+brute-force enumeration, finite differences) or an exact identity.
+"""
+import inspect
+import itertools
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gptq_oracle as go
+from tests.conftest import read_golden
+
+F32 = np.float32
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _random_spd(n, rng, cond_mix=0.5, tokens=None):
+    tokens = tokens or 4 * n
+    X = rng.standard_normal((tokens, n)) @ (np.eye(n) + cond_mix * rng.standard_normal((n, n)))
+    return 2.0 * X.T @ X / tokens, X
+
+
+# ---------------------------------------------------------------------------
+# a1 Hessian: H = 2 X X^T is the Hessian of the layer-output loss
+# (GPTQ knowledge note, "How It Works").  Pinned by finite differences of
+# the loss ||w X||^2, which never forms X^T X.
+# ---------------------------------------------------------------------------
+def test_hessian_is_second_derivative_of_reconstruction_loss():
+    rng = _rng(1)
+    N, n = 37, 6
+    X = rng.standard_normal((N, n))          # tokens x features
+    w0 = rng.standard_normal(n)
+
+    def f(w):
+        return float(np.sum((X @ w) ** 2))   # ||w X||^2 in the pages' layout
+
+    h = 0.5
+    Hfd = np.zeros((n, n))
+    for i in range(n):
+        for j in range(n):
+            ei, ej = np.eye(n)[i] * h, np.eye(n)[j] * h
+            Hfd[i, j] = (f(w0 + ei + ej) - f(w0 + ei) - f(w0 + ej) + f(w0)) / (h * h)
+    H = oracle.hessian(X)
+    np.testing.assert_allclose(H, Hfd, rtol=1e-10, atol=1e-9)
+    # Sampled rows agree with the full matrix.
+    np.testing.assert_allclose(oracle.hessian_rows(X, [4, 1], chunk=5), H[[4, 1]], rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# a2 act-order and damping (hand-worked fixture).
+# ---------------------------------------------------------------------------
+def test_act_order_and_damping_fixture():
+    lines = dict(ln.split(None, 1) for ln in read_golden("act_order_damping.txt"))
+    d = np.array(lines["perm_diag"].split(), dtype=float)
+    expect = np.array(lines["perm_expected"].split(), dtype=int)
+    np.testing.assert_array_equal(oracle.act_order_perm(np.diag(d)), expect)
+
+    H = np.diag([1.0, 2.0, 3.0, 4.0])
+    H[0, 1] = H[1, 0] = 0.5
+    perm = oracle.act_order_perm(H)
+    np.testing.assert_array_equal(perm, [3, 2, 1, 0])
+    Hd, lam = oracle.damp_and_permute(H, perm, 0.01)
+    assert lam == pytest.approx(float(lines["damp_lambda"]), rel=1e-15)
+    np.testing.assert_allclose(np.diag(Hd), np.array(lines["damp_diag"].split(), dtype=float), rtol=1e-15)
+    assert Hd[2, 3] == Hd[3, 2] == 0.5
+
+
+def test_act_order_is_stable_descending():
+    rng = _rng(2)
+    d = rng.integers(0, 5, size=200).astype(float)    # many ties
+    perm = oracle.act_order_perm(np.diag(d))
+    assert sorted(perm.tolist()) == list(range(200))
+    ds = d[perm]
+    assert np.all(ds[:-1] >= ds[1:])
+    for i in range(199):
+        if ds[i] == ds[i + 1]:
+            assert perm[i] < perm[i + 1]
+
+
+# ---------------------------------------------------------------------------
+# a3 the inverse factor.  U upper with positive diagonal and U^T U = Hd^-1 is
+# unique; pinned against a second route (reverse-order Cholesky of Hd, then a
+# triangular inverse) that never forms Hd^-1.
+# ---------------------------------------------------------------------------
+def test_inverse_factor_two_routes():
+    import scipy.linalg as sla
+    rng = _rng(3)
+    for n in (1, 2, 5, 33, 130):
+        Hd, _ = _random_spd(n, rng)
+        U = oracle.inverse_cholesky_upper(Hd)
+        assert np.allclose(np.tril(U, -1), 0)
+        assert np.all(np.diag(U) > 0)
+        np.testing.assert_allclose(U.T @ U @ Hd, np.eye(n), atol=1e-9)
+        J = np.eye(n)[::-1]
+        L = np.linalg.cholesky(J @ Hd @ J)
+        R = J @ L @ J                       # Hd = R R^T, R upper
+        U2 = sla.solve_triangular(R, np.eye(n), lower=False)
+        np.testing.assert_allclose(U, U2, rtol=1e-9, atol=1e-12)
+
+
+def test_not_positive_definite_reports_pivot():
+    H = np.diag([1.0, 2.0, 0.0, 3.0])
+    with pytest.raises(oracle.NotPositiveDefinite) as ei:
+        oracle.inverse_cholesky_upper(H)
+    assert ei.value.index == 3
+    with pytest.raises(oracle.NotPositiveDefinite):
+        oracle.inverse_cholesky_upper(np.zeros((3, 3)))
+
+
+# ---------------------------------------------------------------------------
+# a4 grid parameters (hand-worked fixture).
+# ---------------------------------------------------------------------------
+def test_grid_fixture():
+    for ln in read_golden("grid_asymmetric.txt"):
+        head, vals, sz, codes = [p.strip() for p in ln.split("|")]
+        _, levels = head.split()
+        levels = int(levels)
+        v = np.array(vals.split(), dtype=F32)
+        s_exp, z_exp = sz.split()
+        s, z = oracle.grid_params(v[None, :], levels - 1)
+        assert s[0] == F32(float(s_exp))
+        assert z[0] == float(z_exp)
+        c = oracle.quantize_values(v, s, z, levels - 1)
+        np.testing.assert_array_equal(c, np.array(codes.split(), dtype=F32))
+
+
+def test_grid_reconstruction_error_bounded():
+    rng = _rng(4)
+    for levels in (3, 4, 8, 16):
+        W = rng.standard_normal((50, 64)) * 0.02
+        s, z = oracle.grid_params(W.astype(F32), levels - 1)
+        c = oracle.quantize_values(W, s[:, None], z[:, None], levels - 1)
+        assert c.min() >= 0 and c.max() <= levels - 1
+        what = s[:, None].astype(float) * (c - z[:, None])
+        # Inside the range every value is within half a step of its grid point.
+        assert np.all(np.abs(W.astype(F32) - what) <= 0.5 * s[:, None] * (1 + 1e-5))
+
+
+# ---------------------------------------------------------------------------
+# a5/a6 the sweep.
+# ---------------------------------------------------------------------------
+def test_three_column_fixture():
+    g = dict(ln.split(None, 1) for ln in read_golden("gptq_three_columns.txt"))
+    U = np.array([[float(x) for x in row.split()] for row in g["U"].split("|")])
+    w = np.array(g["w"].split(), dtype=F32).astype(float)[None, :]
+    levels = int(g["levels"])
+    res = oracle.gptq_quantize(w, U, None, levels, 0, block_size=1, record_inputs=True)
+    assert res["scales"][0, 0] == F32(float(g["scale"]))
+    assert res["zeros"][0, 0] == float(g["zero"])
+    np.testing.assert_array_equal(res["codes"][0], np.array(g["codes"].split(), dtype=float))
+    assert res["qin"][0, 1] == pytest.approx(float(g["qin1"]), rel=1e-12)
+    rtn = oracle.rtn_quantize(w, levels, 0)
+    np.testing.assert_array_equal(rtn["codes"][0], np.array(g["rtn_codes"].split(), dtype=float))
+    Hd = np.array([[1, 0.9, 0], [0.9, 1, 0], [0, 0, 1.0]])
+    np.testing.assert_allclose(U.T @ U @ Hd, np.eye(3), atol=1e-12)
+    assert res["row_loss"][0] == pytest.approx(float(g["obs_loss"]), rel=1e-6)
+    for r, key in ((res, "obs_loss"), (rtn, "rtn_obs_loss")):
+        What = oracle.dequantize(r)
+        assert oracle.obs_loss(w, What, Hd, np.arange(3))[0] == pytest.approx(float(g[key]), rel=1e-6)
+
+
+@pytest.mark.parametrize("levels,group,act", [(16, 0, False), (16, 8, True), (8, 16, False),
+                                              (4, 0, True), (3, 8, False)])
+def test_identity_hessian_reduces_to_rtn(levels, group, act):
+    """H = I (any damping): U is diagonal, nothing is propagated, GPTQ = RTN bit for bit."""
+    rng = _rng(5)
+    m, n = 40, 64
+    W = (rng.standard_normal((m, n)) * 0.02).astype(F32).astype(float)
+    res = oracle.gptq_layer(W, H=np.eye(n), levels=levels, group_size=group, act_order=act,
+                            block_size=16)
+    np.testing.assert_array_equal(res["perm"], np.arange(n))     # ties keep natural order
+    rtn = oracle.rtn_quantize(W, levels, group)
+    np.testing.assert_array_equal(res["codes"], rtn["codes"])
+    np.testing.assert_array_equal(res["scales"], rtn["scales"])
+    np.testing.assert_array_equal(res["zeros"], rtn["zeros"])
+    # Diagonal, non-constant H with act-order: still RTN, in processing-order groups.
+    d = rng.uniform(1, 2, size=n)
+    res2 = oracle.gptq_layer(W, H=np.diag(d), levels=levels, group_size=group, act_order=act,
+                             block_size=16)
+    rtn2 = oracle.rtn_quantize(W, levels, group, perm=res2["perm"])
+    np.testing.assert_array_equal(res2["codes"], rtn2["codes"])
+
+
+def _sweep_case(seed, m=7, n=24, levels=16, group=0, act=True, clip=True, block=1, order="right"):
+    rng = _rng(seed)
+    H, _ = _random_spd(n, rng, cond_mix=0.7)
+    W = rng.standard_normal((m, n)) * 0.05
+    perm = oracle.act_order_perm(H) if act else np.arange(n)
+    Hd, _ = oracle.damp_and_permute(H, perm, 0.01)
+    U = oracle.inverse_cholesky_upper(Hd)
+    res = oracle.gptq_quantize(W, U, perm, levels, group, block_size=block, clip=clip,
+                               order=order, record_inputs=True)
+    return W, H, Hd, U, perm, res
+
+
+@pytest.mark.parametrize("seed,levels,group,act,block", [(10, 16, 0, False, 1), (11, 8, 8, True, 1),
+                                                         (12, 4, 4, True, 8), (13, 3, 0, False, 4),
+                                                         (14, 16, 8, True, 8)])
+def test_conditional_least_squares_definition(seed, levels, group, act, block):
+    """The value quantized at step j is the j-th coordinate of
+    argmin_v ||w - v||_{Hd} with v_<j fixed to the grid values already chosen.
+    Solved directly with a linear solve on Hd; U is never used."""
+    W, H, Hd, U, perm, res = _sweep_case(seed, levels=levels, group=group, act=act, block=block)
+    V0 = W[:, perm]
+    n = V0.shape[1]
+    g = res["group_size"]
+    gi = np.zeros(n, int) if g == 0 else np.arange(n) // g
+    What = res["scales"].astype(float)[:, gi] * (res["codes"] - res["zeros"].astype(float)[:, gi])
+    for j in range(n):
+        a, b = slice(0, j), slice(j, n)
+        dA = V0[:, a] - What[:, a]
+        vb = V0[:, b] + np.linalg.solve(Hd[b, b], Hd[b, a] @ dA.T).T
+        np.testing.assert_allclose(res["qin"][:, j], vb[:, 0], rtol=1e-9, atol=1e-12)
+
+
+def test_loss_identity():
+    """sum_j e_j^2 / 2 = 1/2 D Hd D^T = ||D X||^2 + lam/2 ||D||^2 (exact, any grid)."""
+    rng = _rng(20)
+    for trial in range(20):
+        n = int(rng.integers(2, 40))
+        m = int(rng.integers(1, 9))
+        X = rng.standard_normal((3 * n, n)) * np.exp(rng.standard_normal(n))
+        W = rng.standard_normal((m, n)) * 0.05
+        levels = int(rng.choice([3, 4, 8, 16]))
+        group = int(rng.choice([0, 2, 4]))
+        act = bool(rng.integers(0, 2))
+        res = oracle.gptq_layer(W, X=X, levels=levels, group_size=group, act_order=act, block_size=4)
+        D = W - res["What"]
+        np.testing.assert_allclose(res["row_loss"], oracle.obs_loss(W, res["What"], res["Hd"], res["perm"]),
+                                   rtol=1e-9)
+        dx = float(np.sum((D @ X.T) ** 2))
+        np.testing.assert_allclose(res["row_loss"].sum(), dx + 0.5 * res["lam"] * np.sum(D * D), rtol=1e-9)
+        np.testing.assert_allclose(res["loss"], dx, rtol=1e-9)
+
+
+def _babai_nearest_plane(t, G):
+    """Textbook nearest-plane back-substitution for min_y ||t - y||_G over integers,
+    G = R^T R with R upper (Cholesky of G): y_j = rint(t_j + sum_{k>j} R_jk (t_k - y_k) / R_jj)."""
+    R = np.linalg.cholesky(G).T
+    n = t.size
+    y = np.zeros(n)
+    for j in range(n - 1, -1, -1):
+        y[j] = np.rint(t[j] + np.dot(R[j, j + 1:], t[j + 1:] - y[j + 1:]) / R[j, j])
+    return y
+
+
+def test_back_to_front_gptq_is_babai_nearest_plane():
+    """Daily Papers page, abstract on GPTQ and Babai's nearest plane algorithm:
+    run back to front with no clipping, GPTQ equals nearest plane on the lattice of
+    the Hessian.  Grid coordinates: t = w / s, integer y = code - zero."""
+    rng = _rng(30)
+    mism = 0
+    total = 0
+    for trial in range(400):
+        n = int(rng.integers(3, 7))
+        H, _ = _random_spd(n, rng, cond_mix=1.0)
+        w = rng.standard_normal((1, n)) * 0.05
+        back = np.arange(n)[::-1]
+        Hd, _ = oracle.damp_and_permute(H, back, 0.01)
+        U = oracle.inverse_cholesky_upper(Hd)
+        res = oracle.gptq_quantize(w, U, back, 16, 0, block_size=1, clip=False)
+        s, z = res["scales"][0, 0], res["zeros"][0, 0]
+        y_gptq = oracle.unpermute_codes(res["codes"], back)[0] - z
+        Hd_nat, _ = oracle.damp_and_permute(H, None, 0.01)
+        t = w[0].astype(F32).astype(float) / float(s)
+        y_babai = _babai_nearest_plane(t, Hd_nat)
+        mism += int(np.sum(y_gptq != y_babai))
+        total += n
+    assert mism == 0, f"{mism} of {total} coordinates differ"
+
+
+def test_babai_error_bound_and_brute_force_optimum():
+    """No clipping: ||D||^2_{Hd} <= (s^2/4) sum_j U_jj^-2 (Babai's bound).
+    2-bit, n <= 6: the grid optimum found by enumeration is never above the
+    oracle's loss, and the loss of the oracle's codes evaluated directly
+    equals the reported loss."""
+    rng = _rng(31)
+    for trial in range(150):
+        n = int(rng.integers(2, 7))
+        H, _ = _random_spd(n, rng, cond_mix=1.0)
+        w = rng.standard_normal((1, n)) * 0.05
+        Hd, _ = oracle.damp_and_permute(H, None, 0.01)
+        U = oracle.inverse_cholesky_upper(Hd)
+        res = oracle.gptq_quantize(w, U, None, 4, 0, block_size=1, clip=False)
+        s = float(res["scales"][0, 0])
+        D = w - oracle.dequantize(res)
+        lossH = float((D @ Hd @ D.T)[0, 0])
+        assert lossH <= (s * s / 4) * np.sum(np.diag(U) ** -2) * (1 + 1e-9)
+        # brute force over the clipped 2-bit grid
+        resc = oracle.gptq_quantize(w, U, None, 4, 0, block_size=1, clip=True)
+        z = float(resc["zeros"][0, 0])
+        best = np.inf
+        for codes in itertools.product(range(4), repeat=n):
+            d = w[0] - s * (np.array(codes) - z)
+            best = min(best, float(d @ Hd @ d))
+        Dc = w - oracle.dequantize(resc)
+        mine = float((Dc @ Hd @ Dc.T)[0, 0])
+        assert best <= mine * (1 + 1e-12)
+        assert 2 * resc["row_loss"][0] == pytest.approx(mine, rel=1e-9)
+
+
+def test_gptq_not_worse_than_rtn_two_columns():
+    """n <= 2: column 0 is RTN and column 1 is the exact 1-D minimiser, so GPTQ's
+    loss in the damped metric never exceeds RTN's (provable only for n <= 2)."""
+    rng = _rng(32)
+    for trial in range(500):
+        n = int(rng.integers(1, 3))
+        H, _ = _random_spd(n, rng, cond_mix=1.0)
+        w = rng.standard_normal((1, n)) * 0.05
+        levels = int(rng.choice([3, 4, 8, 16]))
+        Hd, _ = oracle.damp_and_permute(H, None, 0.01)
+        U = oracle.inverse_cholesky_upper(Hd)
+        res = oracle.gptq_quantize(w, U, None, levels, 0, block_size=1)
+        rtn = oracle.rtn_quantize(w, levels, 0)
+        lg = oracle.obs_loss(w, oracle.dequantize(res), Hd, np.arange(n))[0]
+        lr = oracle.obs_loss(w, oracle.dequantize(rtn), Hd, np.arange(n))[0]
+        assert lg <= lr * (1 + 1e-12) + 1e-18
+
+
+@pytest.mark.parametrize("levels,group,act", [(16, 0, False), (8, 16, True), (4, 32, False), (3, 0, True)])
+def test_block_size_and_update_order_invariance(levels, group, act):
+    """Lazy batching (GPTQ knowledge note, "How It Works": blocks accumulate
+    corrections before a global update) changes only rounding order: B = 1,
+    right-looking B = 32 and left-looking B = 32 give the same codes."""
+    rng = _rng(40)
+    n, m = 96, 30
+    X = rng.standard_normal((4 * n, n)) @ (np.eye(n) + 0.3 * rng.standard_normal((n, n)))
+    W = rng.standard_normal((m, n)) * 0.05
+    H = oracle.hessian(X)
+    perm = oracle.act_order_perm(H) if act else np.arange(n)
+    Hd, _ = oracle.damp_and_permute(H, perm, 0.01)
+    U = oracle.inverse_cholesky_upper(Hd)
+    r1 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=1)
+    r2 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=32, order="right")
+    r3 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=32, order="left")
+    for r in (r2, r3):
+        np.testing.assert_array_equal(r["codes"], r1["codes"])
+        np.testing.assert_array_equal(r["scales"], r1["scales"])
+        np.testing.assert_allclose(r["E"], r1["E"], rtol=1e-9, atol=1e-12)
+
+
+def test_hessian_scale_invariance_and_row_independence():
+    rng = _rng(41)
+    n, m = 48, 20
+    X = rng.standard_normal((3 * n, n)) * np.exp(rng.standard_normal(n))
+    W = rng.standard_normal((m, n)) * 0.05
+    H = oracle.hessian(X)
+    a = oracle.gptq_layer(W, H=H, levels=8, group_size=16, act_order=True, block_size=16)
+    b = oracle.gptq_layer(W, H=H * 37.0, levels=8, group_size=16, act_order=True, block_size=16)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    rows = [3, 17, 0]
+    c = oracle.gptq_quantize(W[rows], a["U"], a["perm"], 8, 16, block_size=16)
+    np.testing.assert_array_equal(c["codes"], a["codes"][rows])
+    np.testing.assert_array_equal(c["scales"], a["scales"][rows])
+
+
+def test_outputs_original_order_and_group_index():
+    rng = _rng(42)
+    n, m = 40, 5
+    X = rng.standard_normal((3 * n, n)) * np.exp(rng.standard_normal(n))
+    W = rng.standard_normal((m, n)) * 0.05
+    res = oracle.gptq_layer(W, X=X, levels=8, group_size=8, act_order=True, block_size=8)
+    perm = res["perm"]
+    for j in range(n):
+        np.testing.assert_array_equal(res["codes_orig"][:, perm[j]], res["codes"][:, j])
+        assert res["g_idx"][perm[j]] == j // 8
+    # Dequantized weights use the group of each original column.
+    s = res["scales"].astype(float)[:, res["g_idx"]]
+    z = res["zeros"].astype(float)[:, res["g_idx"]]
+    np.testing.assert_allclose(res["What"], s * (res["codes_orig"] - z), rtol=0, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# a7 packing.
+# ---------------------------------------------------------------------------
+def test_packed_layout_fixture_and_sizes():
+    lines = read_golden("packed_layout.txt")
+    kv = {}
+    for ln in lines:
+        if "|" in ln:
+            bits, codes, words = [p.strip() for p in ln.split("|")]
+            c = np.array([codes.split()], dtype=np.int64)
+            w = np.array([[int(x, 16) for x in words.split()]], dtype=np.uint32)
+            np.testing.assert_array_equal(oracle.pack_codes(c, int(bits)), w)
+            np.testing.assert_array_equal(oracle.unpack_codes(w, c.shape[1], int(bits)), c)
+        else:
+            k, v = ln.split()
+            kv[k] = int(v)
+    p = kv["params"]
+    assert p * 4 // 8 == kv["bytes_4bit"]
+    assert p * 16 // 8 == kv["bytes_16bit"]
+    assert kv["bytes_16bit"] // kv["bytes_4bit"] == 4
+    assert oracle.packed_words_per_row(p, 4) * 4 == kv["bytes_4bit"]
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_round_trip(bits):
+    rng = _rng(50 + bits)
+    for n in (1, 7, 32, 33, 95, 130):
+        c = rng.integers(0, 1 << bits, size=(3, n))
+        p = oracle.pack_codes(c, bits)
+        assert p.shape == (3, -(-n * bits // 32))
+        np.testing.assert_array_equal(oracle.unpack_codes(p, n, bits), c)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: a copy of the oracle's sweep with one plausible error must
+# fail at least one of the pins above.
+# ---------------------------------------------------------------------------
+MUTATIONS = {
+    "update sign": ("V[:, j + 1:b1] -= np.outer(e, U[j, j + 1:b1])",
+                    "V[:, j + 1:b1] += np.outer(e, U[j, j + 1:b1])"),
+    "wrong U row": ("V[:, j + 1:b1] -= np.outer(e, U[j, j + 1:b1])",
+                    "V[:, j + 1:b1] -= np.outer(e, U[j + 1:b1, j])"),
+    "no diagonal scaling": ("e = (v - what) / U[j, j]", "e = (v - what)"),
+    "dropped block update": ("V[:, b1:] -= E[:, b0:b1] @ U[b0:b1, b1:]", "pass"),
+    "transposed block update": ("V[:, b1:] -= E[:, b0:b1] @ U[b0:b1, b1:]",
+                                "V[:, b1:] -= E[:, b0:b1] @ U[b1:, b0:b1].T"),
+}
+
+
+def _mutated_sweep(old, new):
+    src = textwrap.dedent(inspect.getsource(go.gptq_quantize))
+    assert old in src
+    ns = dict(go.__dict__)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    return ns["gptq_quantize"]
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistakes_are_caught(name, monkeypatch):
+    mutant = _mutated_sweep(*MUTATIONS[name])
+    monkeypatch.setattr(go, "gptq_quantize", mutant)
+    monkeypatch.setattr(oracle, "gptq_quantize", mutant)
+    caught = []
+    for check in (lambda: test_conditional_least_squares_definition(14, 16, 8, True, 8),
+                  test_loss_identity,
+                  lambda: test_block_size_and_update_order_invariance(16, 0, False)):
+        try:
+            check()
+        except AssertionError:
+            caught.append(check)
+    assert caught, f"mutation '{name}' was not caught by any pin"
