@@ -1,0 +1,171 @@
+/*
+ * gptq.h - C ABI of libgptq.so, a one-shot GPTQ quantizer for one linear
+ * layer on AMD Instinct MI355X (gfx950).
+ *
+ * The method (GPTQ knowledge note, "How It Works"): record the layer's
+ * inputs X, form the Hessian H = 2 X X^T of the layer-output reconstruction
+ * loss, quantize the weight matrix one column at a time in one column order
+ * shared by every row, adjust the still-unquantized columns with
+ * inverse-Hessian information after each column, batch those corrections in
+ * 128-column blocks before one global update, and take the correction rows
+ * from a damped Cholesky formulation.  The result is a low-bit grid with
+ * per-group scales (Wiki "GPTQ", "Technical Approach") and packed weights
+ * (GPTQ knowledge note, "Tradeoffs": packed-weight kernels).
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" point to device memory on the current HIP
+ *    device; "host" pointers to host memory.  The caller owns and allocates
+ *    every buffer, including the workspace (sized by the *_ws_bytes query of
+ *    the call).  The library keeps no device allocation between calls.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Calls are asynchronous and stream-ordered, except
+ *    gptq_prepare_hinv, which synchronises `stream` once to report whether
+ *    the damped Hessian was positive definite.
+ *  - Row-major storage; `ld*` are leading dimensions in elements.
+ *  - Every argument is validated on the host before anything is launched; a
+ *    failed check returns an error and touches no memory.  Device data is
+ *    not validated (NaN/Inf inputs propagate; codes >= 2^bits handed to
+ *    gptq_pack are undefined).  A failed HIP call returns GPTQ_ERR_HIP.
+ *  - Calls on distinct streams with distinct buffers may run concurrently.
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size or leading dimension */
+  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  GPTQ_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the query */
+  GPTQ_ERR_NOT_PD = 4,       /* damped Hessian not positive definite */
+  GPTQ_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */
+} gptq_status;
+
+typedef enum { GPTQ_F32 = 0, GPTQ_F16 = 1, GPTQ_BF16 = 2 } gptq_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* gptq_status_string(int status);
+
+/* ------------------------------------------------------------------------
+ * Stage 1: Hessian accumulation.
+ * GPTQ knowledge note, "How It Works": H = 2 X X^T over the recorded inputs
+ * of the layer.  X is stored tokens x n (activation layout), so
+ *     H <- (reset ? 0 : H) + alpha * X^T X ,  alpha = 2 gives the pages' H.
+ *   H       device, n x n float32, leading dimension n.  Full symmetric on
+ *           return (the upper triangle is computed and mirrored; with
+ *           reset = 0 the upper triangle of the incoming H is the one used).
+ *   X       device, tokens x n, element type x_dtype, leading dimension
+ *           ldx >= n.  Any alignment; rows 16-byte aligned take the fast path.
+ *   tokens  >= 0 (0 with reset = 0 leaves H unchanged).
+ *   ws      device workspace of at least gptq_hessian_ws_bytes(n, tokens,
+ *           x_dtype) bytes (NULL allowed when that is 0).
+ * Products of 16-bit inputs are exact in float32; sums are float32 over
+ * chunks of at most 2048 tokens, then over chunks, then across token
+ * splits in float64.
+ * ---------------------------------------------------------------------- */
+size_t gptq_hessian_ws_bytes(int64_t n, int64_t tokens, int x_dtype);
+gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
+                                    int64_t tokens, int64_t ldx, float alpha, int reset,
+                                    void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 2: damping, act-order and the inverse-Hessian factor.
+ * GPTQ knowledge note, "How It Works": a damped Cholesky formulation
+ * supplies the correction rows.  Computes
+ *   lambda = damp_rel * mean(diag H)
+ *   perm   = identity, or (act_order != 0) the columns sorted by descending
+ *            diag H with ties kept in ascending index (stable)
+ *   H_d    = H[perm][:, perm] + lambda * I
+ *   U      = the upper-triangular factor with positive diagonal such that
+ *            U^T U = H_d^{-1}   (row j of U / U_jj is column j's correction row)
+ * U is obtained as R^{-1} where H_d = R R^T with R upper (a Cholesky
+ * factorisation run from the last index to the first), in float64.
+ *   H        device, n x n float32 (symmetric), read only.
+ *   U        device, n x n float32 output, leading dimension n; lower
+ *            triangle set to 0.
+ *   perm     device, n int32 output (processing position -> original column).
+ *   info_out host, may be NULL: 0, or the 1-based position k at which the
+ *            factorisation of the index-reversed H_d met a non-positive (or
+ *            non-finite) pivot, i.e. the trailing block H_d[n-k:, n-k:] is not
+ *            positive definite.  Then GPTQ_ERR_NOT_PD is returned and U is
+ *            undefined.
+ *   ws       device workspace of gptq_prepare_ws_bytes(n) bytes.
+ * Synchronises `stream` once, at the end.
+ * ---------------------------------------------------------------------- */
+size_t gptq_prepare_ws_bytes(int64_t n);
+gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_rel, int act_order,
+                              float* U, int32_t* perm, int32_t* info_out,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 3: the column sweep with lazy block updates.
+ * GPTQ knowledge note, "How It Works" (one column order for all rows,
+ * 128-column blocks that accumulate corrections before a global update);
+ * Wiki "GPTQ", "Technical Approach" (low-bit grid, group-wise scales).
+ * For processing position j (original column perm[j]) of every row r:
+ *   at a group start: xmin = min(0, min w), xmax = max(0, max w) over the
+ *     current values of the group's columns (whole original row when
+ *     group_size = 0); an all-zero range is taken as [-1, 1];
+ *     s = fl32(fl32(xmax - xmin) / maxq), z = clamp(rint(fl32(-xmin/s)), 0, maxq)
+ *   c = clamp(rint(fl32(w_rj / s)) + z, 0, maxq)      (float32, IEEE division,
+ *                                                     round half to even)
+ *   e = (w_rj - s*(c - z)) / U_jj
+ *   w_rk -= e * U_jk for the later columns k of the block; the later blocks
+ *   receive the block's corrections as one matrix product.
+ * maxq = levels - 1.
+ *   W          device, m x n, element type w_dtype, leading dimension ldw
+ *              >= n; read only (the float32 working copy is in ws).
+ *   U          device, n x n float32 from gptq_prepare_hinv (processing order).
+ *   perm       device, n int32 processing order, or NULL for the identity.
+ *   levels     3 (ternary), 4 (2-bit), 8 (3-bit) or 16 (4-bit).
+ *   group_size 0 (one grid per row) or one of 16, 32, 64, 128.
+ *   block_size 128.
+ *   codes      device, m x n uint8 output in PROCESSING order
+ *              (codes[r*n + j] belongs to original column perm[j]).
+ *   scales     device, m x G float32, G = 1 if group_size = 0 else
+ *              ceil(n / group_size); group g covers processing positions
+ *              [g*group_size, (g+1)*group_size).
+ *   zeros      device, m x G uint8.
+ *   row_loss   device, m float32 = sum_j e_rj^2 / 2 per row, or NULL.
+ *   ws         device workspace of gptq_quantize_ws_bytes(m, n, w_dtype,
+ *              perm != NULL, block_size) bytes.
+ * Every row is independent: running a subset of rows gives those rows'
+ * results exactly.
+ * ---------------------------------------------------------------------- */
+size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int w_dtype, int permuted, int block_size);
+gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                const float* U, const int32_t* perm,
+                                int levels, int group_size, int block_size,
+                                uint8_t* codes, float* scales, uint8_t* zeros,
+                                float* row_loss, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Stage 4: un-permute and pack (GPTQ knowledge note, "Tradeoffs": packed
+ * weights; Wiki "GPTQ", "Performance and Accuracy": 4 bits per weight).
+ *   codes      device, m x n uint8 in processing order (from
+ *              gptq_quantize_layer), values < 2^bits.
+ *   perm       device, n int32 or NULL (identity).
+ *   bits       2, 3 or 4.
+ *   packed     device, m x ld_packed uint32 output; ld_packed >=
+ *              ceil(n*bits/32).  Row r's codes in ORIGINAL column order form
+ *              a little-endian bit stream: code of column k occupies bits
+ *              [k*bits, (k+1)*bits) of the row; unused tail bits are 0;
+ *              words beyond ceil(n*bits/32) are not written.
+ *   g_idx      device, n int32 output or NULL: g_idx[perm[j]] = j / group_size
+ *              (all 0 when group_size = 0).
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t* perm,
+                      int bits, int group_size, uint32_t* packed, int64_t ld_packed,
+                      int32_t* g_idx, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

@@ -1,0 +1,16 @@
+"""One-shot GPTQ quantization of linear layers on AMD Instinct MI355X (gfx950).
+
+The computation lives in libgptq.so (hand-written HIP kernels behind a
+C ABI, declared in include/gptq.h); this package is its Python binding.
+"""
+from ._lib import (  # noqa: F401
+    GptqError,
+    bits_for_levels,
+    gptq_hessian_accumulate,
+    gptq_pack,
+    gptq_prepare_hinv,
+    gptq_quantize_layer,
+    gptq_quantize_linear,
+    load,
+    packed_words,
+)

@@ -1,0 +1,230 @@
+"""Thin ctypes binding of libgptq.so (argument marshalling only).
+
+Every computation runs in the HIP kernels of libgptq.so; this module only
+turns torch tensors into device pointers, allocates outputs and workspaces
+with torch, passes the current HIP stream, and maps status codes to
+exceptions.  The functions carry the C entry points' names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libgptq.so")
+
+GPTQ_OK = 0
+GPTQ_ERR_INVALID_ARG = 1
+GPTQ_ERR_UNSUPPORTED = 2
+GPTQ_ERR_WORKSPACE = 3
+GPTQ_ERR_NOT_PD = 4
+GPTQ_ERR_HIP = 5
+
+GPTQ_F32, GPTQ_F16, GPTQ_BF16 = 0, 1, 2
+
+EXPORTS = (
+    "gptq_status_string",
+    "gptq_hessian_ws_bytes",
+    "gptq_hessian_accumulate",
+    "gptq_prepare_ws_bytes",
+    "gptq_prepare_hinv",
+    "gptq_quantize_ws_bytes",
+    "gptq_quantize_layer",
+    "gptq_pack",
+)
+
+_lib = None
+
+
+class GptqError(RuntimeError):
+    def __init__(self, status: int, where: str, info: int = 0):
+        self.status = status
+        self.info = info
+        name = _lib.gptq_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{where}: {name}" + (f" (info={info})" if info else ""))
+
+
+def load(path: str = LIB_PATH):
+    """Load libgptq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libgptq.so not built at {path}; run "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    i64, vp, sz, i32p = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)
+    C = ctypes.c_int
+    lib.gptq_status_string.restype = ctypes.c_char_p
+    lib.gptq_status_string.argtypes = [C]
+    lib.gptq_hessian_ws_bytes.restype = sz
+    lib.gptq_hessian_ws_bytes.argtypes = [i64, i64, C]
+    lib.gptq_hessian_accumulate.restype = C
+    lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
+    lib.gptq_prepare_ws_bytes.restype = sz
+    lib.gptq_prepare_ws_bytes.argtypes = [i64]
+    lib.gptq_prepare_hinv.restype = C
+    lib.gptq_prepare_hinv.argtypes = [vp, i64, ctypes.c_float, C, vp, vp, i32p, vp, sz, vp]
+    lib.gptq_quantize_ws_bytes.restype = sz
+    lib.gptq_quantize_ws_bytes.argtypes = [i64, i64, C, C, C]
+    lib.gptq_quantize_layer.restype = C
+    lib.gptq_quantize_layer.argtypes = [vp, C, i64, i64, i64, vp, vp, C, C, C, vp, vp, vp, vp, vp, sz, vp]
+    lib.gptq_pack.restype = C
+    lib.gptq_pack.argtypes = [vp, i64, i64, vp, C, C, vp, i64, vp, vp]
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    return {torch.float32: GPTQ_F32, torch.float16: GPTQ_F16, torch.bfloat16: GPTQ_BF16}[t.dtype]
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(rc: int, where: str, info: int = 0):
+    if rc != GPTQ_OK:
+        raise GptqError(rc, where, info)
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    if nbytes == 0:
+        return None
+    return torch.empty(int(nbytes), dtype=torch.uint8, device=device)
+
+
+def _device_check(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous device tensors")
+
+
+def _rows_check(t):
+    """Row-major with unit column stride (any leading dimension)."""
+    if not t.is_cuda or t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("expected a 2-D device tensor with unit column stride")
+
+
+def gptq_hessian_accumulate(H, X, alpha: float = 2.0, reset: bool = False, ws=None, stream=None):
+    """H (n x n float32) <- (0 if reset else H) + alpha * X^T X, X tokens x n."""
+    lib = load()
+    _device_check(H)
+    _rows_check(X)
+    n = H.shape[0]
+    if X.shape[1] != n or tuple(H.shape) != (n, n):
+        raise ValueError("H must be n x n and X tokens x n")
+    tokens = X.shape[0]
+    dt = _dtype_code(X)
+    need = lib.gptq_hessian_ws_bytes(n, tokens, dt)
+    if ws is None:
+        ws = _workspace(need, H.device)
+    rc = lib.gptq_hessian_accumulate(_ptr(H), n, _ptr(X), dt, tokens, X.stride(0) if tokens else n,
+                                     float(alpha), int(bool(reset)), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_hessian_accumulate")
+    return H
+
+
+def gptq_prepare_hinv(H, damp_rel: float = 0.01, act_order: bool = False, U=None, perm=None,
+                      ws=None, stream=None):
+    """Returns (U, perm): U^T U = (H[perm][:, perm] + lambda I)^{-1}, U upper."""
+    torch = _torch()
+    lib = load()
+    _device_check(H)
+    n = H.shape[0]
+    if U is None:
+        U = torch.empty((n, n), dtype=torch.float32, device=H.device)
+    if perm is None:
+        perm = torch.empty((n,), dtype=torch.int32, device=H.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_prepare_ws_bytes(n), H.device)
+    info = ctypes.c_int32(0)
+    rc = lib.gptq_prepare_hinv(_ptr(H), n, float(damp_rel), int(bool(act_order)), _ptr(U), _ptr(perm),
+                               ctypes.byref(info), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_prepare_hinv", info.value)
+    return U, perm
+
+
+def gptq_quantize_layer(W, U, perm=None, levels: int = 16, group_size: int = 0, block_size: int = 128,
+                        want_row_loss: bool = True, out=None, ws=None, stream=None):
+    """Returns dict(codes (m x n uint8, processing order), scales (m x G), zeros (m x G uint8),
+    row_loss (m) or None)."""
+    torch = _torch()
+    lib = load()
+    _device_check(U, perm)
+    _rows_check(W)
+    m, n = W.shape
+    if tuple(U.shape) != (n, n) or (perm is not None and perm.numel() != n):
+        raise ValueError("U must be n x n and perm n long")
+    G = 1 if group_size == 0 else -(-n // group_size)
+    if out is None:
+        out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=W.device),
+                   scales=torch.empty((m, G), dtype=torch.float32, device=W.device),
+                   zeros=torch.empty((m, G), dtype=torch.uint8, device=W.device),
+                   row_loss=torch.empty((m,), dtype=torch.float32, device=W.device) if want_row_loss else None)
+    if ws is None:
+        ws = _workspace(lib.gptq_quantize_ws_bytes(m, n, _dtype_code(W), int(perm is not None), block_size),
+                        W.device)
+    rc = lib.gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, W.stride(0) if m else n, _ptr(U), _ptr(perm),
+                                 int(levels), int(group_size), int(block_size), _ptr(out["codes"]),
+                                 _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out.get("row_loss")),
+                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_quantize_layer")
+    return out
+
+
+def packed_words(n: int, bits: int) -> int:
+    return -(-(n * bits) // 32)
+
+
+def gptq_pack(codes, perm=None, bits: int = 4, group_size: int = 0, want_g_idx: bool = True,
+              packed=None, g_idx=None, stream=None):
+    """Returns (packed m x ceil(n*bits/32) int32 words (bit patterns of uint32), g_idx or None)."""
+    torch = _torch()
+    lib = load()
+    _device_check(codes, perm)
+    m, n = codes.shape
+    if packed is None:
+        packed = torch.empty((m, packed_words(n, bits)), dtype=torch.int32, device=codes.device)
+    if want_g_idx and g_idx is None:
+        g_idx = torch.empty((n,), dtype=torch.int32, device=codes.device)
+    rc = lib.gptq_pack(_ptr(codes), m, n, _ptr(perm), int(bits), int(group_size), _ptr(packed),
+                       packed.stride(0) if m else packed_words(n, bits), _ptr(g_idx), _stream(stream))
+    _check(rc, "gptq_pack")
+    return packed, g_idx
+
+
+def bits_for_levels(levels: int) -> int:
+    return {3: 2, 4: 2, 8: 3, 16: 4}[int(levels)]
+
+
+def gptq_quantize_linear(W, X=None, H=None, levels: int = 16, group_size: int = 0,
+                         damp_rel: float = 0.01, act_order: bool = False, block_size: int = 128,
+                         stream=None):
+    """All four calls in order for one layer (convenience wrapper)."""
+    torch = _torch()
+    n = W.shape[1]
+    if H is None:
+        H = torch.empty((n, n), dtype=torch.float32, device=W.device)
+        gptq_hessian_accumulate(H, X, 2.0, True, stream=stream)
+    U, perm = gptq_prepare_hinv(H, damp_rel, act_order, stream=stream)
+    q = gptq_quantize_layer(W, U, perm if act_order else None, levels, group_size, block_size,
+                            stream=stream)
+    packed, g_idx = gptq_pack(q["codes"], perm if act_order else None, bits_for_levels(levels),
+                              group_size, stream=stream)
+    q.update(H=H, U=U, perm=perm, packed=packed, g_idx=g_idx)
+    return q

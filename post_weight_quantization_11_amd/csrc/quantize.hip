@@ -1,0 +1,426 @@
+// Stage 3: the GPTQ column sweep with lazy 128-column block updates.
+// GPTQ knowledge note, "How It Works": after a column is quantized the
+// columns still in full precision are adjusted with inverse-Hessian
+// information; all rows follow one column order; 128-column blocks
+// accumulate their corrections before a global update.  Wiki "GPTQ",
+// "Technical Approach": low-bit grid with one scale per group.
+//
+// Rows are independent and run in parallel; columns are strictly sequential.
+// For block kb (columns c0 .. c0+127 in processing order):
+//   update_gemm   P = E[:, 0:c0] * U[0:c0, block]   (left-looking form of the
+//                 deferred update; fp32 MFMA 32x32x2, split over K when there
+//                 are too few row tiles to fill the GPU)
+//   sweep         T = W[:, block] - sum(P); then 16-column sub-blocks: each
+//                 row's 16 values are quantized in registers one column at a
+//                 time (the error pushed into the sub-block's later columns
+//                 with FMAs), and the sub-block's errors are pushed into the
+//                 block's later columns with fp32 MFMA 16x16x4.
+// The left-looking form applies each block's deferred corrections in one
+// float32 accumulation (identical to the right-looking "update the rest after
+// each block" form in exact arithmetic) and reads E instead of
+// reading and rewriting the whole remaining weight matrix per block.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kBS = 128;       // lazy block (columns)
+constexpr int kSB = 16;        // register sub-block (columns)
+constexpr int kRowsPerWave = 16;
+constexpr int kWaves = 4;
+constexpr int kRowsPerWG = kRowsPerWave * kWaves;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTP = kBS + 4;   // LDS pitch of the block tile (floats)
+
+// Grid parameters from a value range (float32, IEEE division, half-even).
+__device__ inline void grid_from_range(float xmin, float xmax, float maxq, float& s, float& z,
+                                       float& inv_s) {
+  xmin = fminf(xmin, 0.f);
+  xmax = fmaxf(xmax, 0.f);
+  if (xmax == xmin) {
+    xmin = -1.f;
+    xmax = 1.f;
+  }
+  s = (xmax - xmin) / maxq;
+  z = rintf((-xmin) / s);
+  z = fminf(fmaxf(z, 0.f), maxq);
+  inv_s = 1.f / s;
+}
+
+// c = clamp(rint(fl32(w / s)) + z, 0, maxq).  fl32(w / s) is obtained from
+// the correctly rounded reciprocal inv_s = fl32(1/s) with one residual
+// correction: q0 = fl32(w * inv_s), r = w - q0 * s (exact, fused),
+// q = fl32(q0 + r * inv_s), which equals the correctly rounded quotient.
+__device__ inline float quant_code(float w, float s, float inv_s, float z, float maxq) {
+  const float q0 = w * inv_s;
+  const float r = __builtin_fmaf(-q0, s, w);
+  const float q = __builtin_fmaf(r, inv_s, q0);
+  return fminf(fmaxf(rintf(q) + z, 0.f), maxq);
+}
+
+// Wp[r][j] = W[r][perm[j]] as float32 (processing order).
+template <int DT>
+__global__ __launch_bounds__(256) void permute_w_kernel(const void* __restrict__ W, int64_t ldw, int n,
+                                                        const int32_t* __restrict__ perm,
+                                                        float* __restrict__ Wp) {
+  const int64_t r = blockIdx.x;
+  for (int j = threadIdx.x; j < n; j += 256) {
+    const int pj = min(max(perm[j], 0), n - 1);   // out-of-range entries are clamped, never followed
+    Wp[r * n + j] = load_as_f32<DT>(W, r * ldw + pj);
+  }
+}
+
+// Per-row grid (group_size 0): range of the original row, one wave per row.
+template <int DT>
+__global__ __launch_bounds__(256) void row_grid_kernel(const void* __restrict__ W, int64_t ldw, int m, int n,
+                                                       float maxq, float* __restrict__ scales,
+                                                       uint8_t* __restrict__ zeros) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= m) return;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int j = lane; j < n; j += 64) {
+    const float v = load_as_f32<DT>(W, r * ldw + j);
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  if (lane == 0) {
+    float s, z, inv_s;
+    grid_from_range(mn, mx, maxq, s, z, inv_s);
+    scales[r] = s;
+    zeros[r] = (uint8_t)z;
+  }
+}
+
+// P[sp][r][c] = sum_{k in split sp} E[r][k] * U[k][c0 + c]  (128 x 128 tile per
+// workgroup, 4 waves of 64 x 64, fp32 MFMA 32x32x2, K staged 16 at a time).
+__global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restrict__ E,
+                                                          const float* __restrict__ U, int m, int n, int kb,
+                                                          int kblocks_per_split, float* __restrict__ P) {
+  const int mt = blockIdx.x, sp = blockIdx.y;
+  const int c0 = kb * kBS;
+  const int bw = min(kBS, n - c0);
+  const int k_begin = sp * kblocks_per_split * kBS;
+  const int k_end = min(c0, k_begin + kblocks_per_split * kBS);
+  const int row0 = mt * 128;
+  const bool vec = (n & 3) == 0;
+
+  __shared__ float As[128][17];
+  __shared__ __attribute__((aligned(16))) float Bs[16][kTP];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wr = wave >> 1, wc = wave & 1;
+  floatx16 acc[2][2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = floatx16{};
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 16) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * 2 + i;          // 512 float4 slots: 128 rows x 4
+      const int r = e >> 2, kq = e & 3;
+      const int64_t row = row0 + r;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (row < m) {
+        const float* p = E + row * n + k0 + kq * 4;
+        if (vec) v = *reinterpret_cast<const floatx4*>(p);
+        else v = floatx4{p[0], p[1], p[2], p[3]};
+      }
+      As[r][kq * 4 + 0] = v[0];
+      As[r][kq * 4 + 1] = v[1];
+      As[r][kq * 4 + 2] = v[2];
+      As[r][kq * 4 + 3] = v[3];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid * 2 + i;          // 512 float4 slots: 16 k x 32
+      const int kk = e >> 5, cq = e & 31;
+      const int c = cq * 4;
+      const float* p = U + (int64_t)(k0 + kk) * n + c0 + c;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (vec && c + 4 <= bw) {
+        v = *reinterpret_cast<const floatx4*>(p);
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (c + t < bw) ? p[t] : 0.f;
+      }
+      *reinterpret_cast<floatx4*>(&Bs[kk][c]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 0; k2 < 8; ++k2) {
+      const int k = k2 * 2 + (lane >> 5);
+      float a[2], b[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) a[rb] = As[wr * 64 + rb * 32 + (lane & 31)][k];
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) b[cb] = Bs[k][wc * 64 + cb * 32 + (lane & 31)];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+          acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // 32x32 accumulator: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = row0 + wr * 64 + rb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int col = wc * 64 + cb * 32 + (lane & 31);
+        if (row < m && col < bw) P[((int64_t)sp * m + row) * kBS + col] = acc[rb][cb][r];
+      }
+}
+
+// The in-block sweep of block kb for 64 rows (4 waves x 16 rows; within a
+// wave, lane r < 16 owns row r for the sequential part and all 64 lanes run
+// the MFMA part).
+template <int DT>
+__global__ __launch_bounds__(kThreads) void sweep_kernel(
+    const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
+    const float* __restrict__ P, int nsplit, float maxq, int g, int G, uint8_t* __restrict__ codes,
+    float* __restrict__ E, float* __restrict__ scales, uint8_t* __restrict__ zeros,
+    float* __restrict__ row_loss, int codes_aligned) {
+  __shared__ float Ud[kBS][kBS + 1];
+  __shared__ float invd[kBS];
+  __shared__ __attribute__((aligned(16))) float T[kWaves][kRowsPerWave][kTP];
+  __shared__ float Eb[kWaves][kRowsPerWave][kSB + 1];
+
+  const int c0 = kb * kBS;
+  const int bw = min(kBS, n - c0);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
+
+  for (int e = tid; e < kBS * kBS; e += kThreads) {
+    const int i = e / kBS, j = e % kBS;
+    Ud[i][j] = (i < bw && j < bw && j >= i) ? U[(int64_t)(c0 + i) * n + c0 + j] : 0.f;
+  }
+  for (int j = tid; j < kBS; j += kThreads)
+    invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
+  for (int e = lane; e < kRowsPerWave * kBS; e += 64) {
+    const int r = e / kBS, c = e % kBS;
+    const int64_t row = row0 + r;
+    float v = 0.f;
+    if (row < m && c < bw) {
+      v = load_as_f32<DT>(Wsrc, row * ldw + c0 + c);
+      for (int sp = 0; sp < nsplit; ++sp) v -= P[((int64_t)sp * m + row) * kBS + c];
+    }
+    T[wave][r][c] = v;
+  }
+  __syncthreads();
+
+  const int r = lane & (kRowsPerWave - 1);
+  const int64_t row = row0 + r;
+  const bool owner = lane < kRowsPerWave;
+  const bool active = owner && row < m;
+  float s = 1.f, z = 0.f, inv_s = 1.f;
+  if (g == 0 && active) {
+    s = scales[row * G];
+    z = (float)zeros[row * G];
+    inv_s = 1.f / s;
+  }
+  float loss = 0.f;
+  const int nsb = (bw + kSB - 1) / kSB;
+  const bool vec_codes = (n & 15) == 0 && codes_aligned;
+  const bool vec_e = (n & 3) == 0;
+
+  for (int sb = 0; sb < nsb; ++sb) {
+    const int j0 = sb * kSB;
+    if (g > 0 && ((c0 + j0) % g) == 0) {
+      const int gl = min(g, bw - j0);
+      float mn = T[wave][r][j0], mx = mn;
+      for (int c = 1; c < gl; ++c) {
+        const float v = T[wave][r][j0 + c];
+        mn = fminf(mn, v);
+        mx = fmaxf(mx, v);
+      }
+      grid_from_range(mn, mx, maxq, s, z, inv_s);
+      if (active) {
+        const int gi = (c0 + j0) / g;
+        scales[row * G + gi] = s;
+        zeros[row * G + gi] = (uint8_t)z;
+      }
+    }
+    float w[kSB];
+#pragma unroll
+    for (int jj = 0; jj < kSB; ++jj) w[jj] = T[wave][r][j0 + jj];
+    float eb[kSB];
+    uint32_t cw[kSB / 4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int jj = 0; jj < kSB; ++jj) {
+      if (j0 + jj < bw) {
+        const float c = quant_code(w[jj], s, inv_s, z, maxq);
+        const float what = s * (c - z);
+        const float e = (w[jj] - what) * invd[j0 + jj];
+        eb[jj] = active ? e : 0.f;
+        loss = __builtin_fmaf(e, e, loss);
+        cw[jj >> 2] |= (uint32_t)c << (8 * (jj & 3));
+#pragma unroll
+        for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, Ud[j0 + jj][j0 + kk], w[kk]);
+      } else {
+        eb[jj] = 0.f;
+      }
+    }
+    if (active) {
+      uint8_t* cp = codes + row * n + c0 + j0;
+      float* ep = E + row * n + c0 + j0;
+      if (j0 + kSB <= bw && vec_codes) {
+        *reinterpret_cast<u32x4*>(cp) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+      } else {
+        for (int jj = 0; jj < kSB && j0 + jj < bw; ++jj) cp[jj] = (uint8_t)(cw[jj >> 2] >> (8 * (jj & 3)));
+      }
+      if (j0 + kSB <= bw && vec_e) {
+#pragma unroll
+        for (int q = 0; q < kSB / 4; ++q)
+          reinterpret_cast<floatx4*>(ep)[q] = floatx4{eb[4 * q], eb[4 * q + 1], eb[4 * q + 2], eb[4 * q + 3]};
+      } else {
+        for (int jj = 0; jj < kSB && j0 + jj < bw; ++jj) ep[jj] = eb[jj];
+      }
+    }
+    if (owner) {
+#pragma unroll
+      for (int jj = 0; jj < kSB; ++jj) Eb[wave][r][jj] = eb[jj];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // Push the sub-block's errors into the block's later columns:
+    // T[:, ct] -= Eb * Ud[j0:j0+16, ct] for each later 16-column tile ct.
+    // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, column l%16.
+    for (int ct = sb + 1; ct < nsb; ++ct) {
+      floatx4 acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = T[wave][4 * (lane >> 4) + i][ct * kSB + (lane & 15)];
+#pragma unroll
+      for (int k4 = 0; k4 < 4; ++k4) {
+        const int k = k4 * 4 + (lane >> 4);
+        const float a = -Eb[wave][lane & 15][k];
+        const float b = Ud[j0 + k][ct * kSB + (lane & 15)];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) T[wave][4 * (lane >> 4) + i][ct * kSB + (lane & 15)] = acc[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+  if (active && row_loss != nullptr) row_loss[row] = (kb == 0 ? 0.f : row_loss[row]) + 0.5f * loss;
+}
+
+struct QuantLayout {
+  int nblocks = 0, mtiles = 0, smax = 0;
+  size_t off_E = 0, off_Wp = 0, off_P = 0, total = 0;
+};
+
+QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
+  QuantLayout L;
+  L.nblocks = (int)ceil_div(n, kBS);
+  L.mtiles = (int)ceil_div(m, 128);
+  // Enough K splits for about 512 workgroups in the update GEMM.
+  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1), ceil_div(512, L.mtiles)));
+  const size_t mn = (size_t)m * (size_t)n * sizeof(float);
+  L.off_E = 0;
+  L.off_Wp = align256(L.off_E + mn);
+  L.off_P = align256(L.off_Wp + (permuted ? mn : 0));
+  L.total = align256(L.off_P + (size_t)L.smax * (size_t)m * kBS * sizeof(float));
+  return L;
+}
+
+template <int DT>
+gptq_status launch_sweep(const void* src, int64_t ld, int m, int n, int kb, const float* U, const float* P,
+                         int nsplit, float maxq, int g, int G, uint8_t* codes, float* E, float* scales,
+                         uint8_t* zeros, float* row_loss, hipStream_t st) {
+  const int codes_aligned = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
+  sweep_kernel<DT><<<(unsigned)ceil_div(m, kRowsPerWG), kThreads, 0, st>>>(
+      src, ld, m, n, kb, U, P, nsplit, maxq, g, G, codes, E, scales, zeros, row_loss, codes_aligned);
+  GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int w_dtype, int permuted, int block_size) {
+  (void)w_dtype;
+  (void)block_size;
+  if (m <= 0 || n <= 0) return 0;
+  return quant_layout(m, n, permuted).total;
+}
+
+extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                           const float* U, const int32_t* perm, int levels, int group_size,
+                                           int block_size, uint8_t* codes, float* scales, uint8_t* zeros,
+                                           float* row_loss, void* ws, size_t ws_bytes, void* stream) {
+  if (m < 0 || n < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (!(levels == 3 || levels == 4 || levels == 8 || levels == 16)) return GPTQ_ERR_INVALID_ARG;
+  if (group_size < 0 || block_size <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (block_size != kBS) return GPTQ_ERR_UNSUPPORTED;
+  if (!(group_size == 0 || group_size == 16 || group_size == 32 || group_size == 64 || group_size == 128))
+    return GPTQ_ERR_UNSUPPORTED;
+  if (n > (int64_t)1 << 16 || m > ((int64_t)1 << 31) - 1) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0 || n == 0) return GPTQ_OK;
+  if (W == nullptr || U == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr || ldw < n)
+    return GPTQ_ERR_INVALID_ARG;
+  const QuantLayout L = quant_layout(m, n, perm != nullptr);
+  if (ws == nullptr || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(ws);
+  float* E = reinterpret_cast<float*>(base + L.off_E);
+  float* Wp = reinterpret_cast<float*>(base + L.off_Wp);
+  float* P = reinterpret_cast<float*>(base + L.off_P);
+  const int mi = (int)m, ni = (int)n;
+  const float maxq = (float)(levels - 1);
+  const int G = group_size == 0 ? 1 : (int)ceil_div(n, group_size);
+
+  const void* src = W;
+  int64_t ld = ldw;
+  int sdt = w_dtype;
+  if (perm != nullptr) {
+    if (w_dtype == GPTQ_F32) permute_w_kernel<GPTQ_F32><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
+    else if (w_dtype == GPTQ_F16) permute_w_kernel<GPTQ_F16><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
+    else permute_w_kernel<GPTQ_BF16><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
+    GPTQ_TRY_LAUNCH();
+    src = Wp;
+    ld = n;
+    sdt = GPTQ_F32;
+  }
+  if (group_size == 0) {
+    const unsigned grid = (unsigned)ceil_div(m, 4);
+    if (w_dtype == GPTQ_F32) row_grid_kernel<GPTQ_F32><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
+    else if (w_dtype == GPTQ_F16) row_grid_kernel<GPTQ_F16><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
+    else row_grid_kernel<GPTQ_BF16><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
+    GPTQ_TRY_LAUNCH();
+  }
+  for (int kb = 0; kb < L.nblocks; ++kb) {
+    int nsplit = 0;
+    if (kb > 0) {
+      const int s_target = std::min(kb, L.smax);
+      const int kbps = (int)ceil_div(kb, s_target);
+      nsplit = (int)ceil_div(kb, kbps);
+      update_gemm_kernel<<<dim3((unsigned)L.mtiles, (unsigned)nsplit), 256, 0, st>>>(E, U, mi, ni, kb, kbps, P);
+      GPTQ_TRY_LAUNCH();
+    }
+    gptq_status rc;
+    if (sdt == GPTQ_F32)
+      rc = launch_sweep<GPTQ_F32>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+    else if (sdt == GPTQ_F16)
+      rc = launch_sweep<GPTQ_F16>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+    else
+      rc = launch_sweep<GPTQ_BF16>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+    if (rc != GPTQ_OK) return rc;
+  }
+  return GPTQ_OK;
+}
