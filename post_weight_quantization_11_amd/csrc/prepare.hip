@@ -252,14 +252,16 @@ __global__ __launch_bounds__(kThreads) void chol_block_kernel(double* __restrict
       for (int tj = 0; tj < 2; ++tj)
         acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ti], b[tj], acc[ti][tj], 0, 0, 0);
   }
-  // Accumulator register r of lane l: row 4*(l/16) + r, column l%16 of the 16x16 block.
+  // float64 16x16x4 accumulator on gfx950: register r of lane l holds row
+  // l/16 + 4*r, column l%16 of the 16x16 block (rows interleaved, unlike the
+  // float32 16x16x4 form where lane l holds rows 4*(l/16) .. 4*(l/16)+3).
 #pragma unroll
   for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
     for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = wr * 32 + ti * 16 + 4 * (lane >> 4) + r;
+        const int row = wr * 32 + ti * 16 + (lane >> 4) + 4 * r;
         const int col = wc * 32 + tj * 16 + (lane & 15);
         double* p = Cp + (int64_t)row * np + col;
         const double v = acc[ti][tj][r];

@@ -90,7 +90,13 @@ def test_prepare_parity(g, n, act):
     log(f"prepare n={n} act={act}")
     H32 = _h32(n, seed=200 + n)
     if n == 256:
-        H32[[3, 7, 11], [3, 7, 11]] = H32[5, 5]   # ties in diag(H) for the stable sort
+        # Ties in diag(H) for the stable sort: rescale rows/columns 3, 7, 11
+        # symmetrically (keeps H positive definite), then make the ties exact.
+        d = np.ones(n)
+        idx = [3, 7, 11]
+        d[idx] = np.sqrt(H32[5, 5] / np.diag(H32)[idx].astype(np.float64))
+        H32 = (d[:, None] * H32.astype(np.float64) * d[None, :]).astype(F32)
+        H32[idx, idx] = H32[5, 5]
     U, perm = g.gptq_prepare_hinv(dev(H32), 0.01, act)
     Ho = H32.astype(np.float64)
     po = oracle.act_order_perm(Ho) if act else np.arange(n)
