@@ -11,8 +11,9 @@
 // loads, transposes it in registers and stores it feature-major in LDS, so
 // every MFMA operand is one 16-byte LDS read.  The LDS pitch (144 B) keeps
 // both the transposed stores and the fragment reads free of bank conflicts.
-// LDS is double buffered and the next slab is prefetched into registers
-// while the current one is multiplied.
+// LDS is double buffered, the next stage is prefetched into registers while
+// the current one is multiplied, and MFMA fragments are double buffered in
+// registers (the next 16-token step is read while the MFMAs of this one run).
 //
 // Accuracy: one float32 MFMA accumulator covers at most 32768 tokens (a
 // "split"); each split writes its tile to the workspace and the reduce
@@ -101,48 +102,60 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_kernel(
   const int fc = wave * 8 + (lane >> 3);    // loader: feature chunk of 8 (0..31)
   const int wr = wave >> 1, wc = wave & 1;  // compute quadrant
 
-  u32x4 pre[2][8];
+  u32x4 pre[2][2][8];   // [slot][band][token row]; slot 1 is unused in this variant
 
-  auto gload = [&](int64_t t0) {
+  // Feature chunks of this thread in the two bands; interior chunks of whole
+  // stages take a branch-free path so that all 16 loads are in flight at once.
+  const int f0a = I * kTile + fc * 8, f0b = J * kTile + fc * 8;
+  const bool interior = vec_ok && f0a + 8 <= n && f0b + 8 <= n;
+  const uint16_t* pa = X + f0a;
+  const uint16_t* pb = X + f0b;
+
+  auto gload = [&](u32x4 (&pr)[2][8], int64_t t0) {
+    if (interior && t0 + kKt16 <= t_end) {
+      const int64_t trow = t0 + tg * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pr[0][i] = *reinterpret_cast<const u32x4*>(pa + (trow + i) * ldx);
+        pr[1][i] = *reinterpret_cast<const u32x4*>(pb + (trow + i) * ldx);
+      }
+      return;
+    }
+    // edge: element-wise with bounds (tokens beyond the split, features beyond n are 0)
 #pragma unroll
     for (int band = 0; band < 2; ++band) {
-      const int f0 = (band == 0 ? I : J) * kTile + fc * 8;
+      const int f0 = band == 0 ? f0a : f0b;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t t = t0 + tg * 8 + i;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (t < t_end && f0 < n) {
-          const uint16_t* p = X + t * ldx + f0;
-          if (vec_ok && f0 + 8 <= n) {
-            v = *reinterpret_cast<const u32x4*>(p);
-          } else {
-            uint32_t h[8];
+        const bool rowok = t < t_end;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) h[e] = (f0 + e < n) ? (uint32_t)p[e] : 0u;
-            v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
-          }
+        for (int d = 0; d < 4; ++d) {
+          const int f = f0 + 2 * d;
+          const uint32_t lo = (rowok && f < n) ? (uint32_t)X[t * ldx + f] : 0u;
+          const uint32_t hi = (rowok && f + 1 < n) ? (uint32_t)X[t * ldx + f + 1] : 0u;
+          pr[band][i][d] = lo | (hi << 16);
         }
-        pre[band][i] = v;
       }
     }
   };
 
-  auto lstore = [&](int buf) {
+  // Transposes part q (band q/2, feature pairs 2*(q%2), 2*(q%2)+1) of a
+  // prefetched 8 x 8 block and stores it feature-major into LDS buffer buf.
+  auto lstore_part = [&](const u32x4 (&pr)[2][8], int buf, int q) {
+    const int band = q >> 1;
 #pragma unroll
-    for (int band = 0; band < 2; ++band) {
+    for (int f2 = 2 * (q & 1); f2 < 2 * (q & 1) + 2; ++f2) {
+      u32x4 lo, hi;
 #pragma unroll
-      for (int f2 = 0; f2 < 4; ++f2) {
-        u32x4 lo, hi;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t y = pre[band][2 * e][f2];      // token 2e: features 2f2 (lo) and 2f2+1 (hi)
-          const uint32_t x = pre[band][2 * e + 1][f2];  // token 2e+1
-          lo[e] = (y & 0xFFFFu) | (x << 16);
-          hi[e] = (y >> 16) | (x & 0xFFFF0000u);
-        }
-        *reinterpret_cast<u32x4*>(&lds[buf][band][fc * 8 + 2 * f2][tg * 8]) = lo;
-        *reinterpret_cast<u32x4*>(&lds[buf][band][fc * 8 + 2 * f2 + 1][tg * 8]) = hi;
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t y = pr[band][2 * e][f2];      // token 2e: features 2f2 (lo) and 2f2+1 (hi)
+        const uint32_t x = pr[band][2 * e + 1][f2];  // token 2e+1
+        lo[e] = (y & 0xFFFFu) | (x << 16);
+        hi[e] = (y >> 16) | (x & 0xFFFF0000u);
       }
+      *reinterpret_cast<u32x4*>(&lds[buf][band][fc * 8 + 2 * f2][tg * 8]) = lo;
+      *reinterpret_cast<u32x4*>(&lds[buf][band][fc * 8 + 2 * f2 + 1][tg * 8]) = hi;
     }
   };
 
@@ -158,27 +171,224 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_kernel(
   const int bcol = wc * 128 + (lane & 31);
   const int koff = (lane >> 5) * 8;
 
-  gload(t_begin);
-  lstore(0);
+  auto load_a = [&](int buf, int kk, int rb) {
+    return *reinterpret_cast<const u32x4*>(&lds[buf][0][arow + rb * 32][kk * 16 + koff]);
+  };
+  auto load_b = [&](int buf, int kk, u32x4 (&fb)[4]) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      fb[cb] = *reinterpret_cast<const u32x4*>(&lds[buf][1][bcol + cb * 32][kk * 16 + koff]);
+  };
+
+  // One stage: 64 MFMAs on LDS buffer buf.  Interleaved with them: the
+  // fragment reads that come next (B fragments one 16-token step ahead, A
+  // fragments one row block ahead), the transposed LDS stores of the next
+  // stage (from prefetch slot nxt, when has_next) and the global loads of the
+  // stage after that (into slot fill, when has_fill).  The scheduling hints
+  // keep one or two other instructions between MFMAs so that the MFMA pipe
+  // does not wait for them.
+  auto stage = [&](int buf, u32x4 (&nxt)[2][8], bool has_next, u32x4 (&fill)[2][8], bool has_fill,
+                   int64_t fill_t0) {
+    if (has_fill) gload(fill, fill_t0);
+    u32x4 fb[2][4];
+    u32x4 fa[2];
+    load_b(buf, 0, fb[0]);
+    fa[0] = load_a(buf, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < kKt16 / 16; ++kk) {
+      if (kk + 1 < kKt16 / 16) load_b(buf, kk + 1, fb[(kk + 1) & 1]);
+      if (has_next) lstore_part(nxt, buf ^ 1, kk);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int idx = kk * 4 + rb;
+        if (rb + 1 < 4)
+          fa[(idx + 1) & 1] = load_a(buf, kk, rb + 1);
+        else if (kk + 1 < kKt16 / 16)
+          fa[(idx + 1) & 1] = load_a(buf, kk + 1, 0);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+          acc[rb][cb] = Mfma16<DT>::run(fa[idx & 1], fb[kk & 1][cb], acc[rb][cb]);
+      }
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // 1 MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // up to 2 VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // up to 1 DS read
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // up to 1 DS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // up to 1 VMEM read
+      }
+    }
+  };
+
+  // The next stage is prefetched into registers (slot 0) while this one is
+  // multiplied, then transposed into the other LDS buffer.
+  gload(pre[0], t_begin);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lstore_part(pre[0], 0, q);
   __syncthreads();
   for (int64_t s = 0; s < nstages; ++s) {
     const int buf = (int)(s & 1);
-    if (s + 1 < nstages) gload(t_begin + (s + 1) * kKt16);
+    stage(buf, pre[1], false, pre[0], s + 1 < nstages, t_begin + (s + 1) * kKt16);
+    if (s + 1 < nstages) {
 #pragma unroll
-    for (int kk = 0; kk < kKt16 / 16; ++kk) {
-      u32x4 a[4], b[4];
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-        a[rb] = *reinterpret_cast<const u32x4*>(&lds[buf][0][arow + rb * 32][kk * 16 + koff]);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        b[cb] = *reinterpret_cast<const u32x4*>(&lds[buf][1][bcol + cb * 32][kk * 16 + koff]);
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(a[rb], b[cb], acc[rb][cb]);
+      for (int q = 0; q < 4; ++q) lstore_part(pre[0], buf ^ 1, q);
     }
-    if (s + 1 < nstages) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  store_acc(acc, dst, wave, lane);
+}
+
+// Direct-to-LDS variant for 16-bit X with 8-aligned features (n % 8 == 0,
+// ldx % 8 == 0, 16-byte aligned X).  Token rows are copied HBM -> LDS by
+// global_load_lds (16 bytes per lane, no register staging): one instruction
+// moves one token row of both bands, lanes 0-31 the 256 features of band I
+// and lanes 32-63 those of band J, so an LDS row is [band I | band J] (1024
+// bytes, padded to 1088 so that the transposing reads below are free of bank
+// conflicts).  Stages of kKtD tokens rotate through kNBuf LDS buffers and
+// are loaded kNBuf - 1 stages ahead.  MFMA operands are read with ds_read_b64_tr_b16: within each group
+// of 16 lanes, lane j receives element j%4 of the 8-byte chunks addressed by
+// lanes j/4 + 4e (e = 0..3); with lane j addressing token row t0 + j/4 and
+// features f + 4*(j%4), it receives tokens t0..t0+3 of feature f + j, i.e. a
+// K-contiguous operand.  Feature chunks beyond n are zeroed once; token rows
+// beyond the split are zeroed when their stage is issued.
+constexpr int kRowBytes = 1088;
+constexpr int kKtD = 64;                        // tokens per stage
+constexpr int kNBuf = 2;                        // LDS stage buffers (kNBuf * kStageBytes <= 160 KB)
+constexpr int kAhead = kNBuf - 1;               // stages loaded ahead
+constexpr int kStageBytes = kKtD * kRowBytes;
+constexpr int kRowsPerWave = kKtD / 4;          // direct loads per wave per stage
+
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= v, expcnt = 7 (no wait), lgkmcnt = 0.
+constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4); }
+
+template <int DT>
+__global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
+    const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nb, int ntiles,
+    int nsplit, int64_t tok_per_split, float* __restrict__ partial, int64_t launched) {
+  const int64_t item = xcd_contiguous(blockIdx.x, launched);
+  if (item >= (int64_t)ntiles * nsplit) return;
+  const int split = (int)(item / ntiles);
+  const int tile = (int)(item % ntiles);
+  int I, J;
+  tile_coords(tile, nb, I, J);
+  const int64_t t_begin = (int64_t)split * tok_per_split;
+  const int64_t t_end = min(tokens, t_begin + tok_per_split);
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wr = wave >> 1, wc = wave & 1;
+
+  // This lane's 16-byte chunk in a token row: band I for lanes 0-31, band J for 32-63.
+  const int band = lane >> 5;
+  const int fchunk = (band == 0 ? I : J) * kTile + (lane & 31) * 8;
+  const bool chunk_ok = fchunk < n;            // n % 8 == 0: a chunk is all in or all out
+  const uint16_t* gsrc = X + (chunk_ok ? fchunk : 0);
+
+  if (!chunk_ok) {
+    for (int b = 0; b < kNBuf; ++b)
+      for (int r = wave; r < kKtD; r += 4)
+        *reinterpret_cast<u32x4*>(smem + b * kStageBytes + r * kRowBytes + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // Wave w copies token rows w*8 .. w*8+7 of a stage.
+  auto issue_stage = [&](int buf, int64_t t0) {
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) {
+      const int r = wave * kRowsPerWave + i;
+      const int64_t t = t0 + r;
+      unsigned char* dstrow = smem + buf * kStageBytes + r * kRowBytes;
+      if (t < t_end) {
+        if (chunk_ok) __builtin_amdgcn_global_load_lds(gsrc + t * ldx, (lds_void*)dstrow, 16, 0, 0);
+      } else if (chunk_ok) {
+        *reinterpret_cast<u32x4*>(dstrow + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+
+  floatx16 acc[4][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = floatx16{};
+
+  // Transposed-read addressing (see above): group g = lane/16, j = lane%16.
+  const int g = lane >> 4, j = lane & 15;
+  const int trow = 8 * (g >> 1) + (j >> 2);                 // token row within a 16-token step
+  const int fcol = 16 * (g & 1) + 4 * (j & 3);              // feature offset within a 32-feature block
+  const int a_off = trow * kRowBytes + (wr * 128 + fcol) * 2;
+  const int b_off = trow * kRowBytes + (kTile + wc * 128 + fcol) * 2;
+
+  auto frag = [&](int buf, int off, int kk, int blk) -> u32x4 {
+    const unsigned char* p = smem + buf * kStageBytes + off + kk * 16 * kRowBytes + blk * 64;
+    const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)p);
+    const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4*)(p + 4 * kRowBytes));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
+
+  float* dst = partial + ((int64_t)split * ntiles + tile) * (int64_t)kTileElems;
+  const int64_t nstages = (t_end - t_begin + kKtD - 1) / kKtD;
+
+  // Waits until stage st's loads have landed while the loads of the (up to
+  // kAhead - 1) stages issued after it may stay in flight.  Each full stage
+  // issues exactly kRowsPerWave loads per wave; a partial (last) stage issues
+  // fewer, so it is counted as 0, which only makes the wait stricter.
+  auto full = [&](int64_t st) { return st < nstages && t_begin + (st + 1) * kKtD <= t_end; };
+  auto wait_for = [&](int64_t st) {
+    int later = 0;
+#pragma unroll
+    for (int i = 1; i < kAhead; ++i) later += full(st + i) ? 1 : 0;
+    static_assert(kAhead <= 3, "wait_for handles up to two later stages");
+    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  };
+
+  // Prologue: stages 0 .. kAhead-1 in flight; wait for stage 0.
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i)
+    if (i < nstages) issue_stage(i, t_begin + i * kKtD);
+  wait_for(0);
+  __syncthreads();
+  for (int64_t s = 0; s < nstages; ++s) {
+    const int buf = (int)(s % kNBuf);
+    const bool fill = s + kAhead < nstages;
+    // Fragments of 16-token step kk live in slot kk % 2; the 16 transposing
+    // reads of step kk+1 are issued between the 16 MFMAs of step kk, and the
+    // loads of stage s+kAhead between those of step 0.
+    u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(buf, a_off, 0, rb);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(buf, b_off, 0, cb);
+#pragma unroll
+    for (int kk = 0; kk < kKtD / 16; ++kk) {
+      const int c = kk & 1, nx = c ^ 1;
+      if (kk == 0 && fill) issue_stage((buf + kAhead) % kNBuf, t_begin + (s + kAhead) * kKtD);
+      if (kk + 1 < kKtD / 16) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) fa[nx][rb] = frag(buf, a_off, kk + 1, rb);
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) fb[nx][cb] = frag(buf, b_off, kk + 1, cb);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[c][rb], fb[c][cb], acc[rb][cb]);
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global (direct-to-LDS) load
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // address arithmetic
+      }
+    }
+    // Stage s+1 must have landed; later stages' loads may stay in flight.
+    wait_for(s + 1);
     __syncthreads();
   }
   store_acc(acc, dst, wave, lane);
@@ -374,7 +584,25 @@ extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* 
         partial, p.launched);
   } else {
     const int vec_ok = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
-    if (x_dtype == GPTQ_BF16)
+    const bool direct = vec_ok && (n % 8 == 0);
+    if (direct) {
+      static bool attr_done[2] = {false, false};
+      const int which = x_dtype == GPTQ_BF16 ? 0 : 1;
+      if (!attr_done[which]) {
+        const void* fn = x_dtype == GPTQ_BF16 ? reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_BF16>)
+                                              : reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_F16>);
+        GPTQ_TRY_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kNBuf * kStageBytes));
+        attr_done[which] = true;
+      }
+      if (x_dtype == GPTQ_BF16)
+        syrk16_direct_kernel<GPTQ_BF16><<<(unsigned)p.launched, kThreads, kNBuf * kStageBytes, st>>>(
+            static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit, p.tok_per_split,
+            partial, p.launched);
+      else
+        syrk16_direct_kernel<GPTQ_F16><<<(unsigned)p.launched, kThreads, kNBuf * kStageBytes, st>>>(
+            static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit, p.tok_per_split,
+            partial, p.launched);
+    } else if (x_dtype == GPTQ_BF16)
       syrk16_kernel<GPTQ_BF16><<<(unsigned)p.launched, kThreads, 0, st>>>(
           static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit,
           p.tok_per_split, partial, p.launched, vec_ok);

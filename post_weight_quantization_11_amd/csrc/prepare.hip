@@ -8,12 +8,15 @@
 //   U = R^{-1} = J L^{-1} J       (upper, U^T U = H_d^{-1})
 // so one Cholesky and one triangular inverse (2/3 n^3 flops in all) give U
 // directly; H_d^{-1} is never formed.  Both run in float64, right-looking
-// with 64 x 64 blocks, interleaved in one loop over block columns kb:
-//   potrf_diag(kb)  factor the diagonal block, invert it (one workgroup)
-//   trsm(kb)        panel L[i, kb] = A[i, kb] * inv(L_kk)^T        (MFMA f64)
-//   syrk(kb)        A[i, j] -= L[i, kb] L[j, kb]^T, kb < j <= i    (MFMA f64)
-//   tri_fin(kb)     X[kb, j] = inv(L_kk) T[kb, j], j < kb          (MFMA f64)
-//   tri_upd(kb)     T[i, j] -= L[i, kb] X[kb, j], i > kb, j <= kb  (MFMA f64)
+// with 64 x 64 blocks, interleaved in one loop over block columns kb with two
+// launches per step:
+//   panel(kb)   L[i, kb] = A[i, kb] inv(L_kk)^T                   (MFMA f64)
+//               X[kb, j] = inv(L_kk) T[kb, j], j < kb             (MFMA f64)
+//   update(kb)  A[i, j] -= L[i, kb] L[j, kb]^T, kb < j <= i       (MFMA f64)
+//               T[i, j] -= L[i, kb] X[kb, j], i > kb, j <= kb     (MFMA f64)
+//               + the workgroup that updates block (kb+1, kb+1) then factors
+//                 it (one wave, no barriers) and inverts it (four waves),
+//                 overlapping the rest of the trailing update
 // where X = L^{-1} is built in place of T (forward substitution by block
 // rows).  Matrices are padded to a multiple of 64 with an identity block.
 #include "common.h"
@@ -100,62 +103,95 @@ __global__ void zero_kernel(double* __restrict__ p, int64_t count) {
     p[i] = 0.0;
 }
 
-// Factors the 64 x 64 diagonal block kb in LDS (lower Cholesky), records the
-// first bad pivot, writes L_kk back, and writes inv(L_kk) both to the
-// workspace slot Linv and to the diagonal block of X.
-__global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict__ A, double* __restrict__ X,
-                                                              double* __restrict__ Linv, int np, int n, int kb,
-                                                              int32_t* __restrict__ info) {
-  __shared__ double L[kB][kB + 1];
-  __shared__ double V[kB][kB + 1];
-  const int tid = threadIdx.x;
+// 1/sqrt(d) in float64: hardware estimate refined by two Newton steps.
+__device__ inline double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  double h = __builtin_fma(-0.5 * d * y, y, 0.5);
+  y = __builtin_fma(y, h, y);
+  h = __builtin_fma(-0.5 * d * y, y, 0.5);
+  return __builtin_fma(y, h, y);
+}
+
+__device__ inline double bcast_lane(double v, int lane) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, lane);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), lane);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Factors and inverts the 64 x 64 diagonal block kb; called by all 256
+// threads of a workgroup.
+//  Cholesky (wave 0 only; lane r owns row r in registers, columns are
+//  broadcast with readlane, so no barrier is needed inside the loop):
+//    column j:  y = 1/sqrt(a_jj);  L_rj = a_rj * y (r >= j, so L_jj = sqrt(a_jj));
+//               a_rc -= L_rj L_cj  (j < c <= r)
+//  Inverse (all 4 waves, wave w owns columns w, w+4, ..., w+60): the columns of
+//  V = L^{-1} are independent; V = diag(1/L_jj) T with T = I and, for each row
+//  j, rows r > j: T[r][c] -= (L_rj / L_jj) T[j][c].
+// S is an LDS copy of the block (pitch kB + 1).  L goes back to A, inv(L_kk)
+// to Linv and to X's diagonal block.  A non-positive or non-finite pivot
+// leaves L_jj non-finite or zero (NaN then spreads to every later pivot), so
+// the first bad pivot is the first row whose L_rr is not a positive finite
+// number; it is recorded in *info.
+__device__ inline void factor_diag(double* S, double* __restrict__ A, double* __restrict__ X,
+                                   double* __restrict__ Linv, int np, int n, int kb,
+                                   int32_t* __restrict__ info) {
+  constexpr int P = kB + 1;
+  const int wave = threadIdx.x >> 6;
+  const int r = threadIdx.x & 63;
   const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
-  for (int e = tid; e < kB * kB; e += kThreads) {
-    const int r = e / kB, c = e % kB;
-    L[r][c] = c <= r ? A[base + (int64_t)r * np + c] : 0.0;
+  if (wave == 0) {
+    double a[kB];
+#pragma unroll
+    for (int c = 0; c < kB; ++c) a[c] = c <= r ? S[r * P + c] : 0.0;
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      const double y = rsqrt_f64(bcast_lane(a[j], j));
+      a[j] *= y;
+#pragma unroll
+      for (int c = j + 1; c < kB; ++c) a[c] = __builtin_fma(-a[j], bcast_lane(a[j], c), a[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < kB; ++c) {
+      S[r * P + c] = a[c];
+      if (c <= r) A[base + (int64_t)r * np + c] = a[c];
+    }
+    const double lrr = S[r * P + r];
+    const bool bad = !(lrr > 0.0) || !isfinite(lrr) || !(lrr * lrr > 0.0);
+    const unsigned long long mask = __ballot(bad && kb * kB + r < n);
+    if (r == 0 && mask != 0ull && *info == 0) *info = kb * kB + __builtin_ctzll(mask) + 1;
   }
   __syncthreads();
+  const double my_y = 1.0 / S[r * P + r];   // 1 / L_rr
+  double v[kB / 4];
+#pragma unroll
+  for (int i = 0; i < kB / 4; ++i) v[i] = (wave + 4 * i == r) ? 1.0 : 0.0;
+#pragma unroll
   for (int j = 0; j < kB; ++j) {
-    if (tid == 0) {
-      const double d = L[j][j];
-      const int pos = kb * kB + j;
-      if (!(d > 0.0) || !isfinite(d)) {
-        if (pos < n && *info == 0) *info = pos + 1;
-      }
-      L[j][j] = sqrt(d);
-    }
-    __syncthreads();
-    const double djj = L[j][j];
-    for (int r = j + 1 + tid; r < kB; r += kThreads) L[r][j] /= djj;
-    __syncthreads();
-    // trailing update of the block: L[r][c] -= L[r][j] L[c][j], j < c <= r
-    for (int e = tid; e < kB * kB; e += kThreads) {
-      const int r = e / kB, c = e % kB;
-      if (c > j && c <= r) L[r][c] -= L[r][j] * L[c][j];
-    }
-    __syncthreads();
+    // keep each step's LDS read inside its step (hoisting all of them spills)
+    __asm__ volatile("" ::: "memory");
+    const double l = (j < r ? S[r * P + j] : 0.0) * bcast_lane(my_y, j);
+#pragma unroll
+    for (int i = 0; i < kB / 4; ++i) v[i] = __builtin_fma(-l, bcast_lane(v[i], j), v[i]);
   }
-  // inverse by columns: V = L^{-1} (lower), column c solved by forward substitution
-  if (tid < kB) {
-    const int c = tid;
-    for (int r = 0; r < kB; ++r) V[r][c] = 0.0;
-    V[c][c] = 1.0 / L[c][c];
-    for (int r = c + 1; r < kB; ++r) {
-      double s = 0.0;
-      for (int p = c; p < r; ++p) s += L[r][p] * V[p][c];
-      V[r][c] = -s / L[r][r];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < kB * kB; e += kThreads) {
-    const int r = e / kB, c = e % kB;
-    if (c <= r) A[base + (int64_t)r * np + c] = L[r][c];
-    Linv[e] = V[r][c];
-    X[base + (int64_t)r * np + c] = V[r][c];
+#pragma unroll
+  for (int i = 0; i < kB / 4; ++i) {
+    const int c = wave + 4 * i;
+    const double vv = v[i] * my_y;
+    Linv[r * kB + c] = vv;
+    X[base + (int64_t)r * np + c] = vv;
   }
 }
 
-enum { OP_TRSM = 0, OP_SYRK = 1, OP_TRI_FIN = 2, OP_TRI_UPD = 3 };
+__global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict__ A, double* __restrict__ X,
+                                                              double* __restrict__ Linv, int np, int n, int kb,
+                                                              int32_t* __restrict__ info) {
+  __shared__ double S[kB * (kB + 1)];
+  const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
+  for (int e = threadIdx.x; e < kB * kB; e += kThreads) S[(e >> 6) * (kB + 1) + (e & 63)] = A[base + (int64_t)(e >> 6) * np + (e & 63)];
+  __syncthreads();
+  factor_diag(S, A, X, Linv, np, n, kb, info);
+}
 
 __device__ inline void tri_decode(int t, int& ii, int& jj) {
   // lower-triangle order (ii >= jj), row by row
@@ -166,71 +202,27 @@ __device__ inline void tri_decode(int t, int& ii, int& jj) {
   jj = t - r * (r + 1) / 2;
 }
 
-// One 64 x 64 output block per workgroup, K = 64, float64 MFMA 16x16x4.
-//   TRSM:    C = Aop * B^T          (C = A[i,kb], Aop = A[i,kb], B = inv(L_kk))
-//   SYRK:    C = C - Aop * B^T      (C = A[i,j], Aop = A[i,kb], B = A[j,kb])
-//   TRI_FIN: C = Aop * B            (C = X[kb,j], Aop = inv(L_kk), B = X[kb,j])
-//   TRI_UPD: C = C - Aop * B        (C = X[i,j], Aop = A[i,kb], B = X[kb,j])
-// All operands are loaded into LDS before C is written, so C may alias B.
-template <int OP>
-__global__ __launch_bounds__(kThreads) void chol_block_kernel(double* __restrict__ A, double* __restrict__ X,
-                                                              const double* __restrict__ Linv, int np, int nbk,
-                                                              int kb) {
-  int bi, bj;
-  if (OP == OP_TRSM) {
-    bi = kb + 1 + blockIdx.x;
-    bj = kb;
-  } else if (OP == OP_SYRK) {
-    int ii, jj;
-    tri_decode(blockIdx.x, ii, jj);
-    bi = kb + 1 + ii;
-    bj = kb + 1 + jj;
-  } else if (OP == OP_TRI_FIN) {
-    bi = kb;
-    bj = blockIdx.x;
-  } else {
-    bi = kb + 1 + blockIdx.x / (kb + 1);
-    bj = blockIdx.x % (kb + 1);
-  }
-  if (bi >= nbk) return;
+struct TileLds {
+  double As[kB][kB + 1];   // As[row][k]
+  double Bs[kB][kB + 1];   // Bs[k][col]
+};
 
-  const double* Ap;
-  int64_t lda;
-  const double* Bp;
-  int64_t ldb;
-  double* Cp;
-  bool transB, sub;
-  if (OP == OP_TRSM) {
-    Ap = A + (int64_t)bi * kB * np + (int64_t)kb * kB; lda = np;
-    Bp = Linv; ldb = kB; transB = true; sub = false;
-    Cp = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-  } else if (OP == OP_SYRK) {
-    Ap = A + (int64_t)bi * kB * np + (int64_t)kb * kB; lda = np;
-    Bp = A + (int64_t)bj * kB * np + (int64_t)kb * kB; ldb = np; transB = true; sub = true;
-    Cp = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
-  } else if (OP == OP_TRI_FIN) {
-    Ap = Linv; lda = kB;
-    Bp = X + (int64_t)kb * kB * np + (int64_t)bj * kB; ldb = np; transB = false; sub = false;
-    Cp = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
-  } else {
-    Ap = A + (int64_t)bi * kB * np + (int64_t)kb * kB; lda = np;
-    Bp = X + (int64_t)kb * kB * np + (int64_t)bj * kB; ldb = np; transB = false; sub = true;
-    Cp = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
-  }
-
-  __shared__ double As[kB][kB + 1];   // As[row][k]
-  __shared__ double Bs[kB][kB + 1];   // Bs[k][col]
+// One 64 x 64 output block, K = 64, float64 MFMA 16x16x4, 4 waves of 32 x 32:
+//   C = (sub ? C : 0) - / + Aop * (transB ? B^T : B)
+// All operands are in LDS before C is written, so C may alias Aop or B.
+// If keep != nullptr the result is also left in keep[64][65] (LDS).
+__device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, const double* Bp, int64_t ldb,
+                                   bool transB, double* Cp, int64_t ldc, bool sub, double* keep) {
   const int tid = threadIdx.x;
   for (int e = tid; e < kB * kB; e += kThreads) {
-    const int r = e / kB, c = e % kB;
-    As[r][c] = Ap[(int64_t)r * lda + c];
+    const int r = e >> 6, c = e & 63;
+    t.As[r][c] = Ap[(int64_t)r * lda + c];
     if (transB)
-      Bs[c][r] = Bp[(int64_t)r * ldb + c];
+      t.Bs[c][r] = Bp[(int64_t)r * ldb + c];
     else
-      Bs[r][c] = Bp[(int64_t)r * ldb + c];
+      t.Bs[r][c] = Bp[(int64_t)r * ldb + c];
   }
   __syncthreads();
-
   const int wave = tid >> 6, lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1;
   doublex4 acc[2][2];
@@ -243,15 +235,16 @@ __global__ __launch_bounds__(kThreads) void chol_block_kernel(double* __restrict
     const int k = k4 * 4 + (lane >> 4);
     double a[2], b[2];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) a[ti] = As[wr * 32 + ti * 16 + (lane & 15)][k];
+    for (int ti = 0; ti < 2; ++ti) a[ti] = t.As[wr * 32 + ti * 16 + (lane & 15)][k];
 #pragma unroll
-    for (int tj = 0; tj < 2; ++tj) b[tj] = Bs[k][wc * 32 + tj * 16 + (lane & 15)];
+    for (int tj = 0; tj < 2; ++tj) b[tj] = t.Bs[k][wc * 32 + tj * 16 + (lane & 15)];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
       for (int tj = 0; tj < 2; ++tj)
         acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[ti], b[tj], acc[ti][tj], 0, 0, 0);
   }
+  if (keep) __syncthreads();   // keep aliases As
   // float64 16x16x4 accumulator on gfx950: register r of lane l holds row
   // l/16 + 4*r, column l%16 of the 16x16 block (rows interleaved, unlike the
   // float32 16x16x4 form where lane l holds rows 4*(l/16) .. 4*(l/16)+3).
@@ -263,10 +256,65 @@ __global__ __launch_bounds__(kThreads) void chol_block_kernel(double* __restrict
       for (int r = 0; r < 4; ++r) {
         const int row = wr * 32 + ti * 16 + (lane >> 4) + 4 * r;
         const int col = wc * 32 + tj * 16 + (lane & 15);
-        double* p = Cp + (int64_t)row * np + col;
-        const double v = acc[ti][tj][r];
-        *p = sub ? (*p - v) : v;
+        double* p = Cp + (int64_t)row * ldc + col;
+        const double v = sub ? (*p - acc[ti][tj][r]) : acc[ti][tj][r];
+        *p = v;
+        if (keep) keep[row * (kB + 1) + col] = v;
       }
+}
+
+// Step kb, first launch: panel L[i, kb] = A[i, kb] inv(L_kk)^T for i > kb
+// (blocks 0 .. T-1), and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
+// for j < kb (blocks T .. T+kb-1).
+__global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict__ A, double* __restrict__ X,
+                                                              const double* __restrict__ Linv, int np, int nbk,
+                                                              int kb) {
+  __shared__ TileLds t;
+  const int T = nbk - kb - 1;
+  const int b = blockIdx.x;
+  if (b < T) {
+    const int bi = kb + 1 + b;
+    double* p = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
+    gemm_tile64(t, p, np, Linv, kB, true, p, np, false, nullptr);
+  } else {
+    const int bj = b - T;
+    double* p = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
+    gemm_tile64(t, Linv, kB, p, np, false, p, np, false, nullptr);
+  }
+}
+
+// Step kb, second launch: trailing update A[i, j] -= L[i, kb] L[j, kb]^T for
+// kb < j <= i (blocks 0 .. S-1, block 0 is the next diagonal block, which the
+// same workgroup then factors: wave 0 runs factor_diag_wave on it), and
+// T[i, j] -= L[i, kb] X[kb, j] for i > kb, j <= kb (the rest).
+__global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restrict__ A, double* __restrict__ X,
+                                                               double* __restrict__ Linv, int np, int n, int nbk,
+                                                               int kb, int32_t* __restrict__ info) {
+  __shared__ TileLds t;
+  const int T = nbk - kb - 1;
+  const int S = T * (T + 1) / 2;
+  const int b = blockIdx.x;
+  if (b < S) {
+    int ii, jj;
+    tri_decode(b, ii, jj);
+    const int bi = kb + 1 + ii, bj = kb + 1 + jj;
+    const double* pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
+    const double* pb = A + (int64_t)bj * kB * np + (int64_t)kb * kB;
+    double* pc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
+    double* keep = (b == 0) ? &t.As[0][0] : nullptr;
+    gemm_tile64(t, pa, np, pb, np, true, pc, np, true, keep);
+    if (b == 0) {
+      __syncthreads();
+      factor_diag(&t.As[0][0], A, X, Linv, np, n, kb + 1, info);
+    }
+  } else {
+    const int e = b - S;
+    const int bi = kb + 1 + e / (kb + 1), bj = e % (kb + 1);
+    const double* pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
+    const double* pb = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
+    double* pc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
+    gemm_tile64(t, pa, np, pb, np, false, pc, np, true, nullptr);
+  }
 }
 
 // U[i][j] = X[n-1-i][n-1-j] for i <= j, 0 below the diagonal (float32).
@@ -331,16 +379,13 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   build_reversed_kernel<<<(unsigned)np, kThreads, 0, st>>>(H, ni, np, perm, lam, A);
   zero_kernel<<<2048, kThreads, 0, st>>>(X, (int64_t)np * np);
   GPTQ_TRY_LAUNCH();
+  potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, 0, info);
   for (int kb = 0; kb < nbk; ++kb) {
-    potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, kb, info);
-    const int rest = nbk - kb - 1;
-    if (rest > 0) {
-      chol_block_kernel<OP_TRSM><<<(unsigned)rest, kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
-      chol_block_kernel<OP_SYRK><<<(unsigned)(rest * (rest + 1) / 2), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
-    }
-    if (kb > 0) chol_block_kernel<OP_TRI_FIN><<<(unsigned)kb, kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
-    if (rest > 0)
-      chol_block_kernel<OP_TRI_UPD><<<(unsigned)(rest * (kb + 1)), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
+    const int T = nbk - kb - 1;
+    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(T + kb), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
+    if (T > 0)
+      chol_update_kernel<<<(unsigned)(T * (T + 1) / 2 + T * (kb + 1)), kThreads, 0, st>>>(A, X, Linv, np, ni, nbk,
+                                                                                         kb, info);
     GPTQ_TRY_LAUNCH();
   }
   write_u_kernel<<<(unsigned)n, kThreads, 0, st>>>(X, ni, np, U);

@@ -202,20 +202,49 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
 
   for (int e = tid; e < kBS * kBS; e += kThreads) {
-    const int i = e / kBS, j = e % kBS;
+    const int i = e >> 7, j = e & (kBS - 1);
     Ud[i][j] = (i < bw && j < bw && j >= i) ? U[(int64_t)(c0 + i) * n + c0 + j] : 0.f;
   }
   for (int j = tid; j < kBS; j += kThreads)
     invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
-  for (int e = lane; e < kRowsPerWave * kBS; e += 64) {
-    const int r = e / kBS, c = e % kBS;
-    const int64_t row = row0 + r;
-    float v = 0.f;
-    if (row < m && c < bw) {
-      v = load_as_f32<DT>(Wsrc, row * ldw + c0 + c);
-      for (int sp = 0; sp < nsplit; ++sp) v -= P[((int64_t)sp * m + row) * kBS + c];
+  {
+    // The wave's 16 x 128 tile: slot q of lane l is row (l + 64q) / 32,
+    // columns 4*((l + 64q) % 32) .. +3; all loads of one split are issued
+    // before any is consumed.
+    constexpr int kSlots = kRowsPerWave * kBS / 4 / 64;
+    floatx4 t[kSlots];
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      const int e = lane + 64 * q;
+      const int rr = e >> 5, c = (e & 31) * 4;
+      const int64_t row = row0 + rr;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (row < m) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (c + k < bw) v[k] = load_as_f32<DT>(Wsrc, row * ldw + c0 + c + k);
+      }
+      t[q] = v;
     }
-    T[wave][r][c] = v;
+    for (int sp = 0; sp < nsplit; ++sp) {
+      floatx4 pv[kSlots];
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) {
+        const int e = lane + 64 * q;
+        const int rr = e >> 5, c = (e & 31) * 4;
+        const int64_t row = row0 + rr;
+        pv[q] = row < m ? *reinterpret_cast<const floatx4*>(P + ((int64_t)sp * m + row) * kBS + c)
+                        : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int q = 0; q < kSlots; ++q) t[q] -= pv[q];
+    }
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      const int e = lane + 64 * q;
+      const int rr = e >> 5, c = (e & 31) * 4;
+      *reinterpret_cast<floatx4*>(&T[wave][rr][c]) = t[q];
+    }
   }
   __syncthreads();
 
@@ -237,12 +266,22 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   for (int sb = 0; sb < nsb; ++sb) {
     const int j0 = sb * kSB;
     if (g > 0 && ((c0 + j0) % g) == 0) {
+      // group range over the current values; g is a multiple of 16 and the
+      // group lies inside the block (tail columns beyond bw are excluded)
       const int gl = min(g, bw - j0);
       float mn = T[wave][r][j0], mx = mn;
-      for (int c = 1; c < gl; ++c) {
-        const float v = T[wave][r][j0 + c];
-        mn = fminf(mn, v);
-        mx = fmaxf(mx, v);
+      for (int c4 = 0; c4 < g; c4 += 16) {
+        floatx4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const floatx4*>(&T[wave][r][j0 + c4 + 4 * u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (c4 + 4 * u + k < gl) {
+              mn = fminf(mn, v[u][k]);
+              mx = fmaxf(mx, v[u][k]);
+            }
       }
       grid_from_range(mn, mx, maxq, s, z, inv_s);
       if (active) {
