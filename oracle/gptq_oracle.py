@@ -38,6 +38,8 @@ does not use U, and an exact loss identity).
 from __future__ import annotations
 
 import numpy as np
+import scipy.linalg
+import scipy.linalg.lapack
 
 F32 = np.float32
 F64 = np.float64
@@ -111,18 +113,16 @@ def damp_and_permute(H, perm, damp_rel: float):
 # Plain definition: invert H_d (via its Cholesky factor), then take the upper
 # Cholesky factor of the inverse.
 # ---------------------------------------------------------------------------
-def _cholesky_lower(A) -> np.ndarray:
-    try:
-        return np.linalg.cholesky(A)
-    except np.linalg.LinAlgError:
-        # Locate the first non-positive pivot for the error report.
-        n = A.shape[0]
-        for k in range(1, n + 1):
-            try:
-                np.linalg.cholesky(A[:k, :k])
-            except np.linalg.LinAlgError:
-                raise NotPositiveDefinite(k) from None
-        raise NotPositiveDefinite(n) from None
+def _potrf(A, lower: bool) -> np.ndarray:
+    """LAPACK Cholesky of the symmetric A read from one triangle; the other
+    triangle of the result is zero.  A failure at leading minor k raises
+    NotPositiveDefinite(k) (1-based)."""
+    c, info = scipy.linalg.lapack.dpotrf(A, lower=1 if lower else 0, clean=1)
+    if info > 0:
+        raise NotPositiveDefinite(int(info))
+    if info < 0:
+        raise ValueError(f"dpotrf argument {-info}")
+    return c
 
 
 def inverse_cholesky_upper(Hd) -> np.ndarray:
@@ -133,11 +133,12 @@ def inverse_cholesky_upper(Hd) -> np.ndarray:
         return np.zeros((0, 0), dtype=F64)
     if not np.all(np.isfinite(Hd)):
         raise NotPositiveDefinite(1)
-    L = _cholesky_lower(Hd)
-    Linv = np.linalg.solve(L, np.eye(n))
-    Hinv = Linv.T @ Linv
-    Hinv = 0.5 * (Hinv + Hinv.T)
-    return np.linalg.cholesky(Hinv).T
+    L = _potrf(Hd, lower=True)                       # H_d = L L^T
+    inv, info = scipy.linalg.lapack.dpotri(L, lower=1)  # lower triangle of H_d^{-1}
+    if info != 0:
+        raise NotPositiveDefinite(max(1, int(info)))
+    # The upper triangle of inv^T is the lower triangle of H_d^{-1}.
+    return np.ascontiguousarray(_potrf(inv.T, lower=False))  # H_d^{-1} = U^T U
 
 
 # ---------------------------------------------------------------------------
