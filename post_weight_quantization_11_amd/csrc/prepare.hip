@@ -15,8 +15,8 @@
 //   update(kb)  A[i, j] -= L[i, kb] L[j, kb]^T, kb < j <= i       (MFMA f64)
 //               T[i, j] -= L[i, kb] X[kb, j], i > kb, j <= kb     (MFMA f64)
 //               + the workgroup that updates block (kb+1, kb+1) then factors
-//                 it (one wave, no barriers) and inverts it (four waves),
-//                 overlapping the rest of the trailing update
+//                 and inverts it (16-column leaves, float64 MFMA between
+//                 them), overlapping the rest of the trailing update
 // where X = L^{-1} is built in place of T (forward substitution by block
 // rows).  Matrices are padded to a multiple of 64 with an identity block.
 #include "common.h"
@@ -119,78 +119,229 @@ __device__ inline double bcast_lane(double v, int lane) {
   return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
 }
 
-// Factors and inverts the 64 x 64 diagonal block kb; called by all 256
-// threads of a workgroup.
-//  Cholesky (wave 0 only; lane r owns row r in registers, columns are
-//  broadcast with readlane, so no barrier is needed inside the loop):
-//    column j:  y = 1/sqrt(a_jj);  L_rj = a_rj * y (r >= j, so L_jj = sqrt(a_jj));
-//               a_rc -= L_rj L_cj  (j < c <= r)
-//  Inverse (all 4 waves, wave w owns columns w, w+4, ..., w+60): the columns of
-//  V = L^{-1} are independent; V = diag(1/L_jj) T with T = I and, for each row
-//  j, rows r > j: T[r][c] -= (L_rj / L_jj) T[j][c].
-// S is an LDS copy of the block (pitch kB + 1).  L goes back to A, inv(L_kk)
-// to Linv and to X's diagonal block.  A non-positive or non-finite pivot
-// leaves L_jj non-finite or zero (NaN then spreads to every later pivot), so
-// the first bad pivot is the first row whose L_rr is not a positive finite
-// number; it is recorded in *info.
-__device__ inline void factor_diag(double* S, double* __restrict__ A, double* __restrict__ X,
-                                   double* __restrict__ Linv, int np, int n, int kb,
-                                   int32_t* __restrict__ info) {
-  constexpr int P = kB + 1;
-  const int wave = threadIdx.x >> 6;
-  const int r = threadIdx.x & 63;
-  const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
-  if (wave == 0) {
-    double a[kB];
+// ---------------------------------------------------------------------------
+// The 64 x 64 diagonal block: Cholesky factor and its inverse.
+//
+// The block is split into four 16-column leaves.  Wave 0 factors one leaf at
+// a time for all 64 rows (lane = row; the 16 columns live in registers and
+// pivot columns are broadcast with readlane, so the rows below the leaf's
+// diagonal block come out of the same instructions).  Between leaves all four
+// waves apply the leaf's rank-16 update to the remaining blocks with float64
+// MFMA.  The inverse X = inv(L) is built by 16 x 16 blocks on the other waves
+// while wave 0 factors the next leaf:
+//   X_II = inv(L_II)                 (lane = column, forward substitution)
+//   X_IJ = -X_II sum_{K=J}^{I-1} L_IK X_KJ   (MFMA, J < I)
+// S holds the block (pitch 65) and receives L; Xs (pitch 65) receives X.
+// A non-positive or non-finite pivot leaves L_jj non-finite or zero (NaN then
+// spreads to every later pivot), so the first bad pivot is the first row whose
+// L_rr is not a positive finite number; it is recorded in *info.
+// ---------------------------------------------------------------------------
+constexpr int kP = kB + 1;    // LDS pitch of the 64 x 64 block buffers
+
+struct FactorLds {
+  double yd[kB];              // 1 / L_jj
+  double Ts[3][16][17];       // partial sums of the off-diagonal inverse blocks
+};
+
+// float64 MFMA 16x16x4 operand/accumulator layouts on gfx950: A element
+// (row l%16, k l/16), B element (k l/16, column l%16); accumulator register r
+// of lane l holds row l/16 + 4r, column l%16.
+__device__ __forceinline__ doublex4 load_c16(const double* C, int ldc, int lane) {
+  doublex4 a;
 #pragma unroll
-    for (int c = 0; c < kB; ++c) a[c] = c <= r ? S[r * P + c] : 0.0;
+  for (int r = 0; r < 4; ++r) a[r] = C[((lane >> 4) + 4 * r) * ldc + (lane & 15)];
+  return a;
+}
+
+__device__ __forceinline__ void store_c16(double* C, int ldc, doublex4 a, int lane) {
 #pragma unroll
-    for (int j = 0; j < kB; ++j) {
-      const double y = rsqrt_f64(bcast_lane(a[j], j));
-      a[j] *= y;
+  for (int r = 0; r < 4; ++r) C[((lane >> 4) + 4 * r) * ldc + (lane & 15)] = a[r];
+}
+
+// acc += (neg ? -A : A) B for 16 x 16 row-major blocks in LDS.
+__device__ __forceinline__ doublex4 mm16(doublex4 acc, const double* Ab, int lda, const double* Bb, int ldb,
+                                         bool neg, int lane) {
 #pragma unroll
-      for (int c = j + 1; c < kB; ++c) a[c] = __builtin_fma(-a[j], bcast_lane(a[j], c), a[c]);
-    }
-#pragma unroll
-    for (int c = 0; c < kB; ++c) {
-      S[r * P + c] = a[c];
-      if (c <= r) A[base + (int64_t)r * np + c] = a[c];
-    }
-    const double lrr = S[r * P + r];
-    const bool bad = !(lrr > 0.0) || !isfinite(lrr) || !(lrr * lrr > 0.0);
-    const unsigned long long mask = __ballot(bad && kb * kB + r < n);
-    if (r == 0 && mask != 0ull && *info == 0) *info = kb * kB + __builtin_ctzll(mask) + 1;
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int k = k4 * 4 + (lane >> 4);
+    const double a = Ab[(lane & 15) * lda + k];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(neg ? -a : a, Bb[k * ldb + (lane & 15)], acc, 0, 0, 0);
   }
-  __syncthreads();
-  const double my_y = 1.0 / S[r * P + r];   // 1 / L_rr
-  double v[kB / 4];
+  return acc;
+}
+
+// acc += (neg ? -A : A) Bt^T.
+__device__ __forceinline__ doublex4 mm16_bt(doublex4 acc, const double* Ab, int lda, const double* Bt, int ldbt,
+                                            bool neg, int lane) {
 #pragma unroll
-  for (int i = 0; i < kB / 4; ++i) v[i] = (wave + 4 * i == r) ? 1.0 : 0.0;
+  for (int k4 = 0; k4 < 4; ++k4) {
+    const int k = k4 * 4 + (lane >> 4);
+    const double a = Ab[(lane & 15) * lda + k];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(neg ? -a : a, Bt[(lane & 15) * ldbt + k], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Wave 0: columns 16Q .. 16Q+15 of S for all rows (right-looking inside the
+// leaf); rows above the diagonal are written as zero.
+template <int Q>
+__device__ __forceinline__ void leaf_factor(double* S, double* yd, int lane) {
+  double v[16];
 #pragma unroll
-  for (int j = 0; j < kB; ++j) {
-    // keep each step's LDS read inside its step (hoisting all of them spills)
-    __asm__ volatile("" ::: "memory");
-    const double l = (j < r ? S[r * P + j] : 0.0) * bcast_lane(my_y, j);
-#pragma unroll
-    for (int i = 0; i < kB / 4; ++i) v[i] = __builtin_fma(-l, bcast_lane(v[i], j), v[i]);
+  for (int jj = 0; jj < 16; ++jj) {
+    const int c = 16 * Q + jj;
+    const double s = S[lane * kP + c];
+    v[jj] = c <= lane ? s : 0.0;
   }
 #pragma unroll
-  for (int i = 0; i < kB / 4; ++i) {
-    const int c = wave + 4 * i;
-    const double vv = v[i] * my_y;
-    Linv[r * kB + c] = vv;
-    X[base + (int64_t)r * np + c] = vv;
+  for (int jj = 0; jj < 16; ++jj) {
+    const int j = 16 * Q + jj;
+    const double y = rsqrt_f64(bcast_lane(v[jj], j));
+    v[jj] *= y;
+    yd[j] = y;
+#pragma unroll
+    for (int cc = jj + 1; cc < 16; ++cc) v[cc] = __builtin_fma(-v[jj], bcast_lane(v[jj], 16 * Q + cc), v[cc]);
+  }
+#pragma unroll
+  for (int jj = 0; jj < 16; ++jj) {
+    const int c = 16 * Q + jj;
+    S[lane * kP + c] = c <= lane ? v[jj] : 0.0;
   }
 }
+
+// All waves: blocks (I, J) with Q < J <= I get -= L_IQ L_JQ^T.
+template <int Q>
+__device__ __forceinline__ void leaf_update(double* S, int wave, int lane) {
+  int idx = 0;
+#pragma unroll
+  for (int I = Q + 1; I < 4; ++I)
+#pragma unroll
+    for (int J = Q + 1; J <= I; ++J, ++idx) {
+      if ((idx & 3) != wave) continue;
+      double* C = S + 16 * I * kP + 16 * J;
+      doublex4 acc = load_c16(C, kP, lane);
+      acc = mm16_bt(acc, S + 16 * I * kP + 16 * Q, kP, S + 16 * J * kP + 16 * Q, kP, true, lane);
+      store_c16(C, kP, acc, lane);
+    }
+}
+
+// X_II = inv(L_II): lane & 15 is the column, rows by forward substitution.
+template <int I>
+__device__ __forceinline__ void leaf_inverse(const double* S, double* Xs, const double* yd, int lane) {
+  const int c = lane & 15;
+  double x[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    double p0 = rr == c ? 1.0 : 0.0, p1 = 0.0;
+#pragma unroll
+    for (int k = 0; k < rr; ++k) {
+      const double l = S[(16 * I + rr) * kP + 16 * I + k];
+      if (k & 1)
+        p1 = __builtin_fma(-l, x[k], p1);
+      else
+        p0 = __builtin_fma(-l, x[k], p0);
+    }
+    x[rr] = (p0 + p1) * yd[16 * I + rr];
+  }
+  if (lane < 16) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) Xs[(16 * I + rr) * kP + 16 * I + c] = x[rr];
+  }
+}
+
+// sum_{K=J}^{I-1} L_IK X_KJ
+template <int I, int J>
+__device__ __forceinline__ doublex4 inverse_row_sum(const double* S, const double* Xs, int lane) {
+  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int K = J; K < I; ++K) acc = mm16(acc, S + 16 * I * kP + 16 * K, kP, Xs + 16 * K * kP + 16 * J, kP, false, lane);
+  return acc;
+}
+
+// X_IJ = -X_II T, T (16 x 16, pitch 17) in LDS.
+template <int I, int J>
+__device__ __forceinline__ void inverse_finish(double* Xs, const double* T, int lane) {
+  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+  acc = mm16(acc, Xs + 16 * I * kP + 16 * I, kP, T, 17, true, lane);
+  store_c16(Xs + 16 * I * kP + 16 * J, kP, acc, lane);
+}
+
+template <int I, int J>
+__device__ __forceinline__ void inverse_block(const double* S, double* Xs, double* T, int lane) {
+  store_c16(T, 17, inverse_row_sum<I, J>(S, Xs, lane), lane);
+  inverse_finish<I, J>(Xs, T, lane);
+}
+
+// Factors and inverts the diagonal block kb held in S; all 256 threads.  L
+// goes back to A (lower triangle), inv(L_kk) to Linv and to X's diagonal block.
+__device__ __forceinline__ void factor_diag(double* S, double* Xs, FactorLds& fx, double* __restrict__ A,
+                                            double* __restrict__ X, double* __restrict__ Linv, int np, int n,
+                                            int kb, int32_t* __restrict__ info) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
+  double* T0 = &fx.Ts[0][0][0];
+  double* T1 = &fx.Ts[1][0][0];
+  double* T2 = &fx.Ts[2][0][0];
+  if (wave == 0) leaf_factor<0>(S, fx.yd, lane);
+  __syncthreads();
+  leaf_update<0>(S, wave, lane);
+  __syncthreads();
+  if (wave == 0) leaf_factor<1>(S, fx.yd, lane);
+  if (wave == 1) leaf_inverse<0>(S, Xs, fx.yd, lane);
+  __syncthreads();
+  leaf_update<1>(S, wave, lane);
+  __syncthreads();
+  if (wave == 0) leaf_factor<2>(S, fx.yd, lane);
+  if (wave == 1) {
+    leaf_inverse<1>(S, Xs, fx.yd, lane);
+    inverse_block<1, 0>(S, Xs, T0, lane);
+  }
+  __syncthreads();
+  leaf_update<2>(S, wave, lane);
+  __syncthreads();
+  if (wave == 0) leaf_factor<3>(S, fx.yd, lane);
+  if (wave == 1) leaf_inverse<2>(S, Xs, fx.yd, lane);
+  if (wave == 2) store_c16(T0, 17, inverse_row_sum<2, 0>(S, Xs, lane), lane);
+  if (wave == 3) store_c16(T1, 17, inverse_row_sum<2, 1>(S, Xs, lane), lane);
+  __syncthreads();
+  if (wave == 1) inverse_finish<2, 1>(Xs, T1, lane);
+  if (wave == 2) inverse_finish<2, 0>(Xs, T0, lane);
+  if (wave == 3) leaf_inverse<3>(S, Xs, fx.yd, lane);
+  __syncthreads();
+  if (wave == 1) inverse_block<3, 0>(S, Xs, T0, lane);
+  if (wave == 2) inverse_block<3, 1>(S, Xs, T1, lane);
+  if (wave == 3) inverse_block<3, 2>(S, Xs, T2, lane);
+  if (wave == 0) {
+    const double lrr = S[lane * kP + lane];
+    const bool bad = !(lrr > 0.0) || !isfinite(lrr) || !(lrr * lrr > 0.0);
+    const unsigned long long mask = __ballot(bad && kb * kB + lane < n);
+    if (lane == 0 && mask != 0ull && *info == 0) *info = kb * kB + __builtin_ctzll(mask) + 1;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < kB * kB; e += kThreads) {
+    const int r = e >> 6, c = e & 63;
+    const double xv = c <= r ? Xs[r * kP + c] : 0.0;
+    Linv[e] = xv;
+    X[base + (int64_t)r * np + c] = xv;
+    if (c <= r) A[base + (int64_t)r * np + c] = S[r * kP + c];
+  }
+}
+
+struct TileLds {
+  double As[kB][kP];   // As[row][k]
+  double Bs[kB][kP];   // Bs[k][col]
+};
 
 __global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict__ A, double* __restrict__ X,
                                                               double* __restrict__ Linv, int np, int n, int kb,
                                                               int32_t* __restrict__ info) {
-  __shared__ double S[kB * (kB + 1)];
+  __shared__ TileLds t;
+  __shared__ FactorLds fx;
   const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
-  for (int e = threadIdx.x; e < kB * kB; e += kThreads) S[(e >> 6) * (kB + 1) + (e & 63)] = A[base + (int64_t)(e >> 6) * np + (e & 63)];
+  for (int e = threadIdx.x; e < kB * kB; e += kThreads) t.As[e >> 6][e & 63] = A[base + (int64_t)(e >> 6) * np + (e & 63)];
   __syncthreads();
-  factor_diag(S, A, X, Linv, np, n, kb, info);
+  factor_diag(&t.As[0][0], &t.Bs[0][0], fx, A, X, Linv, np, n, kb, info);
 }
 
 __device__ inline void tri_decode(int t, int& ii, int& jj) {
@@ -202,10 +353,6 @@ __device__ inline void tri_decode(int t, int& ii, int& jj) {
   jj = t - r * (r + 1) / 2;
 }
 
-struct TileLds {
-  double As[kB][kB + 1];   // As[row][k]
-  double Bs[kB][kB + 1];   // Bs[k][col]
-};
 
 // One 64 x 64 output block, K = 64, float64 MFMA 16x16x4, 4 waves of 32 x 32:
 //   C = (sub ? C : 0) - / + Aop * (transB ? B^T : B)
@@ -285,12 +432,13 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
 
 // Step kb, second launch: trailing update A[i, j] -= L[i, kb] L[j, kb]^T for
 // kb < j <= i (blocks 0 .. S-1, block 0 is the next diagonal block, which the
-// same workgroup then factors: wave 0 runs factor_diag_wave on it), and
+// same workgroup then factors and inverts with factor_diag), and
 // T[i, j] -= L[i, kb] X[kb, j] for i > kb, j <= kb (the rest).
 __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restrict__ A, double* __restrict__ X,
                                                                double* __restrict__ Linv, int np, int n, int nbk,
                                                                int kb, int32_t* __restrict__ info) {
   __shared__ TileLds t;
+  __shared__ FactorLds fx;
   const int T = nbk - kb - 1;
   const int S = T * (T + 1) / 2;
   const int b = blockIdx.x;
@@ -305,7 +453,7 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     gemm_tile64(t, pa, np, pb, np, true, pc, np, true, keep);
     if (b == 0) {
       __syncthreads();
-      factor_diag(&t.As[0][0], A, X, Linv, np, n, kb + 1, info);
+      factor_diag(&t.As[0][0], &t.Bs[0][0], fx, A, X, Linv, np, n, kb + 1, info);
     }
   } else {
     const int e = b - S;
