@@ -40,14 +40,42 @@ constexpr int kPitch32 = kKt32 + 1;
 // are split and the splits are summed in float64.
 constexpr int64_t kMaxSplitTokens = 32768;
 
+// Upper-triangle tile t -> (I, J), I <= J.  Tiles are numbered by
+// super-blocks of kGroup x kGroup bands (super-blocks row-major, tiles
+// row-major inside each), so that the ~32 consecutive tiles one XCD runs at a
+// time touch about 12 bands instead of all of them and mostly hit its L2.
+constexpr int kGroup = 8;
 __device__ inline void tile_coords(int t, int nb, int& I, int& J) {
-  int i = 0;
-  while (t >= nb - i) {
-    t -= nb - i;
-    ++i;
+  const int ng = (nb + kGroup - 1) / kGroup;
+  I = J = 0;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int i0 = gi * kGroup, i1 = min(nb, i0 + kGroup);
+    for (int gj = gi; gj < ng; ++gj) {
+      const int j0 = gj * kGroup, j1 = min(nb, j0 + kGroup);
+      if (gj > gi) {
+        const int w = j1 - j0, cnt = (i1 - i0) * w;
+        if (t < cnt) {
+          I = i0 + t / w;
+          J = j0 + t % w;
+          return;
+        }
+        t -= cnt;
+      } else {
+        const int w = i1 - i0, cnt = w * (w + 1) / 2;
+        if (t < cnt) {
+          int i = i0;
+          while (t >= i1 - i) {
+            t -= i1 - i;
+            ++i;
+          }
+          I = i;
+          J = i + t;
+          return;
+        }
+        t -= cnt;
+      }
+    }
   }
-  I = i;
-  J = i + t;
 }
 
 template <int DT> struct Mfma16;
@@ -257,6 +285,7 @@ constexpr int kNBuf = 2;                        // LDS stage buffers (kNBuf * kS
 constexpr int kAhead = kNBuf - 1;               // stages loaded ahead
 constexpr int kStageBytes = kKtD * kRowBytes;
 constexpr int kRowsPerWave = kKtD / 4;          // direct loads per wave per stage
+constexpr int kDirectLdsBytes = kNBuf * kStageBytes;
 
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4;
@@ -333,48 +362,36 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
   float* dst = partial + ((int64_t)split * ntiles + tile) * (int64_t)kTileElems;
   const int64_t nstages = (t_end - t_begin + kKtD - 1) / kKtD;
 
-  // Waits until stage st's loads have landed while the loads of the (up to
-  // kAhead - 1) stages issued after it may stay in flight.  Each full stage
-  // issues exactly kRowsPerWave loads per wave; a partial (last) stage issues
-  // fewer, so it is counted as 0, which only makes the wait stricter.
-  auto full = [&](int64_t st) { return st < nstages && t_begin + (st + 1) * kKtD <= t_end; };
-  auto wait_for = [&](int64_t st) {
-    int later = 0;
-#pragma unroll
-    for (int i = 1; i < kAhead; ++i) later += full(st + i) ? 1 : 0;
-    static_assert(kAhead <= 3, "wait_for handles up to two later stages");
-    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  };
-
-  // Prologue: stages 0 .. kAhead-1 in flight; wait for stage 0.
-#pragma unroll
-  for (int i = 0; i < kAhead; ++i)
-    if (i < nstages) issue_stage(i, t_begin + i * kKtD);
-  wait_for(0);
+  // Pipeline (two LDS buffers): the loads of stage s+1 are in flight while
+  // stage s is multiplied.  The one barrier per stage sits inside the last
+  // 16-token step, after its first eight MFMAs: by then every wave holds that
+  // step's fragments in registers (so buffer s may be refilled) and has
+  // waited for its own loads of stage s+1 (so after the barrier all of stage
+  // s+1 is visible).  The loads of stage s+2 and the fragment reads of stage
+  // s+1's first step are then issued between the last eight MFMAs.
+  static_assert(kNBuf == 2 && kKtD == 64, "pipeline written for two 64-token buffers");
+  if (nstages > 0) issue_stage(0, t_begin);
+  if (nstages > 1) issue_stage(1, t_begin + kKtD);
+  // Stage 0 must land; a full stage 1 (kRowsPerWave loads per wave) may stay
+  // in flight.  A partial stage issues fewer loads, so wait for everything.
+  if (nstages > 1 && t_begin + 2 * kKtD <= t_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
+  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   __syncthreads();
+  u32x4 fa[2][4], fb[2][4];
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(0, a_off, 0, rb);
+#pragma unroll
+  for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(0, b_off, 0, cb);
   for (int64_t s = 0; s < nstages; ++s) {
-    const int buf = (int)(s % kNBuf);
-    const bool fill = s + kAhead < nstages;
-    // Fragments of 16-token step kk live in slot kk % 2; the 16 transposing
-    // reads of step kk+1 are issued between the 16 MFMAs of step kk, and the
-    // loads of stage s+kAhead between those of step 0.
-    u32x4 fa[2][4], fb[2][4];
+    const int buf = (int)(s & 1);
+    const bool more = s + 1 < nstages;
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(buf, a_off, 0, rb);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(buf, b_off, 0, cb);
-#pragma unroll
-    for (int kk = 0; kk < kKtD / 16; ++kk) {
+    for (int kk = 0; kk < 3; ++kk) {
       const int c = kk & 1, nx = c ^ 1;
-      if (kk == 0 && fill) issue_stage((buf + kAhead) % kNBuf, t_begin + (s + kAhead) * kKtD);
-      if (kk + 1 < kKtD / 16) {
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) fa[nx][rb] = frag(buf, a_off, kk + 1, rb);
+      for (int rb = 0; rb < 4; ++rb) fa[nx][rb] = frag(buf, a_off, kk + 1, rb);
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) fb[nx][cb] = frag(buf, b_off, kk + 1, cb);
-      }
+      for (int cb = 0; cb < 4; ++cb) fb[nx][cb] = frag(buf, b_off, kk + 1, cb);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -383,13 +400,32 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
       for (int m = 0; m < 16; ++m) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global (direct-to-LDS) load
         __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // address arithmetic
       }
     }
-    // Stage s+1 must have landed; later stages' loads may stay in flight.
-    wait_for(s + 1);
-    __syncthreads();
+    // Last step (fragments in slot 1): first half of its MFMAs.
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[1][rb], fb[1][cb], acc[rb][cb]);
+    if (more) {
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));           // own loads of stage s+1
+      __syncthreads();
+      if (s + 2 < nstages) issue_stage(buf, t_begin + (s + 2) * kKtD);
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(buf ^ 1, a_off, 0, rb);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(buf ^ 1, b_off, 0, cb);
+    }
+#pragma unroll
+    for (int rb = 2; rb < 4; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[1][rb], fb[1][cb], acc[rb][cb]);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);     // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
+    }
   }
   store_acc(acc, dst, wave, lane);
 }
@@ -591,15 +627,15 @@ extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* 
       if (!attr_done[which]) {
         const void* fn = x_dtype == GPTQ_BF16 ? reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_BF16>)
                                               : reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_F16>);
-        GPTQ_TRY_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kNBuf * kStageBytes));
+        GPTQ_TRY_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDirectLdsBytes));
         attr_done[which] = true;
       }
       if (x_dtype == GPTQ_BF16)
-        syrk16_direct_kernel<GPTQ_BF16><<<(unsigned)p.launched, kThreads, kNBuf * kStageBytes, st>>>(
+        syrk16_direct_kernel<GPTQ_BF16><<<(unsigned)p.launched, kThreads, kDirectLdsBytes, st>>>(
             static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit, p.tok_per_split,
             partial, p.launched);
       else
-        syrk16_direct_kernel<GPTQ_F16><<<(unsigned)p.launched, kThreads, kNBuf * kStageBytes, st>>>(
+        syrk16_direct_kernel<GPTQ_F16><<<(unsigned)p.launched, kThreads, kDirectLdsBytes, st>>>(
             static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit, p.tok_per_split,
             partial, p.launched);
     } else if (x_dtype == GPTQ_BF16)
