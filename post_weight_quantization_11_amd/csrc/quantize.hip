@@ -21,6 +21,8 @@
 // reading and rewriting the whole remaining weight matrix per block.
 #include "common.h"
 
+#include <type_traits>
+
 namespace gptq {
 namespace {
 
@@ -56,6 +58,19 @@ __device__ inline float quant_code(float w, float s, float inv_s, float z, float
   const float r = __builtin_fmaf(-q0, s, w);
   const float q = __builtin_fmaf(r, inv_s, q0);
   return fminf(fmaxf(rintf(q) + z, 0.f), maxq);
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for_impl(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for_impl<I + 1, N>(f);
+  }
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl<0, N>(f);
 }
 
 // Wp[r][j] = W[r][perm[j]] as float32 (processing order).
@@ -201,9 +216,35 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
 
-  for (int e = tid; e < kBS * kBS; e += kThreads) {
-    const int i = e >> 7, j = e & (kBS - 1);
-    Ud[i][j] = (i < bw && j < bw && j >= i) ? U[(int64_t)(c0 + i) * n + c0 + j] : 0.f;
+  {
+    // U's diagonal block, upper triangle (zero below it and beyond bw): 16
+    // float4 slots per thread, every load issued before the first LDS store.
+    const bool vecu = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
+    constexpr int kUSlots = kBS * kBS / 4 / kThreads;
+    floatx4 uv[kUSlots];
+#pragma unroll
+    for (int q = 0; q < kUSlots; ++q) {
+      const int e = tid + kThreads * q;
+      const int i = e >> 5, j = (e & 31) * 4;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (i < bw && j + 3 >= i) {
+        const float* p = U + (int64_t)(c0 + i) * n + c0 + j;
+        if (vecu && j + 4 <= bw) {
+          v = *reinterpret_cast<const floatx4*>(p);
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[k] = j + k < bw ? p[k] : 0.f;
+        }
+      }
+      uv[q] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < kUSlots; ++q) {
+      const int e = tid + kThreads * q;
+      const int i = e >> 5, j = (e & 31) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
+    }
   }
   for (int j = tid; j < kBS; j += kThreads)
     invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
@@ -226,18 +267,26 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
       }
       t[q] = v;
     }
-    for (int sp = 0; sp < nsplit; ++sp) {
-      floatx4 pv[kSlots];
+    // Partial products of the update, split by split in split order; four
+    // splits' loads are in flight at a time.
+    auto load_split = [&](int sp, floatx4 (&pv)[kSlots]) {
 #pragma unroll
       for (int q = 0; q < kSlots; ++q) {
         const int e = lane + 64 * q;
         const int rr = e >> 5, c = (e & 31) * 4;
         const int64_t row = row0 + rr;
-        pv[q] = row < m ? *reinterpret_cast<const floatx4*>(P + ((int64_t)sp * m + row) * kBS + c)
-                        : floatx4{0.f, 0.f, 0.f, 0.f};
+        pv[q] = (sp < nsplit && row < m) ? *reinterpret_cast<const floatx4*>(P + ((int64_t)sp * m + row) * kBS + c)
+                                         : floatx4{0.f, 0.f, 0.f, 0.f};
       }
+    };
+    for (int sp = 0; sp < nsplit; sp += 4) {
+      floatx4 pv[4][kSlots];
 #pragma unroll
-      for (int q = 0; q < kSlots; ++q) t[q] -= pv[q];
+      for (int u = 0; u < 4; ++u) load_split(sp + u, pv[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < kSlots; ++q) t[q] -= pv[u][q];
     }
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
@@ -263,7 +312,15 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   const bool vec_codes = (n & 15) == 0 && codes_aligned;
   const bool vec_e = (n & 3) == 0;
 
-  for (int sb = 0; sb < nsb; ++sb) {
+  // One 16-column sub-block: group statistics at a group start, the
+  // sequential columns (lane r < 16 owns row r), the codes/E stores and the
+  // MFMA push of the sub-block's errors into the block's later columns.  With
+  // FULL (a whole 128-column block) sb is a compile-time constant, every loop
+  // bound is fixed and the next column's U row is read ahead of the current
+  // column's arithmetic.
+  auto sub_block = [&](auto sbc, auto fullc) {
+    constexpr bool FULL = decltype(fullc)::value;
+    const int sb = sbc;
     const int j0 = sb * kSB;
     if (g > 0 && ((c0 + j0) % g) == 0) {
       // group range over the current values; g is a multiple of 16 and the
@@ -295,19 +352,46 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
     for (int jj = 0; jj < kSB; ++jj) w[jj] = T[wave][r][j0 + jj];
     float eb[kSB];
     uint32_t cw[kSB / 4] = {0u, 0u, 0u, 0u};
+    if constexpr (FULL) {
+      float un[kSB];
+      float idn = invd[j0];
 #pragma unroll
-    for (int jj = 0; jj < kSB; ++jj) {
-      if (j0 + jj < bw) {
+      for (int kk = 0; kk < kSB; ++kk) un[kk] = Ud[j0][j0 + kk];
+#pragma unroll
+      for (int jj = 0; jj < kSB; ++jj) {
+        float uc[kSB];
+#pragma unroll
+        for (int kk = 0; kk < kSB; ++kk) uc[kk] = un[kk];
+        const float idc = idn;
+        if (jj + 1 < kSB) {
+          idn = invd[j0 + jj + 1];
+#pragma unroll
+          for (int kk = jj + 2; kk < kSB; ++kk) un[kk] = Ud[j0 + jj + 1][j0 + kk];
+        }
         const float c = quant_code(w[jj], s, inv_s, z, maxq);
         const float what = s * (c - z);
-        const float e = (w[jj] - what) * invd[j0 + jj];
+        const float e = (w[jj] - what) * idc;
         eb[jj] = active ? e : 0.f;
         loss = __builtin_fmaf(e, e, loss);
         cw[jj >> 2] |= (uint32_t)c << (8 * (jj & 3));
 #pragma unroll
-        for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, Ud[j0 + jj][j0 + kk], w[kk]);
-      } else {
-        eb[jj] = 0.f;
+        for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, uc[kk], w[kk]);
+      }
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < kSB; ++jj) {
+        if (j0 + jj < bw) {
+          const float c = quant_code(w[jj], s, inv_s, z, maxq);
+          const float what = s * (c - z);
+          const float e = (w[jj] - what) * invd[j0 + jj];
+          eb[jj] = active ? e : 0.f;
+          loss = __builtin_fmaf(e, e, loss);
+          cw[jj >> 2] |= (uint32_t)c << (8 * (jj & 3));
+#pragma unroll
+          for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, Ud[j0 + jj][j0 + kk], w[kk]);
+        } else {
+          eb[jj] = 0.f;
+        }
       }
     }
     if (active) {
@@ -336,7 +420,7 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
     // Push the sub-block's errors into the block's later columns:
     // T[:, ct] -= Eb * Ud[j0:j0+16, ct] for each later 16-column tile ct.
     // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, column l%16.
-    for (int ct = sb + 1; ct < nsb; ++ct) {
+    auto push_tile = [&](int ct) {
       floatx4 acc;
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = T[wave][4 * (lane >> 4) + i][ct * kSB + (lane & 15)];
@@ -349,10 +433,21 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) T[wave][4 * (lane >> 4) + i][ct * kSB + (lane & 15)] = acc[i];
+    };
+    if constexpr (FULL) {
+#pragma unroll
+      for (int ct = sbc + 1; ct < kBS / kSB; ++ct) push_tile(ct);
+    } else {
+      for (int ct = sb + 1; ct < nsb; ++ct) push_tile(ct);
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (bw == kBS) {
+    static_for<kBS / kSB>([&](auto sbc) { sub_block(sbc, std::true_type{}); });
+  } else {
+    for (int sb = 0; sb < nsb; ++sb) sub_block(sb, std::false_type{});
   }
   if (active && row_loss != nullptr) row_loss[row] = (kb == 0 ? 0.f : row_loss[row]) + 0.5f * loss;
 }
