@@ -112,21 +112,28 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const void* __restrict__ 
   }
 }
 
-// P[sp][r][c] = sum_{k in split sp} E[r][k] * U[k][c0 + c]  (128 x 128 tile per
-// workgroup, 4 waves of 64 x 64, fp32 MFMA 32x32x2, K staged 16 at a time).
+// P[sp][r][c] = sum_{k in split sp} E[r][k] * U[k][c0 + c]: a 128 x 128 tile
+// per workgroup (4 waves of 64 x 64, fp32 MFMA 32x32x2).  K is staged 32 at a
+// time through two LDS buffers: the next stage's E and U slabs are loaded
+// into registers while the current stage is multiplied, then stored to the
+// other buffer, with one barrier per stage.  A split covers whole stages.
+constexpr int kUK = 32;          // K per stage
+constexpr int kAP = kUK + 1;     // LDS pitch of the E slab (floats)
+
 __global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restrict__ E,
                                                           const float* __restrict__ U, int m, int n, int kb,
-                                                          int kblocks_per_split, float* __restrict__ P) {
+                                                          int stages_per_split, float* __restrict__ P) {
   const int mt = blockIdx.x, sp = blockIdx.y;
   const int c0 = kb * kBS;
   const int bw = min(kBS, n - c0);
-  const int k_begin = sp * kblocks_per_split * kBS;
-  const int k_end = min(c0, k_begin + kblocks_per_split * kBS);
+  const int k_begin = sp * stages_per_split * kUK;
+  const int k_end = min(c0, k_begin + stages_per_split * kUK);
   const int row0 = mt * 128;
-  const bool vec = (n & 3) == 0;
+  const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(E) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(U) & 15) == 0;
 
-  __shared__ float As[128][17];
-  __shared__ __attribute__((aligned(16))) float Bs[16][kTP];
+  __shared__ float As[2][128][kAP];
+  __shared__ __attribute__((aligned(16))) float Bs[2][kUK][kTP];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1;
   floatx16 acc[2][2];
@@ -135,28 +142,26 @@ __global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restric
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = floatx16{};
 
-  for (int k0 = k_begin; k0 < k_end; k0 += 16) {
+  // Stage slabs: E 128 x 32 and U 32 x 128, 1024 float4 each, 4 per thread.
+  floatx4 ea[4], ub[4];
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid * 2 + i;          // 512 float4 slots: 128 rows x 4
-      const int r = e >> 2, kq = e & 3;
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e >> 3, k = (e & 7) * 4;
       const int64_t row = row0 + r;
       floatx4 v = {0.f, 0.f, 0.f, 0.f};
       if (row < m) {
-        const float* p = E + row * n + k0 + kq * 4;
+        const float* p = E + row * n + k0 + k;
         if (vec) v = *reinterpret_cast<const floatx4*>(p);
         else v = floatx4{p[0], p[1], p[2], p[3]};
       }
-      As[r][kq * 4 + 0] = v[0];
-      As[r][kq * 4 + 1] = v[1];
-      As[r][kq * 4 + 2] = v[2];
-      As[r][kq * 4 + 3] = v[3];
+      ea[i] = v;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid * 2 + i;          // 512 float4 slots: 16 k x 32
-      const int kk = e >> 5, cq = e & 31;
-      const int c = cq * 4;
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int kk = e >> 5, c = (e & 31) * 4;
       const float* p = U + (int64_t)(k0 + kk) * n + c0 + c;
       floatx4 v = {0.f, 0.f, 0.f, 0.f};
       if (vec && c + 4 <= bw) {
@@ -165,23 +170,51 @@ __global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restric
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (c + t < bw) ? p[t] : 0.f;
       }
-      *reinterpret_cast<floatx4*>(&Bs[kk][c]) = v;
+      ub[i] = v;
     }
-    __syncthreads();
+  };
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int k2 = 0; k2 < 8; ++k2) {
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int r = e >> 3, k = (e & 7) * 4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) As[buf][r][k + t] = ea[i][t];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = tid + 256 * i;
+      const int kk = e >> 5, c = (e & 31) * 4;
+      *reinterpret_cast<floatx4*>(&Bs[buf][kk][c]) = ub[i];
+    }
+  };
+
+  const int nst = (k_end - k_begin) / kUK;
+  if (nst > 0) {
+    gload(k_begin);
+    lstore(0);
+  }
+  __syncthreads();
+  for (int s = 0; s < nst; ++s) {
+    const int buf = s & 1;
+    const bool next = s + 1 < nst;
+    if (next) gload(k_begin + (s + 1) * kUK);
+#pragma unroll
+    for (int k2 = 0; k2 < kUK / 2; ++k2) {
       const int k = k2 * 2 + (lane >> 5);
       float a[2], b[2];
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) a[rb] = As[wr * 64 + rb * 32 + (lane & 31)][k];
+      for (int rb = 0; rb < 2; ++rb) a[rb] = As[buf][wr * 64 + rb * 32 + (lane & 31)][k];
 #pragma unroll
-      for (int cb = 0; cb < 2; ++cb) b[cb] = Bs[k][wc * 64 + cb * 32 + (lane & 31)];
+      for (int cb = 0; cb < 2; ++cb) b[cb] = Bs[buf][k][wc * 64 + cb * 32 + (lane & 31)];
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
     }
+    // Buffer buf ^ 1 was last read in stage s - 1, before the previous barrier.
+    if (next) lstore(buf ^ 1);
     __syncthreads();
   }
   // 32x32 accumulator: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
@@ -210,15 +243,21 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   __shared__ float invd[kBS];
   __shared__ __attribute__((aligned(16))) float T[kWaves][kRowsPerWave][kTP];
   __shared__ float Eb[kWaves][kRowsPerWave][kSB + 1];
+  __shared__ float Gs[kWaves][kRowsPerWave][2];
 
   const int c0 = kb * kBS;
   const int bw = min(kBS, n - c0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
 
+  // Loads: U's diagonal block (upper triangle, zero below it and beyond bw;
+  // 16 float4 slots per thread) and the wave's 16 x 128 slab of W are issued
+  // together; then the split-K partial products of the block update are
+  // subtracted, four splits' loads in flight at a time.  Slot q of lane l of
+  // the slab is row (l + 64q) / 32, columns 4*((l + 64q) % 32) .. +3.
+  constexpr int kSlots = kRowsPerWave * kBS / 4 / 64;
+  floatx4 t[kSlots];
   {
-    // U's diagonal block, upper triangle (zero below it and beyond bw): 16
-    // float4 slots per thread, every load issued before the first LDS store.
     const bool vecu = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
     constexpr int kUSlots = kBS * kBS / 4 / kThreads;
     floatx4 uv[kUSlots];
@@ -239,22 +278,6 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
       uv[q] = v;
     }
 #pragma unroll
-    for (int q = 0; q < kUSlots; ++q) {
-      const int e = tid + kThreads * q;
-      const int i = e >> 5, j = (e & 31) * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
-    }
-  }
-  for (int j = tid; j < kBS; j += kThreads)
-    invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
-  {
-    // The wave's 16 x 128 tile: slot q of lane l is row (l + 64q) / 32,
-    // columns 4*((l + 64q) % 32) .. +3; all loads of one split are issued
-    // before any is consumed.
-    constexpr int kSlots = kRowsPerWave * kBS / 4 / 64;
-    floatx4 t[kSlots];
-#pragma unroll
     for (int q = 0; q < kSlots; ++q) {
       const int e = lane + 64 * q;
       const int rr = e >> 5, c = (e & 31) * 4;
@@ -267,8 +290,17 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
       }
       t[q] = v;
     }
-    // Partial products of the update, split by split in split order; four
-    // splits' loads are in flight at a time.
+#pragma unroll
+    for (int q = 0; q < kUSlots; ++q) {
+      const int e = tid + kThreads * q;
+      const int i = e >> 5, j = (e & 31) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
+    }
+  }
+  for (int j = tid; j < kBS; j += kThreads)
+    invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
+  {
     auto load_split = [&](int sp, floatx4 (&pv)[kSlots]) {
 #pragma unroll
       for (int q = 0; q < kSlots; ++q) {
@@ -293,6 +325,33 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
       const int e = lane + 64 * q;
       const int rr = e >> 5, c = (e & 31) * 4;
       *reinterpret_cast<floatx4*>(&T[wave][rr][c]) = t[q];
+    }
+  }
+  // A group that starts at this block and spans it (g a multiple of 128, or
+  // reaching past n): its range is the slab's, reduced across the 32 lanes
+  // that hold a row; lanes 0 and 32 of slot q publish rows 2q and 2q + 1.
+  const bool block_group = g > 0 && (c0 % g) == 0 && (g % kBS == 0 || c0 + g >= n);
+  if (block_group) {
+#pragma unroll
+    for (int q = 0; q < kSlots; ++q) {
+      const int e = lane + 64 * q;
+      const int c = (e & 31) * 4;
+      float mn = INFINITY, mx = -INFINITY;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (c + k < bw) {
+          mn = fminf(mn, t[q][k]);
+          mx = fmaxf(mx, t[q][k]);
+        }
+#pragma unroll
+      for (int off = 16; off > 0; off >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 32));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 32));
+      }
+      if ((lane & 31) == 0) {
+        Gs[wave][2 * q + (lane >> 5)][0] = mn;
+        Gs[wave][2 * q + (lane >> 5)][1] = mx;
+      }
     }
   }
   __syncthreads();
@@ -322,7 +381,14 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
     constexpr bool FULL = decltype(fullc)::value;
     const int sb = sbc;
     const int j0 = sb * kSB;
-    if (g > 0 && ((c0 + j0) % g) == 0) {
+    if (block_group && sb == 0) {
+      grid_from_range(Gs[wave][r][0], Gs[wave][r][1], maxq, s, z, inv_s);
+      if (active) {
+        const int gi = c0 / g;
+        scales[row * G + gi] = s;
+        zeros[row * G + gi] = (uint8_t)z;
+      }
+    } else if (g > 0 && ((c0 + j0) % g) == 0) {
       // group range over the current values; g is a multiple of 16 and the
       // group lies inside the block (tail columns beyond bw are excluded)
       const int gl = min(g, bw - j0);
@@ -461,8 +527,8 @@ QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
   QuantLayout L;
   L.nblocks = (int)ceil_div(n, kBS);
   L.mtiles = (int)ceil_div(m, 128);
-  // Enough K splits for about 512 workgroups in the update GEMM.
-  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1), ceil_div(512, L.mtiles)));
+  // Enough K splits for about one update-GEMM workgroup per CU.
+  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1), ceil_div(256, L.mtiles)));
   const size_t mn = (size_t)m * (size_t)n * sizeof(float);
   L.off_E = 0;
   L.off_Wp = align256(L.off_E + mn);
@@ -541,10 +607,12 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m
   for (int kb = 0; kb < L.nblocks; ++kb) {
     int nsplit = 0;
     if (kb > 0) {
-      const int s_target = std::min(kb, L.smax);
-      const int kbps = (int)ceil_div(kb, s_target);
-      nsplit = (int)ceil_div(kb, kbps);
-      update_gemm_kernel<<<dim3((unsigned)L.mtiles, (unsigned)nsplit), 256, 0, st>>>(E, U, mi, ni, kb, kbps, P);
+      // Split K = 128 kb into nsplit ranges of whole 32-column stages.
+      const int stages = kb * (kBS / kUK);
+      const int s_target = std::min(stages, L.smax);
+      const int sps = (int)ceil_div(stages, s_target);
+      nsplit = (int)ceil_div(stages, sps);
+      update_gemm_kernel<<<dim3((unsigned)L.mtiles, (unsigned)nsplit), 256, 0, st>>>(E, U, mi, ni, kb, sps, P);
       GPTQ_TRY_LAUNCH();
     }
     gptq_status rc;
