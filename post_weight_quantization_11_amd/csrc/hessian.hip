@@ -21,6 +21,8 @@
 // mirrors the upper triangle.
 #include "common.h"
 
+#include <type_traits>
+
 namespace gptq {
 namespace {
 
@@ -272,17 +274,30 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_kernel(
 // moves one token row of both bands, lanes 0-31 the 256 features of band I
 // and lanes 32-63 those of band J, so an LDS row is [band I | band J] (1024
 // bytes, padded to 1088 so that the transposing reads below are free of bank
-// conflicts).  Stages of kKtD tokens rotate through kNBuf LDS buffers and
-// are loaded kNBuf - 1 stages ahead.  MFMA operands are read with ds_read_b64_tr_b16: within each group
-// of 16 lanes, lane j receives element j%4 of the 8-byte chunks addressed by
-// lanes j/4 + 4e (e = 0..3); with lane j addressing token row t0 + j/4 and
+// conflicts).  Lanes whose 8 features lie beyond n copy features 0-7 instead:
+// those LDS columns only feed outputs beyond n, which the reduction drops.
+// MFMA operands are read with ds_read_b64_tr_b16: within each group of 16
+// lanes, lane j receives element j%4 of the 8-byte chunks addressed by lanes
+// j/4 + 4e (e = 0..3); with lane j addressing token row t0 + j/4 and
 // features f + 4*(j%4), it receives tokens t0..t0+3 of feature f + j, i.e. a
-// K-contiguous operand.  Feature chunks beyond n are zeroed once; token rows
-// beyond the split are zeroed when their stage is issued.
+// K-contiguous operand.
+//
+// Pipeline: stages of 32 tokens (two 16-token MFMA steps) rotate through four
+// LDS buffers.  While stage s is multiplied, the loads of stage s+3 (into the
+// buffer stage s-1 used) are issued one per two MFMAs of its first step, so a
+// wave never waits long at a load for the memory pipeline to accept it, and
+// stages s+1 .. s+3 are in flight.  The one barrier per stage sits inside the
+// second step, after its first eight MFMAs: every wave then holds that step's
+// fragments (buffer s may be refilled from the next stage on) and has waited
+// for its own loads of stage s+1 (visible to all after the barrier); the
+// fragment reads of stage s+1's first step overlap the last eight MFMAs.  The
+// last stage of a split may be partial: its rows past the split load the
+// split's last row and are zeroed once they have landed, before the barrier
+// that publishes the stage.  Stages past the split load into buffers that no
+// step reads.
 constexpr int kRowBytes = 1088;
-constexpr int kKtD = 64;                        // tokens per stage
-constexpr int kNBuf = 2;                        // LDS stage buffers (kNBuf * kStageBytes <= 160 KB)
-constexpr int kAhead = kNBuf - 1;               // stages loaded ahead
+constexpr int kKtD = 32;                        // tokens per stage
+constexpr int kNBuf = 4;                        // LDS stage buffers (kNBuf * kStageBytes <= 160 KB)
 constexpr int kStageBytes = kKtD * kRowBytes;
 constexpr int kRowsPerWave = kKtD / 4;          // direct loads per wave per stage
 constexpr int kDirectLdsBytes = kNBuf * kStageBytes;
@@ -298,6 +313,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nb, int ntiles,
     int nsplit, int64_t tok_per_split, float* __restrict__ partial, int64_t launched) {
+  static_assert(kKtD == 32 && kNBuf == 4, "pipeline written for four 32-token buffers");
   const int64_t item = xcd_contiguous(blockIdx.x, launched);
   if (item >= (int64_t)ntiles * nsplit) return;
   const int split = (int)(item / ntiles);
@@ -314,27 +330,22 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
   // This lane's 16-byte chunk in a token row: band I for lanes 0-31, band J for 32-63.
   const int band = lane >> 5;
   const int fchunk = (band == 0 ? I : J) * kTile + (lane & 31) * 8;
-  const bool chunk_ok = fchunk < n;            // n % 8 == 0: a chunk is all in or all out
-  const uint16_t* gsrc = X + (chunk_ok ? fchunk : 0);
+  const uint16_t* gsrc = X + (fchunk < n ? fchunk : 0);   // n % 8 == 0: a chunk is all in or all out
 
-  if (!chunk_ok) {
-    for (int b = 0; b < kNBuf; ++b)
-      for (int r = wave; r < kKtD; r += 4)
-        *reinterpret_cast<u32x4*>(smem + b * kStageBytes + r * kRowBytes + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-  }
-
-  // Wave w copies token rows w*8 .. w*8+7 of a stage.
-  auto issue_stage = [&](int buf, int64_t t0) {
+  // Wave w copies token rows w*8 .. w*8+7 of a stage.  Rows past the split
+  // are clamped to its last row (a valid address); zero_tail then zeroes them
+  // once the wave's own loads have landed.
+  auto load_row = [&](int buf, int64_t t0, int i) {
+    const int r = wave * kRowsPerWave + i;
+    const int64_t t = min(t0 + r, t_end - 1);
+    __builtin_amdgcn_global_load_lds(gsrc + t * ldx, (lds_void*)(smem + buf * kStageBytes + r * kRowBytes), 16, 0, 0);
+  };
+  auto zero_tail = [&](int buf, int64_t t0) {
 #pragma unroll
     for (int i = 0; i < kRowsPerWave; ++i) {
       const int r = wave * kRowsPerWave + i;
-      const int64_t t = t0 + r;
-      unsigned char* dstrow = smem + buf * kStageBytes + r * kRowBytes;
-      if (t < t_end) {
-        if (chunk_ok) __builtin_amdgcn_global_load_lds(gsrc + t * ldx, (lds_void*)dstrow, 16, 0, 0);
-      } else if (chunk_ok) {
-        *reinterpret_cast<u32x4*>(dstrow + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
+      if (t0 + r >= t_end)
+        *reinterpret_cast<u32x4*>(smem + buf * kStageBytes + r * kRowBytes + lane * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   };
 
@@ -361,61 +372,73 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
 
   float* dst = partial + ((int64_t)split * ntiles + tile) * (int64_t)kTileElems;
   const int64_t nstages = (t_end - t_begin + kKtD - 1) / kKtD;
+  // Stage st is full when all its rows lie in the split (kRowsPerWave loads
+  // per wave); only the last stage of a split can be partial.
+  auto full = [&](int64_t st) { return st < nstages && t_begin + (st + 1) * kKtD <= t_end; };
+  // Waits until stage st has landed while the loads of the (at most two)
+  // stages issued after it, up to stage last, may stay in flight; a partial
+  // one is counted as zero, which only makes the wait stricter.
+  auto wait_landed = [&](int64_t st, int64_t last) {
+    const int later = ((st + 1 <= last && full(st + 1)) ? 1 : 0) + ((st + 2 <= last && full(st + 2)) ? 1 : 0);
+    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  };
 
-  // Pipeline (two LDS buffers): the loads of stage s+1 are in flight while
-  // stage s is multiplied.  The one barrier per stage sits inside the last
-  // 16-token step, after its first eight MFMAs: by then every wave holds that
-  // step's fragments in registers (so buffer s may be refilled) and has
-  // waited for its own loads of stage s+1 (so after the barrier all of stage
-  // s+1 is visible).  The loads of stage s+2 and the fragment reads of stage
-  // s+1's first step are then issued between the last eight MFMAs.
-  static_assert(kNBuf == 2 && kKtD == 64, "pipeline written for two 64-token buffers");
-  if (nstages > 0) issue_stage(0, t_begin);
-  if (nstages > 1) issue_stage(1, t_begin + kKtD);
-  // Stage 0 must land; a full stage 1 (kRowsPerWave loads per wave) may stay
-  // in flight.  A partial stage issues fewer loads, so wait for everything.
-  if (nstages > 1 && t_begin + 2 * kKtD <= t_end) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
-  else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __syncthreads();
   u32x4 fa[2][4], fb[2][4];
+  // Prologue: stages 0 .. kNBuf-2 (a stage past the split only loads its
+  // clamped last row again, into a buffer no step reads).
+#pragma unroll
+  for (int st = 0; st < kNBuf - 1; ++st)
+#pragma unroll
+    for (int i = 0; i < kRowsPerWave; ++i) load_row(st, t_begin + st * kKtD, i);
+  wait_landed(0, kNBuf - 2);
+  if (!full(0)) zero_tail(0, t_begin);
+  __syncthreads();
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(0, a_off, 0, rb);
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(0, b_off, 0, cb);
   for (int64_t s = 0; s < nstages; ++s) {
-    const int buf = (int)(s & 1);
-    const bool more = s + 1 < nstages;
+    const int buf = (int)(s % kNBuf);
+    const int pbuf = (int)((s + kNBuf - 1) % kNBuf);      // the buffer stage s-1 used
+    const int64_t pt0 = t_begin + (s + kNBuf - 1) * kKtD;  // stage s+3, loaded into it
+    // First step (slot 0): fragments of the second step into slot 1, and the
+    // loads of stage s+3 one per two MFMAs.
 #pragma unroll
-    for (int kk = 0; kk < 3; ++kk) {
-      const int c = kk & 1, nx = c ^ 1;
+    for (int rb = 0; rb < 4; ++rb) fa[1][rb] = frag(buf, a_off, 1, rb);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) fa[nx][rb] = frag(buf, a_off, kk + 1, rb);
+    for (int cb = 0; cb < 4; ++cb) fb[1][cb] = frag(buf, b_off, 1, cb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) fb[nx][cb] = frag(buf, b_off, kk + 1, cb);
+    for (int i = 0; i < kRowsPerWave; ++i) load_row(pbuf, pt0, i);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb)
+    for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[c][rb], fb[c][cb], acc[rb][cb]);
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[0][rb], fb[0][cb], acc[rb][cb]);
 #pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // address arithmetic
-      }
+    for (int m = 0; m < 8; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct-to-LDS load
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // address arithmetic
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
     }
-    // Last step (fragments in slot 1): first half of its MFMAs.
+    // Second step (slot 1): first half of its MFMAs.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[1][rb], fb[1][cb], acc[rb][cb]);
-    if (more) {
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));           // own loads of stage s+1
+    if (s + 1 < nstages) {
+      // Stages up to s+3 have been issued; stage s+1 must land.
+      wait_landed(s + 1, s + kNBuf - 1);
+      if (!full(s + 1)) zero_tail((int)((s + 1) % kNBuf), t_begin + (s + 1) * kKtD);
       __syncthreads();
-      if (s + 2 < nstages) issue_stage(buf, t_begin + (s + 2) * kKtD);
+      const int nbuf = (int)((s + 1) % kNBuf);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(buf ^ 1, a_off, 0, rb);
+      for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(nbuf, a_off, 0, rb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(buf ^ 1, b_off, 0, cb);
+      for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(nbuf, b_off, 0, cb);
     }
 #pragma unroll
     for (int rb = 2; rb < 4; ++rb)
@@ -427,6 +450,8 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);     // two LDS reads
     }
   }
+  // No load into LDS may still be in flight when the workgroup ends.
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   store_acc(acc, dst, wave, lane);
 }
 
