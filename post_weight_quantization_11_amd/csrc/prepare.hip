@@ -26,6 +26,7 @@ namespace {
 
 constexpr int kB = 64;        // Cholesky block
 constexpr int kThreads = 256;
+constexpr int kUpdateBlocks = 256;  // workgroups of the trailing-update launch (one per CU)
 
 __global__ void init_scalars_kernel(int32_t* info) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *info = 0;
@@ -431,37 +432,145 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
 }
 
 // Step kb, second launch: trailing update A[i, j] -= L[i, kb] L[j, kb]^T for
-// kb < j <= i (blocks 0 .. S-1, block 0 is the next diagonal block, which the
-// same workgroup then factors and inverts with factor_diag), and
-// T[i, j] -= L[i, kb] X[kb, j] for i > kb, j <= kb (the rest).
+// kb < j <= i ("SYRK" tiles) and T[i, j] -= L[i, kb] X[kb, j] for i > kb,
+// j <= kb ("inverse" tiles).  Tile 0 is the next diagonal block; workgroup 0
+// updates it and then factors and inverts it with factor_diag.  The other
+// workgroups loop over the remaining tiles: the operands of the next tile are
+// loaded into registers while the current tile is multiplied from LDS (two
+// LDS buffers, one barrier per tile), and each C block is read before and
+// written after its MFMAs.  No tile reads what another tile of the launch
+// writes.
+struct UpdateLds {
+  double As[2][kB][kP];
+  double Bs[2][kB][kP];
+};
+
+__device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, double* X, const double*& pa,
+                                       const double*& pb, double*& pc, bool& transB) {
+  if (t < S) {
+    int ii, jj;
+    tri_decode(t, ii, jj);
+    const int bi = kb + 1 + ii, bj = kb + 1 + jj;
+    pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
+    pb = A + (int64_t)bj * kB * np + (int64_t)kb * kB;
+    pc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
+    transB = true;
+  } else {
+    const int e = t - S;
+    const int bi = kb + 1 + e / (kb + 1), bj = e % (kb + 1);
+    pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
+    pb = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
+    pc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
+    transB = false;
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restrict__ A, double* __restrict__ X,
                                                                double* __restrict__ Linv, int np, int n, int nbk,
                                                                int kb, int32_t* __restrict__ info) {
-  __shared__ TileLds t;
+  __shared__ union {
+    TileLds t;
+    UpdateLds u;
+  } lds;
   __shared__ FactorLds fx;
   const int T = nbk - kb - 1;
   const int S = T * (T + 1) / 2;
-  const int b = blockIdx.x;
-  if (b < S) {
-    int ii, jj;
-    tri_decode(b, ii, jj);
-    const int bi = kb + 1 + ii, bj = kb + 1 + jj;
-    const double* pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-    const double* pb = A + (int64_t)bj * kB * np + (int64_t)kb * kB;
-    double* pc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
-    double* keep = (b == 0) ? &t.As[0][0] : nullptr;
-    gemm_tile64(t, pa, np, pb, np, true, pc, np, true, keep);
-    if (b == 0) {
-      __syncthreads();
-      factor_diag(&t.As[0][0], &t.Bs[0][0], fx, A, X, Linv, np, n, kb + 1, info);
+  const int total = S + T * (kb + 1);
+  if (blockIdx.x == 0) {
+    const double *pa, *pb;
+    double* pc;
+    bool tb;
+    update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb);
+    gemm_tile64(lds.t, pa, np, pb, np, tb, pc, np, true, &lds.t.As[0][0]);
+    __syncthreads();
+    factor_diag(&lds.t.As[0][0], &lds.t.Bs[0][0], fx, A, X, Linv, np, n, kb + 1, info);
+    return;
+  }
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int stride = (int)gridDim.x - 1;
+  double ra[16], rb[16];
+  bool rtb = false;
+  auto load_ops = [&](int t) {
+    const double *pa, *pb;
+    double* pc;
+    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, rtb);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = tid + kThreads * i;
+      const int r = e >> 6, c = e & 63;
+      ra[i] = pa[(int64_t)r * np + c];
+      rb[i] = pb[(int64_t)r * np + c];
     }
-  } else {
-    const int e = b - S;
-    const int bi = kb + 1 + e / (kb + 1), bj = e % (kb + 1);
-    const double* pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-    const double* pb = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
-    double* pc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
-    gemm_tile64(t, pa, np, pb, np, false, pc, np, true, nullptr);
+  };
+  auto store_ops = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int e = tid + kThreads * i;
+      const int r = e >> 6, c = e & 63;
+      lds.u.As[buf][r][c] = ra[i];
+      if (rtb)
+        lds.u.Bs[buf][c][r] = rb[i];
+      else
+        lds.u.Bs[buf][r][c] = rb[i];
+    }
+  };
+  int t = (int)blockIdx.x;
+  if (t < total) {
+    load_ops(t);
+    store_ops(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (t < total) {
+    const int tn = t + stride;
+    const double *pa, *pb;
+    double* pc;
+    bool tb;
+    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, tb);
+    if (tn < total) load_ops(tn);
+    // C block in the accumulator layout (row (lane>>4) + 4r of each 16 x 16
+    // block, column lane & 15), read ahead of the MFMAs.
+    doublex4 cv[2][2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cv[ti][tj][r] = pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)];
+    doublex4 acc[2][2];
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = doublex4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k4 = 0; k4 < kB / 4; ++k4) {
+      const int k = k4 * 4 + (lane >> 4);
+      double av[2], bv[2];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti) av[ti] = lds.u.As[buf][wr * 32 + ti * 16 + (lane & 15)][k];
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj) bv[tj] = lds.u.Bs[buf][k][wc * 32 + tj * 16 + (lane & 15)];
+#pragma unroll
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+          acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ti], bv[tj], acc[ti][tj], 0, 0, 0);
+    }
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)] =
+              cv[ti][tj][r] - acc[ti][tj][r];
+    // Buffer buf ^ 1 was last read before the previous barrier.
+    if (tn < total) store_ops(buf ^ 1);
+    __syncthreads();
+    buf ^= 1;
+    t = tn;
   }
 }
 
@@ -532,7 +641,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
     const int T = nbk - kb - 1;
     if (T + kb > 0) chol_panel_kernel<<<(unsigned)(T + kb), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
     if (T > 0)
-      chol_update_kernel<<<(unsigned)(T * (T + 1) / 2 + T * (kb + 1)), kThreads, 0, st>>>(A, X, Linv, np, ni, nbk,
+      chol_update_kernel<<<(unsigned)std::min(T * (T + 1) / 2 + T * (kb + 1), kUpdateBlocks), kThreads, 0, st>>>(A, X, Linv, np, ni, nbk,
                                                                                          kb, info);
     GPTQ_TRY_LAUNCH();
   }
