@@ -55,6 +55,31 @@ def to_device(st):
     return torch.from_numpy(st.raw).cuda()
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hessian_attn_proj_4096_traffic.md")
+TRAFFIC_SOURCES = [os.path.join(ROOT, "post_weight_quantization_11_amd", "csrc", f) for f in ("hessian.hip", "common.h")]
+
+
+def measured_traffic(config):
+    """HBM bytes per Hessian call from the committed FETCH_SIZE/WRITE_SIZE
+    profile of the 4096-wide workload, or None when that profile was taken on
+    other kernel sources than the ones built here (or for other workloads)."""
+    import hashlib
+    if config != 2 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.split(":")[0].strip() in ("traffic_bytes_per_launch", "sources_sha256"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    if fields.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
 def bits_of(levels):
     return {3: 2, 4: 2, 8: 3, 16: 4}[levels]
 
@@ -247,7 +272,8 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(args.config),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)",
             "algorithmic": f"n(n+1)N = {flops_h:.4g} flop per launch",
         },
         "sanity": {"codes_in_range": codes_ok, "finite": finite},
