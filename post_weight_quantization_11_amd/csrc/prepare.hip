@@ -412,22 +412,51 @@ __device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, co
 }
 
 // Step kb, first launch: panel L[i, kb] = A[i, kb] inv(L_kk)^T for i > kb
-// (blocks 0 .. T-1), and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
-// for j < kb (blocks T .. T+kb-1).
+// (tiles 0 .. T-1) and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
+// for j < kb (tiles T .. T+kb-1), four workgroups per 64 x 64 tile.  A
+// workgroup owns 16 output rows of a panel tile (which read only those rows)
+// or 16 output columns of an inverse-row tile (which read only those
+// columns), so results go back in place without races; each wave computes
+// one 16 x 16 block with 16 float64 MFMAs.
 __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict__ A, double* __restrict__ X,
                                                               const double* __restrict__ Linv, int np, int nbk,
                                                               int kb) {
-  __shared__ TileLds t;
+  __shared__ double Ls[kB][kP];      // inv(L_kk)
+  __shared__ double Ps[kB][17];      // the tile's 16 rows (transposed) or 16 columns, [k][16]
   const int T = nbk - kb - 1;
-  const int b = blockIdx.x;
-  if (b < T) {
-    const int bi = kb + 1 + b;
-    double* p = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-    gemm_tile64(t, p, np, Linv, kB, true, p, np, false, nullptr);
-  } else {
-    const int bj = b - T;
-    double* p = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
-    gemm_tile64(t, Linv, kB, p, np, false, p, np, false, nullptr);
+  const int tile = (int)(blockIdx.x >> 2), part = (int)(blockIdx.x & 3);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const bool panel = tile < T;
+  double* p = panel ? A + (int64_t)(kb + 1 + tile) * kB * np + (int64_t)kb * kB + (int64_t)part * 16 * np
+                    : X + (int64_t)kb * kB * np + (int64_t)(tile - T) * kB + part * 16;
+  for (int e = tid; e < kB * kB; e += kThreads) Ls[e >> 6][e & 63] = Linv[e];
+  for (int e = tid; e < kB * 16; e += kThreads) {
+    if (panel) {
+      const int r = e >> 6, k = e & 63;
+      Ps[k][r] = p[(int64_t)r * np + k];
+    } else {
+      const int k = e >> 4, c = e & 15;
+      Ps[k][c] = p[(int64_t)k * np + c];
+    }
+  }
+  __syncthreads();
+  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int k4 = 0; k4 < kB / 4; ++k4) {
+    const int k = k4 * 4 + (lane >> 4);
+    // panel: C = P Linv^T (A element P[row][k], B element Linv[col][k]);
+    // inverse row: C = Linv P (A element Linv[row][k], B element P[k][col]).
+    const double a = panel ? Ps[k][lane & 15] : Ls[wave * 16 + (lane & 15)][k];
+    const double b = panel ? Ls[wave * 16 + (lane & 15)][k] : Ps[k][lane & 15];
+    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = (lane >> 4) + 4 * r, col = lane & 15;
+    if (panel)
+      p[(int64_t)row * np + wave * 16 + col] = acc[r];
+    else
+      p[(int64_t)(wave * 16 + row) * np + col] = acc[r];
   }
 }
 
@@ -446,11 +475,12 @@ struct UpdateLds {
 };
 
 __device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, double* X, const double*& pa,
-                                       const double*& pb, double*& pc, bool& transB) {
+                                       const double*& pb, double*& pc, bool& transB, int& bi_out) {
   if (t < S) {
     int ii, jj;
     tri_decode(t, ii, jj);
     const int bi = kb + 1 + ii, bj = kb + 1 + jj;
+    bi_out = bi;
     pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
     pb = A + (int64_t)bj * kB * np + (int64_t)kb * kB;
     pc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
@@ -458,6 +488,7 @@ __device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, 
   } else {
     const int e = t - S;
     const int bi = kb + 1 + e / (kb + 1), bj = e % (kb + 1);
+    bi_out = bi;
     pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
     pb = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
     pc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
@@ -480,7 +511,8 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     const double *pa, *pb;
     double* pc;
     bool tb;
-    update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb);
+    int bi;
+    update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb, bi);
     gemm_tile64(lds.t, pa, np, pb, np, tb, pc, np, true, &lds.t.As[0][0]);
     __syncthreads();
     factor_diag(&lds.t.As[0][0], &lds.t.Bs[0][0], fx, A, X, Linv, np, n, kb + 1, info);
@@ -488,18 +520,27 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1;
-  const int stride = (int)gridDim.x - 1;
+  // Workgroup b takes a contiguous range of the row-major tile list, so
+  // consecutive tiles mostly share their block row bi and with it the
+  // L[bi, kb] operand, which is then not loaded again.
+  const int per = (total - 1 + (int)gridDim.x - 2) / ((int)gridDim.x - 1);
+  const int t_lo = 1 + ((int)blockIdx.x - 1) * per;
+  const int t_hi = min(total, t_lo + per);
   double ra[16], rb[16];
   bool rtb = false;
+  int ra_row = -1;
   auto load_ops = [&](int t) {
     const double *pa, *pb;
     double* pc;
-    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, rtb);
+    int bi;
+    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, rtb, bi);
+    const bool new_a = bi != ra_row;
+    ra_row = bi;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = tid + kThreads * i;
       const int r = e >> 6, c = e & 63;
-      ra[i] = pa[(int64_t)r * np + c];
+      if (new_a) ra[i] = pa[(int64_t)r * np + c];
       rb[i] = pb[(int64_t)r * np + c];
     }
   };
@@ -515,20 +556,21 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
         lds.u.Bs[buf][r][c] = rb[i];
     }
   };
-  int t = (int)blockIdx.x;
-  if (t < total) {
+  int t = t_lo;
+  if (t < t_hi) {
     load_ops(t);
     store_ops(0);
   }
   __syncthreads();
   int buf = 0;
-  while (t < total) {
-    const int tn = t + stride;
+  while (t < t_hi) {
+    const int tn = t + 1;
     const double *pa, *pb;
     double* pc;
     bool tb;
-    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, tb);
-    if (tn < total) load_ops(tn);
+    int bi;
+    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, tb, bi);
+    if (tn < t_hi) load_ops(tn);
     // C block in the accumulator layout (row (lane>>4) + 4r of each 16 x 16
     // block, column lane & 15), read ahead of the MFMAs.
     doublex4 cv[2][2];
@@ -567,7 +609,7 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
           pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)] =
               cv[ti][tj][r] - acc[ti][tj][r];
     // Buffer buf ^ 1 was last read before the previous barrier.
-    if (tn < total) store_ops(buf ^ 1);
+    if (tn < t_hi) store_ops(buf ^ 1);
     __syncthreads();
     buf ^= 1;
     t = tn;
@@ -639,7 +681,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, 0, info);
   for (int kb = 0; kb < nbk; ++kb) {
     const int T = nbk - kb - 1;
-    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(T + kb), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
+    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(4 * (T + kb)), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
     if (T > 0)
       chol_update_kernel<<<(unsigned)std::min(T * (T + 1) / 2 + T * (kb + 1), kUpdateBlocks), kThreads, 0, st>>>(A, X, Linv, np, ni, nbk,
                                                                                          kb, info);
