@@ -120,20 +120,25 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const void* __restrict__ 
 constexpr int kUK = 32;          // K per stage
 constexpr int kAP = kUK + 1;     // LDS pitch of the E slab (floats)
 
-__global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restrict__ E,
-                                                          const float* __restrict__ U, int m, int n, int kb,
-                                                          int stages_per_split, float* __restrict__ P) {
-  const int mt = blockIdx.x, sp = blockIdx.y;
+struct GemmLds {
+  float As[2][128][kAP];
+  __attribute__((aligned(16))) float Bs[2][kUK][kTP];
+};
+
+// Split sp of the row tile mt: K range [sp * stages_per_split * 32, ...)
+// clipped to k_limit, for the columns of block kb.
+__device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, const float* __restrict__ U, int m,
+                                                 int n, int kb, int k_limit, int stages_per_split,
+                                                 float* __restrict__ P, int mt, int sp, GemmLds& L) {
   const int c0 = kb * kBS;
   const int bw = min(kBS, n - c0);
   const int k_begin = sp * stages_per_split * kUK;
-  const int k_end = min(c0, k_begin + stages_per_split * kUK);
+  const int k_end = min(k_limit, k_begin + stages_per_split * kUK);
   const int row0 = mt * 128;
   const bool vec = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(E) & 15) == 0 &&
                    (reinterpret_cast<uintptr_t>(U) & 15) == 0;
-
-  __shared__ float As[2][128][kAP];
-  __shared__ __attribute__((aligned(16))) float Bs[2][kUK][kTP];
+  auto& As = L.As;
+  auto& Bs = L.Bs;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int wr = wave >> 1, wc = wave & 1;
   floatx16 acc[2][2];
@@ -233,22 +238,36 @@ __global__ __launch_bounds__(256) void update_gemm_kernel(const float* __restric
 // The in-block sweep of block kb for 64 rows (4 waves x 16 rows; within a
 // wave, lane r < 16 owns row r for the sequential part and all 64 lanes run
 // the MFMA part).
+struct SweepLds {
+  float Ud[kBS][kBS + 1];
+  float invd[kBS];
+  __attribute__((aligned(16))) float T[kWaves][kRowsPerWave][kTP];
+  float Eb[kWaves][kRowsPerWave][kSB + 1];
+  float Gs[kWaves][kRowsPerWave][2];
+};
+
+// Block kb for rows wg*64 .. wg*64+63.  The block's deferred update arrives
+// as nsplit partial products P[sp] (m x 128 each) and, when use_last, the
+// product Plast = E[:, block kb-1] U[block kb-1, block kb] that the previous
+// block's sweep left for these rows.  When make_next, the rows' errors of
+// this block are kept in the tile as its columns are finished and
+// E[:, block kb] U[block kb, block kb+1] is written to Plast at the end.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void sweep_kernel(
+__device__ __forceinline__ void sweep_body(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
-    const float* __restrict__ P, int nsplit, float maxq, int g, int G, uint8_t* __restrict__ codes,
-    float* __restrict__ E, float* __restrict__ scales, uint8_t* __restrict__ zeros,
-    float* __restrict__ row_loss, int codes_aligned) {
-  __shared__ float Ud[kBS][kBS + 1];
-  __shared__ float invd[kBS];
-  __shared__ __attribute__((aligned(16))) float T[kWaves][kRowsPerWave][kTP];
-  __shared__ float Eb[kWaves][kRowsPerWave][kSB + 1];
-  __shared__ float Gs[kWaves][kRowsPerWave][2];
+    const float* __restrict__ P, int nsplit, float* __restrict__ Plast, int use_last, int make_next, float maxq,
+    int g, int G, uint8_t* __restrict__ codes, float* __restrict__ E, float* __restrict__ scales,
+    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, int wg, SweepLds& S) {
+  auto& Ud = S.Ud;
+  auto& invd = S.invd;
+  auto& T = S.T;
+  auto& Eb = S.Eb;
+  auto& Gs = S.Gs;
 
   const int c0 = kb * kBS;
   const int bw = min(kBS, n - c0);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerWG + wave * kRowsPerWave;
+  const int64_t row0 = (int64_t)wg * kRowsPerWG + wave * kRowsPerWave;
 
   // Loads: U's diagonal block (upper triangle, zero below it and beyond bw;
   // 16 float4 slots per thread) and the wave's 16 x 128 slab of W are issued
@@ -301,17 +320,20 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   for (int j = tid; j < kBS; j += kThreads)
     invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
   {
+    // Partial products in order: P[0] .. P[nsplit-1], then Plast.
+    const int nsub = nsplit + (use_last ? 1 : 0);
     auto load_split = [&](int sp, floatx4 (&pv)[kSlots]) {
+      const float* src = sp < nsplit ? P + (int64_t)sp * m * kBS : Plast;
 #pragma unroll
       for (int q = 0; q < kSlots; ++q) {
         const int e = lane + 64 * q;
         const int rr = e >> 5, c = (e & 31) * 4;
         const int64_t row = row0 + rr;
-        pv[q] = (sp < nsplit && row < m) ? *reinterpret_cast<const floatx4*>(P + ((int64_t)sp * m + row) * kBS + c)
-                                         : floatx4{0.f, 0.f, 0.f, 0.f};
+        pv[q] = (sp < nsub && row < m) ? *reinterpret_cast<const floatx4*>(src + row * kBS + c)
+                                       : floatx4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    for (int sp = 0; sp < nsplit; sp += 4) {
+    for (int sp = 0; sp < nsub; sp += 4) {
       floatx4 pv[4][kSlots];
 #pragma unroll
       for (int u = 0; u < 4; ++u) load_split(sp + u, pv[u]);
@@ -377,10 +399,63 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
   // FULL (a whole 128-column block) sb is a compile-time constant, every loop
   // bound is fixed and the next column's U row is read ahead of the current
   // column's arithmetic.
+  // With make_next (whole blocks only), Plast = E[rows, block] U[block,
+  // block kb+1] is built as the sweep goes: once sub-block sb is finished by
+  // every wave, its 16 rows of U's diagonal block are dead and receive the
+  // matching 16 rows of the off-diagonal tile U[c0 + .., c0 + 128 + ..]
+  // (prefetched into registers at the start of the sub-block), and the
+  // previous sub-block's slice E[:, 16] x U_off[16, 128] is accumulated with
+  // 32 fp32 MFMA 16x16x4 per wave.
+  const int c0n = c0 + kBS;
+  const int bwn = min(kBS, n - c0n);
+  const bool vecu_n = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
+  floatx4 pacc[kBS / 16];
+#pragma unroll
+  for (int ct = 0; ct < kBS / 16; ++ct) pacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+  floatx4 uo[2];
+  auto uoff_load = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + kThreads * i;       // 16 rows x 32 float4
+      const int rr = e >> 5, c = (e & 31) * 4;
+      const float* p = U + (int64_t)(c0 + j0 + rr) * n + c0n + c;
+      floatx4 v = {0.f, 0.f, 0.f, 0.f};
+      if (vecu_n && c + 4 <= bwn) {
+        v = *reinterpret_cast<const floatx4*>(p);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = c + k < bwn ? p[k] : 0.f;
+      }
+      uo[i] = v;
+    }
+  };
+  auto uoff_store = [&](int j0) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + kThreads * i;
+      const int rr = e >> 5, c = (e & 31) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) Ud[j0 + rr][c + k] = uo[i][k];
+    }
+  };
+  auto uoff_accumulate = [&](int j0) {
+#pragma unroll
+    for (int k4 = 0; k4 < kSB / 4; ++k4) {
+      const int k = k4 * 4 + (lane >> 4);
+      const float a = T[wave][lane & 15][j0 + k];
+#pragma unroll
+      for (int ct = 0; ct < kBS / 16; ++ct)
+        pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ud[j0 + k][ct * 16 + (lane & 15)], pacc[ct], 0, 0, 0);
+    }
+  };
+
   auto sub_block = [&](auto sbc, auto fullc) {
     constexpr bool FULL = decltype(fullc)::value;
     const int sb = sbc;
     const int j0 = sb * kSB;
+    if constexpr (FULL) {
+      if (make_next) uoff_load(j0);
+    }
     if (block_group && sb == 0) {
       grid_from_range(Gs[wave][r][0], Gs[wave][r][1], maxq, s, z, inv_s);
       if (active) {
@@ -506,9 +581,22 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
     } else {
       for (int ct = sb + 1; ct < nsb; ++ct) push_tile(ct);
     }
+    // The sub-block's columns are finished: keep their errors in the tile.
+    if (make_next && owner) {
+#pragma unroll
+      for (int q = 0; q < kSB / 4; ++q)
+        *reinterpret_cast<floatx4*>(&T[wave][r][j0 + 4 * q]) = floatx4{eb[4 * q], eb[4 * q + 1], eb[4 * q + 2], eb[4 * q + 3]};
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (FULL) {
+      if (make_next) {
+        __syncthreads();              // every wave is done with U's rows j0 .. j0+15
+        uoff_store(j0);
+        if (sb > 0) uoff_accumulate(j0 - kSB);   // stored before this barrier
+      }
+    }
   };
   if (bw == kBS) {
     static_for<kBS / kSB>([&](auto sbc) { sub_block(sbc, std::true_type{}); });
@@ -516,34 +604,79 @@ __global__ __launch_bounds__(kThreads) void sweep_kernel(
     for (int sb = 0; sb < nsb; ++sb) sub_block(sb, std::false_type{});
   }
   if (active && row_loss != nullptr) row_loss[row] = (kb == 0 ? 0.f : row_loss[row]) + 0.5f * loss;
+  if (make_next) {
+    // Last slice, then Plast[rows] = E[rows, block kb] U[block kb, block kb+1].
+    __syncthreads();
+    uoff_accumulate(kBS - kSB);
+    // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, column l%16.
+#pragma unroll
+    for (int ct = 0; ct < kBS / 16; ++ct)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t grow = row0 + 4 * (lane >> 4) + i;
+        if (grow < m) Plast[grow * kBS + ct * 16 + (lane & 15)] = pacc[ct][i];
+      }
+  }
+}
+
+// One launch per block kb: workgroups 0 .. nsw-1 sweep block kb (64 rows
+// each); workgroups nsw .. compute the partial products of block kb+1's
+// deferred update over the columns before block kb (the last block's share
+// comes from the sweep itself), split over K in ranges of sps stages.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void quant_block_kernel(
+    const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
+    const float* __restrict__ Pcur, int nsplit, float* __restrict__ Plast, int use_last, int make_next,
+    float maxq, int g, int G, uint8_t* __restrict__ codes, float* __restrict__ E, float* __restrict__ scales,
+    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, int nsw, int mtiles, int sps,
+    float* __restrict__ Pnext) {
+  __shared__ union {
+    SweepLds s;
+    GemmLds g;
+  } lds;
+  const int wg = (int)blockIdx.x;
+  if (wg < nsw) {
+    sweep_body<DT>(Wsrc, ldw, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales,
+                   zeros, row_loss, codes_aligned, wg, lds.s);
+  } else {
+    const int gid = wg - nsw;
+    update_gemm_body(E, U, m, n, kb + 1, kb * kBS, sps, Pnext, gid % mtiles, gid / mtiles, lds.g);
+  }
 }
 
 struct QuantLayout {
-  int nblocks = 0, mtiles = 0, smax = 0;
-  size_t off_E = 0, off_Wp = 0, off_P = 0, total = 0;
+  int nblocks = 0, mtiles = 0, nsw = 0, smax = 0;
+  size_t off_E = 0, off_Wp = 0, off_P = 0, off_Plast = 0, pstride = 0, total = 0;
 };
 
 QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
   QuantLayout L;
   L.nblocks = (int)ceil_div(n, kBS);
   L.mtiles = (int)ceil_div(m, 128);
-  // Enough K splits for about one update-GEMM workgroup per CU.
-  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1), ceil_div(256, L.mtiles)));
+  L.nsw = (int)ceil_div(m, kRowsPerWG);
+  // K splits of the update so that sweep and update workgroups together
+  // about fill the 256 CUs (at least one split).
+  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1),
+                                                       (256 - std::min<int64_t>(L.nsw, 255)) / L.mtiles));
   const size_t mn = (size_t)m * (size_t)n * sizeof(float);
+  L.pstride = (size_t)L.smax * (size_t)m * kBS;   // floats per partial-product buffer
   L.off_E = 0;
   L.off_Wp = align256(L.off_E + mn);
   L.off_P = align256(L.off_Wp + (permuted ? mn : 0));
-  L.total = align256(L.off_P + (size_t)L.smax * (size_t)m * kBS * sizeof(float));
+  L.off_Plast = align256(L.off_P + 2 * L.pstride * sizeof(float));
+  L.total = align256(L.off_Plast + (size_t)m * kBS * sizeof(float));
   return L;
 }
 
 template <int DT>
-gptq_status launch_sweep(const void* src, int64_t ld, int m, int n, int kb, const float* U, const float* P,
-                         int nsplit, float maxq, int g, int G, uint8_t* codes, float* E, float* scales,
-                         uint8_t* zeros, float* row_loss, hipStream_t st) {
+gptq_status launch_block(const void* src, int64_t ld, int m, int n, int kb, const float* U, const float* Pcur,
+                         int nsplit, float* Plast, int use_last, int make_next, float maxq, int g, int G,
+                         uint8_t* codes, float* E, float* scales, uint8_t* zeros, float* row_loss, int nsw,
+                         int mtiles, int ngemm, int sps, float* Pnext, hipStream_t st) {
   const int codes_aligned = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
-  sweep_kernel<DT><<<(unsigned)ceil_div(m, kRowsPerWG), kThreads, 0, st>>>(
-      src, ld, m, n, kb, U, P, nsplit, maxq, g, G, codes, E, scales, zeros, row_loss, codes_aligned);
+  quant_block_kernel<DT><<<(unsigned)(nsw + ngemm), kThreads, 0, st>>>(
+      src, ld, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales, zeros,
+      row_loss, codes_aligned, nsw, mtiles, sps, Pnext);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
@@ -604,25 +737,34 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m
     else row_grid_kernel<GPTQ_BF16><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
     GPTQ_TRY_LAUNCH();
   }
+  float* Plast = reinterpret_cast<float*>(base + L.off_Plast);
+  int ns_cur = 0;   // partial products of block kb's update, from the previous launch
   for (int kb = 0; kb < L.nblocks; ++kb) {
-    int nsplit = 0;
-    if (kb > 0) {
-      // Split K = 128 kb into nsplit ranges of whole 32-column stages.
+    const int use_last = kb >= 1;
+    const int make_next = kb + 1 < L.nblocks;
+    int ns_next = 0, sps = 0;
+    if (make_next && kb >= 1) {
+      // Block kb+1's update over columns [0, 128 kb) in ranges of whole 32-column stages.
       const int stages = kb * (kBS / kUK);
       const int s_target = std::min(stages, L.smax);
-      const int sps = (int)ceil_div(stages, s_target);
-      nsplit = (int)ceil_div(stages, sps);
-      update_gemm_kernel<<<dim3((unsigned)L.mtiles, (unsigned)nsplit), 256, 0, st>>>(E, U, mi, ni, kb, sps, P);
-      GPTQ_TRY_LAUNCH();
+      sps = (int)ceil_div(stages, s_target);
+      ns_next = (int)ceil_div(stages, sps);
     }
+    const float* Pcur = P + (size_t)(kb & 1) * L.pstride;
+    float* Pnext = P + (size_t)((kb + 1) & 1) * L.pstride;
+    const int ngemm = L.mtiles * ns_next;
     gptq_status rc;
     if (sdt == GPTQ_F32)
-      rc = launch_sweep<GPTQ_F32>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+      rc = launch_block<GPTQ_F32>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size, G,
+                                  codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
     else if (sdt == GPTQ_F16)
-      rc = launch_sweep<GPTQ_F16>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+      rc = launch_block<GPTQ_F16>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size, G,
+                                  codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
     else
-      rc = launch_sweep<GPTQ_BF16>(src, ld, mi, ni, kb, U, P, nsplit, maxq, group_size, G, codes, E, scales, zeros, row_loss, st);
+      rc = launch_block<GPTQ_BF16>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size,
+                                   G, codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
     if (rc != GPTQ_OK) return rc;
+    ns_cur = ns_next;
   }
   return GPTQ_OK;
 }
