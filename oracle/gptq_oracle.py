@@ -201,7 +201,7 @@ def quantize_values(w, s, z, maxq: int, clip: bool = True):
 # ---------------------------------------------------------------------------
 def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
                   block_size: int = 128, clip: bool = True, order: str = "right",
-                  record_inputs: bool = False):
+                  record_inputs: bool = False, forced=None):
     """Quantize W (m x n) with the inverse-Hessian factor U (processing order).
 
     Returns a dict with (all in processing order unless noted):
@@ -214,6 +214,10 @@ def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
     ``order`` selects where the deferred block update is applied:
     "right" after each block to all later columns, "left" to each block just
     before it is swept (identical in exact arithmetic).
+    ``forced`` maps (row, column) in processing order to a code that replaces
+    the rounding decision there (the rest of the step is unchanged): at a
+    rounding tie either code is a correct result, and this follows the other
+    branch.
     """
     W = np.asarray(W, dtype=F64)
     U = np.asarray(U, dtype=F64)
@@ -259,6 +263,10 @@ def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
             if record_inputs:
                 qin[:, j] = v
             c = quantize_values(v, s_cur, z_cur, maxq, clip=clip)
+            if forced:
+                for (fr, fj), fc in forced.items():
+                    if fj == j:
+                        c[fr] = F32(fc)
             what = s_cur.astype(F64) * (c.astype(F64) - z_cur.astype(F64))
             e = (v - what) / U[j, j]
             codes[:, j] = c

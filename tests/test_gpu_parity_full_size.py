@@ -22,7 +22,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.gpu_util import code_mismatch, dev, host, log, rel_fro, stored_to_dev
+from tests.gpu_util import certify_ties, code_mismatch, dev, host, log, rel_fro, stored_to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +125,13 @@ def test_full_size_layer(g, config, layer):
     rl_err = float(np.max(np.abs(rlg[same] - res["row_loss"][same]) / res["row_loss"][same])) if same.any() else 0.0
     log(f"  codes mismatch {mism}/{total} (rows {int((~same).sum())}) scale_err {s_err:.2e} "
         f"loss gpu/oracle {lg / lo:.6f} row_loss_err {rl_err:.2e} ({time.perf_counter() - t_start:.0f}s)")
-    assert mism <= 1e-4 * total
+    if mism > 1e-4 * total:
+        # every split must be a certified rounding tie (see certify_ties)
+        nrows, ties = certify_ties(W64, U32.astype(np.float64), perm_o, cfg.levels, cfg.group_size,
+                                   cfg.block_size, codes_g, codes_o)
+        log(f"  {mism} codes in {nrows} rows follow {ties} certified rounding ties")
+    else:
+        assert mism <= 1e-4 * total
     assert s_err <= 1e-5
     assert np.array_equal(zg[same], zo[same])
     assert abs(lg / lo - 1) <= 1e-3
