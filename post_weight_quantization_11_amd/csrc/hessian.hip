@@ -314,10 +314,20 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nb, int ntiles,
     int nsplit, int64_t tok_per_split, float* __restrict__ partial, int64_t launched) {
   static_assert(kKtD == 32 && kNBuf == 4, "pipeline written for four 32-token buffers");
-  const int64_t item = xcd_contiguous(blockIdx.x, launched);
-  if (item >= (int64_t)ntiles * nsplit) return;
-  const int split = (int)(item / ntiles);
-  const int tile = (int)(item % ntiles);
+  // XCD x owns tiles [x*tpx, (x+1)*tpx) of every split (consecutive in the
+  // band-blocked order, so they share few bands in its L2) and all XCDs walk
+  // the splits in step, so the rows one XCD misses in L2 are the rows the
+  // others read at the same time.
+  (void)launched;
+  const int xcd = (int)(blockIdx.x % kXcds);
+  const int64_t idx = blockIdx.x / kXcds;
+  const int tpx = (ntiles + kXcds - 1) / kXcds;
+  const int t0x = xcd * tpx;
+  const int tx = min(ntiles, t0x + tpx) - t0x;
+  if (tx <= 0) return;
+  const int split = (int)(idx / tx);
+  const int tile = t0x + (int)(idx % tx);
+  if (split >= nsplit) return;
   int I, J;
   tile_coords(tile, nb, I, J);
   const int64_t t_begin = (int64_t)split * tok_per_split;
@@ -604,7 +614,9 @@ SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype) {
       p.tok_per_split = cands[i].tps;
       break;
     }
-  p.launched = round_up((int64_t)p.ntiles * p.nsplit, kXcds);
+  // Covers both work mappings: XCD-contiguous items, and per-XCD tile subsets
+  // (kXcds x ceil(ntiles / kXcds) tiles per split).
+  p.launched = (int64_t)kXcds * ceil_div(p.ntiles, kXcds) * p.nsplit;
   return p;
 }
 
