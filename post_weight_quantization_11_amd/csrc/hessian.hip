@@ -309,6 +309,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= v, expcnt = 7 (no wait), lgkmcnt = 0.
 constexpr int waitcnt_vm(int v) { return (v & 15) | ((v >> 4) << 14) | (7 << 4); }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// orders global memory, which makes every wave drain all of its loads in
+// flight at each barrier; the direct-to-LDS loads are waited for explicitly.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nb, int ntiles,
@@ -334,21 +343,34 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
   const int64_t t_end = min(tokens, t_begin + tok_per_split);
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wr = wave >> 1, wc = wave & 1;
 
   // This lane's 16-byte chunk in a token row: band I for lanes 0-31, band J for 32-63.
   const int band = lane >> 5;
   const int fchunk = (band == 0 ? I : J) * kTile + (lane & 31) * 8;
-  const uint16_t* gsrc = X + (fchunk < n ? fchunk : 0);   // n % 8 == 0: a chunk is all in or all out
+  const uint32_t lane_bytes = (uint32_t)(fchunk < n ? fchunk : 0) * 2u;  // n % 8 == 0: a chunk is all in or all out
 
-  // Wave w copies token rows w*8 .. w*8+7 of a stage.  Rows past the split
-  // are clamped to its last row (a valid address); zero_tail then zeroes them
-  // once the wave's own loads have landed.
+  // Wave w copies token rows w*8 .. w*8+7 of a stage.  The row address and
+  // the LDS destination are the same for the whole wave (scalar registers);
+  // only the 16-byte chunk differs per lane.  Rows past the split are clamped
+  // to its last row (a valid address); zero_tail then zeroes them once the
+  // wave's own loads have landed.
+  //
+  // The load is issued by hand: when the compiler sees a direct-to-LDS load
+  // it cannot tell which of the four stage buffers it writes, so it would
+  // make every later LDS read and the barrier wait for all loads in flight,
+  // which leaves the pipeline no more than half a stage of lead.  The waits
+  // the pipeline needs are explicit (wait_landed).  M0 holds the LDS
+  // destination; one wait state separates its write from the load.
   auto load_row = [&](int buf, int64_t t0, int i) {
     const int r = wave * kRowsPerWave + i;
     const int64_t t = min(t0 + r, t_end - 1);
-    __builtin_amdgcn_global_load_lds(gsrc + t * ldx, (lds_void*)(smem + buf * kStageBytes + r * kRowBytes), 16, 0, 0);
+    const uint16_t* row = X + t * ldx;
+    const uint32_t dst_lds = (uint32_t)reinterpret_cast<uintptr_t>((lds_void*)(smem + buf * kStageBytes + r * kRowBytes));
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(dst_lds), "v"(lane_bytes), "s"(row) : "memory", "m0");
   };
   auto zero_tail = [&](int buf, int64_t t0) {
 #pragma unroll
@@ -404,7 +426,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     for (int i = 0; i < kRowsPerWave; ++i) load_row(st, t_begin + st * kKtD, i);
   wait_landed(0, kNBuf - 2);
   if (!full(0)) zero_tail(0, t_begin);
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(0, a_off, 0, rb);
 #pragma unroll
@@ -414,13 +436,18 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     const int pbuf = (int)((s + kNBuf - 1) % kNBuf);      // the buffer stage s-1 used
     const int64_t pt0 = t_begin + (s + kNBuf - 1) * kKtD;  // stage s+3, loaded into it
     // First step (slot 0): fragments of the second step into slot 1, and the
-    // loads of stage s+3 one per two MFMAs.
+    // loads of stage s+3 one per two MFMAs.  The hand-issued loads keep their
+    // place among the LDS reads, so the two are interleaved here.
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) fa[1][rb] = frag(buf, a_off, 1, rb);
+    for (int k = 0; k < 4; ++k) {
+      fa[1][k] = frag(buf, a_off, 1, k);
+      load_row(pbuf, pt0, k);
+    }
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) fb[1][cb] = frag(buf, b_off, 1, cb);
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) load_row(pbuf, pt0, i);
+    for (int k = 0; k < 4; ++k) {
+      fb[1][k] = frag(buf, b_off, 1, k);
+      load_row(pbuf, pt0, 4 + k);
+    }
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
@@ -429,10 +456,9 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     for (int m = 0; m < 8; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct-to-LDS load
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // address arithmetic
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct-to-LDS load
     }
     // Second step (slot 1): first half of its MFMAs.
 #pragma unroll
@@ -443,7 +469,7 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
       // Stages up to s+3 have been issued; stage s+1 must land.
       wait_landed(s + 1, s + kNBuf - 1);
       if (!full(s + 1)) zero_tail((int)((s + 1) % kNBuf), t_begin + (s + 1) * kKtD);
-      __syncthreads();
+      lds_barrier();
       const int nbuf = (int)((s + 1) % kNBuf);
 #pragma unroll
       for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(nbuf, a_off, 0, rb);
