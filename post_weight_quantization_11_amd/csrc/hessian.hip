@@ -282,24 +282,25 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_kernel(
 // features f + 4*(j%4), it receives tokens t0..t0+3 of feature f + j, i.e. a
 // K-contiguous operand.
 //
-// Pipeline: stages of 32 tokens (two 16-token MFMA steps) rotate through four
-// LDS buffers.  While stage s is multiplied, the loads of stage s+3 (into the
-// buffer stage s-1 used) are issued one per two MFMAs of its first step, so a
-// wave never waits long at a load for the memory pipeline to accept it, and
-// stages s+1 .. s+3 are in flight.  The one barrier per stage sits inside the
-// second step, after its first eight MFMAs: every wave then holds that step's
-// fragments (buffer s may be refilled from the next stage on) and has waited
-// for its own loads of stage s+1 (visible to all after the barrier); the
-// fragment reads of stage s+1's first step overlap the last eight MFMAs.  The
-// last stage of a split may be partial: its rows past the split load the
-// split's last row and are zeroed once they have landed, before the barrier
-// that publishes the stage.  Stages past the split load into buffers that no
-// step reads.
+// Pipeline: stages of 64 tokens (four 16-token MFMA steps) alternate between
+// two LDS buffers.  While stage s is multiplied, the loads of stage s+1 go into
+// the other buffer (last read before the previous barrier), one per two MFMAs
+// of the first two steps, so a wave never waits long at a load for the memory
+// pipeline to accept it and the loads have two steps and more to land.  The
+// one barrier per stage sits inside the last step, after its first eight
+// MFMAs: every wave then holds that step's fragments (buffer s may be refilled
+// from the next stage on) and has waited for its own loads of stage s+1
+// (visible to all after the barrier); the fragment reads of stage s+1's first
+// step overlap the last eight MFMAs.  The last stage of a split may be
+// partial: its rows past the split load the split's last row and are zeroed
+// once they have landed, before the barrier that publishes the stage.
 constexpr int kRowBytes = 1088;
-constexpr int kKtD = 32;                        // tokens per stage
-constexpr int kNBuf = 4;                        // LDS stage buffers (kNBuf * kStageBytes <= 160 KB)
+constexpr int kKtD = 64;                        // tokens per stage
+constexpr int kSteps = kKtD / 16;               // MFMA steps per stage
+constexpr int kNBuf = 2;                        // LDS stage buffers (kNBuf * kStageBytes <= 160 KB)
 constexpr int kStageBytes = kKtD * kRowBytes;
 constexpr int kRowsPerWave = kKtD / 4;          // direct loads per wave per stage
+constexpr int kLoadSteps = 2;                   // steps that issue them, kRowsPerWave / 8 each
 constexpr int kDirectLdsBytes = kNBuf * kStageBytes;
 
 typedef short short4v __attribute__((ext_vector_type(4)));
@@ -322,7 +323,8 @@ template <int DT>
 __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
     const uint16_t* __restrict__ X, int64_t ldx, int n, int64_t tokens, int nb, int ntiles,
     int nsplit, int64_t tok_per_split, float* __restrict__ partial, int64_t launched) {
-  static_assert(kKtD == 32 && kNBuf == 4, "pipeline written for four 32-token buffers");
+  static_assert(kNBuf == 2 && kSteps % 2 == 0 && kLoadSteps < kSteps && kRowsPerWave == 8 * kLoadSteps,
+                "pipeline written for two buffers, an even number of steps and 8 loads per loading step");
   // XCD x owns tiles [x*tpx, (x+1)*tpx) of every split (consecutive in the
   // band-blocked order, so they share few bands in its L2) and all XCDs walk
   // the splits in step, so the rows one XCD misses in L2 are the rows the
@@ -352,17 +354,17 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
   const int fchunk = (band == 0 ? I : J) * kTile + (lane & 31) * 8;
   const uint32_t lane_bytes = (uint32_t)(fchunk < n ? fchunk : 0) * 2u;  // n % 8 == 0: a chunk is all in or all out
 
-  // Wave w copies token rows w*8 .. w*8+7 of a stage.  The row address and
+  // Wave w copies token rows 16w .. 16w+15 of a stage.  The row address and
   // the LDS destination are the same for the whole wave (scalar registers);
   // only the 16-byte chunk differs per lane.  Rows past the split are clamped
   // to its last row (a valid address); zero_tail then zeroes them once the
   // wave's own loads have landed.
   //
   // The load is issued by hand: when the compiler sees a direct-to-LDS load
-  // it cannot tell which of the four stage buffers it writes, so it would
-  // make every later LDS read and the barrier wait for all loads in flight,
-  // which leaves the pipeline no more than half a stage of lead.  The waits
-  // the pipeline needs are explicit (wait_landed).  M0 holds the LDS
+  // it cannot tell which stage buffer it writes, so it would make every
+  // later LDS read and the barrier wait for all loads in flight, including
+  // the ones just issued for the next stage.  The waits the pipeline needs
+  // are explicit (before each barrier).  M0 holds the LDS
   // destination; one wait state separates its write from the load.
   auto load_row = [&](int buf, int64_t t0, int i) {
     const int r = wave * kRowsPerWave + i;
@@ -404,27 +406,15 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
 
   float* dst = partial + ((int64_t)split * ntiles + tile) * (int64_t)kTileElems;
   const int64_t nstages = (t_end - t_begin + kKtD - 1) / kKtD;
-  // Stage st is full when all its rows lie in the split (kRowsPerWave loads
-  // per wave); only the last stage of a split can be partial.
-  auto full = [&](int64_t st) { return st < nstages && t_begin + (st + 1) * kKtD <= t_end; };
-  // Waits until stage st has landed while the loads of the (at most two)
-  // stages issued after it, up to stage last, may stay in flight; a partial
-  // one is counted as zero, which only makes the wait stricter.
-  auto wait_landed = [&](int64_t st, int64_t last) {
-    const int later = ((st + 1 <= last && full(st + 1)) ? 1 : 0) + ((st + 2 <= last && full(st + 2)) ? 1 : 0);
-    if (later == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kRowsPerWave));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kRowsPerWave));
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  };
+  // Stage st is full when all its rows lie in the split; only the last stage
+  // of a split can be partial.
+  auto full = [&](int64_t st) { return t_begin + (st + 1) * kKtD <= t_end; };
 
   u32x4 fa[2][4], fb[2][4];
-  // Prologue: stages 0 .. kNBuf-2 (a stage past the split only loads its
-  // clamped last row again, into a buffer no step reads).
+  // Prologue: stage 0.
 #pragma unroll
-  for (int st = 0; st < kNBuf - 1; ++st)
-#pragma unroll
-    for (int i = 0; i < kRowsPerWave; ++i) load_row(st, t_begin + st * kKtD, i);
-  wait_landed(0, kNBuf - 2);
+  for (int i = 0; i < kRowsPerWave; ++i) load_row(0, t_begin, i);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
   if (!full(0)) zero_tail(0, t_begin);
   lds_barrier();
 #pragma unroll
@@ -432,49 +422,56 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(0, b_off, 0, cb);
   for (int64_t s = 0; s < nstages; ++s) {
-    const int buf = (int)(s % kNBuf);
-    const int pbuf = (int)((s + kNBuf - 1) % kNBuf);      // the buffer stage s-1 used
-    const int64_t pt0 = t_begin + (s + kNBuf - 1) * kKtD;  // stage s+3, loaded into it
-    // First step (slot 0): fragments of the second step into slot 1, and the
-    // loads of stage s+3 one per two MFMAs.  The hand-issued loads keep their
-    // place among the LDS reads, so the two are interleaved here.
+    const int buf = (int)(s & 1);
+    const int64_t nt0 = t_begin + (s + 1) * kKtD;          // stage s+1, loaded into buffer buf^1
+    const bool more = s + 1 < nstages;
+    // Steps 0 .. kSteps-2: the next step's fragments into the other slot and,
+    // in the first kLoadSteps steps, eight loads of stage s+1 each.  The last
+    // stage loads too (its clamped last row, into the buffer no step reads
+    // any more), which keeps the loop free of branches around the loads.
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      fa[1][k] = frag(buf, a_off, 1, k);
-      load_row(pbuf, pt0, k);
+    for (int q = 0; q < kSteps - 1; ++q) {
+      const int cur = q & 1, nxt = cur ^ 1;
+      const bool ld = q < kLoadSteps;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        fa[nxt][k] = frag(buf, a_off, q + 1, k);
+        if (ld) load_row(buf ^ 1, nt0, 8 * q + k);
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        fb[nxt][k] = frag(buf, b_off, q + 1, k);
+        if (ld) load_row(buf ^ 1, nt0, 8 * q + 4 + k);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[cur][rb], fb[cur][cb], acc[rb][cb]);
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // a direct-to-LDS load, if any
+      }
     }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      fb[1][k] = frag(buf, b_off, 1, k);
-      load_row(pbuf, pt0, 4 + k);
-    }
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[0][rb], fb[0][cb], acc[rb][cb]);
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one direct-to-LDS load
-    }
-    // Second step (slot 1): first half of its MFMAs.
+    // Last step (slot 1): first half of its MFMAs.
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = Mfma16<DT>::run(fa[1][rb], fb[1][cb], acc[rb][cb]);
-    if (s + 1 < nstages) {
-      // Stages up to s+3 have been issued; stage s+1 must land.
-      wait_landed(s + 1, s + kNBuf - 1);
-      if (!full(s + 1)) zero_tail((int)((s + 1) % kNBuf), t_begin + (s + 1) * kKtD);
+    if (more) {
+      // This wave's loads of stage s+1 have landed and its LDS reads of
+      // buffer buf are done (lgkmcnt 0) before the barrier publishes the one
+      // and frees the other.
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+      if (!full(s + 1)) zero_tail(buf ^ 1, nt0);
       lds_barrier();
-      const int nbuf = (int)((s + 1) % kNBuf);
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(nbuf, a_off, 0, rb);
+      for (int rb = 0; rb < 4; ++rb) fa[0][rb] = frag(buf ^ 1, a_off, 0, rb);
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(nbuf, b_off, 0, cb);
+      for (int cb = 0; cb < 4; ++cb) fb[0][cb] = frag(buf ^ 1, b_off, 0, cb);
     }
 #pragma unroll
     for (int rb = 2; rb < 4; ++rb)
