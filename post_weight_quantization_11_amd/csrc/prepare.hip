@@ -273,11 +273,11 @@ __device__ __forceinline__ void inverse_block(const double* S, double* Xs, doubl
   inverse_finish<I, J>(Xs, T, lane);
 }
 
-// Factors and inverts the diagonal block kb held in S; all 256 threads.  L
-// goes back to A (lower triangle), inv(L_kk) to Linv and to X's diagonal block.
-__device__ __forceinline__ void factor_diag(double* S, double* Xs, FactorLds& fx, double* __restrict__ A,
-                                            double* __restrict__ X, double* __restrict__ Linv, int np, int n,
-                                            int kb, int32_t* __restrict__ info) {
+// Factors and inverts the diagonal block kb held in S; all 256 threads.
+// inv(L_kk) goes to Linv and to X's diagonal block.
+__device__ __forceinline__ void factor_diag(double* S, double* Xs, FactorLds& fx, double* __restrict__ X,
+                                            double* __restrict__ Linv, int np, int n, int kb,
+                                            int32_t* __restrict__ info) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
@@ -320,12 +320,13 @@ __device__ __forceinline__ void factor_diag(double* S, double* Xs, FactorLds& fx
     if (lane == 0 && mask != 0ull && *info == 0) *info = kb * kB + __builtin_ctzll(mask) + 1;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < kB * kB; e += kThreads) {
-    const int r = e >> 6, c = e & 63;
-    const double xv = c <= r ? Xs[r * kP + c] : 0.0;
-    Linv[e] = xv;
-    X[base + (int64_t)r * np + c] = xv;
-    if (c <= r) A[base + (int64_t)r * np + c] = S[r * kP + c];
+  // Two elements per thread and store.  The factor itself is not written
+  // back: nothing reads the diagonal blocks of L after this point.
+  for (int e = threadIdx.x; e < kB * kB / 2; e += kThreads) {
+    const int r = e >> 5, c = (e & 31) * 2;
+    const double2 xv = {c <= r ? Xs[r * kP + c] : 0.0, c + 1 <= r ? Xs[r * kP + c + 1] : 0.0};
+    *reinterpret_cast<double2*>(Linv + r * kB + c) = xv;
+    *reinterpret_cast<double2*>(X + base + (int64_t)r * np + c) = xv;
   }
 }
 
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict
   const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
   for (int e = threadIdx.x; e < kB * kB; e += kThreads) t.As[e >> 6][e & 63] = A[base + (int64_t)(e >> 6) * np + (e & 63)];
   __syncthreads();
-  factor_diag(&t.As[0][0], &t.Bs[0][0], fx, A, X, Linv, np, n, kb, info);
+  factor_diag(&t.As[0][0], &t.Bs[0][0], fx, X, Linv, np, n, kb, info);
 }
 
 __device__ inline void tri_decode(int t, int& ii, int& jj) {
@@ -515,7 +516,7 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb, bi);
     gemm_tile64(lds.t, pa, np, pb, np, tb, pc, np, true, &lds.t.As[0][0]);
     __syncthreads();
-    factor_diag(&lds.t.As[0][0], &lds.t.Bs[0][0], fx, A, X, Linv, np, n, kb + 1, info);
+    factor_diag(&lds.t.As[0][0], &lds.t.Bs[0][0], fx, X, Linv, np, n, kb + 1, info);
     return;
   }
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
