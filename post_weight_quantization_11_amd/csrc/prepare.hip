@@ -104,12 +104,13 @@ __global__ void zero_kernel(double* __restrict__ p, int64_t count) {
     p[i] = 0.0;
 }
 
-// 1/sqrt(d) in float64: hardware estimate refined by two Newton steps.
+// 1/sqrt(d) in float64: hardware estimate (relative error below 2^-24,
+// measured over random inputs on gfx950) refined by one Newton step (below
+// 2^-47).  It sits on the column chain of every diagonal factor; that
+// accuracy is far beyond what the float32 U kept at the end can show.
 __device__ inline double rsqrt_f64(double d) {
-  double y = __builtin_amdgcn_rsq(d);
-  double h = __builtin_fma(-0.5 * d * y, y, 0.5);
-  y = __builtin_fma(y, h, y);
-  h = __builtin_fma(-0.5 * d * y, y, 0.5);
+  const double y = __builtin_amdgcn_rsq(d);
+  const double h = __builtin_fma(-0.5 * d * y, y, 0.5);
   return __builtin_fma(y, h, y);
 }
 
