@@ -32,6 +32,7 @@ constexpr int kRowsPerWave = 16;
 constexpr int kWaves = 4;
 constexpr int kRowsPerWG = kRowsPerWave * kWaves;
 constexpr int kThreads = 64 * kWaves;
+static_assert(kThreads >= kBS, "one thread per column of the diagonal block");
 constexpr int kTP = kBS + 4;   // LDS pitch of the block tile (floats)
 
 // Grid parameters from a value range (float32, IEEE division, half-even).
@@ -83,6 +84,23 @@ __global__ __launch_bounds__(256) void permute_w_kernel(const void* __restrict__
     const int pj = min(max(perm[j], 0), n - 1);   // out-of-range entries are clamped, never followed
     Wp[r * n + j] = load_as_f32<DT>(W, r * ldw + pj);
   }
+}
+
+// Four consecutive elements of W as float32; i is a multiple of 4 and the
+// element address is 16-byte (float32) or 8-byte (16-bit types) aligned.
+template <int DT> __device__ inline floatx4 load4_as_f32(const void* p, int64_t i);
+template <> __device__ inline floatx4 load4_as_f32<GPTQ_F32>(const void* p, int64_t i) {
+  return *reinterpret_cast<const floatx4*>(static_cast<const float*>(p) + i);
+}
+template <> __device__ inline floatx4 load4_as_f32<GPTQ_F16>(const void* p, int64_t i) {
+  typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+  const half4 h = *reinterpret_cast<const half4*>(static_cast<const _Float16*>(p) + i);
+  return floatx4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+template <> __device__ inline floatx4 load4_as_f32<GPTQ_BF16>(const void* p, int64_t i) {
+  const uint2 b = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(p) + i);
+  return floatx4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16),
+                 __uint_as_float(b.y & 0xffff0000u)};
 }
 
 // Per-row grid (group_size 0): range of the original row, one wave per row.
@@ -270,57 +288,70 @@ __device__ __forceinline__ void sweep_body(
   const int64_t row0 = (int64_t)wg * kRowsPerWG + wave * kRowsPerWave;
 
   // Loads: U's diagonal block (upper triangle, zero below it and beyond bw;
-  // 16 float4 slots per thread) and the wave's 16 x 128 slab of W are issued
-  // together; then the split-K partial products of the block update are
-  // subtracted, four splits' loads in flight at a time.  Slot q of lane l of
-  // the slab is row (l + 64q) / 32, columns 4*((l + 64q) % 32) .. +3.
+  // 16 float4 slots per thread), the wave's 16 x 128 slab of W and the first
+  // kPIn split-K partial products of the block update (P[0] .. P[nsplit-1],
+  // then Plast) are all issued before any of them is waited for, so they
+  // share one memory round trip; further partials follow kPIn at a time.
+  // Slot q of lane l of the slab is row (l + 64q) / 32, columns
+  // 4*((l + 64q) % 32) .. +3.
   constexpr int kSlots = kRowsPerWave * kBS / 4 / 64;
+  constexpr int kPIn = 4;
   floatx4 t[kSlots];
   {
     const bool vecu = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
     constexpr int kUSlots = kBS * kBS / 4 / kThreads;
+    // A whole block with aligned rows takes one 16-byte load per U slot and
+    // one 16-byte (or, for 16-bit W, 8-byte) load per W slot, with no
+    // per-element tests; the lower triangle of the diagonal block is loaded
+    // and masked when it is stored to LDS.
+    const bool fast = bw == kBS && vecu && (ldw & 3) == 0 &&
+                      (reinterpret_cast<uintptr_t>(Wsrc) & (DT == GPTQ_F32 ? 15 : 7)) == 0;
     floatx4 uv[kUSlots];
+    if (fast) {
 #pragma unroll
-    for (int q = 0; q < kUSlots; ++q) {
-      const int e = tid + kThreads * q;
-      const int i = e >> 5, j = (e & 31) * 4;
-      floatx4 v = {0.f, 0.f, 0.f, 0.f};
-      if (i < bw && j + 3 >= i) {
-        const float* p = U + (int64_t)(c0 + i) * n + c0 + j;
-        if (vecu && j + 4 <= bw) {
-          v = *reinterpret_cast<const floatx4*>(p);
-        } else {
+      for (int q = 0; q < kUSlots; ++q) {
+        const int e = tid + kThreads * q;
+        const int i = e >> 5, j = (e & 31) * 4;
+        uv[q] = *reinterpret_cast<const floatx4*>(U + (int64_t)(c0 + i) * n + c0 + j);
+      }
 #pragma unroll
-          for (int k = 0; k < 4; ++k) v[k] = j + k < bw ? p[k] : 0.f;
+      for (int q = 0; q < kSlots; ++q) {
+        const int e = lane + 64 * q;
+        const int rr = e >> 5, c = (e & 31) * 4;
+        const int64_t row = row0 + rr;
+        t[q] = row < m ? load4_as_f32<DT>(Wsrc, row * ldw + c0 + c) : floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < kUSlots; ++q) {
+        const int e = tid + kThreads * q;
+        const int i = e >> 5, j = (e & 31) * 4;
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+        if (i < bw && j + 3 >= i) {
+          const float* p = U + (int64_t)(c0 + i) * n + c0 + j;
+          if (vecu && j + 4 <= bw) {
+            v = *reinterpret_cast<const floatx4*>(p);
+          } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) v[k] = j + k < bw ? p[k] : 0.f;
+          }
         }
+        uv[q] = v;
       }
-      uv[q] = v;
-    }
 #pragma unroll
-    for (int q = 0; q < kSlots; ++q) {
-      const int e = lane + 64 * q;
-      const int rr = e >> 5, c = (e & 31) * 4;
-      const int64_t row = row0 + rr;
-      floatx4 v = {0.f, 0.f, 0.f, 0.f};
-      if (row < m) {
+      for (int q = 0; q < kSlots; ++q) {
+        const int e = lane + 64 * q;
+        const int rr = e >> 5, c = (e & 31) * 4;
+        const int64_t row = row0 + rr;
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+        if (row < m) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (c + k < bw) v[k] = load_as_f32<DT>(Wsrc, row * ldw + c0 + c + k);
+          for (int k = 0; k < 4; ++k)
+            if (c + k < bw) v[k] = load_as_f32<DT>(Wsrc, row * ldw + c0 + c + k);
+        }
+        t[q] = v;
       }
-      t[q] = v;
     }
-#pragma unroll
-    for (int q = 0; q < kUSlots; ++q) {
-      const int e = tid + kThreads * q;
-      const int i = e >> 5, j = (e & 31) * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
-    }
-  }
-  for (int j = tid; j < kBS; j += kThreads)
-    invd[j] = j < bw ? 1.f / U[(int64_t)(c0 + j) * n + c0 + j] : 0.f;
-  {
-    // Partial products in order: P[0] .. P[nsplit-1], then Plast.
     const int nsub = nsplit + (use_last ? 1 : 0);
     auto load_split = [&](int sp, floatx4 (&pv)[kSlots]) {
       const float* src = sp < nsplit ? P + (int64_t)sp * m * kBS : Plast;
@@ -333,12 +364,25 @@ __device__ __forceinline__ void sweep_body(
                                        : floatx4{0.f, 0.f, 0.f, 0.f};
       }
     };
-    for (int sp = 0; sp < nsub; sp += 4) {
-      floatx4 pv[4][kSlots];
+    floatx4 pv[kPIn][kSlots];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) load_split(sp + u, pv[u]);
+    for (int u = 0; u < kPIn; ++u) load_split(u, pv[u]);
+    const float dj = tid < bw ? U[(int64_t)(c0 + tid) * n + c0 + tid] : 1.f;   // kThreads >= kBS
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+    for (int q = 0; q < kUSlots; ++q) {
+      const int e = tid + kThreads * q;
+      const int i = e >> 5, j = (e & 31) * 4;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
+    }
+    if (tid < kBS) invd[tid] = tid < bw ? 1.f / dj : 0.f;
+    for (int sp = 0; sp < nsub; sp += kPIn) {
+      if (sp > 0) {
+#pragma unroll
+        for (int u = 0; u < kPIn; ++u) load_split(sp + u, pv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < kPIn; ++u)
 #pragma unroll
         for (int q = 0; q < kSlots; ++q) t[q] -= pv[u][q];
     }
