@@ -444,52 +444,34 @@ __device__ __forceinline__ void sweep_body(
   // bound is fixed and the next column's U row is read ahead of the current
   // column's arithmetic.
   // With make_next (whole blocks only), Plast = E[rows, block] U[block,
-  // block kb+1] is built as the sweep goes: once sub-block sb is finished by
-  // every wave, its 16 rows of U's diagonal block are dead and receive the
-  // matching 16 rows of the off-diagonal tile U[c0 + .., c0 + 128 + ..]
-  // (prefetched into registers at the start of the sub-block), and the
-  // previous sub-block's slice E[:, 16] x U_off[16, 128] is accumulated with
-  // 32 fp32 MFMA 16x16x4 per wave.
+  // block kb+1] is built as the sweep goes: each wave reads the MFMA B
+  // fragments of the off-diagonal tile's 16 rows for sub-block sb straight
+  // from global memory at the start of the sub-block (no LDS staging, so the
+  // waves never wait for one another), and while it runs sub-block sb+1's
+  // columns accumulates sub-block sb's slice E[:, 16] x U_off[16, 128] with
+  // 32 fp32 MFMA 16x16x4 (the last slice after the block).
   const int c0n = c0 + kBS;
   const int bwn = min(kBS, n - c0n);
-  const bool vecu_n = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
   floatx4 pacc[kBS / 16];
 #pragma unroll
   for (int ct = 0; ct < kBS / 16; ++ct) pacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-  floatx4 uo[2];
-  auto uoff_load = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + kThreads * i;       // 16 rows x 32 float4
-      const int rr = e >> 5, c = (e & 31) * 4;
-      const float* p = U + (int64_t)(c0 + j0 + rr) * n + c0n + c;
-      floatx4 v = {0.f, 0.f, 0.f, 0.f};
-      if (vecu_n && c + 4 <= bwn) {
-        v = *reinterpret_cast<const floatx4*>(p);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[k] = c + k < bwn ? p[k] : 0.f;
-      }
-      uo[i] = v;
-    }
-  };
-  auto uoff_store = [&](int j0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = tid + kThreads * i;
-      const int rr = e >> 5, c = (e & 31) * 4;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) Ud[j0 + rr][c + k] = uo[i][k];
-    }
-  };
-  auto uoff_accumulate = [&](int j0) {
+  // B element (k, column) of 16x16x4: k = 4*k4 + lane/16, column lane%16.
+  float uf[2][kSB / 4][kBS / 16];
+  auto uoff_load = [&](int j0, float (&f)[kSB / 4][kBS / 16]) {
 #pragma unroll
     for (int k4 = 0; k4 < kSB / 4; ++k4) {
-      const int k = k4 * 4 + (lane >> 4);
-      const float a = T[wave][lane & 15][j0 + k];
+      const float* p = U + (int64_t)(c0 + j0 + 4 * k4 + (lane >> 4)) * n + c0n + (lane & 15);
+#pragma unroll
+      for (int ct = 0; ct < kBS / 16; ++ct) f[k4][ct] = ct * 16 + (lane & 15) < bwn ? p[ct * 16] : 0.f;
+    }
+  };
+  auto uoff_accumulate = [&](int j0, const float (&f)[kSB / 4][kBS / 16]) {
+#pragma unroll
+    for (int k4 = 0; k4 < kSB / 4; ++k4) {
+      const float a = T[wave][lane & 15][j0 + 4 * k4 + (lane >> 4)];
 #pragma unroll
       for (int ct = 0; ct < kBS / 16; ++ct)
-        pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Ud[j0 + k][ct * 16 + (lane & 15)], pacc[ct], 0, 0, 0);
+        pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, f[k4][ct], pacc[ct], 0, 0, 0);
     }
   };
 
@@ -498,7 +480,7 @@ __device__ __forceinline__ void sweep_body(
     const int sb = sbc;
     const int j0 = sb * kSB;
     if constexpr (FULL) {
-      if (make_next) uoff_load(j0);
+      uoff_load(j0, uf[sb & 1]);   // all zero (and no access) when there is no next block
     }
     if (block_group && sb == 0) {
       grid_from_range(Gs[wave][r][0], Gs[wave][r][1], maxq, s, z, inv_s);
@@ -542,8 +524,23 @@ __device__ __forceinline__ void sweep_body(
       float idn = invd[j0];
 #pragma unroll
       for (int kk = 0; kk < kSB; ++kk) un[kk] = Ud[j0][j0 + kk];
+      // The previous sub-block's Plast slice (independent of this chain) is
+      // spread over the columns, two MFMAs per column, so that the matrix
+      // core works while the column chain waits on its own latencies.
+      constexpr bool kSlice = decltype(sbc)::value > 0;
+      float pa[kSB / 4];
+      if constexpr (kSlice) {
+#pragma unroll
+        for (int k4 = 0; k4 < kSB / 4; ++k4) pa[k4] = T[wave][lane & 15][j0 - kSB + 4 * k4 + (lane >> 4)];
+      }
 #pragma unroll
       for (int jj = 0; jj < kSB; ++jj) {
+        if constexpr (kSlice) {
+          const int k4 = jj >> 2, ct = 2 * (jj & 3);
+          const auto& f = uf[(decltype(sbc)::value - 1) & 1];
+          pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct], pacc[ct], 0, 0, 0);
+          pacc[ct + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct + 1], pacc[ct + 1], 0, 0, 0);
+        }
         float uc[kSB];
 #pragma unroll
         for (int kk = 0; kk < kSB; ++kk) uc[kk] = un[kk];
@@ -634,13 +631,6 @@ __device__ __forceinline__ void sweep_body(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if constexpr (FULL) {
-      if (make_next) {
-        __syncthreads();              // every wave is done with U's rows j0 .. j0+15
-        uoff_store(j0);
-        if (sb > 0) uoff_accumulate(j0 - kSB);   // stored before this barrier
-      }
-    }
   };
   if (bw == kBS) {
     static_for<kBS / kSB>([&](auto sbc) { sub_block(sbc, std::true_type{}); });
@@ -650,8 +640,7 @@ __device__ __forceinline__ void sweep_body(
   if (active && row_loss != nullptr) row_loss[row] = (kb == 0 ? 0.f : row_loss[row]) + 0.5f * loss;
   if (make_next) {
     // Last slice, then Plast[rows] = E[rows, block kb] U[block kb, block kb+1].
-    __syncthreads();
-    uoff_accumulate(kBS - kSB);
+    uoff_accumulate(kBS - kSB, uf[(kBS / kSB - 1) & 1]);
     // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, column l%16.
 #pragma unroll
     for (int ct = 0; ct < kBS / 16; ++ct)
