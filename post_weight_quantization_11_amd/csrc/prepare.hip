@@ -78,13 +78,16 @@ __global__ __launch_bounds__(kThreads) void act_order_kernel(const float* __rest
 }
 
 // A[i][j] = H[q_i][q_j] + lambda * (i == j), q_i = perm[n-1-i]; identity padding.
+// Only the lower block triangle (block column <= block row) is written:
+// nothing reads A's blocks above the diagonal.
 __global__ __launch_bounds__(kThreads) void build_reversed_kernel(
     const float* __restrict__ H, int n, int np, const int32_t* __restrict__ perm,
     const double* __restrict__ lam, double* __restrict__ A) {
   const int i = blockIdx.x;
   const double l = *lam;
   const int qi = i < n ? min(max(perm[n - 1 - i], 0), n - 1) : 0;
-  for (int j = threadIdx.x; j < np; j += kThreads) {
+  const int jend = (i / kB + 1) * kB;
+  for (int j = threadIdx.x; j < jend; j += kThreads) {
     double v;
     if (i < n && j < n) {
       const int qj = min(max(perm[n - 1 - j], 0), n - 1);
@@ -95,13 +98,6 @@ __global__ __launch_bounds__(kThreads) void build_reversed_kernel(
     }
     A[(int64_t)i * np + j] = v;
   }
-}
-
-// Zero X (the inverse under construction).
-__global__ void zero_kernel(double* __restrict__ p, int64_t count) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count;
-       i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0.0;
 }
 
 // 1/sqrt(d) in float64: hardware estimate (relative error below 2^-24,
@@ -574,15 +570,25 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, tb, bi);
     if (tn < t_hi) load_ops(tn);
     // C block in the accumulator layout (row (lane>>4) + 4r of each 16 x 16
-    // block, column lane & 15), read ahead of the MFMAs.
+    // block, column lane & 15), read ahead of the MFMAs.  An inverse tile
+    // T[i, kb] is touched here for the first time and starts from zero (X is
+    // never cleared as a whole).
+    const bool first = t >= S && (t - S) % (kb + 1) == kb;
     doublex4 cv[2][2];
+    if (first) {
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+      for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
-      for (int tj = 0; tj < 2; ++tj)
+        for (int tj = 0; tj < 2; ++tj) cv[ti][tj] = doublex4{0.0, 0.0, 0.0, 0.0};
+    } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          cv[ti][tj][r] = pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)];
+      for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            cv[ti][tj][r] = pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)];
+    }
     doublex4 acc[2][2];
 #pragma unroll
     for (int ti = 0; ti < 2; ++ti)
@@ -678,7 +684,6 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   damp_kernel<<<1, kThreads, 0, st>>>(H, ni, (double)damp_rel, lam);
   act_order_kernel<<<(unsigned)ceil_div(n, kThreads), kThreads, 0, st>>>(H, ni, act_order, perm);
   build_reversed_kernel<<<(unsigned)np, kThreads, 0, st>>>(H, ni, np, perm, lam, A);
-  zero_kernel<<<2048, kThreads, 0, st>>>(X, (int64_t)np * np);
   GPTQ_TRY_LAUNCH();
   potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, 0, info);
   for (int kb = 0; kb < nbk; ++kb) {

@@ -264,3 +264,33 @@ def test_end_to_end_single_linear_256(g):
     _check_quant(q, res, W64, res["H"], "e2e")
     same = ~np.any(host(q["codes"]).astype(np.int64) != res["codes"], axis=1)
     np.testing.assert_array_equal(host(q["packed"]).view(np.uint32)[same], res["packed"][same])
+
+
+# ---------------------------------------------------------------------------
+# Workspaces: no stage may depend on what a caller's workspace held before
+# the call (the kernels never clear them as a whole).
+# ---------------------------------------------------------------------------
+def test_results_do_not_depend_on_workspace_contents(g):
+    import torch
+    from post_weight_quantization_11_amd import _lib
+    lib = _lib.load()
+    n, m, tokens = 224, 96, 700          # padded prepare, a partial last block
+    X = stored_to_dev(_x(tokens, n, "bf16", 4242))
+    runs = []
+    for fill in (0x00, 0xFF):   # 0xFF bytes: NaN in every float type
+        log(f"workspace fill 0x{fill:02x}")
+        wsh = torch.full((int(lib.gptq_hessian_ws_bytes(n, tokens, 2)),), fill, dtype=torch.uint8, device="cuda")
+        H = torch.empty((n, n), dtype=torch.float32, device="cuda")
+        g.gptq_hessian_accumulate(H, X, reset=True, ws=wsh)
+        wsp = torch.full((int(lib.gptq_prepare_ws_bytes(n)),), fill, dtype=torch.uint8, device="cuda")
+        U, perm = g.gptq_prepare_hinv(H, 0.01, True, ws=wsp)
+        W = stored_to_dev(wl.gaussian_w(m, n, 77, 0.02, "bf16"))
+        wsq = torch.full((int(lib.gptq_quantize_ws_bytes(m, n, 2, 1, 128)),), fill, dtype=torch.uint8,
+                         device="cuda")
+        q = g.gptq_quantize_layer(W, U, perm, 16, 32, 128, ws=wsq)
+        torch.cuda.synchronize()
+        runs.append([host(H), host(U), host(perm), host(q["codes"]), host(q["scales"]), host(q["zeros"]),
+                     host(q["row_loss"])])
+    for a, b in zip(*runs):
+        np.testing.assert_array_equal(a, b)
+    assert np.all(np.isfinite(runs[0][1])) and np.all(np.isfinite(runs[0][6]))
