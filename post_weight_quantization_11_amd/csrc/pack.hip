@@ -14,11 +14,29 @@ constexpr int kThreads = 256;
 
 template <int BITS>
 __device__ inline void pack32(const uint8_t* src, int count, uint32_t (&out)[BITS]) {
+  // 32 codes as bytes: two 16-byte reads when the segment is whole and
+  // aligned (rows of a multiple of 16 codes), else one byte at a time.
+  uint32_t b[8];
+  if (count == 32 && (reinterpret_cast<uintptr_t>(src) & 15) == 0) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(src);
+    const uint4 hi = *reinterpret_cast<const uint4*>(src + 16);
+    b[0] = lo.x; b[1] = lo.y; b[2] = lo.z; b[3] = lo.w;
+    b[4] = hi.x; b[5] = hi.y; b[6] = hi.z; b[7] = hi.w;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      uint32_t v = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (4 * q + t < count) v |= (uint32_t)src[4 * q + t] << (8 * t);
+      b[q] = v;
+    }
+  }
 #pragma unroll
   for (int w = 0; w < BITS; ++w) out[w] = 0u;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
-    const uint32_t c = k < count ? (uint32_t)src[k] : 0u;
+    const uint32_t c = (b[k >> 2] >> (8 * (k & 3))) & 0xffu;
     const int bit = k * BITS;
     out[bit >> 5] |= c << (bit & 31);
     if ((bit & 31) + BITS > 32) out[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
@@ -29,7 +47,7 @@ template <int BITS>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t* __restrict__ codes, int n,
                                                         const int32_t* __restrict__ perm,
                                                         uint32_t* __restrict__ packed, int64_t ldp) {
-  extern __shared__ uint8_t row_s[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t row_s[];
   const int64_t r = blockIdx.x;
   const uint8_t* src = codes + r * n;
   if (perm != nullptr) {
