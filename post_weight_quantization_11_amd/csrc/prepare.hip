@@ -427,7 +427,11 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
   const bool panel = tile < T;
   double* p = panel ? A + (int64_t)(kb + 1 + tile) * kB * np + (int64_t)kb * kB + (int64_t)part * 16 * np
                     : X + (int64_t)kb * kB * np + (int64_t)(tile - T) * kB + part * 16;
-  for (int e = tid; e < kB * kB; e += kThreads) Ls[e >> 6][e & 63] = Linv[e];
+  for (int e = tid; e < kB * kB / 2; e += kThreads) {
+    const double2 v = reinterpret_cast<const double2*>(Linv)[e];
+    Ls[e >> 5][(e & 31) * 2] = v.x;
+    Ls[e >> 5][(e & 31) * 2 + 1] = v.y;
+  }
   for (int e = tid; e < kB * 16; e += kThreads) {
     if (panel) {
       const int r = e >> 6, k = e & 63;
@@ -438,7 +442,8 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
     }
   }
   __syncthreads();
-  doublex4 acc = {0.0, 0.0, 0.0, 0.0};
+  // Two accumulators (even and odd k4) halve the dependent MFMA chain.
+  doublex4 acc2[2] = {{0.0, 0.0, 0.0, 0.0}, {0.0, 0.0, 0.0, 0.0}};
 #pragma unroll
   for (int k4 = 0; k4 < kB / 4; ++k4) {
     const int k = k4 * 4 + (lane >> 4);
@@ -446,8 +451,9 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
     // inverse row: C = Linv P (A element Linv[row][k], B element P[k][col]).
     const double a = panel ? Ps[k][lane & 15] : Ls[wave * 16 + (lane & 15)][k];
     const double b = panel ? Ls[wave * 16 + (lane & 15)][k] : Ps[k][lane & 15];
-    acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc, 0, 0, 0);
+    acc2[k4 & 1] = __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, acc2[k4 & 1], 0, 0, 0);
   }
+  const doublex4 acc = acc2[0] + acc2[1];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = (lane >> 4) + 4 * r, col = lane & 15;
