@@ -338,7 +338,12 @@ __global__ __launch_bounds__(kThreads) void potrf_diag_kernel(double* __restrict
   __shared__ TileLds t;
   __shared__ FactorLds fx;
   const int64_t base = (int64_t)kb * kB * np + (int64_t)kb * kB;
-  for (int e = threadIdx.x; e < kB * kB; e += kThreads) t.As[e >> 6][e & 63] = A[base + (int64_t)(e >> 6) * np + (e & 63)];
+  for (int e = threadIdx.x; e < kB * kB / 2; e += kThreads) {
+    const int r = e >> 5, c = (e & 31) * 2;
+    const double2 v = *reinterpret_cast<const double2*>(A + base + (int64_t)r * np + c);
+    t.As[r][c] = v.x;
+    t.As[r][c + 1] = v.y;
+  }
   __syncthreads();
   factor_diag(&t.As[0][0], &t.Bs[0][0], fx, X, Linv, np, n, kb, info);
 }
@@ -360,13 +365,20 @@ __device__ inline void tri_decode(int t, int& ii, int& jj) {
 __device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, const double* Bp, int64_t ldb,
                                    bool transB, double* Cp, int64_t ldc, bool sub, double* keep) {
   const int tid = threadIdx.x;
-  for (int e = tid; e < kB * kB; e += kThreads) {
-    const int r = e >> 6, c = e & 63;
-    t.As[r][c] = Ap[(int64_t)r * lda + c];
-    if (transB)
-      t.Bs[c][r] = Bp[(int64_t)r * ldb + c];
-    else
-      t.Bs[r][c] = Bp[(int64_t)r * ldb + c];
+  // Two elements per load (every operand row starts 16-byte aligned).
+  for (int e = tid; e < kB * kB / 2; e += kThreads) {
+    const int r = e >> 5, c = (e & 31) * 2;
+    const double2 a = *reinterpret_cast<const double2*>(Ap + (int64_t)r * lda + c);
+    const double2 b = *reinterpret_cast<const double2*>(Bp + (int64_t)r * ldb + c);
+    t.As[r][c] = a.x;
+    t.As[r][c + 1] = a.y;
+    if (transB) {
+      t.Bs[c][r] = b.x;
+      t.Bs[c + 1][r] = b.y;
+    } else {
+      t.Bs[r][c] = b.x;
+      t.Bs[r][c + 1] = b.y;
+    }
   }
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
@@ -530,9 +542,10 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   const int per = (total - 1 + (int)gridDim.x - 2) / ((int)gridDim.x - 1);
   const int t_lo = 1 + ((int)blockIdx.x - 1) * per;
   const int t_hi = min(total, t_lo + per);
-  double ra[16], rb[16];
+  double2 ra[8], rb[8];
   bool rtb = false;
   int ra_row = -1;
+  // Operand tiles two elements per load: element pair (r, c..c+1) of slot i.
   auto load_ops = [&](int t) {
     const double *pa, *pb;
     double* pc;
@@ -541,23 +554,27 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     const bool new_a = bi != ra_row;
     ra_row = bi;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int e = tid + kThreads * i;
-      const int r = e >> 6, c = e & 63;
-      if (new_a) ra[i] = pa[(int64_t)r * np + c];
-      rb[i] = pb[(int64_t)r * np + c];
+      const int r = e >> 5, c = (e & 31) * 2;
+      if (new_a) ra[i] = *reinterpret_cast<const double2*>(pa + (int64_t)r * np + c);
+      rb[i] = *reinterpret_cast<const double2*>(pb + (int64_t)r * np + c);
     }
   };
   auto store_ops = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int e = tid + kThreads * i;
-      const int r = e >> 6, c = e & 63;
-      lds.u.As[buf][r][c] = ra[i];
-      if (rtb)
-        lds.u.Bs[buf][c][r] = rb[i];
-      else
-        lds.u.Bs[buf][r][c] = rb[i];
+      const int r = e >> 5, c = (e & 31) * 2;
+      lds.u.As[buf][r][c] = ra[i].x;
+      lds.u.As[buf][r][c + 1] = ra[i].y;
+      if (rtb) {
+        lds.u.Bs[buf][c][r] = rb[i].x;
+        lds.u.Bs[buf][c + 1][r] = rb[i].y;
+      } else {
+        lds.u.Bs[buf][r][c] = rb[i].x;
+        lds.u.Bs[buf][r][c + 1] = rb[i].y;
+      }
     }
   };
   int t = t_lo;
