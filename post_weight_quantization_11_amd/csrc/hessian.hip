@@ -365,7 +365,10 @@ __global__ __launch_bounds__(kThreads, 1) void syrk16_direct_kernel(
   // later LDS read and the barrier wait for all loads in flight, including
   // the ones just issued for the next stage.  The waits the pipeline needs
   // are explicit (before each barrier).  M0 holds the LDS
-  // destination; one wait state separates its write from the load.
+  // destination; one wait state separates its write from the load.  The
+  // compiler does not keep M0 live across the statement, so the kernel
+  // must not index registers dynamically (which would use M0): every
+  // fragment and accumulator index here is a compile-time constant.
   auto load_row = [&](int buf, int64_t t0, int i) {
     const int r = wave * kRowsPerWave + i;
     const int64_t t = min(t0 + r, t_end - 1);
