@@ -450,28 +450,44 @@ __device__ __forceinline__ void sweep_body(
   // waves never wait for one another), and while it runs sub-block sb+1's
   // columns accumulates sub-block sb's slice E[:, 16] x U_off[16, 128] with
   // 32 fp32 MFMA 16x16x4 (the last slice after the block).
+  // The accumulator's columns are permuted so that each lane's B values are
+  // four adjacent floats: output tile ct, MFMA column c stands for block
+  // column 64*(ct/4) + 4*c + ct%4.  A lane then reads its 32 values of a
+  // slice with eight 16-byte loads, and writes Plast with 16-byte stores.
   const int c0n = c0 + kBS;
   const int bwn = min(kBS, n - c0n);
   floatx4 pacc[kBS / 16];
 #pragma unroll
   for (int ct = 0; ct < kBS / 16; ++ct) pacc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-  // B element (k, column) of 16x16x4: k = 4*k4 + lane/16, column lane%16.
-  float uf[2][kSB / 4][kBS / 16];
-  auto uoff_load = [&](int j0, float (&f)[kSB / 4][kBS / 16]) {
+  const bool vec_uo = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
+  // uf[k4][h][t]: B element (k = 4*k4 + lane/16) of tile ct = 4*h + t, i.e.
+  // U_off[k, 64*h + 4*(lane%16) + t].
+  floatx4 uf[2][kSB / 4][2];
+  auto uoff_load = [&](int j0, floatx4 (&f)[kSB / 4][2]) {
 #pragma unroll
     for (int k4 = 0; k4 < kSB / 4; ++k4) {
-      const float* p = U + (int64_t)(c0 + j0 + 4 * k4 + (lane >> 4)) * n + c0n + (lane & 15);
+      const float* p = U + (int64_t)(c0 + j0 + 4 * k4 + (lane >> 4)) * n + c0n + 4 * (lane & 15);
 #pragma unroll
-      for (int ct = 0; ct < kBS / 16; ++ct) f[k4][ct] = ct * 16 + (lane & 15) < bwn ? p[ct * 16] : 0.f;
+      for (int h = 0; h < 2; ++h) {
+        const int c = 64 * h + 4 * (lane & 15);
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+        if (vec_uo && c + 4 <= bwn) {
+          v = *reinterpret_cast<const floatx4*>(p + 64 * h);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) v[t] = c + t < bwn ? p[64 * h + t] : 0.f;
+        }
+        f[k4][h] = v;
+      }
     }
   };
-  auto uoff_accumulate = [&](int j0, const float (&f)[kSB / 4][kBS / 16]) {
+  auto uoff_accumulate = [&](int j0, const floatx4 (&f)[kSB / 4][2]) {
 #pragma unroll
     for (int k4 = 0; k4 < kSB / 4; ++k4) {
       const float a = T[wave][lane & 15][j0 + 4 * k4 + (lane >> 4)];
 #pragma unroll
       for (int ct = 0; ct < kBS / 16; ++ct)
-        pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, f[k4][ct], pacc[ct], 0, 0, 0);
+        pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, f[k4][ct >> 2][ct & 3], pacc[ct], 0, 0, 0);
     }
   };
 
@@ -538,8 +554,9 @@ __device__ __forceinline__ void sweep_body(
         if constexpr (kSlice) {
           const int k4 = jj >> 2, ct = 2 * (jj & 3);
           const auto& f = uf[(decltype(sbc)::value - 1) & 1];
-          pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct], pacc[ct], 0, 0, 0);
-          pacc[ct + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct + 1], pacc[ct + 1], 0, 0, 0);
+          pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct >> 2][ct & 3], pacc[ct], 0, 0, 0);
+          pacc[ct + 1] =
+              __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][(ct + 1) >> 2][(ct + 1) & 3], pacc[ct + 1], 0, 0, 0);
         }
         float uc[kSB];
 #pragma unroll
@@ -641,14 +658,25 @@ __device__ __forceinline__ void sweep_body(
   if (make_next) {
     // Last slice, then Plast[rows] = E[rows, block kb] U[block kb, block kb+1].
     uoff_accumulate(kBS - kSB, uf[(kBS / kSB - 1) & 1]);
-    // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, column l%16.
+    // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, MFMA
+    // column l%16, so tiles 4h .. 4h+3 hold block columns 64h + 4*(l%16) + 0..3.
+    const bool vec_pl = (reinterpret_cast<uintptr_t>(Plast) & 15) == 0;
 #pragma unroll
-    for (int ct = 0; ct < kBS / 16; ++ct)
+    for (int i = 0; i < 4; ++i) {
+      const int64_t grow = row0 + 4 * (lane >> 4) + i;
+      if (grow >= m) continue;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t grow = row0 + 4 * (lane >> 4) + i;
-        if (grow < m) Plast[grow * kBS + ct * 16 + (lane & 15)] = pacc[ct][i];
+      for (int h = 0; h < 2; ++h) {
+        float* d = Plast + grow * kBS + 64 * h + 4 * (lane & 15);
+        const floatx4 v = {pacc[4 * h][i], pacc[4 * h + 1][i], pacc[4 * h + 2][i], pacc[4 * h + 3][i]};
+        if (vec_pl) {
+          *reinterpret_cast<floatx4*>(d) = v;
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) d[t] = v[t];
+        }
       }
+    }
   }
 }
 
