@@ -422,15 +422,16 @@ __device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, co
 }
 
 // Step kb, first launch: panel L[i, kb] = A[i, kb] inv(L_kk)^T for i > kb
-// (tiles 0 .. T-1) and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
+// (tiles 0 .. T-1; also written transposed to Lt[k][i], the row-major B
+// operand of the trailing update) and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
 // for j < kb (tiles T .. T+kb-1), four workgroups per 64 x 64 tile.  A
 // workgroup owns 16 output rows of a panel tile (which read only those rows)
 // or 16 output columns of an inverse-row tile (which read only those
 // columns), so results go back in place without races; each wave computes
 // one 16 x 16 block with 16 float64 MFMAs.
 __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict__ A, double* __restrict__ X,
-                                                              const double* __restrict__ Linv, int np, int nbk,
-                                                              int kb) {
+                                                              const double* __restrict__ Linv,
+                                                              double* __restrict__ Lt, int np, int nbk, int kb) {
   __shared__ double Ls[kB][kP];      // inv(L_kk)
   __shared__ double Ps[kB][17];      // the tile's 16 rows (transposed) or 16 columns, [k][16]
   const int T = nbk - kb - 1;
@@ -469,9 +470,10 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = (lane >> 4) + 4 * r, col = lane & 15;
-    if (panel)
+    if (panel) {
       p[(int64_t)row * np + wave * 16 + col] = acc[r];
-    else
+      Lt[(int64_t)(wave * 16 + col) * np + (kb + 1 + tile) * kB + part * 16 + row] = acc[r];
+    } else
       p[(int64_t)(wave * 16 + row) * np + col] = acc[r];
   }
 }
@@ -479,17 +481,13 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
 // Step kb, second launch: trailing update A[i, j] -= L[i, kb] L[j, kb]^T for
 // kb < j <= i ("SYRK" tiles) and T[i, j] -= L[i, kb] X[kb, j] for i > kb,
 // j <= kb ("inverse" tiles).  Tile 0 is the next diagonal block; workgroup 0
-// updates it and then factors and inverts it with factor_diag.  The other
-// workgroups loop over the remaining tiles: the operands of the next tile are
-// loaded into registers while the current tile is multiplied from LDS (two
-// LDS buffers, one barrier per tile), and each C block is read before and
-// written after its MFMAs.  No tile reads what another tile of the launch
-// writes.
-struct UpdateLds {
-  double As[2][kB][kP];
-  double Bs[2][kB][kP];
-};
-
+// updates it and then factors and inverts it with factor_diag.  Every wave of
+// the other workgroups owns a contiguous range of half tiles (32 rows x 64
+// columns) and runs each on its own: operands go from global memory (mostly
+// L2) straight into MFMA registers in 16-column-deep chunks, the next chunk
+// in flight while the current one multiplies, so no wave waits for another
+// and loads, stores and MFMAs of one wave overlap.  No tile reads what another
+// tile of the launch writes.
 __device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, double* X, const double*& pa,
                                        const double*& pb, double*& pc, bool& transB, int& bi_out) {
   if (t < S) {
@@ -512,13 +510,23 @@ __device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, 
   }
 }
 
+// Half tiles per workgroup of the trailing update (one per wave at a time).
+constexpr int kUpdWaves = kThreads / 64;
+
+// Workgroups for step kb's update launch: workgroup 0 plus enough for about
+// one half tile per wave, at most one workgroup per CU.
+inline int update_grid(int nbk, int kb) {
+  const int T = nbk - kb - 1;
+  const int total = T * (T + 1) / 2 + T * (kb + 1);
+  const int units = 2 * (total - 1);
+  return 1 + std::min((units + kUpdWaves - 1) / kUpdWaves, kUpdateBlocks - 1);
+}
+
 __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restrict__ A, double* __restrict__ X,
-                                                               double* __restrict__ Linv, int np, int n, int nbk,
+                                                               double* __restrict__ Linv,
+                                                               const double* __restrict__ Lt, int np, int n, int nbk,
                                                                int kb, int32_t* __restrict__ info) {
-  __shared__ union {
-    TileLds t;
-    UpdateLds u;
-  } lds;
+  __shared__ TileLds tl;
   __shared__ FactorLds fx;
   const int T = nbk - kb - 1;
   const int S = T * (T + 1) / 2;
@@ -529,121 +537,143 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     bool tb;
     int bi;
     update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb, bi);
-    gemm_tile64(lds.t, pa, np, pb, np, tb, pc, np, true, &lds.t.As[0][0]);
+    gemm_tile64(tl, pa, np, pb, np, tb, pc, np, true, &tl.As[0][0]);
     __syncthreads();
-    factor_diag(&lds.t.As[0][0], &lds.t.Bs[0][0], fx, X, Linv, np, n, kb + 1, info);
+    factor_diag(&tl.As[0][0], &tl.Bs[0][0], fx, X, Linv, np, n, kb + 1, info);
     return;
   }
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int wr = wave >> 1, wc = wave & 1;
-  // Workgroup b takes a contiguous range of the row-major tile list, so
-  // consecutive tiles mostly share their block row bi and with it the
-  // L[bi, kb] operand, which is then not loaded again.
-  const int per = (total - 1 + (int)gridDim.x - 2) / ((int)gridDim.x - 1);
-  const int t_lo = 1 + ((int)blockIdx.x - 1) * per;
-  const int t_hi = min(total, t_lo + per);
-  double2 ra[8], rb[8];
-  bool rtb = false;
-  int ra_row = -1;
-  // Operand tiles two elements per load: element pair (r, c..c+1) of slot i.
-  auto load_ops = [&](int t) {
-    const double *pa, *pb;
-    double* pc;
-    int bi;
-    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, rtb, bi);
-    const bool new_a = bi != ra_row;
-    ra_row = bi;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + kThreads * i;
-      const int r = e >> 5, c = (e & 31) * 2;
-      if (new_a) ra[i] = *reinterpret_cast<const double2*>(pa + (int64_t)r * np + c);
-      rb[i] = *reinterpret_cast<const double2*>(pb + (int64_t)r * np + c);
-    }
+  // Half tile u covers tile u/2 (tiles 1 .. total-1), rows 32*(u%2) .. +31.
+  const int lane = threadIdx.x & 63;
+  const int gw = ((int)blockIdx.x - 1) * kUpdWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nw = ((int)gridDim.x - 1) * kUpdWaves;
+  const int units = 2 * (total - 1);
+  const int per = (units + nw - 1) / nw;
+  const int u_lo = 2 + gw * per;
+  const int u_hi = min(2 + units, u_lo + per);
+  if (u_lo >= u_hi) return;
+  // float64 MFMA 16x16x4: A element (row l%16, k l/16), B element (k l/16,
+  // column l%16), accumulator register r of lane l: row l/16 + 4r, column
+  // l%16.  The contraction index and the output columns are permuted so that
+  // every load and store is 16 bytes wide: MFMA step s (0..15) with lane
+  // quarter q = l/16 stands for k = 8*(s/2) + 2q + s%2 (a lane's two steps
+  // 2j, 2j+1 read one adjacent pair of k of its A row), and column block cb
+  // (0..3) with MFMA column c stands for tile column 32*(cb/2) + 2c + cb%2
+  // (blocks 2p and 2p+1 read one adjacent pair of columns of a B row and of
+  // a C row).  B is row-major over k for both kinds of tile: Lt[k][j] for a
+  // SYRK tile, X[kb rows k][j] for an inverse tile.
+  const int q = lane >> 4, c16 = lane & 15;
+  constexpr int kChunk = 4;                    // MFMA steps per chunk (16 of k)
+  constexpr int kChunks = kB / 4 / kChunk;
+  // One chunk: a[rb][jj] = A row rb*16 + c16 at the k pair of steps 2jj,
+  // 2jj+1; b[ss][pp] = B row of step ss at columns 32pp + 2*c16 + 0..1.
+  struct Chunk {
+    double2 a[2][kChunk / 2];
+    double2 b[kChunk][2];
   };
-  auto store_ops = [&](int buf) {
+  auto load_chunk = [&](Chunk& ck, const double* ua, const double* ub, int ch) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int e = tid + kThreads * i;
-      const int r = e >> 5, c = (e & 31) * 2;
-      lds.u.As[buf][r][c] = ra[i].x;
-      lds.u.As[buf][r][c + 1] = ra[i].y;
-      if (rtb) {
-        lds.u.Bs[buf][c][r] = rb[i].x;
-        lds.u.Bs[buf][c + 1][r] = rb[i].y;
-      } else {
-        lds.u.Bs[buf][r][c] = rb[i].x;
-        lds.u.Bs[buf][r][c + 1] = rb[i].y;
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int jj = 0; jj < kChunk / 2; ++jj) {
+        const int k = 8 * (ch * kChunk / 2 + jj) + 2 * q;
+        ck.a[rb][jj] = *reinterpret_cast<const double2*>(ua + (int64_t)(rb * 16 + c16) * np + k);
       }
-    }
+#pragma unroll
+    for (int ss = 0; ss < kChunk; ++ss)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const int st = ch * kChunk + ss;
+        const int k = 8 * (st >> 1) + 2 * q + (st & 1);
+        ck.b[ss][pp] = *reinterpret_cast<const double2*>(ub + (int64_t)k * np + 32 * pp + 2 * c16);
+      }
   };
-  int t = t_lo;
-  if (t < t_hi) {
-    load_ops(t);
-    store_ops(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (t < t_hi) {
-    const int tn = t + 1;
-    const double *pa, *pb;
-    double* pc;
-    bool tb;
-    int bi;
-    update_tile_ref(t, S, kb, np, A, X, pa, pb, pc, tb, bi);
-    if (tn < t_hi) load_ops(tn);
-    // C block in the accumulator layout (row (lane>>4) + 4r of each 16 x 16
-    // block, column lane & 15), read ahead of the MFMAs.  An inverse tile
-    // T[i, kb] is touched here for the first time and starts from zero (X is
-    // never cleared as a whole).
-    const bool first = t >= S && (t - S) % (kb + 1) == kb;
-    doublex4 cv[2][2];
-    if (first) {
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj) cv[ti][tj] = doublex4{0.0, 0.0, 0.0, 0.0};
+  // Unit u's operands: A rows of the half tile, the B block (row-major over
+  // k, leading dimension np), the C rows.
+  auto unit_ref = [&](int u, const double*& ua, const double*& ub, double*& uc) {
+    const int t = u >> 1;
+    int bi, bj;
+    if (t < S) {
+      int ii, jj;
+      tri_decode(t, ii, jj);
+      bi = kb + 1 + ii;
+      bj = kb + 1 + jj;
+      ub = Lt + (int64_t)bj * kB;
+      uc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
     } else {
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            cv[ti][tj][r] = pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)];
+      const int e = t - S;
+      bi = kb + 1 + e / (kb + 1);
+      bj = e % (kb + 1);
+      ub = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
+      uc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
     }
-    doublex4 acc[2][2];
+    ua = A + ((int64_t)bi * kB + (u & 1) * 32) * np + (int64_t)kb * kB;
+    uc += (int64_t)(u & 1) * 32 * np;
+  };
+  Chunk ck[2];
+  const double *pa, *pb;
+  double* pc;
+  unit_ref(u_lo, pa, pb, pc);
+  load_chunk(ck[0], pa, pb, 0);
+  for (int u = u_lo; u < u_hi; ++u) {
+    const int t = u >> 1;
+    // C in the accumulator layout: cv[rb][pp][r] = row rb*16 + q + 4r,
+    // columns 32pp + 2*c16 + 0..1 (column blocks 2pp, 2pp+1).  An inverse
+    // tile T[i, kb] is touched here for the first time: its old contents
+    // (X is never cleared as a whole) are read but replaced by zero.
+    const bool first = t >= S && (t - S) % (kb + 1) == kb;
+    double2 cv[2][2][4];
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-      for (int tj = 0; tj < 2; ++tj) acc[ti][tj] = doublex4{0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int k4 = 0; k4 < kB / 4; ++k4) {
-      const int k = k4 * 4 + (lane >> 4);
-      double av[2], bv[2];
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti) av[ti] = lds.u.As[buf][wr * 32 + ti * 16 + (lane & 15)][k];
-#pragma unroll
-      for (int tj = 0; tj < 2; ++tj) bv[tj] = lds.u.Bs[buf][k][wc * 32 + tj * 16 + (lane & 15)];
-#pragma unroll
-      for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-        for (int tj = 0; tj < 2; ++tj)
-          acc[ti][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(av[ti], bv[tj], acc[ti][tj], 0, 0, 0);
-    }
-#pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
-#pragma unroll
-      for (int tj = 0; tj < 2; ++tj)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          pc[(int64_t)(wr * 32 + ti * 16 + (lane >> 4) + 4 * r) * np + wc * 32 + tj * 16 + (lane & 15)] =
-              cv[ti][tj][r] - acc[ti][tj][r];
-    // Buffer buf ^ 1 was last read before the previous barrier.
-    if (tn < t_hi) store_ops(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    t = tn;
+          cv[rb][pp][r] =
+              *reinterpret_cast<const double2*>(pc + (int64_t)(rb * 16 + q + 4 * r) * np + 32 * pp + 2 * c16);
+    doublex4 acc[2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) acc[rb][cb] = doublex4{0.0, 0.0, 0.0, 0.0};
+    // The next unit's first chunk is loaded during this unit's last one (the
+    // last unit loads its own first chunk again, which is never used).
+    const double *na, *nb;
+    double* nc;
+    unit_ref(u + 1 < u_hi ? u + 1 : u, na, nb, nc);
+#pragma unroll
+    for (int ch = 0; ch < kChunks; ++ch) {
+      Chunk& cur = ck[ch & 1];
+      Chunk& nxt = ck[(ch + 1) & 1];
+      if (ch + 1 < kChunks)
+        load_chunk(nxt, pa, pb, ch + 1);
+      else
+        load_chunk(nxt, na, nb, 0);
+#pragma unroll
+      for (int ss = 0; ss < kChunk; ++ss)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const double av = (ss & 1) ? cur.a[rb][ss >> 1].y : cur.a[rb][ss >> 1].x;
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const double bv = (cb & 1) ? cur.b[ss][cb >> 1].y : cur.b[ss][cb >> 1].x;
+            acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[rb][cb], 0, 0, 0);
+          }
+        }
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const double2 c = cv[rb][pp][r];
+          const double c0 = first ? 0.0 : c.x, c1 = first ? 0.0 : c.y;
+          *reinterpret_cast<double2*>(pc + (int64_t)(rb * 16 + q + 4 * r) * np + 32 * pp + 2 * c16) =
+              double2{c0 - acc[rb][2 * pp][r], c1 - acc[rb][2 * pp + 1][r]};
+        }
+    pa = na;
+    pb = nb;
+    pc = nc;
   }
 }
 
@@ -658,7 +688,7 @@ __global__ __launch_bounds__(kThreads) void write_u_kernel(const double* __restr
 
 struct PrepLayout {
   int64_t np;
-  size_t off_A, off_X, off_Linv, off_lam, off_info, total;
+  size_t off_A, off_X, off_Linv, off_Lt, off_lam, off_info, total;
 };
 
 PrepLayout prep_layout(int64_t n) {
@@ -668,7 +698,8 @@ PrepLayout prep_layout(int64_t n) {
   L.off_A = 0;
   L.off_X = align256(L.off_A + mat);
   L.off_Linv = align256(L.off_X + mat);
-  L.off_lam = align256(L.off_Linv + (size_t)kB * kB * sizeof(double));
+  L.off_Lt = align256(L.off_Linv + (size_t)kB * kB * sizeof(double));
+  L.off_lam = align256(L.off_Lt + (size_t)kB * (size_t)L.np * sizeof(double));
   L.off_info = align256(L.off_lam + sizeof(double));
   L.total = align256(L.off_info + sizeof(int32_t));
   return L;
@@ -699,6 +730,7 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   double* A = reinterpret_cast<double*>(base + L.off_A);
   double* X = reinterpret_cast<double*>(base + L.off_X);
   double* Linv = reinterpret_cast<double*>(base + L.off_Linv);
+  double* Lt = reinterpret_cast<double*>(base + L.off_Lt);
   double* lam = reinterpret_cast<double*>(base + L.off_lam);
   int32_t* info = reinterpret_cast<int32_t*>(base + L.off_info);
   const int ni = (int)n, np = (int)L.np, nbk = (int)(L.np / kB);
@@ -711,10 +743,9 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, 0, info);
   for (int kb = 0; kb < nbk; ++kb) {
     const int T = nbk - kb - 1;
-    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(4 * (T + kb)), kThreads, 0, st>>>(A, X, Linv, np, nbk, kb);
+    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(4 * (T + kb)), kThreads, 0, st>>>(A, X, Linv, Lt, np, nbk, kb);
     if (T > 0)
-      chol_update_kernel<<<(unsigned)std::min(T * (T + 1) / 2 + T * (kb + 1), kUpdateBlocks), kThreads, 0, st>>>(A, X, Linv, np, ni, nbk,
-                                                                                         kb, info);
+      chol_update_kernel<<<(unsigned)update_grid(nbk, kb), kThreads, 0, st>>>(A, X, Linv, Lt, np, ni, nbk, kb, info);
     GPTQ_TRY_LAUNCH();
   }
   write_u_kernel<<<(unsigned)n, kThreads, 0, st>>>(X, ni, np, U);
