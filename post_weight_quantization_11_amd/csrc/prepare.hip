@@ -543,8 +543,16 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     return;
   }
   // Half tile u covers tile u/2 (tiles 1 .. total-1), rows 32*(u%2) .. +31.
+  // Workgroups are dispatched to the 8 XCDs round-robin (workgroup b on XCD
+  // b mod 8); the workers of one XCD take consecutive ranges, so each XCD
+  // works on one band of block rows and its L2 holds that band's panel rows
+  // instead of the whole panel.
   const int lane = threadIdx.x & 63;
-  const int gw = ((int)blockIdx.x - 1) * kUpdWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int G = (int)gridDim.x, xcd = (int)blockIdx.x & 7, slot = (int)blockIdx.x >> 3;
+  int before = 0;
+  for (int y = 0; y < xcd; ++y) before += (G - y + 7) / 8 - (y == 0 ? 1 : 0);
+  const int worker = before + slot - (xcd == 0 ? 1 : 0);
+  const int gw = worker * kUpdWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nw = ((int)gridDim.x - 1) * kUpdWaves;
   const int units = 2 * (total - 1);
   const int per = (units + nw - 1) / nw;
