@@ -23,5 +23,8 @@ from .gptq_oracle import (  # noqa: F401
     pack_codes,
     unpack_codes,
     packed_words_per_row,
+    dequantize_packed,
+    dequant_matmul,
+    dequant_matmul_bound,
     gptq_layer,
 )

@@ -396,6 +396,44 @@ def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# f2: reading the packed weights back (GPTQ knowledge note, "Tradeoffs": the
+# speed of a quantized model rests on kernels that consume packed weights,
+# inference being limited by weight memory traffic; anthology record
+# SOTA-185, "The scope worth holding onto": decode is bandwidth-bound).
+# ---------------------------------------------------------------------------
+def dequantize_packed(packed, n: int, bits: int, scales, zeros, g_idx) -> np.ndarray:
+    """W^[r, k] = s[r, g_idx[k]] * (c[r, k] - z[r, g_idx[k]]), float64.
+
+    ``packed`` is the row-wise LSB-first bit stream of pack_codes (original
+    column order); ``g_idx`` gives each original column's group.
+    """
+    codes = unpack_codes(packed, n, bits).astype(F64)
+    gi = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=F64)[:, gi]
+    z = np.asarray(zeros, dtype=F64)[:, gi]
+    return s * (codes - z)
+
+
+def dequant_matmul(packed, n: int, bits: int, scales, zeros, g_idx, X) -> np.ndarray:
+    """Y = X W^T (batch x m), float64, W^ from dequantize_packed."""
+    What = dequantize_packed(packed, n, bits, scales, zeros, g_idx)
+    return np.asarray(X, dtype=F64) @ What.T
+
+
+def dequant_matmul_bound(packed, n: int, bits: int, scales, zeros, g_idx, X) -> np.ndarray:
+    """M[b, r] = sum_k s[r, g_k] (c[r, k] + z[r, g_k]) |X[b, k]|, float64.
+
+    The scale of the rounding error of any float32 evaluation of
+    dequant_matmul that forms s * (sum c x - z sum x) or sum s (c - z) x.
+    """
+    codes = unpack_codes(packed, n, bits).astype(F64)
+    gi = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=F64)[:, gi]
+    z = np.asarray(zeros, dtype=F64)[:, gi]
+    return np.abs(np.asarray(X, dtype=F64)) @ (s * (codes + z)).T
+
+
+# ---------------------------------------------------------------------------
 # End to end for one layer.
 # ---------------------------------------------------------------------------
 def gptq_layer(W, X=None, H=None, levels: int = 16, group_size: int = 0,

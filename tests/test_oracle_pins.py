@@ -450,3 +450,40 @@ def test_planted_mistakes_are_caught(name, monkeypatch):
         except AssertionError:
             caught.append(check)
     assert caught, f"mutation '{name}' was not caught by any pin"
+
+
+# ---------------------------------------------------------------------------
+# f2 reading the packed weights back.
+# ---------------------------------------------------------------------------
+def test_dequant_matvec_fixture():
+    kv = dict(ln.split(None, 1) for ln in read_golden("dequant_matvec.txt"))
+    bits, n = int(kv["bits"]), int(kv["n"])
+    g_idx = np.array(kv["g_idx"].split(), dtype=np.int32)
+    codes = np.array([kv["codes0"].split(), kv["codes1"].split()], dtype=np.int64)
+    words = np.array([[int(kv["word0"], 16)], [int(kv["word1"], 16)]], dtype=np.uint32)
+    scales = np.array([kv["scales0"].split(), kv["scales1"].split()], dtype=np.float32)
+    zeros = np.array([kv["zeros0"].split(), kv["zeros1"].split()], dtype=np.uint8)
+    X = np.array([kv["x0"].split(), kv["x1"].split()], dtype=np.float64)
+    Y = np.array([kv["y0"].split(), kv["y1"].split()], dtype=np.float64)
+    np.testing.assert_array_equal(oracle.pack_codes(codes, bits), words)
+    np.testing.assert_array_equal(oracle.unpack_codes(words, n, bits), codes)
+    np.testing.assert_array_equal(oracle.dequant_matmul(words, n, bits, scales, zeros, g_idx, X), Y)
+
+
+@pytest.mark.parametrize("levels,group,act", [(16, 0, False), (8, 32, True), (4, 64, False), (3, 16, True)])
+def test_dequant_packed_matches_the_sweep_dequantization(levels, group, act):
+    # Two routes to W^: dequantize() reads the sweep's processing-order codes
+    # and groups and un-permutes; dequantize_packed() reads the packed stream
+    # in original order and looks each column's group up in g_idx.
+    rng = np.random.default_rng(7 + levels + group)
+    m, n = 6, 96
+    W = rng.normal(0.0, 0.02, size=(m, n))
+    X = rng.standard_normal((300, n)) * np.exp(rng.normal(0.0, 1.0, size=n))
+    res = oracle.gptq_layer(W, X=X, levels=levels, group_size=group, act_order=act)
+    Wp = oracle.dequantize_packed(res["packed"], n, res["bits"], res["scales"], res["zeros"], res["g_idx"])
+    np.testing.assert_array_equal(Wp, res["What"])
+    xb = rng.standard_normal((3, n))
+    np.testing.assert_allclose(oracle.dequant_matmul(res["packed"], n, res["bits"], res["scales"], res["zeros"],
+                                                     res["g_idx"], xb), xb @ res["What"].T, rtol=1e-12, atol=1e-15)
+    M = oracle.dequant_matmul_bound(res["packed"], n, res["bits"], res["scales"], res["zeros"], res["g_idx"], xb)
+    assert np.all(M >= np.abs(xb) @ np.abs(res["What"]).T)
