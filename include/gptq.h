@@ -164,6 +164,34 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t*
                       int bits, int group_size, uint32_t* packed, int64_t ld_packed,
                       int32_t* g_idx, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Reading the packed weights back: matrix-vector product for decode
+ * (GPTQ knowledge note, "Tradeoffs": the speed of a quantized model rests on
+ * kernels that consume the packed weights, inference being limited by weight
+ * memory traffic; anthology record SOTA-185, "The scope worth holding onto":
+ * decode is bandwidth-bound).
+ *   Y[b, r] = sum_k scales[r, g(k)] * (c[r, k] - zeros[r, g(k)]) * X[b, k]
+ * for b < batch, r < m, where c[r, k] is column k's code in row r of `packed`.
+ *   packed     device, m x ld_packed uint32 in the layout gptq_pack writes
+ *              (bits 2, 3 or 4; ld_packed >= ceil(n*bits/32)).
+ *   scales     device, m x G float32; zeros device, m x G uint8 (G >= 1).
+ *   g_idx      device, n int32 (the group of each column, < G) or NULL: then
+ *              g(k) = k / group_size, or 0 when group_size = 0.  gptq_pack's
+ *              g_idx output (act-order) can be passed as is.
+ *   X          device, batch x ldx IEEE binary16 (ldx >= n).
+ *   Y          device, batch x ldy float32 output (ldy >= m), overwritten.
+ *   batch      1 .. GPTQ_GEMV_MAX_BATCH (else GPTQ_ERR_UNSUPPORTED).
+ * Accumulation is float32; the rounding error of Y[b, r] is bounded by a
+ * small multiple of (n/32 + 64) 2^-24 sum_k s (c + z) |X[b, k]|.  Group
+ * indices in g_idx are not validated (an index >= G reads out of bounds).
+ * No workspace.
+ * ---------------------------------------------------------------------- */
+#define GPTQ_GEMV_MAX_BATCH 8
+gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed,
+                              int bits, const float* scales, const uint8_t* zeros, int64_t G,
+                              int group_size, const int32_t* g_idx, const uint16_t* X,
+                              int64_t batch, int64_t ldx, float* Y, int64_t ldy, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,10 @@ EXPORTS = (
     "gptq_quantize_ws_bytes",
     "gptq_quantize_layer",
     "gptq_pack",
+    "gptq_dequant_gemv",
 )
+
+GEMV_MAX_BATCH = 8
 
 _lib = None
 
@@ -71,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.gptq_quantize_layer.argtypes = [vp, C, i64, i64, i64, vp, vp, C, C, C, vp, vp, vp, vp, vp, sz, vp]
     lib.gptq_pack.restype = C
     lib.gptq_pack.argtypes = [vp, i64, i64, vp, C, C, vp, i64, vp, vp]
+    lib.gptq_dequant_gemv.restype = C
+    lib.gptq_dequant_gemv.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, vp, i64, i64, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -206,6 +211,37 @@ def gptq_pack(codes, perm=None, bits: int = 4, group_size: int = 0, want_g_idx: 
                        packed.stride(0) if m else packed_words(n, bits), _ptr(g_idx), _stream(stream))
     _check(rc, "gptq_pack")
     return packed, g_idx
+
+
+def gptq_dequant_gemv(packed, scales, zeros, X, n: int, bits: int, group_size: int = 0, g_idx=None,
+                      Y=None, stream=None):
+    """Y (batch x m float32) = X W^T with W^ read from the packed codes.
+
+    packed: m x ld words (int32 bit patterns, as gptq_pack returns); scales
+    m x G float32; zeros m x G uint8; X batch x n float16 (any leading
+    dimension); g_idx n int32 or None (groups of group_size columns).
+    """
+    torch = _torch()
+    lib = load()
+    _rows_check(packed)
+    _rows_check(X)
+    _device_check(scales, zeros, g_idx)
+    if X.dtype != torch.float16:
+        raise ValueError("X must be float16")
+    m = packed.shape[0]
+    batch = X.shape[0]
+    if X.shape[1] != n:
+        raise ValueError("X must have n columns")
+    if Y is None:
+        Y = torch.empty((batch, m), dtype=torch.float32, device=X.device)
+    else:
+        _rows_check(Y)
+    G = scales.shape[1] if scales.dim() == 2 else 1
+    rc = lib.gptq_dequant_gemv(_ptr(packed), m, int(n), packed.stride(0), int(bits), _ptr(scales), _ptr(zeros),
+                               int(G), int(group_size), _ptr(g_idx), _ptr(X), batch, X.stride(0), _ptr(Y),
+                               Y.stride(0), _stream(stream))
+    _check(rc, "gptq_dequant_gemv")
+    return Y
 
 
 def bits_for_levels(levels: int) -> int:

@@ -1,0 +1,301 @@
+// Reading the packed weights back: Y = X W^T straight from the packed codes,
+// for decode-sized batches.
+// GPTQ knowledge note, "Tradeoffs": the speed of a quantized model rests on
+// kernels that consume the packed weights, inference being limited by weight
+// memory traffic; anthology record SOTA-185, "The scope worth holding onto":
+// decode is bandwidth-bound.
+//
+//   Y[b, r] = sum_k s[r, g_k] (c[r, k] - z[r, g_k]) X[b, k]
+//
+// One wave owns kRows rows; lane l walks the row's 32-column segments l,
+// l + 64, ...  A segment is `bits` consecutive words of a row.  Its codes are
+// turned into float16 subnormals c * 2^-24 (a b-bit code is exactly the
+// mantissa of a subnormal whose exponent field is 0), two per register, and
+// multiplied into float32 by v_dot2_f32_f16 against the same two columns of
+// X, so decoding costs about one masked shift per two codes.  Codes are
+// paired as (c_i, c_{i+H}) with H = 4 (4-bit), 8 (2-bit) or 16 (3-bit) so
+// that one shift and one mask extract a pair; the matching X pairs are
+// rearranged once per segment (v_perm_b32) and shared by the wave's rows.
+// When the 32 columns of a segment share one group (per-row grids, or
+// contiguous groups of a multiple of 32 columns):
+//   y += s * (2^24 * sum_k c_k x_k - z * sum_k x_k)
+// with sum x formed once per segment.  Otherwise (g_idx given, or groups not a
+// multiple of 32) each code takes its own group: y += s_g (c - z_g) x in
+// float32.
+#include "common.h"
+
+namespace gptq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRows = 4;  // rows per wave
+constexpr int kSeg = 32;  // columns per lane segment
+constexpr float kTwo24 = 16777216.0f;
+
+typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
+
+// X pair (x_a, x_{a+H}) from the natural pairs xn[t] = (x_{2t}, x_{2t+1});
+// H is even, so both halves come from the same position of their pair.
+__device__ inline uint32_t x_pair(const uint32_t (&xn)[kSeg / 2], int a, int h) {
+  const uint32_t lo = xn[a >> 1], hi = xn[(a + h) >> 1];
+  return __builtin_amdgcn_perm(hi, lo, (a & 1) ? 0x07060302u : 0x05040100u);
+}
+
+// Code pairs of one segment, pair j = (c_{a_j}, c_{a_j + H}) as two float16
+// subnormals; a_j and H follow the bit width.
+template <int BITS> struct Decode;
+
+template <> struct Decode<4> {
+  static constexpr int H = 4;
+  __device__ static int first(int j) { return 8 * (j >> 2) + (j & 3); }
+  __device__ static void pairs(const uint32_t (&w)[4], uint32_t (&p)[kSeg / 2]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[4 * q + i] = (w[q] >> (4 * i)) & 0x000F000Fu;
+  }
+};
+
+template <> struct Decode<2> {
+  static constexpr int H = 8;
+  __device__ static int first(int j) { return 16 * (j >> 3) + (j & 7); }
+  __device__ static void pairs(const uint32_t (&w)[2], uint32_t (&p)[kSeg / 2]) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[8 * q + i] = (w[q] >> (2 * i)) & 0x00030003u;
+  }
+};
+
+template <> struct Decode<3> {
+  static constexpr int H = 16;
+  __device__ static int first(int j) { return j; }
+  __device__ static void pairs(const uint32_t (&w)[3], uint32_t (&p)[kSeg / 2]) {
+    // bits 0..47 hold codes 0..15, bits 48..95 codes 16..31
+    const uint64_t lo = (uint64_t)w[0] | ((uint64_t)(w[1] & 0xFFFFu) << 32);
+    const uint64_t hi = (uint64_t)(w[1] >> 16) | ((uint64_t)w[2] << 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      p[i] = (uint32_t)((lo >> (3 * i)) & 7u) | ((uint32_t)((hi >> (3 * i)) & 7u) << 16);
+  }
+};
+
+// Code k (0..31) of a segment from its words.
+template <int BITS>
+__device__ inline uint32_t code_at(const uint32_t (&w)[BITS], int k) {
+  const int bit = k * BITS, q = bit >> 5, off = bit & 31;
+  uint32_t v = w[q] >> off;
+  if (off + BITS > 32) v |= w[q + 1] << (32 - off);
+  return v & ((1u << BITS) - 1u);
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// NB = batch rows of X handled (a multiple of the runtime batch's round-up);
+// PER_CODE selects the per-code group path.
+template <int BITS, int NB, bool PER_CODE>
+__global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
+    const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int G, int group_size, const int32_t* __restrict__ g_idx,
+    const uint16_t* __restrict__ X, int batch, int64_t ldx, float* __restrict__ Y, int64_t ldy, int vec_w,
+    int vec_x) {
+  using D = Decode<BITS>;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r0 = ((int)blockIdx.x * kWaves + wave) * kRows;
+  if (r0 >= m) return;
+  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nw = (int)(((int64_t)n * BITS + 31) / 32);  // words per row
+  float yacc[kRows][NB];
+#pragma unroll
+  for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yacc[rr][b] = 0.f;
+
+  for (int seg = lane; seg < nseg; seg += 64) {
+    const int k0 = seg * kSeg;
+    const bool whole = k0 + kSeg <= n;
+    // X of the segment: natural f16 pairs per batch row (zero past n and past batch).
+    uint32_t xn[NB][kSeg / 2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const uint16_t* xr = X + (int64_t)(b < batch ? b : 0) * ldx + k0;
+      if (b < batch && whole && vec_x) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(xr + 8 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xn[b][4 * v + e] = t[e];
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kSeg / 2; ++t) {
+          const uint32_t lo = (b < batch && k0 + 2 * t < n) ? xr[2 * t] : 0u;
+          const uint32_t hi = (b < batch && k0 + 2 * t + 1 < n) ? xr[2 * t + 1] : 0u;
+          xn[b][t] = lo | (hi << 16);
+        }
+      }
+    }
+    if constexpr (!PER_CODE) {
+      // X pairs in decode order and the segment sums of X.
+      uint32_t xq[NB][kSeg / 2];
+      float xs[NB];
+      const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in float16
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        xs[b] = 0.f;
+#pragma unroll
+        for (int j = 0; j < kSeg / 2; ++j) {
+          xq[b][j] = x_pair(xn[b], D::first(j), D::H);
+          xs[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xn[b][j]),
+                                         __builtin_bit_cast(half2_t, ones),
+                                         xs[b], false);
+        }
+      }
+      const int g = group_size > 0 ? k0 / group_size : 0;
+#pragma unroll
+      for (int rr = 0; rr < kRows; ++rr) {
+        const int r = r0 + rr;
+        if (r >= m) break;
+        const uint32_t* wr = packed + (int64_t)r * ldp + (int64_t)seg * BITS;
+        uint32_t w[BITS];
+        if (whole && vec_w && BITS != 3) {
+          if constexpr (BITS == 4) {
+            const u32x4 t = *reinterpret_cast<const u32x4*>(wr);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = t[e];
+          } else if constexpr (BITS == 2) {
+            const uint2 t = *reinterpret_cast<const uint2*>(wr);
+            w[0] = t.x;
+            w[1] = t.y;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < BITS; ++e) w[e] = seg * BITS + e < nw ? wr[e] : 0u;
+        }
+        uint32_t p[kSeg / 2];
+        D::pairs(w, p);
+        const float s = scales[(int64_t)r * G + g];
+        const float z = (float)zeros[(int64_t)r * G + g];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < kSeg / 2; ++j)
+            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, p[j]),
+                                       __builtin_bit_cast(half2_t, xq[b][j]),
+                                       a, false);
+          yacc[rr][b] = __builtin_fmaf(s, __builtin_fmaf(a, kTwo24, -z * xs[b]), yacc[rr][b]);
+        }
+      }
+    } else {
+      // Each code its own group.
+      uint32_t w[kRows][BITS];
+#pragma unroll
+      for (int rr = 0; rr < kRows; ++rr) {
+        const uint32_t* wr = packed + (int64_t)(r0 + rr < m ? r0 + rr : r0) * ldp + (int64_t)seg * BITS;
+#pragma unroll
+        for (int e = 0; e < BITS; ++e) w[rr][e] = seg * BITS + e < nw ? wr[e] : 0u;
+      }
+#pragma unroll 4
+      for (int k = 0; k < kSeg; ++k) {
+        const int col = k0 + k < n ? k0 + k : n - 1;
+        const int gk = g_idx != nullptr ? g_idx[col] : (group_size > 0 ? col / group_size : 0);
+        float xk[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+          xk[b] = (float)__builtin_bit_cast(_Float16, (uint16_t)(xn[b][k >> 1] >> (16 * (k & 1))));
+#pragma unroll
+        for (int rr = 0; rr < kRows; ++rr) {
+          const int r = r0 + rr;
+          if (r >= m) break;
+          const float wk = scales[(int64_t)r * G + gk] * ((float)code_at<BITS>(w[rr], k) - (float)zeros[(int64_t)r * G + gk]);
+#pragma unroll
+          for (int b = 0; b < NB; ++b) yacc[rr][b] = __builtin_fmaf(wk, xk[b], yacc[rr][b]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kRows; ++rr)
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = wave_sum(yacc[rr][b]);
+      if (lane == 0 && r0 + rr < m && b < batch) Y[(int64_t)b * ldy + r0 + rr] = v;
+    }
+}
+
+template <int BITS, int NB, bool PC>
+void launch_nb(unsigned grid, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
+               const uint8_t* zeros, int G, int group_size, const int32_t* g_idx, const uint16_t* X, int batch,
+               int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x) {
+  dequant_gemv_kernel<BITS, NB, PC><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, group_size, g_idx,
+                                                               X, batch, ldx, Y, ldy, vec_w, vec_x);
+}
+
+template <int BITS, bool PC>
+void launch_bits(unsigned grid, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp,
+                 const float* scales, const uint8_t* zeros, int G, int group_size, const int32_t* g_idx,
+                 const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x) {
+  if (batch == 1)
+    launch_nb<BITS, 1, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                           vec_w, vec_x);
+  else if (batch == 2)
+    launch_nb<BITS, 2, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                           vec_w, vec_x);
+  else if (batch <= 4)
+    launch_nb<BITS, 4, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                           vec_w, vec_x);
+  else
+    launch_nb<BITS, 8, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                           vec_w, vec_x);
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
+                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
+                                         const int32_t* g_idx, const uint16_t* X, int64_t batch, int64_t ldx,
+                                         float* Y, int64_t ldy, void* stream) {
+  if (m < 0 || n < 0 || group_size < 0 || G < 1) return GPTQ_ERR_INVALID_ARG;
+  if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
+  if (batch < 1 || batch > GPTQ_GEMV_MAX_BATCH) return GPTQ_ERR_UNSUPPORTED;
+  if (m > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 30) || G > ((int64_t)1 << 30)) return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0) return GPTQ_OK;
+  if (ld_packed < ceil_div(n * bits, 32) || ldx < n || ldy < m) return GPTQ_ERR_INVALID_ARG;
+  if (g_idx == nullptr && group_size > 0 && G < ceil_div(n, group_size)) return GPTQ_ERR_INVALID_ARG;
+  if (Y == nullptr || (n > 0 && (packed == nullptr || scales == nullptr || zeros == nullptr || X == nullptr)))
+    return GPTQ_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
+  const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
+  const bool per_code = g_idx != nullptr || (group_size > 0 && group_size % 32 != 0);
+  const unsigned grid = (unsigned)ceil_div(m, (int64_t)kRows * kWaves);
+  const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
+#define GPTQ_GEMV_BITS(B)                                                                                      \
+  do {                                                                                                         \
+    if (per_code)                                                                                              \
+      launch_bits<B, true>(grid, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
+                           ldx, Y, ldy, vec_w, vec_x);                                                         \
+    else                                                                                                       \
+      launch_bits<B, false>(grid, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
+                            ldx, Y, ldy, vec_w, vec_x);                                                        \
+  } while (0)
+  if (bits == 2)
+    GPTQ_GEMV_BITS(2);
+  else if (bits == 3)
+    GPTQ_GEMV_BITS(3);
+  else
+    GPTQ_GEMV_BITS(4);
+#undef GPTQ_GEMV_BITS
+  GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}

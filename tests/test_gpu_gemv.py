@@ -1,0 +1,155 @@
+"""Parity of the packed-weight matrix-vector product (gptq_dequant_gemv,
+through the C ABI) with the oracle's dequant_matmul.
+
+Inputs are seeded codes, scales and zeros packed by the oracle; X is float16
+on both sides.  The bar is the float32 rounding bound of the kernel's
+arithmetic: every segment of 32 columns is summed as s (sum c x - z sum x) or,
+per code, s (c - z) x, so |Y - Y_oracle| <= (n/32 + 80) 2^-23 M with
+M = sum_k s (c + z) |x| (oracle.dequant_matmul_bound).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g(gpu_lib):
+    import post_weight_quantization_11_amd as g
+    return g
+
+
+def _layer(m, n, bits, group, act, seed, ld_extra=0):
+    """Seeded packed layer: codes, per-group scales/zeros, g_idx as gptq_pack gives it."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 31])))
+    maxq = (1 << bits) - 1
+    codes = rng.integers(0, maxq + 1, size=(m, n), dtype=np.int64)
+    G = 1 if group == 0 else -(-n // group)
+    scales = (rng.uniform(0.5, 2.0, size=(m, G)) * 1e-2).astype(np.float32)
+    zeros = rng.integers(0, maxq + 1, size=(m, G)).astype(np.uint8)
+    perm = rng.permutation(n) if act else np.arange(n)
+    g_idx = oracle.group_index(perm, group)
+    words = oracle.pack_codes(codes, bits)
+    packed = np.zeros((m, words.shape[1] + ld_extra), dtype=np.uint32)
+    packed[:, :words.shape[1]] = words
+    return dict(packed=packed, nw=words.shape[1], scales=scales, zeros=zeros, g_idx=g_idx, G=G)
+
+
+def _x(batch, n, seed, ldx=None):
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 32])))
+    x = rng.standard_normal((batch, n)).astype(np.float16)
+    if ldx is None:
+        return x, x
+    buf = np.zeros((batch, ldx), dtype=np.float16)
+    buf[:, :n] = x
+    return x, buf
+
+
+def _run(g, L, X16, Xbuf, n, bits, group, pass_gidx):
+    import torch
+    packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
+    xd = torch.from_numpy(Xbuf).cuda()[:, :n] if Xbuf.shape[1] != n else torch.from_numpy(Xbuf).cuda()
+    Y = g.gptq_dequant_gemv(packed, dev(L["scales"]), dev(L["zeros"], "u8"), xd, n, bits,
+                            group_size=group, g_idx=dev(L["g_idx"], "i32") if pass_gidx else None)
+    torch.cuda.synchronize()
+    return host(Y).astype(np.float64)
+
+
+def _check(Y, L, X16, n, bits):
+    words = L["packed"][:, :L["nw"]]
+    Yo = oracle.dequant_matmul(words, n, bits, L["scales"], L["zeros"], L["g_idx"], X16.astype(np.float64))
+    M = oracle.dequant_matmul_bound(words, n, bits, L["scales"], L["zeros"], L["g_idx"], X16.astype(np.float64))
+    tol = (n / 32 + 80) * 2.0 ** -23 * M
+    err = np.abs(Y - Yo)
+    log(f"  max |err| / tol = {float(np.max(err / np.maximum(tol, 1e-300))):.3e}")
+    assert np.all(err <= tol)
+
+
+CASES = [
+    # m, n, bits, group, act, pass g_idx, batch
+    (70, 1000, 4, 0, False, False, 1),      # per-row grid, ragged n and m
+    (64, 4096, 4, 128, False, False, 1),    # contiguous groups
+    (96, 1024, 3, 128, True, True, 3),      # act-order groups through g_idx
+    (33, 500, 2, 64, False, False, 8),      # 2-bit g64, full batch
+    (48, 777, 3, 0, False, False, 2),       # 3-bit per-row, words straddle
+    (40, 640, 4, 128, False, True, 4),      # contiguous groups passed as g_idx
+    (20, 320, 2, 16, False, False, 5),      # groups narrower than a segment
+    (1, 33, 4, 0, False, False, 1),         # one row, one column past a segment
+]
+
+
+@pytest.mark.parametrize("m,n,bits,group,act,pass_gidx,batch", CASES)
+def test_dequant_gemv_parity(g, m, n, bits, group, act, pass_gidx, batch):
+    log(f"dequant_gemv m={m} n={n} bits={bits} group={group} act={act} g_idx={pass_gidx} batch={batch}")
+    L = _layer(m, n, bits, group, act, seed=m * 7 + n + bits)
+    X16, Xbuf = _x(batch, n, seed=n + batch)
+    Y = _run(g, L, X16, Xbuf, n, bits, group, pass_gidx)
+    _check(Y, L, X16, n, bits)
+
+
+def test_dequant_gemv_padded_strides(g):
+    # ld_packed and ldx above the minimum (and not multiples of the vector
+    # width): the unaligned path.
+    m, n, bits, group = 50, 1000, 4, 64
+    log("dequant_gemv padded strides")
+    L = _layer(m, n, bits, group, False, seed=5, ld_extra=3)
+    X16, Xbuf = _x(2, n, seed=6, ldx=n + 5)
+    Y = _run(g, L, X16, Xbuf, n, bits, group, False)
+    _check(Y, L, X16, n, bits)
+
+
+def test_dequant_gemv_edges(g):
+    import torch
+    import post_weight_quantization_11_amd._lib as Lb
+    log("dequant_gemv edges")
+    L = _layer(8, 64, 4, 0, False, seed=1)
+    packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
+    s, z = dev(L["scales"]), dev(L["zeros"], "u8")
+    # batch above the limit
+    with pytest.raises(Lb.GptqError) as ei:
+        g.gptq_dequant_gemv(packed, s, z, torch.zeros((9, 64), dtype=torch.float16, device="cuda"), 64, 4)
+    assert ei.value.status == Lb.GPTQ_ERR_UNSUPPORTED
+    # unsupported bit width
+    with pytest.raises(Lb.GptqError) as ei:
+        g.gptq_dequant_gemv(packed, s, z, torch.zeros((1, 64), dtype=torch.float16, device="cuda"), 64, 5)
+    assert ei.value.status == Lb.GPTQ_ERR_INVALID_ARG
+    # too few groups for the group size
+    with pytest.raises(Lb.GptqError) as ei:
+        g.gptq_dequant_gemv(packed, s, z, torch.zeros((1, 64), dtype=torch.float16, device="cuda"), 64, 4,
+                            group_size=32)
+    assert ei.value.status == Lb.GPTQ_ERR_INVALID_ARG
+    # n = 0: Y is all zero
+    Y = g.gptq_dequant_gemv(packed[:, :0], s, z, torch.zeros((2, 0), dtype=torch.float16, device="cuda"), 0, 4,
+                            Y=torch.full((2, 8), 7.0, device="cuda"))
+    torch.cuda.synchronize()
+    assert np.all(host(Y) == 0)
+
+
+def test_dequant_gemv_full_size_layer(g):
+    # The 175B-class fc1 layer (49152 x 12288, 4-bit per-row) at batch 1, the
+    # shape the decode measurement times; sampled rows against the oracle.
+    import torch
+    m, n, bits = 49152, 12288, 4
+    log("dequant_gemv full size 49152 x 12288")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([11, 33])))
+    nw = oracle.packed_words_per_row(n, bits)
+    words = rng.integers(0, 1 << 32, size=(m, nw), dtype=np.uint64).astype(np.uint32)
+    scales = (rng.uniform(0.5, 2.0, size=(m, 1)) * 1e-2).astype(np.float32)
+    zeros = rng.integers(0, 16, size=(m, 1)).astype(np.uint8)
+    g_idx = np.zeros(n, dtype=np.int32)
+    X16 = rng.standard_normal((1, n)).astype(np.float16)
+    Y = g.gptq_dequant_gemv(torch.from_numpy(words.view(np.int32)).cuda(), dev(scales), dev(zeros, "u8"),
+                            torch.from_numpy(X16).cuda(), n, bits)
+    torch.cuda.synchronize()
+    Yg = host(Y).astype(np.float64)
+    rows = np.sort(rng.choice(m, size=64, replace=False))
+    rows[0], rows[-1] = 0, m - 1
+    Yo = oracle.dequant_matmul(words[rows], n, bits, scales[rows], zeros[rows], g_idx, X16.astype(np.float64))
+    M = oracle.dequant_matmul_bound(words[rows], n, bits, scales[rows], zeros[rows], g_idx, X16.astype(np.float64))
+    tol = (n / 32 + 80) * 2.0 ** -23 * M
+    err = np.abs(Yg[:, rows] - Yo)
+    log(f"  max |err| / tol = {float(np.max(err / tol)):.3e}")
+    assert np.all(err <= tol)
