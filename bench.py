@@ -15,6 +15,11 @@ oracle's time on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                        [--no-cpu] [--copy-calibration]
+
+`--gemv` instead times the packed-weight decode product gptq_dequant_gemv
+(Y = X W^T from the packed codes) on the 175B-class fc1 layer, 49152 x
+12288 4-bit per-row, batch `--gemv-batch` (default 1), and prints its own
+JSON line with the HBM roofline record.
 """
 from __future__ import annotations
 
@@ -129,6 +134,80 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total):
     }
 
 
+def bench_gemv(args):
+    """Decode product on the 175B-class fc1 layer (49152 x 12288, 4-bit per-row)."""
+    import torch
+    import post_weight_quantization_11_amd as g
+    m, n, bits, batch = 49152, 12288, 4, args.gemv_batch
+    torch.cuda.set_device(0)
+    gen = torch.Generator(device="cuda").manual_seed(2023)
+    nw = g.packed_words(n, bits)
+    packed = torch.randint(-2**31, 2**31 - 1, (m, nw), dtype=torch.int32, device="cuda", generator=gen)
+    scales = torch.rand((m, 1), device="cuda", generator=gen) * 0.015 + 0.005
+    zeros = torch.randint(0, 1 << bits, (m, 1), dtype=torch.uint8, device="cuda", generator=gen)
+    X = torch.randn((batch, n), device="cuda", generator=gen).half()
+    Y = torch.empty((batch, m), device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        g.gptq_dequant_gemv(packed, scales, zeros, X, n, bits, Y=Y)
+    torch.cuda.synchronize()
+    # HIP events around each launch on the launching stream: the kernel's own duration.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        g.gptq_dequant_gemv(packed, scales, zeros, X, n, bits, Y=Y)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    us = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+    nbytes = float(m) * nw * 4 + m * 5 + batch * n * 2 + batch * m * 4
+    rec = {
+        "metric": "packed-weight decode product time (us), HBM GB/s",
+        "value": us,
+        "unit": "us per call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 x 4-bit codes, f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "175B-class fc1 decode product", "m": m, "n": n, "bits": bits, "group_size": 0,
+                   "batch": batch, "parallelism": "1 GPU"},
+        "roofline": {
+            "kernel": "dequant_gemv_kernel<4> (gptq_dequant_gemv), HIP events around each launch",
+            "bound": "hbm",
+            "achieved": nbytes / (us * 1e-6) / 1e9,
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+            "traffic": None,
+            "algorithmic": f"packed words + scales/zeros + X + Y = {nbytes:.4g} bytes per launch",
+        },
+    }
+    if not args.no_cpu:
+        import oracle
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:  # pragma: no cover
+            threads = os.cpu_count() or 1
+        rows = 8192
+        w = packed[:rows].cpu().numpy().view(np.uint32)
+        s_, z_ = scales[:rows].cpu().numpy(), zeros[:rows].cpu().numpy()
+        x = X.cpu().numpy().astype(np.float64)
+        t1 = time.perf_counter()
+        oracle.dequant_matmul(w, n, bits, s_, z_, np.zeros(n, dtype=np.int32), x)
+        cpu = time.perf_counter() - t1
+        rec["cpu_baseline"] = {"value": cpu * (m / rows) * 1e6, "unit": "us per call", "cores": int(threads),
+                               "kind": "oracle",
+                               "sample": f"oracle.dequant_matmul on {rows} of the {m} rows, scaled by {m // rows}"}
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -138,6 +217,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--gemv", action="store_true", help="time the packed-weight decode product instead")
+    ap.add_argument("--gemv-batch", type=int, default=1)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -150,6 +231,9 @@ def main():
     from post_weight_quantization_11_amd import _lib
 
     lib = g.load()
+    if args.gemv:
+        bench_gemv(args)
+        return
     cfg = wl.WORKLOADS[args.config]
     layer = cfg.layers[0]
     m, n, N = layer.m, layer.n, cfg.tokens

@@ -29,9 +29,13 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kRows = 4;  // rows per wave
+// Rows per wave (8 for small batches was measured: no faster on the large
+// layer, slower on small ones).
+template <int NB> constexpr int rows_per_wave() { return 4; }
 constexpr int kSeg = 32;  // columns per lane segment
 constexpr float kTwo24 = 16777216.0f;
+constexpr int64_t kGridCap = 2048;            // workgroups at most (8 per CU)
+constexpr size_t kMaxStageBytes = 64 * 1024;  // LDS for staged (s, s*z) pairs
 
 typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -103,14 +107,34 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
     const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
     const uint8_t* __restrict__ zeros, int G, int group_size, const int32_t* __restrict__ g_idx,
     const uint16_t* __restrict__ X, int batch, int64_t ldx, float* __restrict__ Y, int64_t ldy, int vec_w,
-    int vec_x) {
+    int vec_x, int stage_sz) {
   using D = Decode<BITS>;
+  constexpr int kRows = rows_per_wave<NB>();
+  extern __shared__ float2 sz_lds[];  // per wave: kRows x G pairs (s, s*z), per-code path
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  const int r0 = ((int)blockIdx.x * kWaves + wave) * kRows;
-  if (r0 >= m) return;
   const int nseg = (n + kSeg - 1) / kSeg;
   const int nw = (int)(((int64_t)n * BITS + 31) / 32);  // words per row
+  const int ngroups = (m + kRows - 1) / kRows;
+  for (int rg = (int)blockIdx.x * kWaves + wave; rg < ngroups; rg += (int)gridDim.x * kWaves) {
+  const int r0 = rg * kRows;
+  float2* szw = sz_lds + (size_t)wave * kRows * G;
+  if constexpr (PER_CODE) {
+    if (stage_sz) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      for (int e = lane; e < kRows * G; e += 64) {
+        const int rr = e / G, gg = e - rr * G;
+        const int r = r0 + rr < m ? r0 + rr : m - 1;
+        const float sc = scales[(int64_t)r * G + gg];
+        szw[e] = make_float2(sc, sc * (float)zeros[(int64_t)r * G + gg]);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+  }
   float yacc[kRows][NB];
 #pragma unroll
   for (int rr = 0; rr < kRows; ++rr)
@@ -166,17 +190,18 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
         uint32_t w[BITS];
         if (whole && vec_w && BITS != 3) {
           if constexpr (BITS == 4) {
-            const u32x4 t = *reinterpret_cast<const u32x4*>(wr);
+            const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr));
 #pragma unroll
             for (int e = 0; e < 4; ++e) w[e] = t[e];
           } else if constexpr (BITS == 2) {
-            const uint2 t = *reinterpret_cast<const uint2*>(wr);
-            w[0] = t.x;
-            w[1] = t.y;
+            typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+            const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wr));
+            w[0] = t[0];
+            w[1] = t[1];
           }
         } else {
 #pragma unroll
-          for (int e = 0; e < BITS; ++e) w[e] = seg * BITS + e < nw ? wr[e] : 0u;
+          for (int e = 0; e < BITS; ++e) w[e] = seg * BITS + e < nw ? __builtin_nontemporal_load(wr + e) : 0u;
         }
         uint32_t p[kSeg / 2];
         D::pairs(w, p);
@@ -214,9 +239,18 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
         for (int rr = 0; rr < kRows; ++rr) {
           const int r = r0 + rr;
           if (r >= m) break;
-          const float wk = scales[(int64_t)r * G + gk] * ((float)code_at<BITS>(w[rr], k) - (float)zeros[(int64_t)r * G + gk]);
+          const float c = (float)code_at<BITS>(w[rr], k);
+          float2 q;
+          if (stage_sz) {
+            q = szw[rr * G + gk];
+          } else {
+            const float sc = scales[(int64_t)r * G + gk];
+            q = make_float2(sc, sc * (float)zeros[(int64_t)r * G + gk]);
+          }
+          // s (c - z) x as c (s x) - (s z) x
 #pragma unroll
-          for (int b = 0; b < NB; ++b) yacc[rr][b] = __builtin_fmaf(wk, xk[b], yacc[rr][b]);
+          for (int b = 0; b < NB; ++b)
+            yacc[rr][b] = __builtin_fmaf(c, q.x * xk[b], __builtin_fmaf(-q.y, xk[b], yacc[rr][b]));
         }
       }
     }
@@ -228,31 +262,38 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
       const float v = wave_sum(yacc[rr][b]);
       if (lane == 0 && r0 + rr < m && b < batch) Y[(int64_t)b * ldy + r0 + rr] = v;
     }
+  }
 }
 
 template <int BITS, int NB, bool PC>
-void launch_nb(unsigned grid, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
-               const uint8_t* zeros, int G, int group_size, const int32_t* g_idx, const uint16_t* X, int batch,
-               int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x) {
-  dequant_gemv_kernel<BITS, NB, PC><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, group_size, g_idx,
-                                                               X, batch, ldx, Y, ldy, vec_w, vec_x);
+void launch_nb(size_t shm_per_row, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp,
+               const float* scales, const uint8_t* zeros, int G, int group_size, const int32_t* g_idx,
+               const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x) {
+  constexpr int rows = rows_per_wave<NB>();
+  // Waves loop over groups of `rows` rows; at most kGridCap workgroups.
+  const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(m, (int64_t)rows * kWaves), kGridCap);
+  // Per-code path: each wave stages its rows' (s, s*z) in LDS when they fit.
+  const size_t need = shm_per_row * rows * kWaves;
+  const size_t shm = PC && need <= kMaxStageBytes ? need : 0;
+  dequant_gemv_kernel<BITS, NB, PC><<<grid, kThreads, shm, st>>>(packed, m, n, ldp, scales, zeros, G, group_size,
+                                                                 g_idx, X, batch, ldx, Y, ldy, vec_w, vec_x, shm > 0);
 }
 
 template <int BITS, bool PC>
-void launch_bits(unsigned grid, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp,
+void launch_bits(size_t shm, hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp,
                  const float* scales, const uint8_t* zeros, int G, int group_size, const int32_t* g_idx,
                  const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x) {
   if (batch == 1)
-    launch_nb<BITS, 1, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+    launch_nb<BITS, 1, PC>(shm, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
                            vec_w, vec_x);
   else if (batch == 2)
-    launch_nb<BITS, 2, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+    launch_nb<BITS, 2, PC>(shm, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
                            vec_w, vec_x);
   else if (batch <= 4)
-    launch_nb<BITS, 4, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+    launch_nb<BITS, 4, PC>(shm, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
                            vec_w, vec_x);
   else
-    launch_nb<BITS, 8, PC>(grid, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+    launch_nb<BITS, 8, PC>(shm, st, packed, m, n, ldp, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
                            vec_w, vec_x);
 }
 
@@ -278,15 +319,15 @@ extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int6
   const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
   const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
   const bool per_code = g_idx != nullptr || (group_size > 0 && group_size % 32 != 0);
-  const unsigned grid = (unsigned)ceil_div(m, (int64_t)kRows * kWaves);
+  const size_t shm_per_row = (size_t)G * sizeof(float2);
   const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
 #define GPTQ_GEMV_BITS(B)                                                                                      \
   do {                                                                                                         \
     if (per_code)                                                                                              \
-      launch_bits<B, true>(grid, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
+      launch_bits<B, true>(shm_per_row, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
                            ldx, Y, ldy, vec_w, vec_x);                                                         \
     else                                                                                                       \
-      launch_bits<B, false>(grid, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
+      launch_bits<B, false>(0, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
                             ldx, Y, ldy, vec_w, vec_x);                                                        \
   } while (0)
   if (bits == 2)
