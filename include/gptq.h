@@ -184,13 +184,29 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t*
  * Accumulation is float32; the rounding error of Y[b, r] is bounded by a
  * small multiple of (n/32 + 64) 2^-24 sum_k s (c + z) |X[b, k]|.  Group
  * indices in g_idx are not validated (an index >= G reads out of bounds).
- * No workspace.
+ * Batches of 3 or more with g_idx NULL and group_size 0 or a multiple of 128
+ * run on the matrix cores (as gptq_dequant_gemm).  No workspace.
  * ---------------------------------------------------------------------- */
 #define GPTQ_GEMV_MAX_BATCH 8
 gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed,
                               int bits, const float* scales, const uint8_t* zeros, int64_t G,
                               int group_size, const int32_t* g_idx, const uint16_t* X,
                               int64_t batch, int64_t ldx, float* Y, int64_t ldy, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Reading the packed weights back on the matrix cores, for any batch
+ * (batched decode and prefill; same sources as gptq_dequant_gemv): the same
+ * Y as gptq_dequant_gemv for batch >= 1 rows of X.  Groups are contiguous:
+ * group_size 0 (one group per row) or a multiple of 128 columns, with
+ * g(k) = k / group_size; other group sizes return GPTQ_ERR_UNSUPPORTED
+ * (gptq_dequant_gemv takes them, and act-order g_idx, for batch <= 8).
+ * Arguments as for gptq_dequant_gemv (batch 0 is a no-op); the rounding
+ * error has the same bound.  No workspace.
+ * ---------------------------------------------------------------------- */
+gptq_status gptq_dequant_gemm(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed,
+                              int bits, const float* scales, const uint8_t* zeros, int64_t G,
+                              int group_size, const uint16_t* X, int64_t batch, int64_t ldx,
+                              float* Y, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

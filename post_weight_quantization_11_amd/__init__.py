@@ -6,6 +6,7 @@ C ABI, declared in include/gptq.h); this package is its Python binding.
 from ._lib import (  # noqa: F401
     GptqError,
     bits_for_levels,
+    gptq_dequant_gemm,
     gptq_dequant_gemv,
     gptq_hessian_accumulate,
     gptq_pack,

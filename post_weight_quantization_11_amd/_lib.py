@@ -32,6 +32,7 @@ EXPORTS = (
     "gptq_quantize_layer",
     "gptq_pack",
     "gptq_dequant_gemv",
+    "gptq_dequant_gemm",
 )
 
 GEMV_MAX_BATCH = 8
@@ -76,6 +77,8 @@ def load(path: str = LIB_PATH):
     lib.gptq_pack.argtypes = [vp, i64, i64, vp, C, C, vp, i64, vp, vp]
     lib.gptq_dequant_gemv.restype = C
     lib.gptq_dequant_gemv.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, vp, i64, i64, vp, i64, vp]
+    lib.gptq_dequant_gemm.restype = C
+    lib.gptq_dequant_gemm.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, i64, i64, vp, i64, vp]
     _lib = lib
     return lib
 
@@ -241,6 +244,32 @@ def gptq_dequant_gemv(packed, scales, zeros, X, n: int, bits: int, group_size: i
                                int(G), int(group_size), _ptr(g_idx), _ptr(X), batch, X.stride(0), _ptr(Y),
                                Y.stride(0), _stream(stream))
     _check(rc, "gptq_dequant_gemv")
+    return Y
+
+
+def gptq_dequant_gemm(packed, scales, zeros, X, n: int, bits: int, group_size: int = 0, Y=None, stream=None):
+    """Y (batch x m float32) = X W^T on the matrix cores, any batch; groups of
+    group_size columns (0 or a multiple of 128), no g_idx."""
+    torch = _torch()
+    lib = load()
+    _rows_check(packed)
+    _rows_check(X)
+    _device_check(scales, zeros)
+    if X.dtype != torch.float16:
+        raise ValueError("X must be float16")
+    m = packed.shape[0]
+    batch = X.shape[0]
+    if X.shape[1] != n:
+        raise ValueError("X must have n columns")
+    if Y is None:
+        Y = torch.empty((batch, m), dtype=torch.float32, device=X.device)
+    else:
+        _rows_check(Y)
+    G = scales.shape[1] if scales.dim() == 2 else 1
+    rc = lib.gptq_dequant_gemm(_ptr(packed), m, int(n), packed.stride(0), int(bits), _ptr(scales), _ptr(zeros),
+                               int(G), int(group_size), _ptr(X), batch, X.stride(0), _ptr(Y), Y.stride(0),
+                               _stream(stream))
+    _check(rc, "gptq_dequant_gemm")
     return Y
 
 

@@ -227,7 +227,7 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
 #pragma unroll
         for (int e = 0; e < BITS; ++e) w[rr][e] = seg * BITS + e < nw ? wr[e] : 0u;
       }
-#pragma unroll 4
+#pragma unroll
       for (int k = 0; k < kSeg; ++k) {
         const int col = k0 + k < n ? k0 + k : n - 1;
         const int gk = g_idx != nullptr ? g_idx[col] : (group_size > 0 ? col / group_size : 0);
@@ -262,6 +262,207 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
       const float v = wave_sum(yacc[rr][b]);
       if (lane == 0 && r0 + rr < m && b < batch) Y[(int64_t)b * ldy + r0 + rr] = v;
     }
+  }
+}
+
+
+// Matrix-core path (any batch, per-row grids or contiguous groups of a
+// multiple of 128 columns, no g_idx).  The same subnormal code pairs are the
+// A operand of v_mfma_f32_16x16x32_f16 (A element (row l%16, k 8*(l/16) + e),
+// B element (k 8*(l/16) + e, column l%16), accumulator register i of lane l:
+// row 4*(l/16) + i, column l%16 — checked with an in-bounds probe).  A chunk
+// is 128 columns: lane quarter q takes segment 4*chunk + q, and MFMA j of the
+// chunk takes the segment's code pairs 4j .. 4j+3 (8 columns per quarter), so
+// a chunk never straddles a group.  sum x per column comes from one more MFMA
+// with all-ones subnormal codes.  At the end of each group:
+//   y += s * (2^24 * acc - z * 2^24 * acc_ones).
+// A workgroup owns 16*RT rows and 16*NT columns of Y (batch rows of X); its
+// four waves split the chunks and add their partial sums through LDS in a
+// fixed order.  The next chunk's words and X are loaded while the current one
+// multiplies.
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+__device__ inline half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  return __builtin_bit_cast(half8_t, v);
+}
+
+template <int BITS, int RT, int NT>
+__global__ __launch_bounds__(kThreads) void dequant_mfma_kernel(
+    const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int G, int group_size, const uint16_t* __restrict__ X, int batch,
+    int64_t ldx, float* __restrict__ Y, int64_t ldy, int vec_w, int vec_x) {
+  using D = Decode<BITS>;
+  __shared__ floatx4 red[kWaves - 1][RT][NT][64];
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int r0 = (int)blockIdx.x * 16 * RT;
+  const int c0 = (int)blockIdx.y * 16 * NT;
+  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nw = (int)(((int64_t)n * BITS + 31) / 32);
+  const int nchunk = (nseg + 3) / 4;
+  const int gchunks = group_size > 0 ? group_size / 128 : nchunk;
+  // The workgroup's waves share the rows and split the chunks (columns).
+  const int c_lo = wave * nchunk / kWaves, c_hi = (wave + 1) * nchunk / kWaves;
+  floatx4 acc[RT][NT], accx[NT], yacc[RT][NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    accx[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = yacc[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  const half8_t ones = as_half8(0x00010001u, 0x00010001u, 0x00010001u, 0x00010001u);
+  // Operands of one chunk as loaded: row words and natural X pairs.
+  struct Raw {
+    uint32_t w[RT][BITS];
+    uint32_t xn[NT][kSeg / 2];
+  };
+  auto load = [&](Raw& o, int ch) {
+    const int seg = 4 * ch + q;
+    const int k0 = seg * kSeg;
+    const bool whole = k0 + kSeg <= n;  // implies seg < nseg
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int row = r0 + 16 * rt + c16;
+      const uint32_t* wr = packed + (int64_t)(row < m ? row : r0) * ldp + (int64_t)seg * BITS;
+      if (row < m && whole && vec_w && BITS == 4) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr));
+#pragma unroll
+        for (int e = 0; e < BITS; ++e) o.w[rt][e] = t[e & 3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < BITS; ++e)
+          o.w[rt][e] = (row < m && seg < nseg && seg * BITS + e < nw) ? __builtin_nontemporal_load(wr + e) : 0u;
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      // Every lane loads (from row min(b, batch-1)) so the wave does not
+      // branch on the batch; rows past the batch are zeroed afterwards.
+      const int b = c0 + 16 * nt + c16;
+      const uint32_t keep = b < batch ? 0xFFFFFFFFu : 0u;
+      const uint16_t* xr = X + (int64_t)(b < batch ? b : batch - 1) * ldx + k0;
+      if (whole && vec_x) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(xr + 8 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o.xn[nt][4 * v + e] = t[e] & keep;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kSeg / 2; ++t) {
+          const uint32_t lo = k0 + 2 * t < n ? xr[2 * t] : 0u;
+          const uint32_t hi = k0 + 2 * t + 1 < n ? xr[2 * t + 1] : 0u;
+          o.xn[nt][t] = (lo | (hi << 16)) & keep;
+        }
+      }
+    }
+  };
+  auto compute = [&](const Raw& cur, int ch) {
+    half8_t bop[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bop[nt][j] = as_half8(x_pair(cur.xn[nt], D::first(4 * j), D::H), x_pair(cur.xn[nt], D::first(4 * j + 1), D::H),
+                              x_pair(cur.xn[nt], D::first(4 * j + 2), D::H), x_pair(cur.xn[nt], D::first(4 * j + 3), D::H));
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      uint32_t p[kSeg / 2];
+      D::pairs(cur.w[rt], p);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const half8_t aop = as_half8(p[4 * j], p[4 * j + 1], p[4 * j + 2], p[4 * j + 3]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[nt][j], acc[rt][nt], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) accx[nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, bop[nt][j], accx[nt], 0, 0, 0);
+    if ((ch + 1) % gchunks == 0 || ch + 1 == c_hi) {
+      const int g = group_size > 0 ? ch / gchunks : 0;
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = r0 + 16 * rt + 4 * q + i;
+          const float sc = row < m ? scales[(int64_t)row * G + g] : 0.f;
+          const float z = row < m ? (float)zeros[(int64_t)row * G + g] : 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            yacc[rt][nt][i] = __builtin_fmaf(sc, __builtin_fmaf(acc[rt][nt][i], kTwo24, -z * (accx[nt][i] * kTwo24)),
+                                             yacc[rt][nt][i]);
+        }
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        accx[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) acc[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  // Two named buffers (a runtime index into an array of them would put the
+  // operands in scratch memory): the next chunk loads while one multiplies.
+  Raw b0, b1;
+  if (c_lo < c_hi) load(b0, c_lo);
+  for (int ch = c_lo; ch < c_hi; ch += 2) {
+    if (ch + 1 < c_hi) load(b1, ch + 1);
+    compute(b0, ch);
+    if (ch + 1 < c_hi) {
+      if (ch + 2 < c_hi) load(b0, ch + 2);
+      compute(b1, ch + 1);
+    }
+  }
+  // Partial sums of waves 1..3 through LDS; wave 0 adds them in wave order.
+  if (wave > 0) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) red[wave - 1][rt][nt][lane] = yacc[rt][nt];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      floatx4 v = yacc[rt][nt];
+#pragma unroll
+      for (int w = 0; w < kWaves - 1; ++w) v += red[w][rt][nt][lane];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 16 * rt + 4 * q + i, col = c0 + 16 * nt + c16;
+        if (row < m && col < batch) Y[(int64_t)col * ldy + row] = v[i];
+      }
+    }
+}
+
+template <int BITS, int RT, int NT>
+void launch_mfma(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
+                 const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx, float* Y,
+                 int64_t ldy, int vec_w, int vec_x) {
+  const dim3 grid((unsigned)ceil_div(m, (int64_t)16 * RT), (unsigned)ceil_div(batch, (int64_t)16 * NT));
+  dequant_mfma_kernel<BITS, RT, NT><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, group_size, X,
+                                                               batch, ldx, Y, ldy, vec_w, vec_x);
+}
+
+template <int BITS>
+void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
+                       const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx,
+                       float* Y, int64_t ldy, int vec_w, int vec_x) {
+  // Decode-sized batches: one 16-column tile, 16 or 64 rows per workgroup
+  // (more workgroups for short layers); larger batches: 32 rows x 64 columns.
+  if (batch <= 16) {
+    if (m <= 16384)
+      launch_mfma<BITS, 1, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
+    else
+      launch_mfma<BITS, 4, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
+  } else {
+    launch_mfma<BITS, 2, 4>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
   }
 }
 
@@ -319,6 +520,19 @@ extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int6
   const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
   const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
   const bool per_code = g_idx != nullptr || (group_size > 0 && group_size % 32 != 0);
+  if (!per_code && group_size % 128 == 0 && batch >= 3) {
+    // From three rows of X on, the matrix-core kernel is faster (one dot2 per
+    // code pair per X row makes the VALU kernel compute-bound).
+    const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
+    if (bits == 2)
+      launch_mfma_shape<2>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    else if (bits == 3)
+      launch_mfma_shape<3>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    else
+      launch_mfma_shape<4>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    GPTQ_TRY_LAUNCH();
+    return GPTQ_OK;
+  }
   const size_t shm_per_row = (size_t)G * sizeof(float2);
   const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
 #define GPTQ_GEMV_BITS(B)                                                                                      \
@@ -337,6 +551,35 @@ extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int6
   else
     GPTQ_GEMV_BITS(4);
 #undef GPTQ_GEMV_BITS
+  GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}
+
+extern "C" gptq_status gptq_dequant_gemm(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
+                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
+                                         const uint16_t* X, int64_t batch, int64_t ldx, float* Y, int64_t ldy,
+                                         void* stream) {
+  if (m < 0 || n < 0 || group_size < 0 || G < 1 || batch < 0) return GPTQ_ERR_INVALID_ARG;
+  if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
+  if (group_size % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
+  if (m > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 30) || G > ((int64_t)1 << 30) ||
+      ceil_div(batch, 64) > 65535)
+    return GPTQ_ERR_UNSUPPORTED;
+  if (m == 0 || batch == 0) return GPTQ_OK;
+  if (ld_packed < ceil_div(n * bits, 32) || ldx < n || ldy < m) return GPTQ_ERR_INVALID_ARG;
+  if (group_size > 0 && G < ceil_div(n, group_size)) return GPTQ_ERR_INVALID_ARG;
+  if (Y == nullptr || (n > 0 && (packed == nullptr || scales == nullptr || zeros == nullptr || X == nullptr)))
+    return GPTQ_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
+  const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
+  const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
+  if (bits == 2)
+    launch_mfma_shape<2>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+  else if (bits == 3)
+    launch_mfma_shape<3>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+  else
+    launch_mfma_shape<4>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }

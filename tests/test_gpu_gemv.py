@@ -78,6 +78,8 @@ CASES = [
     (40, 640, 4, 128, False, True, 4),      # contiguous groups passed as g_idx
     (20, 320, 2, 16, False, False, 5),      # groups narrower than a segment
     (1, 33, 4, 0, False, False, 1),         # one row, one column past a segment
+    (77, 1000, 4, 128, False, False, 3),    # batch >= 3, contiguous groups: matrix-core kernel
+    (50, 640, 2, 0, False, False, 8),       # per-row, full batch: matrix-core kernel
 ]
 
 
@@ -153,3 +155,58 @@ def test_dequant_gemv_full_size_layer(g):
     err = np.abs(Yg[:, rows] - Yo)
     log(f"  max |err| / tol = {float(np.max(err / tol)):.3e}")
     assert np.all(err <= tol)
+
+
+# ---------------------------------------------------------------------------
+# Matrix-core product (gptq_dequant_gemm), any batch.
+# ---------------------------------------------------------------------------
+def _run_gemm(g, L, Xbuf, n, bits, group):
+    import torch
+    packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
+    xd = torch.from_numpy(Xbuf).cuda()
+    if Xbuf.shape[1] != n:
+        xd = xd[:, :n]
+    Y = g.gptq_dequant_gemm(packed, dev(L["scales"]), dev(L["zeros"], "u8"), xd, n, bits, group_size=group)
+    torch.cuda.synchronize()
+    return host(Y).astype(np.float64)
+
+
+GEMM_CASES = [
+    # m, n, bits, group, batch
+    (70, 1000, 4, 0, 1),        # ragged m and n, per-row
+    (64, 1024, 4, 128, 5),      # contiguous groups, batch inside one tile
+    (40, 1000, 3, 128, 16),     # 3-bit, partial last group, full tile
+    (33, 500, 2, 256, 17),      # 2-bit, two column tiles
+    (20000, 384, 4, 0, 2),      # many rows (32 rows per wave)
+    (96, 640, 4, 128, 100),     # prefill-sized batch, several 64-column tiles
+]
+
+
+@pytest.mark.parametrize("m,n,bits,group,batch", GEMM_CASES)
+def test_dequant_gemm_parity(g, m, n, bits, group, batch):
+    log(f"dequant_gemm m={m} n={n} bits={bits} group={group} batch={batch}")
+    L = _layer(m, n, bits, group, False, seed=m + 3 * n + bits)
+    X16, Xbuf = _x(batch, n, seed=2 * n + batch)
+    Y = _run_gemm(g, L, Xbuf, n, bits, group)
+    _check(Y, L, X16, n, bits)
+
+
+def test_dequant_gemm_padded_strides_and_edges(g):
+    import torch
+    import post_weight_quantization_11_amd._lib as Lb
+    log("dequant_gemm padded strides and edges")
+    m, n, bits, group = 50, 1000, 4, 128
+    L = _layer(m, n, bits, group, False, seed=8, ld_extra=3)
+    X16, Xbuf = _x(3, n, seed=9, ldx=n + 5)
+    _check(_run_gemm(g, L, Xbuf, n, bits, group), L, X16, n, bits)
+    packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
+    s, z = dev(L["scales"]), dev(L["zeros"], "u8")
+    # groups that are not a multiple of 128 columns
+    with pytest.raises(Lb.GptqError) as ei:
+        g.gptq_dequant_gemm(packed, s, z, torch.zeros((2, n), dtype=torch.float16, device="cuda"), n, bits,
+                            group_size=64)
+    assert ei.value.status == Lb.GPTQ_ERR_UNSUPPORTED
+    # batch 0 is a no-op
+    Y = g.gptq_dequant_gemm(packed, s, z, torch.zeros((0, n), dtype=torch.float16, device="cuda"), n, bits,
+                            group_size=group)
+    assert tuple(Y.shape) == (0, m)
