@@ -16,6 +16,13 @@ oracle's time on a bounded sample of the same workload.
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
                        [--no-cpu] [--copy-calibration]
 
+`--decoder` instead times the sequential whole-decoder pass (post_weight_
+quantization_11_amd.decoder): 32 Llama-7B-shaped blocks of random bf16
+weights, 128 x 2048 calibration tokens fed through the already-quantized
+blocks, 2-bit g64 (`--levels 3` for the ternary variant); one JSON line with
+the total time and its split over Hessian / prepare / quantize / pack /
+forward (HIP events on the stream).
+
 `--gemv` instead times the packed-weight decode product gptq_dequant_gemv
 (Y = X W^T from the packed codes) on the 175B-class fc1 layer, 49152 x
 12288 4-bit per-row, batch `--gemv-batch` (default 1), and prints its own
@@ -134,6 +141,72 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total):
     }
 
 
+def bench_decoder(args):
+    """Sequential whole-decoder pass, Llama-7B shapes, random weights."""
+    import contextlib
+    import torch
+    from post_weight_quantization_11_amd import decoder as dec
+    shape = dataclasses_replace(dec.LLAMA_7B, n_blocks=args.decoder_blocks)
+    seqs, S = args.decoder_seqs, args.decoder_seq_len
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    blocks = dec.random_blocks(shape, seed=2024, device="cuda", dtype=torch.bfloat16)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    X0 = torch.randn((seqs * S, shape.d_model), device="cuda", generator=gen).to(torch.bfloat16)
+    torch.cuda.synchronize()
+    log(f"decoder weights and inputs generated in {time.perf_counter() - t0:.1f}s")
+    stream = torch.cuda.current_stream()
+    marks = []
+
+    @contextlib.contextmanager
+    def timer(name):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        yield
+        e1.record(stream)
+        marks.append((name, e0, e1))
+
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    Xout, res = dec.quantize_decoder(blocks, X0, shape, seqs, S, levels=args.levels, group_size=args.group_size,
+                                     act_order=False, timer=timer)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t1
+    split = {}
+    for name, e0, e1 in marks:
+        split[name] = split.get(name, 0.0) + e0.elapsed_time(e1) / 1e3
+    nlayers = len(res) * len(dec.LINEARS)
+    finite = bool(torch.isfinite(Xout.float()).all().item())
+    rec = {
+        "metric": "whole-decoder GPTQ pass time (s), layers/s",
+        "value": wall,
+        "unit": "s",
+        "n_gpus": 1,
+        "steps": 1,
+        "warmup": 0,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 forward, f32/f64 quantizer",
+        "data": "synthetic",
+        "config": {"workload": "Llama-7B-shaped decoder pass", "blocks": shape.n_blocks, "d_model": shape.d_model,
+                   "d_ff": shape.d_ff, "heads": shape.n_heads, "seqs": seqs, "seq_len": S, "levels": args.levels,
+                   "group_size": args.group_size, "parallelism": "1 GPU"},
+        "layers": nlayers,
+        "layers_per_s": nlayers / wall,
+        "stage_s": split,
+        "quantizer_s": sum(v for k, v in split.items() if k != "forward"),
+        "sanity": {"finite_output": finite},
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def dataclasses_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)
+
+
 def bench_gemv(args):
     """Decode product on the 175B-class fc1 layer (49152 x 12288, 4-bit per-row)."""
     import torch
@@ -220,6 +293,12 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--gemv", action="store_true", help="time the packed-weight decode product instead")
     ap.add_argument("--gemv-batch", type=int, default=1)
+    ap.add_argument("--decoder", action="store_true", help="time the whole-decoder pass instead")
+    ap.add_argument("--decoder-blocks", type=int, default=32)
+    ap.add_argument("--decoder-seqs", type=int, default=128)
+    ap.add_argument("--decoder-seq-len", type=int, default=2048)
+    ap.add_argument("--levels", type=int, default=4)
+    ap.add_argument("--group-size", type=int, default=64)
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -234,6 +313,9 @@ def main():
     lib = g.load()
     if args.gemv:
         bench_gemv(args)
+        return
+    if args.decoder:
+        bench_decoder(args)
         return
     cfg = wl.WORKLOADS[args.config]
     layer = cfg.layers[0]

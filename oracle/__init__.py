@@ -28,3 +28,4 @@ from .gptq_oracle import (  # noqa: F401
     dequant_matmul_bound,
     gptq_layer,
 )
+from . import decoder_oracle  # noqa: F401,E402

@@ -487,3 +487,77 @@ def test_dequant_packed_matches_the_sweep_dequantization(levels, group, act):
                                                      res["g_idx"], xb), xb @ res["What"].T, rtol=1e-12, atol=1e-15)
     M = oracle.dequant_matmul_bound(res["packed"], n, res["bits"], res["scales"], res["zeros"], res["g_idx"], xb)
     assert np.all(M >= np.abs(xb) @ np.abs(res["What"]).T)
+
+
+# ---------------------------------------------------------------------------
+# f1 whole-decoder pass (oracle.decoder_oracle).
+# ---------------------------------------------------------------------------
+def test_decoder_pieces_closed_forms():
+    D = oracle.decoder_oracle
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 12)) * 3.0
+    y = D.rms_norm(x, eps=1e-6)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + 1e-6), rtol=1e-12)
+    # RoPE: position 0 is the identity, norms of rotated pairs are kept, and
+    # <rope(q) at m, rope(k) at n> depends only on m - n.
+    q = rng.standard_normal((1, 6, 2, 8))
+    k = rng.standard_normal((1, 6, 2, 8))
+    rq, rk = D.rope(np.repeat(q[:, :1], 6, axis=1)), D.rope(np.repeat(k[:, :1], 6, axis=1))
+    np.testing.assert_allclose(rq[:, 0], q[:, 0], rtol=0, atol=0)
+    np.testing.assert_allclose(np.linalg.norm(rq, axis=-1), np.linalg.norm(np.repeat(q[:, :1], 6, axis=1), axis=-1),
+                               rtol=1e-12)
+    d1 = np.sum(rq[0, 4] * rk[0, 1], axis=-1)
+    d2 = np.sum(rq[0, 5] * rk[0, 2], axis=-1)
+    np.testing.assert_allclose(d1, d2, rtol=1e-10)
+    # Causal attention: position 0 sees only itself (output = v_0); with two
+    # positions and q0 = k0 = 0, q1 . k1 = 0, k0 = 0: position 1 averages v0, v1.
+    Iq = np.eye(4)
+    h = np.array([[1.0, 2.0, 0.0, 0.0], [0.0, 0.0, 3.0, 5.0]])
+    Wz = np.zeros((4, 4))
+    out = D.attention(h, Wz, Wz, Iq, n_heads=1, seqs=1, seq_len=2)
+    np.testing.assert_allclose(out[0], h[0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(out[1], 0.5 * (h[0] + h[1]), rtol=1e-15)
+
+
+def _forward_inputs(blocks_what, X, n_heads, seqs, seq_len):
+    """Layer inputs of every block recomputed token-block by token-block from
+    the final (dequantized) weights -- a second, independent formulation of
+    which activations each layer sees."""
+    D = oracle.decoder_oracle
+    inputs = []
+    for W in blocks_what:
+        h = D.rms_norm(X)
+        parts = [D.attention(h[s * seq_len:(s + 1) * seq_len], W["q"], W["k"], W["v"], n_heads, 1, seq_len)
+                 for s in range(seqs)]
+        a = np.concatenate(parts, axis=0)
+        X = X + a @ W["o"].T
+        h2 = D.rms_norm(X)
+        mm = D.silu(h2 @ W["gate"].T) * (h2 @ W["up"].T)
+        X = X + mm @ W["down"].T
+        inputs.append(dict(q=h, k=h, v=h, o=a, gate=h2, up=h2, down=mm))
+    return X, inputs
+
+
+@pytest.mark.parametrize("levels,group,act", [(4, 32, False), (3, 0, True)])
+def test_decoder_pass_feeds_each_layer_the_quantized_predecessors(levels, group, act):
+    # The loss identity sum_j e_rj^2/2 = 1/2 (w - w^) H_d (w - w^)^T holds for
+    # each layer exactly when its Hessian was formed from the inputs the
+    # sequential protocol defines (quantized earlier layers).
+    D = oracle.decoder_oracle
+    rng = np.random.default_rng(11 + levels)
+    d, f, heads, nb, seqs, S = 32, 64, 2, 2, 3, 16
+    blocks = [{k: (rng.standard_normal(shp) * 0.1).astype(np.float32)
+               for k, shp in dict(q=(d, d), k=(d, d), v=(d, d), o=(d, d), gate=(f, d), up=(f, d), down=(d, f)).items()}
+              for _ in range(nb)]
+    X0 = rng.standard_normal((seqs * S, d))
+    Xo, res = D.quantize_decoder(blocks, X0, heads, seqs, S, levels=levels, group_size=group, act_order=act)
+    Xr, inputs = _forward_inputs([{k: r[k]["What"] for k in r} for r in res], X0, heads, seqs, S)
+    np.testing.assert_allclose(Xo, Xr, rtol=1e-10, atol=1e-12)
+    for b in range(nb):
+        assert np.array_equal(res[b]["q"]["perm"], res[b]["k"]["perm"])
+        assert np.array_equal(res[b]["gate"]["perm"], res[b]["up"]["perm"])
+        for name, r in res[b].items():
+            H = oracle.hessian(inputs[b][name].astype(np.float32).astype(np.float64))
+            Hd, _ = oracle.damp_and_permute(H, r["perm"], 0.01)
+            np.testing.assert_allclose(oracle.obs_loss(r["W"], r["What"], Hd, r["perm"]), r["row_loss"], rtol=1e-7)
