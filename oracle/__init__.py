@@ -26,6 +26,8 @@ from .gptq_oracle import (  # noqa: F401
     dequantize_packed,
     dequant_matmul,
     dequant_matmul_bound,
+    asymmetric_target,
+    gptaq_layer,
     gptq_layer,
 )
 from . import decoder_oracle  # noqa: F401,E402

@@ -396,6 +396,44 @@ def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# f3: asymmetric calibration (GPTAQ / GPTQv2 abstract on the Daily Papers page
+# and the mlsanity page: the quantized layer's output, computed on the
+# quantized model's inputs Xq, is matched to the full-precision layer's output
+# on the full-precision inputs Xf).  The pages print no closed form.  Reading
+# taken (a derivation, not the paper's algorithm): with
+#   W' = argmin_V ||Xq V^T - Xf W^T||_F^2 = W Xf^T Xq (Xq^T Xq)^{-1}
+# every Q satisfies ||Xq Q^T - Xf W^T||^2 = ||Xq (Q - W')^T||^2 + const
+# (Xq W'^T is the projection of Xf W^T onto the column space of Xq), so the
+# objective is GPTQ's with H = 2 Xq^T Xq applied to the target W'.  The
+# inverse carries GPTQ's own damping: W' = W Hc^T H_d^{-1}, Hc = 2 Xq^T Xf,
+# H_d = H + lambda I, which makes W' the ridge solution with penalty
+# (lambda/2) ||V||^2.
+# ---------------------------------------------------------------------------
+def asymmetric_target(W, Xq, Xf, damp_rel: float) -> np.ndarray:
+    """W' = W Hc^T (H + lambda I)^{-1}, float64 (original column order)."""
+    Xq = np.asarray(Xq, dtype=F64)
+    Xf = np.asarray(Xf, dtype=F64)
+    H = 2.0 * (Xq.T @ Xq)
+    lam = damp_rel * float(np.mean(np.diag(H)))
+    Hc = 2.0 * (Xq.T @ Xf)
+    G = np.asarray(W, dtype=F64) @ Hc.T
+    return np.linalg.solve(H + lam * np.eye(H.shape[0]), G.T).T
+
+
+def gptaq_layer(W, Xq, Xf, levels: int = 16, group_size: int = 0, block_size: int = 128,
+                damp_rel: float = 0.01, act_order: bool = False):
+    """GPTQ with H = 2 Xq^T Xq on the target W' (asymmetric_target)."""
+    H = hessian(Xq)
+    perm = act_order_perm(H) if act_order else np.arange(H.shape[0])
+    Hd, lam = damp_and_permute(H, perm, damp_rel)
+    U = inverse_cholesky_upper(Hd)
+    Wt = asymmetric_target(W, Xq, Xf, damp_rel)
+    res = gptq_quantize(Wt, U, perm, levels, group_size, block_size)
+    res.update(Wt=Wt, H=H, Hd=Hd, lam=lam, U=U)
+    return res
+
+
+# ---------------------------------------------------------------------------
 # f2: reading the packed weights back (GPTQ knowledge note, "Tradeoffs": the
 # speed of a quantized model rests on kernels that consume packed weights,
 # inference being limited by weight memory traffic; anthology record

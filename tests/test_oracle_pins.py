@@ -561,3 +561,38 @@ def test_decoder_pass_feeds_each_layer_the_quantized_predecessors(levels, group,
             H = oracle.hessian(inputs[b][name].astype(np.float32).astype(np.float64))
             Hd, _ = oracle.damp_and_permute(H, r["perm"], 0.01)
             np.testing.assert_allclose(oracle.obs_loss(r["W"], r["What"], Hd, r["perm"]), r["row_loss"], rtol=1e-7)
+
+
+# ---------------------------------------------------------------------------
+# f3 asymmetric calibration target.
+# ---------------------------------------------------------------------------
+def test_asymmetric_target_properties():
+    rng = np.random.default_rng(21)
+    T, n, m = 400, 24, 7
+    W = rng.standard_normal((m, n))
+    Xf = rng.standard_normal((T, n)) * np.exp(rng.normal(0, 0.5, size=n))
+    Xq = Xf + 0.05 * rng.standard_normal((T, n))
+    # Same inputs, no damping: the target is W itself.
+    np.testing.assert_allclose(oracle.asymmetric_target(W, Xf, Xf, 0.0), W, rtol=1e-9, atol=1e-11)
+    # No damping: ||Xq Q^T - Xf W^T||^2 = ||Xq (Q - W')^T||^2 + ||Xq W'^T - Xf W^T||^2 for any Q.
+    Wt = oracle.asymmetric_target(W, Xq, Xf, 0.0)
+    Q = np.round(W * 3) / 3
+    lhs = np.sum((Xq @ Q.T - Xf @ W.T) ** 2)
+    rhs = np.sum((Xq @ (Q - Wt).T) ** 2) + np.sum((Xq @ Wt.T - Xf @ W.T) ** 2)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-10)
+    # Damped: W' is the ridge solution, Xq^T (Xq W'^T - Xf W^T) + (lambda/2) W'^T = 0.
+    damp = 0.01
+    Wd = oracle.asymmetric_target(W, Xq, Xf, damp)
+    lam = damp * np.mean(np.diag(2 * Xq.T @ Xq))
+    grad = Xq.T @ (Xq @ Wd.T - Xf @ W.T) + 0.5 * lam * Wd.T
+    assert np.max(np.abs(grad)) <= 1e-9 * np.max(np.abs(Xq.T @ Xf @ W.T))
+
+
+def test_gptaq_reduces_to_gptq_on_symmetric_inputs():
+    rng = np.random.default_rng(22)
+    W = rng.normal(0, 0.02, size=(5, 40))
+    X = rng.standard_normal((300, 40)) * np.exp(rng.normal(0, 1.0, size=40))
+    a = oracle.gptaq_layer(W, X, X, levels=8, group_size=0, damp_rel=0.0, act_order=True)
+    b = oracle.gptq_layer(W, X=X, levels=8, group_size=0, damp_rel=0.0, act_order=True)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_allclose(a["Wt"], W, rtol=1e-9, atol=1e-12)
