@@ -165,6 +165,31 @@ gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t*
                       int32_t* g_idx, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Asymmetric calibration (GPTAQ / GPTQv2 abstract, Daily Papers and mlsanity
+ * pages: the quantized layer's output on the quantized model's inputs Xq is
+ * matched to the full-precision output on the full-precision inputs Xf).
+ * Because ||Xq Q^T - Xf W^T||^2 = ||Xq (Q - W')^T||^2 + const for the
+ * least-squares target W' (a derivation: the pages give no closed form), the
+ * method is GPTQ with H = 2 Xq^T Xq applied to W'.  This call forms
+ *   W' = W Hc^T H_d^{-1},   Hc = 2 Xq^T Xf,   H_d^{-1} = U^T U,
+ * with GPTQ's own damping inside U.  Typical use: one
+ * gptq_hessian_accumulate over [Xq | Xf] (tokens x 2n, side by side) gives
+ * H (top-left n x n block, prepared as usual) and Hc (top-right block);
+ * then gptq_quantize_layer(W', U, perm).
+ *   W      device, m x n (ldw >= n), element type w_dtype; read only.
+ *   Hc     device, n x n float32, leading dimension ldhc >= n.
+ *   U, perm  from gptq_prepare_hinv on H (perm NULL for the identity).
+ *   Wt     device, m x n float32 output (ldwt >= n), original column order.
+ *   ws     device workspace of gptq_asym_target_ws_bytes(m, n) bytes.
+ * float32 products (matrix cores), float32 rounding of W Hc^T, of the product
+ * with U^T and with U.
+ * ---------------------------------------------------------------------- */
+size_t gptq_asym_target_ws_bytes(int64_t m, int64_t n);
+gptq_status gptq_asym_target(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                             const float* Hc, int64_t ldhc, const float* U, const int32_t* perm,
+                             float* Wt, int64_t ldwt, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Reading the packed weights back: matrix-vector product for decode
  * (GPTQ knowledge note, "Tradeoffs": the speed of a quantized model rests on
  * kernels that consume the packed weights, inference being limited by weight

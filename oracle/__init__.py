@@ -27,6 +27,7 @@ from .gptq_oracle import (  # noqa: F401
     dequant_matmul,
     dequant_matmul_bound,
     asymmetric_target,
+    asymmetric_target_from_hessians,
     gptaq_layer,
     gptq_layer,
 )

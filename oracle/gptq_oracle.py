@@ -409,15 +409,19 @@ def unpack_codes(packed, n: int, bits: int) -> np.ndarray:
 # H_d = H + lambda I, which makes W' the ridge solution with penalty
 # (lambda/2) ||V||^2.
 # ---------------------------------------------------------------------------
+def asymmetric_target_from_hessians(W, H, Hc, damp_rel: float) -> np.ndarray:
+    """W' = W Hc^T (H + lambda I)^{-1} with lambda = damp_rel mean(diag H), float64."""
+    H = np.asarray(H, dtype=F64)
+    lam = damp_rel * float(np.mean(np.diag(H)))
+    G = np.asarray(W, dtype=F64) @ np.asarray(Hc, dtype=F64).T
+    return np.linalg.solve(H + lam * np.eye(H.shape[0]), G.T).T
+
+
 def asymmetric_target(W, Xq, Xf, damp_rel: float) -> np.ndarray:
-    """W' = W Hc^T (H + lambda I)^{-1}, float64 (original column order)."""
+    """W' from the inputs: H = 2 Xq^T Xq, Hc = 2 Xq^T Xf (original column order)."""
     Xq = np.asarray(Xq, dtype=F64)
     Xf = np.asarray(Xf, dtype=F64)
-    H = 2.0 * (Xq.T @ Xq)
-    lam = damp_rel * float(np.mean(np.diag(H)))
-    Hc = 2.0 * (Xq.T @ Xf)
-    G = np.asarray(W, dtype=F64) @ Hc.T
-    return np.linalg.solve(H + lam * np.eye(H.shape[0]), G.T).T
+    return asymmetric_target_from_hessians(W, 2.0 * (Xq.T @ Xq), 2.0 * (Xq.T @ Xf), damp_rel)
 
 
 def gptaq_layer(W, Xq, Xf, levels: int = 16, group_size: int = 0, block_size: int = 128,

@@ -6,6 +6,8 @@ C ABI, declared in include/gptq.h); this package is its Python binding.
 from ._lib import (  # noqa: F401
     GptqError,
     bits_for_levels,
+    gptaq_quantize_linear,
+    gptq_asym_target,
     gptq_dequant_gemm,
     gptq_dequant_gemv,
     gptq_hessian_accumulate,

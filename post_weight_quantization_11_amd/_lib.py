@@ -33,6 +33,8 @@ EXPORTS = (
     "gptq_pack",
     "gptq_dequant_gemv",
     "gptq_dequant_gemm",
+    "gptq_asym_target_ws_bytes",
+    "gptq_asym_target",
 )
 
 GEMV_MAX_BATCH = 8
@@ -77,6 +79,10 @@ def load(path: str = LIB_PATH):
     lib.gptq_pack.argtypes = [vp, i64, i64, vp, C, C, vp, i64, vp, vp]
     lib.gptq_dequant_gemv.restype = C
     lib.gptq_dequant_gemv.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, vp, i64, i64, vp, i64, vp]
+    lib.gptq_asym_target_ws_bytes.restype = sz
+    lib.gptq_asym_target_ws_bytes.argtypes = [i64, i64]
+    lib.gptq_asym_target.restype = C
+    lib.gptq_asym_target.argtypes = [vp, C, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp]
     lib.gptq_dequant_gemm.restype = C
     lib.gptq_dequant_gemm.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, i64, i64, vp, i64, vp]
     _lib = lib
@@ -271,6 +277,44 @@ def gptq_dequant_gemm(packed, scales, zeros, X, n: int, bits: int, group_size: i
                                _stream(stream))
     _check(rc, "gptq_dequant_gemm")
     return Y
+
+
+def gptq_asym_target(W, Hc, U, perm=None, Wt=None, ws=None, stream=None):
+    """W' (m x n float32) = W Hc^T U^T U permuted back; Hc n x n (any leading dimension)."""
+    torch = _torch()
+    lib = load()
+    _rows_check(W)
+    _rows_check(Hc)
+    _device_check(U, perm)
+    m, n = W.shape
+    if Wt is None:
+        Wt = torch.empty((m, n), dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_asym_target_ws_bytes(m, n), W.device)
+    rc = lib.gptq_asym_target(_ptr(W), _dtype_code(W), m, n, W.stride(0) if m else n, _ptr(Hc), Hc.stride(0),
+                              _ptr(U), _ptr(perm), _ptr(Wt), Wt.stride(0) if m else n, _ptr(ws),
+                              0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_asym_target")
+    return Wt
+
+
+def gptaq_quantize_linear(W, Xq, Xf, levels: int = 16, group_size: int = 0, damp_rel: float = 0.01,
+                          act_order: bool = False, block_size: int = 128, stream=None):
+    """Asymmetric calibration for one layer: one Hessian call over [Xq | Xf],
+    prepare on the Xq block, the target W', then the usual sweep and pack."""
+    torch = _torch()
+    n = W.shape[1]
+    Xcat = torch.cat([Xq, Xf], dim=1)
+    H2 = torch.empty((2 * n, 2 * n), dtype=torch.float32, device=W.device)
+    gptq_hessian_accumulate(H2, Xcat, 2.0, True, stream=stream)
+    H = H2[:n, :n].contiguous()
+    U, perm = gptq_prepare_hinv(H, damp_rel, act_order, stream=stream)
+    p = perm if act_order else None
+    Wt = gptq_asym_target(W, H2[:n, n:], U, p, stream=stream)
+    q = gptq_quantize_layer(Wt, U, p, levels, group_size, block_size, stream=stream)
+    packed, g_idx = gptq_pack(q["codes"], p, bits_for_levels(levels), group_size, stream=stream)
+    q.update(H=H, Hc=H2[:n, n:], U=U, perm=perm, Wt=Wt, packed=packed, g_idx=g_idx)
+    return q
 
 
 def bits_for_levels(levels: int) -> int:
