@@ -23,6 +23,11 @@ blocks, 2-bit g64 (`--levels 3` for the ternary variant); one JSON line with
 the total time and its split over Hessian / prepare / quantize / pack /
 forward (HIP events on the stream).
 
+`--gptaq` instead times the asymmetric-calibration variant on the 4096 x 4096
+layer (Xq = the quantized model's inputs, here X plus 5% noise; Xf = X):
+one Hessian call over [Xq | Xf], prepare, the target W' (three float32
+matrix products), sweep, pack; one JSON line with the per-stage times.
+
 `--gemv` instead times the packed-weight decode product gptq_dequant_gemv
 (Y = X W^T from the packed codes) on the 175B-class fc1 layer, 49152 x
 12288 4-bit per-row, batch `--gemv-batch` (default 1), and prints its own
@@ -202,6 +207,75 @@ def bench_decoder(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_gptaq(args):
+    """Asymmetric calibration on the Llama-7B attention projection (4096 x 4096, 262144 tokens)."""
+    import torch
+    import post_weight_quantization_11_amd as g
+    cfg = wl.WORKLOADS[2]
+    m, n, N = 4096, 4096, cfg.tokens
+    torch.cuda.set_device(0)
+    L = wl.workload_layer(2, 0)
+    X = to_device(L.x_all())
+    Wd = to_device(L.W)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    Xcat = torch.empty((N, 2 * n), dtype=torch.bfloat16, device="cuda")
+    Xcat[:, n:] = X
+    Xcat[:, :n] = (X.float() * (1.0 + 0.05 * torch.randn(X.shape, device="cuda", generator=gen))).to(torch.bfloat16)
+    del X
+    H2 = torch.empty((2 * n, 2 * n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    names = ["hessian", "prepare", "target", "quantize", "pack"]
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        mark(0)
+        g.gptq_hessian_accumulate(H2, Xcat, 2.0, True)
+        mark(1)
+        H = H2[:n, :n].contiguous()
+        U, perm = g.gptq_prepare_hinv(H, cfg.damp_rel, False)
+        mark(2)
+        Wt = g.gptq_asym_target(Wd, H2[:n, n:], U, None)
+        mark(3)
+        q = g.gptq_quantize_layer(Wt, U, None, cfg.levels, cfg.group_size, cfg.block_size)
+        mark(4)
+        g.gptq_pack(q["codes"], None, bits_of(cfg.levels), cfg.group_size)
+        mark(5)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    st = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, k in enumerate(names)}
+    tflops_t = 3 * 2.0 * m * n * n / (st["target"] * 1e-3) / 1e12
+    rec = {
+        "metric": "GPTAQ per-layer time (ms), asymmetric calibration",
+        "value": wall * 1e3,
+        "unit": "ms per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, f32/f64 quantizer",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + ", asymmetric calibration (Xq = X with 5% noise)", "m": m, "n": n,
+                   "tokens": N, "levels": cfg.levels, "group_size": cfg.group_size, "parallelism": "1 GPU"},
+        "stage_ms": st,
+        "target_roofline": {"bound": "mfma", "achieved": tflops_t, "peak": PEAK_F32_TFLOPS, "unit": "TFLOP/s",
+                            "frac": tflops_t / PEAK_F32_TFLOPS,
+                            "algorithmic": "3 m n^2 multiply-adds (W Hc^T, x U^T, x U)"},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def dataclasses_replace(obj, **kw):
     import dataclasses
     return dataclasses.replace(obj, **kw)
@@ -297,6 +371,7 @@ def main():
     ap.add_argument("--decoder-blocks", type=int, default=32)
     ap.add_argument("--decoder-seqs", type=int, default=128)
     ap.add_argument("--decoder-seq-len", type=int, default=2048)
+    ap.add_argument("--gptaq", action="store_true", help="time the asymmetric-calibration variant instead")
     ap.add_argument("--levels", type=int, default=4)
     ap.add_argument("--group-size", type=int, default=64)
     args = ap.parse_args()
@@ -316,6 +391,9 @@ def main():
         return
     if args.decoder:
         bench_decoder(args)
+        return
+    if args.gptaq:
+        bench_gptaq(args)
         return
     cfg = wl.WORKLOADS[args.config]
     layer = cfg.layers[0]

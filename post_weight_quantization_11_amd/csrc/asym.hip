@@ -6,7 +6,8 @@
 // GPTQ's with H = 2 Xq^T Xq on the target W'.  With GPTQ's damping,
 //   W' = W Hc^T H_d^{-1},  Hc = 2 Xq^T Xf,  H_d^{-1} = U^T U (processing order),
 // computed as three float32 matrix products on the matrix cores:
-//   G = W Hc^T,  Gp = G[:, perm],  T = Gp U^T,  Wp = T U,  W'[:, perm] = Wp.
+//   G = W Hc^T,  Gp = G[:, perm],  T = Gp U^T,  Wp = T U,  W'[:, perm] = Wp,
+// the two products with U skipping the K ranges where U is zero.
 // Hc and H come from one gptq_hessian_accumulate call on [Xq | Xf].
 #include "common.h"
 
@@ -41,7 +42,10 @@ __device__ inline floatx4 load_a4(const void* A, int64_t off, bool vec, int vali
 // MFMA 32x32x2, 128 x 128 tiles per workgroup (4 waves of 64 x 64), K staged
 // 32 deep through two LDS buffers with the next stage loaded into registers
 // while the current one multiplies.
-template <int DT, bool BT>
+// TRI = 1: B^T with B upper triangular (B[i][k] = 0 for k < i), so a column
+// tile starting at col0 needs K from col0 on; TRI = 2: B upper triangular
+// (B[k][j] = 0 for k > j), so a column tile needs K below col0 + kTN only.
+template <int DT, bool BT, int TRI>
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const void* __restrict__ A, int64_t lda,
                                                             const float* __restrict__ B, int64_t ldb,
                                                             float* __restrict__ C, int64_t ldc, int M, int N,
@@ -121,16 +125,18 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(const void* __restri
       }
     }
   };
-  const int nst = (K + kTK - 1) / kTK;
+  const int k_lo = TRI == 1 ? col0 : 0;
+  const int k_hi = TRI == 2 ? min(K, col0 + kTN) : K;
+  const int nst = k_hi > k_lo ? (k_hi - k_lo + kTK - 1) / kTK : 0;
   if (nst > 0) {
-    gload(0);
+    gload(k_lo);
     lstore(0);
   }
   __syncthreads();
   for (int s = 0; s < nst; ++s) {
     const int buf = s & 1;
     const bool next = s + 1 < nst;
-    if (next) gload((s + 1) * kTK);
+    if (next) gload(k_lo + (s + 1) * kTK);
 #pragma unroll
     for (int k2 = 0; k2 < kTK / 2; ++k2) {
       const int k = k2 * 2 + (lane >> 5);
@@ -176,11 +182,11 @@ __global__ __launch_bounds__(kThreads) void permute_cols_kernel(const float* __r
   }
 }
 
-template <int DT, bool BT>
+template <int DT, bool BT, int TRI = 0>
 void gemm(hipStream_t st, const void* A, int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc, int M,
           int N, int K) {
   const dim3 grid((unsigned)ceil_div(N, kTN), (unsigned)ceil_div(M, kTM));
-  gemm_f32_kernel<DT, BT><<<grid, kThreads, 0, st>>>(A, lda, B, ldb, C, ldc, M, N, K);
+  gemm_f32_kernel<DT, BT, TRI><<<grid, kThreads, 0, st>>>(A, lda, B, ldb, C, ldc, M, N, K);
 }
 
 }  // namespace
@@ -224,15 +230,15 @@ extern "C" gptq_status gptq_asym_target(const void* W, int w_dtype, int64_t m, i
   }
   // T = Gp U^T, then Wp = T U (H_d^{-1} = U^T U in processing order)
   float* tb = perm != nullptr ? b0 : b1;
-  gemm<GPTQ_F32, true>(st, gp, n, U, n, tb, n, M, N, N);
+  gemm<GPTQ_F32, true, 1>(st, gp, n, U, n, tb, n, M, N, N);
   GPTQ_TRY_LAUNCH();
   if (perm != nullptr) {
     float* wp = b1;
-    gemm<GPTQ_F32, false>(st, tb, n, U, n, wp, n, M, N, N);
+    gemm<GPTQ_F32, false, 2>(st, tb, n, U, n, wp, n, M, N, N);
     GPTQ_TRY_LAUNCH();
     permute_cols_kernel<false><<<(unsigned)m, kThreads, 0, st>>>(wp, n, perm, N, Wt, ldwt);
   } else {
-    gemm<GPTQ_F32, false>(st, tb, n, U, n, Wt, ldwt, M, N, N);
+    gemm<GPTQ_F32, false, 2>(st, tb, n, U, n, Wt, ldwt, M, N, N);
   }
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
