@@ -53,6 +53,7 @@ template <int BITS> struct Decode;
 template <> struct Decode<4> {
   static constexpr int H = 4;
   __device__ static int first(int j) { return 8 * (j >> 2) + (j & 3); }
+  __device__ static uint32_t pair(const uint32_t (&w)[4], int j) { return (w[j >> 2] >> (4 * (j & 3))) & 0x000F000Fu; }
   __device__ static void pairs(const uint32_t (&w)[4], uint32_t (&p)[kSeg / 2]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -64,6 +65,7 @@ template <> struct Decode<4> {
 template <> struct Decode<2> {
   static constexpr int H = 8;
   __device__ static int first(int j) { return 16 * (j >> 3) + (j & 7); }
+  __device__ static uint32_t pair(const uint32_t (&w)[2], int j) { return (w[j >> 3] >> (2 * (j & 7))) & 0x00030003u; }
   __device__ static void pairs(const uint32_t (&w)[2], uint32_t (&p)[kSeg / 2]) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -75,6 +77,11 @@ template <> struct Decode<2> {
 template <> struct Decode<3> {
   static constexpr int H = 16;
   __device__ static int first(int j) { return j; }
+  __device__ static uint32_t pair(const uint32_t (&w)[3], int j) {
+    const uint64_t lo = (uint64_t)w[0] | ((uint64_t)(w[1] & 0xFFFFu) << 32);
+    const uint64_t hi = (uint64_t)(w[1] >> 16) | ((uint64_t)w[2] << 16);
+    return (uint32_t)((lo >> (3 * j)) & 7u) | ((uint32_t)((hi >> (3 * j)) & 7u) << 16);
+  }
   __device__ static void pairs(const uint32_t (&w)[3], uint32_t (&p)[kSeg / 2]) {
     // bits 0..47 hold codes 0..15, bits 48..95 codes 16..31
     const uint64_t lo = (uint64_t)w[0] | ((uint64_t)(w[1] & 0xFFFFu) << 32);
@@ -441,6 +448,179 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_kernel(
     }
 }
 
+
+// Prefill-sized batches: a workgroup owns 128 rows of W x 128 rows of X
+// (4 waves as 2 x 2, each 64 x 64 = 4 x 4 MFMA tiles).  Per 128-column chunk
+// the X tile is staged once in LDS, already in code-pair order
+// (Xs[b][segment][pair] = (x_a, x_{a+H}) as in x_pair), so each MFMA B
+// operand is one 16-byte LDS read; the codes are decoded straight into A
+// registers as in the kernel above; the next chunk's X and codes are loaded
+// into registers while the current chunk multiplies.
+constexpr int kPM = 128, kPN = 128;
+
+template <int BITS>
+__global__ __launch_bounds__(kThreads) void dequant_gemm_lds_kernel(
+    const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int G, int group_size, const uint16_t* __restrict__ X, int batch,
+    int64_t ldx, float* __restrict__ Y, int64_t ldy, int vec_w, int vec_x) {
+  using D = Decode<BITS>;
+  __shared__ __attribute__((aligned(16))) uint32_t Xs[2][kPN][4][kSeg / 2];
+  __shared__ __attribute__((aligned(16))) float Xsum[2][kPN][4];   // sum of each staged segment
+  const int tid = threadIdx.x, lane = tid & 63, q = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wave >> 1, wc = wave & 1;
+  const int r0 = (int)blockIdx.x * kPM + wr * 64;   // this wave's first row
+  const int b0 = (int)blockIdx.y * kPN;             // the workgroup's first X row
+  const int nseg = (n + kSeg - 1) / kSeg;
+  const int nw = (int)(((int64_t)n * BITS + 31) / 32);
+  const int nchunk = (nseg + 3) / 4;
+  const int gchunks = group_size > 0 ? group_size / 128 : nchunk;
+  floatx4 acc[4][4], yacc[4][4];
+  float xsg[4];   // sum of X over the current group's columns, for X row of column tile nt
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) {
+    xsg[nt] = 0.f;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) acc[rt][nt] = yacc[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+  // X staging: thread t handles (X row t/2, segments 2*(t%2), 2*(t%2)+1) of the tile.
+  const int xb = tid >> 1, xs0 = 2 * (tid & 1);
+  struct Raw {
+    uint32_t xn[2][kSeg / 2];
+    uint32_t w[4][BITS];
+  };
+  auto load = [&](Raw& o, int ch) {
+    const int brow = b0 + xb;
+    const uint32_t keep = brow < batch ? 0xFFFFFFFFu : 0u;
+    const uint16_t* xr = X + (int64_t)(brow < batch ? brow : batch - 1) * ldx;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int k0 = (4 * ch + xs0 + u) * kSeg;
+      if (k0 + kSeg <= n && vec_x) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const u32x4 t = *reinterpret_cast<const u32x4*>(xr + k0 + 8 * v);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o.xn[u][4 * v + e] = t[e] & keep;
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kSeg / 2; ++t) {
+          const uint32_t lo = k0 + 2 * t < n ? xr[k0 + 2 * t] : 0u;
+          const uint32_t hi = k0 + 2 * t + 1 < n ? xr[k0 + 2 * t + 1] : 0u;
+          o.xn[u][t] = (lo | (hi << 16)) & keep;
+        }
+      }
+    }
+    const int seg = 4 * ch + q;
+    const bool whole = (seg + 1) * kSeg <= n;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      const int row = r0 + 16 * rt + c16;
+      const uint32_t* wr_ = packed + (int64_t)(row < m ? row : 0) * ldp + (int64_t)seg * BITS;
+      if (row < m && whole && vec_w && BITS == 4) {
+        const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr_));
+#pragma unroll
+        for (int e = 0; e < BITS; ++e) o.w[rt][e] = t[e & 3];
+      } else {
+#pragma unroll
+        for (int e = 0; e < BITS; ++e)
+          o.w[rt][e] = (row < m && seg < nseg && seg * BITS + e < nw) ? __builtin_nontemporal_load(wr_ + e) : 0u;
+      }
+    }
+  };
+  auto stage = [&](const Raw& o, int buf) {
+    const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0) in float16
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float sx = 0.f;
+#pragma unroll
+      for (int j = 0; j < kSeg / 2; j += 4) {
+        const u32x4 v = {x_pair(o.xn[u], D::first(j), D::H), x_pair(o.xn[u], D::first(j + 1), D::H),
+                         x_pair(o.xn[u], D::first(j + 2), D::H), x_pair(o.xn[u], D::first(j + 3), D::H)};
+        *reinterpret_cast<u32x4*>(&Xs[buf][xb][xs0 + u][j]) = v;
+      }
+#pragma unroll
+      for (int t = 0; t < kSeg / 2; ++t)
+        sx = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, o.xn[u][t]), __builtin_bit_cast(half2_t, one2), sx,
+                                    false);
+      Xsum[buf][xb][xs0 + u] = sx;
+    }
+  };
+  auto compute = [&](const Raw& o, int buf, int ch) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const floatx4 sv = *reinterpret_cast<const floatx4*>(&Xsum[buf][wc * 64 + 16 * nt + c16][0]);
+      xsg[nt] += (sv[0] + sv[1]) + (sv[2] + sv[3]);
+    }
+    // MFMA step j: the four B operands, then each row tile's four code pairs.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half8_t bop[4];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(&Xs[buf][wc * 64 + 16 * nt + c16][q][4 * j]);
+        bop[nt] = as_half8(v[0], v[1], v[2], v[3]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const half8_t aop = as_half8(D::pair(o.w[rt], 4 * j), D::pair(o.w[rt], 4 * j + 1),
+                                     D::pair(o.w[rt], 4 * j + 2), D::pair(o.w[rt], 4 * j + 3));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+          acc[rt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop, bop[nt], acc[rt][nt], 0, 0, 0);
+      }
+    }
+    if ((ch + 1) % gchunks == 0 || ch + 1 == nchunk) {
+      const int g = group_size > 0 ? ch / gchunks : 0;
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = r0 + 16 * rt + 4 * q + i;
+          const float sc = row < m ? scales[(int64_t)row * G + g] : 0.f;
+          const float szc = sc * (row < m ? (float)zeros[(int64_t)row * G + g] : 0.f);
+          const float s24 = sc * kTwo24;
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt)
+            yacc[rt][nt][i] = __builtin_fmaf(s24, acc[rt][nt][i], __builtin_fmaf(-szc, xsg[nt], yacc[rt][nt][i]));
+        }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        xsg[nt] = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) acc[rt][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+  };
+  // Two named register buffers (see the kernel above) and two LDS buffers.
+  Raw ra, rb;
+  load(ra, 0);
+  stage(ra, 0);
+  __syncthreads();
+  for (int ch = 0; ch < nchunk; ch += 2) {
+    if (ch + 1 < nchunk) load(rb, ch + 1);
+    compute(ra, 0, ch);
+    if (ch + 1 < nchunk) {
+      stage(rb, 1);           // buffer 1 was last read before the previous barrier
+      __syncthreads();
+      if (ch + 2 < nchunk) load(ra, ch + 2);
+      compute(rb, 1, ch + 1);
+      if (ch + 2 < nchunk) stage(ra, 0);
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = r0 + 16 * rt + 4 * q + i, col = b0 + wc * 64 + 16 * nt + c16;
+        if (row < m && col < batch) Y[(int64_t)col * ldy + row] = yacc[rt][nt][i];
+      }
+}
+
 template <int BITS, int RT, int NT>
 void launch_mfma(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
                  const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx, float* Y,
@@ -455,14 +635,17 @@ void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int
                        const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx,
                        float* Y, int64_t ldy, int vec_w, int vec_x) {
   // Decode-sized batches: one 16-column tile, 16 or 64 rows per workgroup
-  // (more workgroups for short layers); larger batches: 32 rows x 64 columns.
+  // (more workgroups for short layers); larger batches: 128 x 128 tiles with
+  // X staged in LDS.
   if (batch <= 16) {
     if (m <= 16384)
       launch_mfma<BITS, 1, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
     else
       launch_mfma<BITS, 4, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
   } else {
-    launch_mfma<BITS, 2, 4>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
+    const dim3 grid((unsigned)ceil_div(m, (int64_t)kPM), (unsigned)ceil_div(batch, (int64_t)kPN));
+    dequant_gemm_lds_kernel<BITS><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, group_size, X,
+                                                             batch, ldx, Y, ldy, vec_w, vec_x);
   }
 }
 
@@ -563,7 +746,7 @@ extern "C" gptq_status gptq_dequant_gemm(const uint32_t* packed, int64_t m, int6
   if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
   if (group_size % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
   if (m > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 30) || G > ((int64_t)1 << 30) ||
-      ceil_div(batch, 64) > 65535)
+      ceil_div(batch, 128) > 65535)
     return GPTQ_ERR_UNSUPPORTED;
   if (m == 0 || batch == 0) return GPTQ_OK;
   if (ld_packed < ceil_div(n * bits, 32) || ldx < n || ldy < m) return GPTQ_ERR_INVALID_ARG;

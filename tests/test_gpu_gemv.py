@@ -178,7 +178,9 @@ GEMM_CASES = [
     (40, 1000, 3, 128, 16),     # 3-bit, partial last group, full tile
     (33, 500, 2, 256, 17),      # 2-bit, two column tiles
     (20000, 384, 4, 0, 2),      # many rows (32 rows per wave)
-    (96, 640, 4, 128, 100),     # prefill-sized batch, several 64-column tiles
+    (96, 640, 4, 128, 100),     # prefill-sized batch (128 x 128 tiles, X staged in LDS)
+    (300, 1000, 3, 0, 257),     # prefill, ragged rows, columns and batch, 3-bit
+    (130, 512, 2, 256, 130),    # prefill, 2-bit groups of 256
 ]
 
 
