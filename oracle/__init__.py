@@ -29,6 +29,10 @@ from .gptq_oracle import (  # noqa: F401
     asymmetric_target,
     asymmetric_target_from_hessians,
     gptaq_layer,
+    lowrank_basis,
+    lowrank_hessian,
+    lowrank_compensation,
+    gptq_lora_layer,
     gptq_layer,
 )
 from . import decoder_oracle  # noqa: F401,E402

@@ -476,6 +476,77 @@ def dequant_matmul_bound(packed, n: int, bits: int, scales, zeros, g_idx, X) -> 
 
 
 # ---------------------------------------------------------------------------
+# f4: low-rank correction folded into the GPTQ pass (Daily Papers page,
+# GPTQ-intrinsic LoRA abstract): the weights are approximated as Q + L R and
+# judged by the layer-wise objective ||X W - X (Q + L R)||_F^2 (there W is
+# in x out; here W is out x in, so the correction of W is (L R)^T, L n x r,
+# R r x m), with the choice L = V_r, the top-r right singular vectors of X.
+# The page names a Hessian augmentation but prints no formula.  Reading taken
+# (a derivation from the stated objective): for a fixed L the objective is a
+# least-squares problem in R whose minimiser is
+#   R* = M^{-1} L^T H (W - Q)^T,  M = L^T H L,  H = 2 X^T X,
+# and substituting R* leaves, for every Q,
+#   ||(W - Q - R*^T L^T) X^T||^2 = 1/2 tr(D H_L D^T),  D = W - Q,
+#   H_L = H - H L M^{-1} L^T H,
+# so the GPTQ pass runs unchanged (act-order, damping, U, sweep) on H_L and R*
+# is formed from its result.  With L = V_r, H_L = 2 (X - X_r)^T (X - X_r):
+# the rank-r residual that replaces ||X||_F^2 in the page's error bound.
+# H_L depends on L only through its column span.
+# ---------------------------------------------------------------------------
+def lowrank_basis(H, r: int) -> np.ndarray:
+    """V_r: eigenvectors of H for its r largest eigenvalues (n x r, float64).
+
+    H = 2 X^T X, so these are the top-r right singular vectors of X.
+    """
+    H = np.asarray(H, dtype=F64)
+    if r == 0:
+        return np.zeros((H.shape[0], 0), dtype=F64)
+    w, V = np.linalg.eigh(H)
+    return V[:, np.argsort(w)[::-1][:r]]
+
+
+def lowrank_hessian(H, L):
+    """(H_L, K): H_L = H - H L M^{-1} L^T H and K = H L M^{-1}, M = L^T H L."""
+    H = np.asarray(H, dtype=F64)
+    L = np.asarray(L, dtype=F64)
+    if L.shape[1] == 0:
+        return H.copy(), np.zeros((H.shape[0], 0), dtype=F64)
+    HL = H @ L
+    M = L.T @ HL
+    K = np.linalg.solve(M, HL.T).T
+    return H - K @ HL.T, K
+
+
+def lowrank_compensation(W, What, K) -> np.ndarray:
+    """R* = K^T (W - W^)^T (r x m): the least-squares R for the quantized W^."""
+    D = np.asarray(W, dtype=F64) - np.asarray(What, dtype=F64)
+    return (D @ np.asarray(K, dtype=F64)).T
+
+
+def gptq_lora_layer(W, X=None, H=None, rank: int = 16, levels: int = 16, group_size: int = 0,
+                    block_size: int = 128, damp_rel: float = 0.01, act_order: bool = False, L=None):
+    """GPTQ on the augmented Hessian H_L with L = V_r (or the given L), then R*.
+
+    Returns gptq_layer's dictionary for H_L plus H (the undamped calibration
+    Hessian), L, K, R and loss_joint = 1/2 tr(D H D^T) with D = W - W^ - R^T L^T.
+    """
+    W = np.asarray(W, dtype=F64)
+    if H is None:
+        H = hessian(X)
+    H = np.asarray(H, dtype=F64)
+    if L is None:
+        L = lowrank_basis(H, rank)
+    HL, K = lowrank_hessian(H, L)
+    res = gptq_layer(W, H=HL, levels=levels, group_size=group_size, block_size=block_size,
+                     damp_rel=damp_rel, act_order=act_order)
+    R = lowrank_compensation(W, res["What"], K)
+    D = W - res["What"] - R.T @ np.asarray(L, dtype=F64).T
+    res.update(H_aug=res["H"], H=H, L=np.asarray(L, dtype=F64), K=K, R=R,
+               loss_joint=0.5 * float(np.sum((D @ H) * D)))
+    return res
+
+
+# ---------------------------------------------------------------------------
 # End to end for one layer.
 # ---------------------------------------------------------------------------
 def gptq_layer(W, X=None, H=None, levels: int = 16, group_size: int = 0,

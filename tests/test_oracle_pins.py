@@ -596,3 +596,118 @@ def test_gptaq_reduces_to_gptq_on_symmetric_inputs():
     b = oracle.gptq_layer(W, X=X, levels=8, group_size=0, damp_rel=0.0, act_order=True)
     np.testing.assert_array_equal(a["codes"], b["codes"])
     np.testing.assert_allclose(a["Wt"], W, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# f4 low-rank correction (GPTQ-intrinsic LoRA abstract, Daily Papers page).
+# Pinned without the closed forms: for every code vector on a small grid the
+# joint optimum over R is found by a least-squares solve on X L (H_L is never
+# formed), and L = V_r against a truncated SVD of X.
+# ---------------------------------------------------------------------------
+def _lora_inputs(seed, T=40, n=5, m=3, spikes=(6.0, 3.0)):
+    rng = _rng(seed)
+    X = rng.standard_normal((T, n))
+    for s in spikes:
+        X += s * np.outer(rng.standard_normal(T), rng.standard_normal(n)) / np.sqrt(n)
+    return X, rng.standard_normal((m, n)), rng
+
+
+def test_lowrank_hessian_is_the_joint_optimum_over_r():
+    X, W, rng = _lora_inputs(31)
+    n = X.shape[1]
+    H = 2.0 * X.T @ X
+    for r in (1, 2):
+        Ls = (oracle.lowrank_basis(H, r), np.linalg.qr(rng.standard_normal((n, r)))[0])
+        for L in Ls:
+            HL, K = oracle.lowrank_hessian(H, L)
+            XL = X @ L
+            for w in W:
+                s = (w.max() - w.min()) / 3.0
+                z = np.round(-w.min() / s)
+                for codes in itertools.product(range(4), repeat=n):
+                    what = s * (np.asarray(codes, dtype=np.float64) - z)
+                    y = X @ (w - what)
+                    rho = np.linalg.lstsq(XL, y, rcond=None)[0]
+                    best = float(np.sum((y - XL @ rho) ** 2))
+                    d = w - what
+                    closed = 0.5 * float(d @ HL @ d)
+                    assert abs(closed - best) <= 1e-9 * float(np.sum(y ** 2)) + 1e-12
+                    R = oracle.lowrank_compensation(w[None, :], what[None, :], K)
+                    np.testing.assert_allclose(R[:, 0], rho, rtol=1e-8, atol=1e-10)
+
+
+def test_lowrank_basis_is_the_truncated_svd():
+    X, _, _ = _lora_inputs(32, T=60, n=7, spikes=(9.0, 5.0, 2.5))
+    H = 2.0 * X.T @ X
+    Vt = np.linalg.svd(X, full_matrices=False)[2]
+    for r in (1, 2, 3):
+        L = oracle.lowrank_basis(H, r)
+        Vr = Vt[:r].T
+        np.testing.assert_allclose(L @ L.T, Vr @ Vr.T, atol=1e-10)
+        np.testing.assert_allclose(L.T @ L, np.eye(r), atol=1e-12)
+        Xp = X - X @ Vr @ Vr.T
+        HL, _ = oracle.lowrank_hessian(H, L)
+        np.testing.assert_allclose(HL, 2.0 * Xp.T @ Xp, atol=1e-9 * np.max(np.abs(H)))
+
+
+def test_lowrank_depends_on_the_span_only():
+    X, W, rng = _lora_inputs(33, T=50, n=8, m=4)
+    H = 2.0 * X.T @ X
+    L = np.linalg.qr(rng.standard_normal((8, 3)))[0]
+    A = rng.standard_normal((3, 3)) + 3 * np.eye(3)          # any invertible change of basis
+    HL1, K1 = oracle.lowrank_hessian(H, L)
+    HL2, K2 = oracle.lowrank_hessian(H, L @ A)
+    np.testing.assert_allclose(HL1, HL2, atol=1e-10 * np.max(np.abs(H)))
+    What = np.round(W * 2) / 2
+    C1 = oracle.lowrank_compensation(W, What, K1).T @ L.T
+    C2 = oracle.lowrank_compensation(W, What, K2).T @ (L @ A).T
+    np.testing.assert_allclose(C1, C2, atol=1e-10)
+    # H_L annihilates the span (H_L L = 0) and stays positive semidefinite.
+    assert np.max(np.abs(HL1 @ L)) <= 1e-10 * np.max(np.abs(H))
+    assert np.min(np.linalg.eigvalsh(HL1)) >= -1e-10 * np.max(np.abs(H))
+
+
+@pytest.mark.parametrize("levels,group,act", [(4, 0, False), (8, 4, True)])
+def test_lora_layer_loss_and_rank_zero(levels, group, act):
+    X, W, _ = _lora_inputs(34, T=80, n=12, m=6, spikes=(8.0, 4.0))
+    H = 2.0 * X.T @ X
+    res = oracle.gptq_lora_layer(W, X=X, rank=2, levels=levels, group_size=group, act_order=act,
+                                 damp_rel=0.01, block_size=4)
+    D = W - res["What"]
+    Dj = D - res["R"].T @ res["L"].T
+    direct = float(np.sum((Dj @ X.T) ** 2))
+    np.testing.assert_allclose(res["loss_joint"], direct, rtol=1e-9)
+    np.testing.assert_allclose(direct, 0.5 * float(np.sum((D @ res["H_aug"]) * D)), rtol=1e-9)
+    assert direct <= float(np.sum((D @ X.T) ** 2)) * (1 + 1e-12)     # R* is no worse than R = 0
+    r0 = oracle.gptq_lora_layer(W, X=X, rank=0, levels=levels, group_size=group, act_order=act, block_size=4)
+    plain = oracle.gptq_layer(W, X=X, levels=levels, group_size=group, act_order=act, block_size=4)
+    np.testing.assert_array_equal(r0["codes"], plain["codes"])
+    assert r0["R"].shape == (0, W.shape[0])
+
+
+LOWRANK_MUTATIONS = {
+    "M instead of its inverse": ("lowrank_hessian", "K = np.linalg.solve(M, HL.T).T", "K = HL @ M"),
+    "downdate sign": ("lowrank_hessian", "return H - K @ HL.T, K", "return H + K @ HL.T, K"),
+    "dropped H in H L": ("lowrank_hessian", "HL = H @ L", "HL = L"),
+    "compensation sign": ("lowrank_compensation", "D = np.asarray(W, dtype=F64) - np.asarray(What, dtype=F64)",
+                          "D = np.asarray(What, dtype=F64) - np.asarray(W, dtype=F64)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LOWRANK_MUTATIONS))
+def test_lowrank_planted_mistakes_are_caught(name, monkeypatch):
+    fn, old, new = LOWRANK_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(getattr(go, fn)))
+    assert old in src
+    ns = dict(go.__dict__)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    monkeypatch.setattr(go, fn, ns[fn])
+    monkeypatch.setattr(oracle, fn, ns[fn])
+    caught = []
+    for check in (test_lowrank_hessian_is_the_joint_optimum_over_r, test_lowrank_basis_is_the_truncated_svd,
+                  test_lowrank_depends_on_the_span_only):
+        try:
+            check()
+        except AssertionError:
+            caught.append(check)
+    assert caught, f"mutation '{name}' was not caught by any pin"
