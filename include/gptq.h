@@ -190,6 +190,73 @@ gptq_status gptq_asym_target(const void* W, int w_dtype, int64_t m, int64_t n, i
                              float* Wt, int64_t ldwt, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Low-rank correction folded into the GPTQ pass (GPTQ-intrinsic LoRA
+ * abstract, Daily Papers page): W is approximated as Q + (L R)^T with L
+ * n x r and R r x m, judged by ||(W - Q - R^T L^T) X^T||^2, with the choice
+ * L = V_r (top-r right singular vectors of X).  The page prints no formula
+ * for its Hessian augmentation; the one used here follows from the
+ * objective: for a fixed L the least-squares R is
+ *   R* = K^T (W - Q)^T,   K = H L M^{-1},   M = L^T H L,
+ * and what is left to minimise over Q is GPTQ's objective with
+ *   H_L = H - H L M^{-1} L^T H.
+ * Sequence: gptq_hessian_accumulate (H) -> gptq_lowrank_basis (L) ->
+ * gptq_lowrank_hessian (H_L, K) -> gptq_prepare_hinv(H_L) ->
+ * gptq_quantize_layer -> gptq_pack -> gptq_lowrank_compensation (R*).
+ * H_L and R* depend on L only through its column span.
+ * Float64 arithmetic throughout; H and H_L are float32, R float32.
+ * Matrices with r columns (Omega, L, K) are device float64, row-major
+ * n x r (leading dimension r).  1 <= r <= GPTQ_LOWRANK_MAX_RANK, r <= n.
+ * ---------------------------------------------------------------------- */
+#define GPTQ_LOWRANK_MAX_RANK 64
+
+/* Workspace for all three calls below on a layer of m rows (m may be 0 for
+ * the first two); 0 for an invalid n or r. */
+size_t gptq_lowrank_ws_bytes(int64_t m, int64_t n, int64_t r);
+
+/* L = V_r by subspace iteration: Q_0 = orth(Omega), Q_{t+1} = orth(H Q_t)
+ * for `iters` steps, orthonormalised by Cholesky-QR, plus one final
+ * Cholesky-QR pass.  The span converges to that of V_r at the rate
+ * (lambda_{r+1} / lambda_r)^iters of H's eigenvalues.
+ *   H      device, n x n float32 symmetric (ldh >= n), e.g. from
+ *          gptq_hessian_accumulate; rows are read as columns.
+ *   Omega  device, n x r float64 starting block (random numbers drawn by
+ *          the caller); read only.
+ *   iters  >= 0.
+ *   L      device, n x r float64 output, orthonormal columns.
+ * Synchronises `stream` once; returns GPTQ_ERR_NOT_PD if a Cholesky-QR
+ * Gram matrix was not positive definite (a rank-deficient block). */
+gptq_status gptq_lowrank_basis(const float* H, int64_t n, int64_t ldh, int64_t r, const double* Omega,
+                               int iters, double* L, void* ws, size_t ws_bytes, void* stream);
+
+/* H_L = H - Z Z^T and K = Z C^{-1}, where Z = H L C^{-T} and C C^T = L^T H L
+ * (Cholesky).
+ *   H      device, n x n float32 symmetric (ldh >= n).
+ *   L      device, n x r float64 (any basis of the correction's span).
+ *   H_L    device, n x n float32 output (ldhl >= n), symmetric; must not
+ *          alias H.  Pass it to gptq_prepare_hinv (act-order and damping
+ *          then apply to H_L).
+ *   K      device, n x r float64 output (for gptq_lowrank_compensation).
+ * Synchronises `stream` once; returns GPTQ_ERR_NOT_PD if L^T H L is not
+ * positive definite. */
+gptq_status gptq_lowrank_hessian(const float* H, int64_t n, int64_t ldh, const double* L, int64_t r,
+                                 float* H_L, int64_t ldhl, double* K, void* ws, size_t ws_bytes,
+                                 void* stream);
+
+/* R[a][i] = sum_c K[c][a] (W[i][c] - W^[i][c]): the least-squares R for the
+ * quantized weights W^[i][perm[j]] = scales[i][g(j)] (codes[i][j] -
+ * zeros[i][g(j)]), g(j) = j / group_size (0 when group_size = 0).
+ *   W, w_dtype, m, n, ldw   the layer as given to gptq_quantize_layer.
+ *   codes, scales, zeros    gptq_quantize_layer's outputs (processing order).
+ *   group_size, perm        as given to gptq_quantize_layer (perm may be NULL).
+ *   K      device, n x r float64 from gptq_lowrank_hessian.
+ *   R      device, r x m float32 output (ldr >= m).
+ * Does not synchronise. */
+gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                      const uint8_t* codes, const float* scales, const uint8_t* zeros,
+                                      int group_size, const int32_t* perm, const double* K, int64_t r,
+                                      float* R, int64_t ldr, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Reading the packed weights back: matrix-vector product for decode
  * (GPTQ knowledge note, "Tradeoffs": the speed of a quantized model rests on
  * kernels that consume the packed weights, inference being limited by weight

@@ -524,9 +524,13 @@ def lowrank_compensation(W, What, K) -> np.ndarray:
 
 
 def gptq_lora_layer(W, X=None, H=None, rank: int = 16, levels: int = 16, group_size: int = 0,
-                    block_size: int = 128, damp_rel: float = 0.01, act_order: bool = False, L=None):
+                    block_size: int = 128, damp_rel: float = 0.01, act_order: bool = False, L=None,
+                    hl_float32: bool = False):
     """GPTQ on the augmented Hessian H_L with L = V_r (or the given L), then R*.
 
+    hl_float32 rounds H_L to float32 before the GPTQ pass, the precision in
+    which a float32 Hessian interface hands it on (act-order then sorts the
+    same numbers on both sides of such an interface).
     Returns gptq_layer's dictionary for H_L plus H (the undamped calibration
     Hessian), L, K, R and loss_joint = 1/2 tr(D H D^T) with D = W - W^ - R^T L^T.
     """
@@ -537,6 +541,8 @@ def gptq_lora_layer(W, X=None, H=None, rank: int = 16, levels: int = 16, group_s
     if L is None:
         L = lowrank_basis(H, rank)
     HL, K = lowrank_hessian(H, L)
+    if hl_float32:
+        HL = HL.astype(F32).astype(F64)
     res = gptq_layer(W, H=HL, levels=levels, group_size=group_size, block_size=block_size,
                      damp_rel=damp_rel, act_order=act_order)
     R = lowrank_compensation(W, res["What"], K)

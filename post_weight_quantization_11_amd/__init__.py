@@ -11,6 +11,10 @@ from ._lib import (  # noqa: F401
     gptq_dequant_gemm,
     gptq_dequant_gemv,
     gptq_hessian_accumulate,
+    gptq_lora_quantize_linear,
+    gptq_lowrank_basis,
+    gptq_lowrank_compensation,
+    gptq_lowrank_hessian,
     gptq_pack,
     gptq_prepare_hinv,
     gptq_quantize_layer,

@@ -35,9 +35,14 @@ EXPORTS = (
     "gptq_dequant_gemm",
     "gptq_asym_target_ws_bytes",
     "gptq_asym_target",
+    "gptq_lowrank_ws_bytes",
+    "gptq_lowrank_basis",
+    "gptq_lowrank_hessian",
+    "gptq_lowrank_compensation",
 )
 
 GEMV_MAX_BATCH = 8
+LOWRANK_MAX_RANK = 64
 
 _lib = None
 
@@ -85,6 +90,15 @@ def load(path: str = LIB_PATH):
     lib.gptq_asym_target.argtypes = [vp, C, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp]
     lib.gptq_dequant_gemm.restype = C
     lib.gptq_dequant_gemm.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, i64, i64, vp, i64, vp]
+    lib.gptq_lowrank_ws_bytes.restype = sz
+    lib.gptq_lowrank_ws_bytes.argtypes = [i64, i64, i64]
+    lib.gptq_lowrank_basis.restype = C
+    lib.gptq_lowrank_basis.argtypes = [vp, i64, i64, i64, vp, C, vp, vp, sz, vp]
+    lib.gptq_lowrank_hessian.restype = C
+    lib.gptq_lowrank_hessian.argtypes = [vp, i64, i64, vp, i64, vp, i64, vp, vp, sz, vp]
+    lib.gptq_lowrank_compensation.restype = C
+    lib.gptq_lowrank_compensation.argtypes = [vp, C, i64, i64, i64, vp, vp, vp, C, vp, vp, i64, vp, i64, vp, sz,
+                                              vp]
     _lib = lib
     return lib
 
@@ -314,6 +328,89 @@ def gptaq_quantize_linear(W, Xq, Xf, levels: int = 16, group_size: int = 0, damp
     q = gptq_quantize_layer(Wt, U, p, levels, group_size, block_size, stream=stream)
     packed, g_idx = gptq_pack(q["codes"], p, bits_for_levels(levels), group_size, stream=stream)
     q.update(H=H, Hc=H2[:n, n:], U=U, perm=perm, Wt=Wt, packed=packed, g_idx=g_idx)
+    return q
+
+
+def gptq_lowrank_basis(H, Omega, iters: int = 10, L=None, ws=None, stream=None):
+    """L (n x r float64, orthonormal columns) spanning H's top-r eigenvectors by
+    subspace iteration from the caller's n x r float64 block Omega."""
+    torch = _torch()
+    lib = load()
+    _rows_check(H)
+    _device_check(Omega, L)
+    n, r = Omega.shape
+    if L is None:
+        L = torch.empty((n, r), dtype=torch.float64, device=H.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_lowrank_ws_bytes(0, n, r), H.device)
+    rc = lib.gptq_lowrank_basis(_ptr(H), n, H.stride(0), r, _ptr(Omega), int(iters), _ptr(L), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_lowrank_basis")
+    return L
+
+
+def gptq_lowrank_hessian(H, L, H_L=None, K=None, ws=None, stream=None):
+    """(H_L, K): H_L = H - H L M^{-1} L^T H (n x n float32), K = H L M^{-1}
+    (n x r float64), M = L^T H L."""
+    torch = _torch()
+    lib = load()
+    _rows_check(H)
+    _device_check(L, K)
+    n, r = L.shape
+    if H_L is None:
+        H_L = torch.empty((n, n), dtype=torch.float32, device=H.device)
+    if K is None:
+        K = torch.empty((n, r), dtype=torch.float64, device=H.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_lowrank_ws_bytes(0, n, r), H.device)
+    rc = lib.gptq_lowrank_hessian(_ptr(H), n, H.stride(0), _ptr(L), r, _ptr(H_L), H_L.stride(0), _ptr(K),
+                                  _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_lowrank_hessian")
+    return H_L, K
+
+
+def gptq_lowrank_compensation(W, q, K, perm=None, group_size: int = 0, R=None, ws=None, stream=None):
+    """R (r x m float32) = K^T (W - W^)^T for gptq_quantize_layer's output q."""
+    torch = _torch()
+    lib = load()
+    _rows_check(W)
+    _device_check(K, perm, q["codes"], q["scales"], q["zeros"])
+    m, n = W.shape
+    r = K.shape[1]
+    if R is None:
+        R = torch.empty((r, m), dtype=torch.float32, device=W.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_lowrank_ws_bytes(m, n, r), W.device)
+    rc = lib.gptq_lowrank_compensation(_ptr(W), _dtype_code(W), m, n, W.stride(0), _ptr(q["codes"]),
+                                       _ptr(q["scales"]), _ptr(q["zeros"]), int(group_size), _ptr(perm), _ptr(K),
+                                       r, _ptr(R), R.stride(0), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream))
+    _check(rc, "gptq_lowrank_compensation")
+    return R
+
+
+def gptq_lora_quantize_linear(W, X=None, H=None, rank: int = 16, levels: int = 16, group_size: int = 0,
+                              damp_rel: float = 0.01, act_order: bool = False, block_size: int = 128,
+                              iters: int = 10, seed: int = 0, Omega=None, stream=None):
+    """GPTQ with the low-rank correction for one layer: H, L = V_r (subspace
+    iteration from Omega, by default a seeded standard normal n x r block),
+    H_L and K, then prepare/quantize/pack on H_L and finally R."""
+    torch = _torch()
+    n = W.shape[1]
+    if H is None:
+        H = torch.empty((n, n), dtype=torch.float32, device=W.device)
+        gptq_hessian_accumulate(H, X, 2.0, True, stream=stream)
+    if Omega is None:
+        gen = torch.Generator(device=W.device).manual_seed(int(seed))
+        Omega = torch.randn((n, rank), generator=gen, device=W.device, dtype=torch.float64)
+    L = gptq_lowrank_basis(H, Omega, iters, stream=stream)
+    H_L, K = gptq_lowrank_hessian(H, L, stream=stream)
+    U, perm = gptq_prepare_hinv(H_L, damp_rel, act_order, stream=stream)
+    p = perm if act_order else None
+    q = gptq_quantize_layer(W, U, p, levels, group_size, block_size, stream=stream)
+    packed, g_idx = gptq_pack(q["codes"], p, bits_for_levels(levels), group_size, stream=stream)
+    R = gptq_lowrank_compensation(W, q, K, p, group_size, stream=stream)
+    q.update(H=H, L=L, H_L=H_L, K=K, U=U, perm=perm, packed=packed, g_idx=g_idx, R=R)
     return q
 
 

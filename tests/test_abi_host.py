@@ -132,3 +132,38 @@ def test_pack_argument_errors(lib):
     assert f(_fake(), 4, 64, _null(), 4, 0, _fake(), 7, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
     assert f(_null(), 4, 64, _null(), 4, 0, _fake(), 8, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
     assert f(_fake(), 4, 0, _null(), 4, 0, _fake(), 8, _null(), _null()) == _lib.GPTQ_OK
+
+
+def test_lowrank_argument_errors(lib):
+    assert lib.gptq_lowrank_ws_bytes(0, 0, 1) == 0
+    assert lib.gptq_lowrank_ws_bytes(0, 100, 0) == 0
+    assert lib.gptq_lowrank_ws_bytes(0, 100, 65) == 0          # above GPTQ_LOWRANK_MAX_RANK
+    assert lib.gptq_lowrank_ws_bytes(0, 8, 9) == 0             # r > n
+    ws = lib.gptq_lowrank_ws_bytes(0, 4096, 64)
+    assert ws >= 2 * 4096 * 64 * 8
+    assert lib.gptq_lowrank_ws_bytes(11008, 4096, 64) >= ws
+    big = 1 << 30
+    f = lib.gptq_lowrank_basis
+    assert f(_fake(), 100, 100, 65, _fake(), 4, _fake(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 99, 8, _fake(), 4, _fake(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 100, 8, _fake(), -1, _fake(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 100, 8, _null(), 4, _fake(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 100, 8, _fake(), 4, _fake(), _fake(), 16, _null()) == _lib.GPTQ_ERR_WORKSPACE
+    f = lib.gptq_lowrank_hessian
+    hl = ctypes.c_void_p(0x2000)
+    assert f(_fake(), 100, 100, _fake(), 8, hl, 100, _null(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 100, _fake(), 8, hl, 99, _fake(), _fake(), big, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 100, 100, _fake(), 8, _fake(), 100, _fake(), _fake(), big,
+             _null()) == _lib.GPTQ_ERR_INVALID_ARG                # H_L aliases H
+    assert f(_fake(), 100, 100, _fake(), 8, hl, 100, _fake(), _null(), 0, _null()) == _lib.GPTQ_ERR_WORKSPACE
+    f = lib.gptq_lowrank_compensation
+    args = [_fake(), 2, 50, 100, 100, _fake(), _fake(), _fake(), 0, _null(), _fake(), 8, _fake(), 50, _fake(), big,
+            _null()]
+    bad = list(args); bad[1] = 7                                   # dtype
+    assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
+    bad = list(args); bad[13] = 49                                 # ldr < m
+    assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
+    bad = list(args); bad[8] = -4                                  # group size
+    assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
+    bad = list(args); bad[15] = 16                                 # workspace
+    assert f(*bad) == _lib.GPTQ_ERR_WORKSPACE
