@@ -28,6 +28,12 @@ layer (Xq = the quantized model's inputs, here X plus 5% noise; Xf = X):
 one Hessian call over [Xq | Xf], prepare, the target W' (three float32
 matrix products), sweep, pack; one JSON line with the per-stage times.
 
+`--lora` instead times GPTQ with the low-rank correction (GPTQ-intrinsic
+LoRA reading) on the same 4096 x 4096 layer: Hessian, the rank-`--rank`
+basis (subspace iteration, `--lora-iters` steps), the augmented Hessian H_L,
+prepare / sweep / pack on H_L and the compensation R; one JSON line with the
+per-stage times and their float64 roofline fractions.
+
 `--gemv` instead times the packed-weight decode product gptq_dequant_gemv
 (Y = X W^T from the packed codes) on the 175B-class fc1 layer, 49152 x
 12288 4-bit per-row, batch `--gemv-batch` (default 1), and prints its own
@@ -276,6 +282,86 @@ def bench_gptaq(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_lora(args):
+    """Low-rank corrected GPTQ on the Llama-7B attention projection (4096 x 4096, 262144 tokens)."""
+    import torch
+    import post_weight_quantization_11_amd as g
+    cfg = wl.WORKLOADS[2]
+    m, n, N, r, iters = 4096, 4096, cfg.tokens, args.rank, args.lora_iters
+    torch.cuda.set_device(0)
+    L = wl.workload_layer(2, 0)
+    X = to_device(L.x_all())
+    Wd = to_device(L.W)
+    H = torch.empty((n, n), dtype=torch.float32, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    Omega = torch.randn((n, r), generator=gen, device="cuda", dtype=torch.float64)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    names = ["hessian", "basis", "lowrank_hessian", "prepare", "quantize", "pack", "compensation"]
+    out = {}
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
+        mark(0)
+        g.gptq_hessian_accumulate(H, X, 2.0, True)
+        mark(1)
+        Lb = g.gptq_lowrank_basis(H, Omega, iters)
+        mark(2)
+        HL, K = g.gptq_lowrank_hessian(H, Lb)
+        mark(3)
+        U, perm = g.gptq_prepare_hinv(HL, cfg.damp_rel, False)
+        mark(4)
+        q = g.gptq_quantize_layer(Wd, U, None, cfg.levels, cfg.group_size, cfg.block_size)
+        mark(5)
+        g.gptq_pack(q["codes"], None, bits_of(cfg.levels), cfg.group_size)
+        mark(6)
+        R = g.gptq_lowrank_compensation(Wd, q, K, None, cfg.group_size)
+        mark(7)
+        out.update(q=q, R=R, L=Lb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    st = {k: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs])) for i, k in enumerate(names)}
+    # Algorithmic float64 flops: H Q per iteration (2 n^2 r) plus the Cholesky-QR
+    # Gram and triangular products (4 n r^2 per pass, iters + 2 passes); H L and
+    # the downdate (4 n^2 r) plus L^T H L, C^{-T} and C^{-1} (6 n r^2); R (2 m n r).
+    fl = {"basis": iters * 2.0 * n * n * r + (iters + 2) * 4.0 * n * r * r,
+          "lowrank_hessian": 4.0 * n * n * r + 6.0 * n * r * r,
+          "compensation": 2.0 * m * n * r}
+    roof = {k: {"ms": st[k], "tflops": fl[k] / (st[k] * 1e-3) / 1e12,
+                "frac": fl[k] / (st[k] * 1e-3) / 1e12 / PEAK_F64_TFLOPS} for k in fl}
+    Lh = out["L"]
+    orth = float((Lh.T @ Lh - torch.eye(r, dtype=torch.float64, device="cuda")).abs().max())
+    rec = {
+        "metric": "GPTQ with low-rank correction, per-layer time (ms)",
+        "value": wall * 1e3,
+        "unit": "ms per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 inputs, f64 low-rank stages, f32/f64 quantizer",
+        "data": "synthetic",
+        "config": {"workload": cfg.name + f", rank-{r} correction (L = V_r by {iters} subspace iterations)",
+                   "m": m, "n": n, "tokens": N, "rank": r, "iters": iters, "levels": cfg.levels,
+                   "group_size": cfg.group_size, "parallelism": "1 GPU"},
+        "stage_ms": st,
+        "lowrank_roofline": {"bound": "f64 VALU", "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s", "stages": roof},
+        "sanity": {"L_orthonormal_maxerr": orth, "R_finite": bool(torch.isfinite(out["R"]).all())},
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def dataclasses_replace(obj, **kw):
     import dataclasses
     return dataclasses.replace(obj, **kw)
@@ -372,6 +458,9 @@ def main():
     ap.add_argument("--decoder-seqs", type=int, default=128)
     ap.add_argument("--decoder-seq-len", type=int, default=2048)
     ap.add_argument("--gptaq", action="store_true", help="time the asymmetric-calibration variant instead")
+    ap.add_argument("--lora", action="store_true", help="time GPTQ with the low-rank correction instead")
+    ap.add_argument("--rank", type=int, default=64)
+    ap.add_argument("--lora-iters", type=int, default=10)
     ap.add_argument("--levels", type=int, default=4)
     ap.add_argument("--group-size", type=int, default=64)
     args = ap.parse_args()
@@ -394,6 +483,9 @@ def main():
         return
     if args.gptaq:
         bench_gptaq(args)
+        return
+    if args.lora:
+        bench_lora(args)
         return
     cfg = wl.WORKLOADS[args.config]
     layer = cfg.layers[0]

@@ -13,12 +13,12 @@
 //
 // All arithmetic is float64; H and H_L are float32 (the precision in which
 // gptq_hessian_accumulate writes H and gptq_prepare_hinv reads it), R is
-// float32.  Matrices of r columns (L, K, Omega and the internal Y, Z) are
-// row-major n x r.  The products are small next to the Hessian (n^2 r
-// multiply-adds for H L and for H_L, m n r for R*), so they run as plain
-// float64 VALU tiles: 64-row output tiles of all r <= 64 columns, 4 x 4 per
-// thread, K staged 32 deep through LDS and split over workgroups with a
-// fixed-order float64 reduction (results do not depend on timing).
+// float32.  Matrices of r columns (L, K, Omega and the internal Y) are
+// row-major n x r.  The n^2 r products (H L and the downdate H - Z Z^T) run
+// on the float64 matrix cores; the r x r Cholesky factor and the row-wise
+// triangular solves are register-resident single-wave kernels; the m n r
+// compensation product is a float64 VALU tile kernel.  Products split over K
+// are summed in a fixed order (results do not depend on timing).
 #include "common.h"
 
 namespace gptq {
@@ -33,21 +33,17 @@ constexpr int kTargetBlocks = 512;
 
 static_assert(kR == 64, "the tile shapes assume a 64-column rank tile");
 
-// A operand of the tall product Out(p, a) = sum_k A(p, k) B(k, a).
-enum AMode { kHessianT = 0, kMatT = 1, kDelta = 2 };
-
+// The compensation product Out(p, a) = sum_k D(p, k) B(k, a): D = W - W^ in
+// processing order (formed on the fly), B = K with rows gathered through perm.
 struct TallArgs {
-  // A
-  const void* A;       // kHessianT: float H (n x n, ld); kMatT: double (K x P, ld); kDelta: W (m x n, ld)
+  const void* A;          // W (m x n, leading dimension lda)
   int64_t lda;
-  int w_dtype;         // kDelta
-  const uint8_t* codes;   // kDelta: m x n, processing order
-  const float* scales;    // kDelta: m x G
-  const uint8_t* zeros;   // kDelta: m x G
-  int64_t G, group;       // kDelta
-  const int32_t* perm;    // kDelta: A's column k is W's column perm[k]; B's row k is perm[k]; may be NULL
-  // B: K x r float64, row-major (ld r), rows gathered through perm in kDelta
-  const double* B;
+  const uint8_t* codes;   // m x n, processing order
+  const float* scales;    // m x G
+  const uint8_t* zeros;   // m x G
+  int64_t G, group;
+  const int32_t* perm;    // D's column k is W's column perm[k], B's row k is perm[k]; may be NULL
+  const double* B;        // K x r float64, row-major (leading dimension ldb)
   int64_t ldb;
   int64_t P, K, r;
   int64_t kchunk;      // K per split (multiple of kTK)
@@ -59,49 +55,34 @@ __device__ inline double w_elem(const void* W, int64_t i) {
   return static_cast<double>(load_as_f32<DT>(W, i));
 }
 
-template <int MODE, int DT>
+// As[kk][pp] = D(p0 + pp, k0 + kk) = W[p][perm[k]] - s (c - z): exactly the
+// float64 difference of the stored weight and its dequantized value (s is
+// float32 and c - z a small integer, so s (c - z) is exact); 0 outside.
+template <int DT>
 __device__ inline void load_a_stage(const TallArgs& a, double (*As)[kPitch], int64_t p0, int64_t k0, int tid) {
-  if (MODE == kHessianT || MODE == kMatT) {
-    // A(p, k) = Src[k][p]: row k of the source is read contiguously along p.
-    const int pp = tid & 63;
+  const int kk = tid & 31;
 #pragma unroll
-    for (int it = 0; it < kTK / 4; ++it) {
-      const int kk = (tid >> 6) + 4 * it;
-      const int64_t p = p0 + pp, k = k0 + kk;
-      double v = 0.0;
-      if (p < a.P && k < a.K) {
-        if (MODE == kHessianT) v = static_cast<double>(static_cast<const float*>(a.A)[k * a.lda + p]);
-        else v = static_cast<const double*>(a.A)[k * a.lda + p];
-      }
-      As[kk][pp] = v;
+  for (int it = 0; it < kTP / 8; ++it) {
+    const int pp = (tid >> 5) + 8 * it;
+    const int64_t p = p0 + pp, k = k0 + kk;
+    double v = 0.0;
+    if (p < a.P && k < a.K) {
+      const int64_t col = a.perm ? static_cast<int64_t>(a.perm[k]) : k;
+      const int64_t g = a.group ? k / a.group : 0;
+      const double s = static_cast<double>(a.scales[p * a.G + g]);
+      const double c = static_cast<double>(a.codes[p * a.K + k]);
+      const double z = static_cast<double>(a.zeros[p * a.G + g]);
+      v = w_elem<DT>(a.A, p * a.lda + col) - s * (c - z);
     }
-  } else {
-    // A(p, k) = W[p][perm[k]] - s (c - z) for row p, processing column k:
-    // exactly the float64 difference of the stored weight and its dequantized
-    // value (s is float32 and c - z a small integer, so s (c - z) is exact).
-    const int kk = tid & 31;
-#pragma unroll
-    for (int it = 0; it < kTP / 8; ++it) {
-      const int pp = (tid >> 5) + 8 * it;
-      const int64_t p = p0 + pp, k = k0 + kk;
-      double v = 0.0;
-      if (p < a.P && k < a.K) {
-        const int64_t col = a.perm ? static_cast<int64_t>(a.perm[k]) : k;
-        const int64_t g = a.group ? k / a.group : 0;
-        const double s = static_cast<double>(a.scales[p * a.G + g]);
-        const double c = static_cast<double>(a.codes[p * a.K + k]);
-        const double z = static_cast<double>(a.zeros[p * a.G + g]);
-        v = w_elem<DT>(a.A, p * a.lda + col) - s * (c - z);
-      }
-      As[kk][pp] = v;
-    }
+    As[kk][pp] = v;
   }
 }
 
-// part[s][p][a] = sum over split s's K range of A(p, k) B(k, a), for one
-// 64-row tile (blockIdx.x) and one split (blockIdx.y).
-template <int MODE, int DT>
-__global__ __launch_bounds__(kThreads) void tall_product_kernel(TallArgs a) {
+// part[s][p][a] = sum over split s's K range of D(p, k) B(k, a), for one
+// 64-row tile (blockIdx.x) and one split (blockIdx.y): 4 x 4 outputs per
+// thread, K staged 32 deep through LDS.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void compensation_kernel(TallArgs a) {
   __shared__ __attribute__((aligned(16))) double As[kTK][kPitch];
   __shared__ __attribute__((aligned(16))) double Bs[kTK][kPitch];
   const int tid = threadIdx.x;
@@ -116,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void tall_product_kernel(TallArgs a) {
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
 
   for (int64_t k0 = kbeg; k0 < kend; k0 += kTK) {
-    load_a_stage<MODE, DT>(a, As, p0, k0, tid);
+    load_a_stage<DT>(a, As, p0, k0, tid);
     {
       const int col = tid & 63;
 #pragma unroll
@@ -125,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void tall_product_kernel(TallArgs a) {
         const int64_t k = k0 + kk;
         double v = 0.0;
         if (k < kend && col < a.r) {
-          const int64_t row = (MODE == kDelta && a.perm) ? static_cast<int64_t>(a.perm[k]) : k;
+          const int64_t row = a.perm ? static_cast<int64_t>(a.perm[k]) : k;
           v = a.B[row * a.ldb + col];
         }
         Bs[kk][col] = v;
@@ -155,6 +136,98 @@ __global__ __launch_bounds__(kThreads) void tall_product_kernel(TallArgs a) {
   }
 }
 
+// The same product on the matrix cores for A(p, k) = S[k][p] (S float32 or
+// float64, widened exactly): float64 MFMA 16x16x4 (A element (row l%16,
+// k l/16), B element (k l/16, column l%16), accumulator register i of lane l
+// at row l/16 + 4i, column l%16).  A workgroup owns kMP rows and all kR
+// columns; its four waves take every fourth 4-deep K step of the split, keep
+// kDepth steps of operands in flight, and are summed through LDS in wave
+// order at the end.
+constexpr int kMP = 32;                   // rows per workgroup
+constexpr int kDepth = 8;                 // K steps in flight per wave
+constexpr int kMChunk = 16 * kDepth;      // K granularity of a split
+
+template <typename ST>
+__global__ __launch_bounds__(kThreads) void tall_mfma_kernel(const ST* __restrict__ S, int64_t lds_,
+                                                             const double* __restrict__ B, int64_t ldb, int64_t P,
+                                                             int64_t K, int r, int64_t kchunk,
+                                                             double* __restrict__ part) {
+  __shared__ double red[3][kMP][kR + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kl = lane >> 4, cl = lane & 15;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kMP;
+  const int64_t kbeg = static_cast<int64_t>(blockIdx.y) * kchunk;
+  const int64_t kend = kbeg + kchunk < K ? kbeg + kchunk : K;
+  const int64_t kw = kbeg + 4 * wave + kl;       // this lane's K index in step 0
+  const int nst = kbeg + 4 * wave < kend ? static_cast<int>((kend - kbeg - 4 * wave + 15) / 16) : 0;
+  const int64_t pa = p0 + cl, pb = p0 + 16 + cl;
+  const bool pa_in = pa < P, pb_in = pb < P;
+  bool c_in[4];
+#pragma unroll
+  for (int tj = 0; tj < 4; ++tj) c_in[tj] = 16 * tj + cl < r;
+  double a0[kDepth], a1[kDepth], b[kDepth][4];
+  doublex4 acc[2][4];
+#pragma unroll
+  for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) acc[ti][tj] = doublex4{0.0, 0.0, 0.0, 0.0};
+
+#define GPTQ_TALL_LOAD(d, step)                                                     \
+  do {                                                                              \
+    const int64_t k_ = kw + 16 * static_cast<int64_t>(step);                       \
+    const bool kin_ = k_ < kend;                                                    \
+    a0[d] = (kin_ && pa_in) ? static_cast<double>(S[k_ * lds_ + pa]) : 0.0;        \
+    a1[d] = (kin_ && pb_in) ? static_cast<double>(S[k_ * lds_ + pb]) : 0.0;        \
+    _Pragma("unroll") for (int tj = 0; tj < 4; ++tj)                                \
+      b[d][tj] = (kin_ && c_in[tj]) ? B[k_ * ldb + 16 * tj + cl] : 0.0;             \
+  } while (0)
+
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) GPTQ_TALL_LOAD(d, d);
+  for (int s0 = 0; s0 < nst; s0 += kDepth) {
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) {
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj) {
+        acc[0][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a0[d], b[d][tj], acc[0][tj], 0, 0, 0);
+        acc[1][tj] = __builtin_amdgcn_mfma_f64_16x16x4f64(a1[d], b[d][tj], acc[1][tj], 0, 0, 0);
+      }
+      GPTQ_TALL_LOAD(d, s0 + d + kDepth);
+    }
+  }
+#undef GPTQ_TALL_LOAD
+
+  if (wave > 0) {
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave - 1][16 * ti + kl + 4 * i][16 * tj + cl] = acc[ti][tj][i];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    double* out = part + static_cast<int64_t>(blockIdx.y) * P * kR;
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * ti + kl + 4 * i;
+        const int64_t p = p0 + row;
+        if (p >= P) continue;
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+          const int col = 16 * tj + cl;
+          double v = acc[ti][tj][i];
+          v += red[0][row][col];
+          v += red[1][row][col];
+          v += red[2][row][col];
+          out[p * kR + col] = v;
+        }
+      }
+  }
+}
+
 // Sums the splits in split order.  TRANSPOSE_F32: R[a][p] = (float) sum
 // (ld ldo); else Out[p][a] = sum (float64, ld ldo).
 template <bool TRANSPOSE_F32>
@@ -172,158 +245,205 @@ __global__ __launch_bounds__(kThreads) void reduce_splits_kernel(const double* _
   else static_cast<double*>(out)[p * ldo + c] = s;
 }
 
-// One workgroup: G = sum of the splits of the r x r product (lower triangle
-// used), G = C C^T (Cholesky, lower), Cinv = C^{-1} (lower).  C lives in the
-// lower triangle of Gs; column c of C^{-1} below its diagonal is built in row c
-// of Gs above the diagonal (Gs[c][i] = Cinv[i][c], i > c).  A pivot that is
-// not a positive finite number sets *flag to 1; reset clears it first.
-__global__ __launch_bounds__(kThreads) void small_cholesky_kernel(const double* __restrict__ part, int splits,
-                                                                  int r, double* __restrict__ C,
-                                                                  double* __restrict__ Cinv,
-                                                                  int32_t* __restrict__ flag, int reset) {
+// One wave: G (r x r, leading dimension r, lower triangle used) = C C^T
+// (Cholesky, lower).  G is staged through LDS with coalesced loads, then lane
+// i keeps row i in registers; rows and columns past r are those of the
+// identity, so every loop runs the full kR steps with compile-time indices.
+// Step k takes C[k][k] from lane k (readlane), scales column k and publishes
+// it through LDS for the trailing update.  Writes C
+// (kR x kR, zero above the diagonal and past r) and dinv[a] = 1 / C[a][a]
+// (0 past r).  A pivot that is not a positive finite number sets *flag to 1
+// (reset clears the flag first).
+constexpr int kMaxGramSplits = 8;   // K splits of the r x r Gram products
+
+__device__ __forceinline__ double lane_value(double v, int lane) {
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(__double2loint(v)), lane);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(__double2hiint(v)), lane);
+  return __hiloint2double(hi, lo);
+}
+
+// Step K of the register-resident Cholesky (lane i holds row i in g); the
+// steps are chained at compile time so every register index is static.
+template <int K>
+__device__ __forceinline__ void cholesky_step(double (&g)[kR], double* col, int i, int& bad, double& diag) {
+  const double d = lane_value(g[K], K);              // current G[K][K], held by lane K
+  double c = 1.0;
+  if (d > 0.0 && d < INFINITY) c = sqrt(d);
+  else bad = 1;
+  const double lik = i == K ? c : (i > K ? g[K] / c : 0.0);
+  if (i == K) diag = c;
+  g[K] = lik;
+  col[i] = lik;
+  __syncthreads();
+#pragma unroll
+  for (int j = K + 1; j < kR; ++j) g[j] = __builtin_fma(-lik, col[j], g[j]);
+  __syncthreads();
+  if constexpr (K + 1 < kR) cholesky_step<K + 1>(g, col, i, bad, diag);
+}
+
+__global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __restrict__ G, int r,
+                                                            double* __restrict__ C, double* __restrict__ dinv,
+                                                            int32_t* __restrict__ flag, int reset) {
   __shared__ double Gs[kR][kR + 1];
-  const int tid = threadIdx.x;
-  int bad = 0;  // meaningful in thread 0 only
-  for (int e = tid; e < kR * kR; e += kThreads) {
-    const int i = e / kR, j = e % kR;
-    double s = 0.0;
-    if (i < r && j <= i)
-      for (int t = 0; t < splits; ++t) s += part[(static_cast<int64_t>(t) * r + i) * kR + j];
-    Gs[i][j] = s;
+  __shared__ double col[kR];
+  const int i = threadIdx.x;
+  for (int e = i; e < kR * kR; e += 64) {
+    const int a = e / kR, b = e % kR;
+    Gs[a][b] = a < r ? (b <= a ? G[a * r + b] : 0.0) : (a == b ? 1.0 : 0.0);
   }
   __syncthreads();
-  for (int k = 0; k < r; ++k) {
-    if (tid == 0) {
-      const double d = Gs[k][k];
-      if (!(d > 0.0) || !(d < INFINITY)) {
-        bad = 1;
-        Gs[k][k] = 1.0;
-      } else {
-        Gs[k][k] = sqrt(d);
-      }
-    }
-    __syncthreads();
-    const double dk = Gs[k][k];
-    for (int i = k + 1 + tid; i < r; i += kThreads) Gs[i][k] /= dk;
-    __syncthreads();
-    const int w = r - k - 1;
-    for (int e = tid; e < w * w; e += kThreads) {
-      const int i = k + 1 + e / w, j = k + 1 + e % w;
-      if (j <= i) Gs[i][j] = __builtin_fma(-Gs[i][k], Gs[j][k], Gs[i][j]);
-    }
-    __syncthreads();
-  }
-  // Column c of C^{-1} by forward substitution, one thread per column:
-  // X[c][c] = 1 / C[c][c], X[i][c] = -(sum_{k=c}^{i-1} C[i][k] X[k][c]) / C[i][i].
-  if (tid < r) {
-    const int c = tid;
-    const double xcc = 1.0 / Gs[c][c];
-    for (int i = c + 1; i < r; ++i) {
-      double s = Gs[i][c] * xcc;
-      for (int k = c + 1; k < i; ++k) s = __builtin_fma(Gs[i][k], Gs[c][k], s);
-      Gs[c][i] = -s / Gs[i][i];
-    }
-  }
-  __syncthreads();
-  for (int e = tid; e < kR * kR; e += kThreads) {
-    const int i = e / kR, j = e % kR;
-    const bool in = i < r && j <= i;
-    C[e] = in ? Gs[i][j] : 0.0;
-    Cinv[e] = !in ? 0.0 : (i == j ? 1.0 / Gs[i][i] : Gs[j][i]);
-  }
-  if (tid == 0) {
+  double g[kR];
+#pragma unroll
+  for (int j = 0; j < kR; ++j) g[j] = Gs[i][j];
+  int bad = 0;
+  double diag = 1.0;
+  cholesky_step<0>(g, col, i, bad, diag);
+#pragma unroll
+  for (int j = 0; j < kR; ++j) C[i * kR + j] = (i < r && j <= i) ? g[j] : 0.0;
+  dinv[i] = i < r ? 1.0 / diag : 0.0;
+  if (i == 0) {
     const int32_t prev = reset ? 0 : *flag;
     *flag = prev | bad;
   }
 }
 
-// Out = Y T for Y n x r, T r x r: TRANS_INV: T = Cinv^T (Y C^{-T});
-// else T = Cinv (Z C^{-1}).  16 rows per workgroup.
-template <bool TRANS_INV>
-__global__ __launch_bounds__(kThreads) void right_multiply_kernel(const double* __restrict__ Y,
-                                                                  const double* __restrict__ Cinv, int64_t n,
-                                                                  int r, double* __restrict__ Out) {
-  __shared__ double Ts[kR][kR + 1];
-  __shared__ double Ys[16][kR + 1];
-  const int tid = threadIdx.x;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 16;
-  for (int e = tid; e < kR * kR; e += kThreads) {
-    const int b = e / kR, c = e % kR;
-    Ts[b][c] = TRANS_INV ? Cinv[c * kR + b] : Cinv[b * kR + c];
-  }
-  for (int e = tid; e < 16 * kR; e += kThreads) {
-    const int ii = e / kR, b = e % kR;
-    const int64_t i = i0 + ii;
-    Ys[ii][b] = (i < n && b < r) ? Y[i * r + b] : 0.0;
-  }
-  __syncthreads();
-  const int c = tid & 63;
-  const int ib = (tid >> 6) * 4;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  for (int b = 0; b < r; ++b) {
-    const double t = Ts[b][c];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) acc[u] = __builtin_fma(Ys[ib + u][b], t, acc[u]);
-  }
-  if (c < r) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t i = i0 + ib + u;
-      if (i < n) Out[i * r + c] = acc[u];
-    }
+// Row-wise triangular solves with the factor C (lower, kR x kR, zero past r)
+// and dinv of the last small_cholesky_kernel, one lane per row of Y (n x r),
+// 64 rows per workgroup.  C's lower triangle and dinv sit in LDS (every lane
+// reads the same entry); the rows go HBM -> LDS -> registers and back through
+// LDS, so the solves themselves are straight-line code on registers.
+//   Z row:  z C^T = y  (forward substitution; Z = Y C^{-T})
+//   K row:  k C = z    (back substitution;   K = Z C^{-1})
+// Both run column by column (each finished entry is subtracted from all later
+// ones at once).  Entries past r stay 0 because dinv is 0 there.
+// WITH_K = false writes Z (n x r) to Out; WITH_K = true writes Z transposed
+// (r x n) to Zt and K (n x r) to Out.
+constexpr int kTri = kR * (kR + 1) / 2;
+
+__device__ __forceinline__ void rows_to_lds(const double* __restrict__ Y, int64_t i0, int64_t n, int r,
+                                            double (*V)[kR + 1]) {
+  for (int rr = 0; rr < 64; ++rr) {
+    const int64_t i = i0 + rr;
+    V[rr][threadIdx.x] = (i < n && static_cast<int>(threadIdx.x) < r) ? Y[i * r + threadIdx.x] : 0.0;
   }
 }
 
-// H_L[i][j] = (float)(H[i][j] - sum_a Z[i][a] Z[j][a]), 64 x 64 tiles.  The
-// products and their order are the same for (i, j) and (j, i), so H_L is
-// exactly symmetric when H is.
-__global__ __launch_bounds__(kThreads) void downdate_kernel(const float* __restrict__ H, int64_t ldh,
-                                                            const double* __restrict__ Z, int64_t n, int r,
-                                                            float* __restrict__ HL, int64_t ldhl) {
-  // Z rows of the tile, transposed ([a][row]); consecutive threads take
-  // consecutive rows (conflict-free LDS stores, Z itself is L2-resident).
-  __shared__ double Zi[kR][kTP];
-  __shared__ double Zj[kR][kTP];
+__device__ __forceinline__ void lds_to_rows(const double (*V)[kR + 1], int64_t i0, int64_t n, int r,
+                                            double* __restrict__ Out) {
+  for (int rr = 0; rr < 64; ++rr) {
+    const int64_t i = i0 + rr;
+    if (i < n && static_cast<int>(threadIdx.x) < r) Out[i * r + threadIdx.x] = V[rr][threadIdx.x];
+  }
+}
+
+template <bool WITH_K>
+__global__ __launch_bounds__(64) void solve_rows_kernel(const double* __restrict__ Cg, const double* __restrict__ dg,
+                                                        const double* __restrict__ Y, int64_t n, int r,
+                                                        double* __restrict__ Out, double* __restrict__ Zt) {
+  __shared__ double C[kTri];             // row a of the lower triangle at a (a + 1) / 2
+  __shared__ double dinv[kR];
+  __shared__ double V[64][kR + 1];
   const int tid = threadIdx.x;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.y) * kTP, j0 = static_cast<int64_t>(blockIdx.x) * kTP;
-  for (int e = tid; e < kR * kTP; e += kThreads) {
-    const int rr = e % kTP, a = e / kTP;
-    const int64_t i = i0 + rr, j = j0 + rr;
-    Zi[a][rr] = (i < n && a < r) ? Z[i * r + a] : 0.0;
-    Zj[a][rr] = (j < n && a < r) ? Z[j * r + a] : 0.0;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
+  for (int a = 0; a < kR; ++a)
+    if (tid <= a) C[a * (a + 1) / 2 + tid] = Cg[a * kR + tid];
+  dinv[tid] = dg[tid];
+  rows_to_lds(Y, i0, n, r, V);
+  __syncthreads();
+  double v[kR];
+#pragma unroll
+  for (int a = 0; a < kR; ++a) v[a] = V[tid][a];
+#pragma unroll
+  for (int b = 0; b < kR; ++b) {
+    v[b] *= dinv[b];
+#pragma unroll
+    for (int a = b + 1; a < kR; ++a) v[a] = __builtin_fma(-C[a * (a + 1) / 2 + b], v[b], v[a]);
+  }
+#pragma unroll
+  for (int a = 0; a < kR; ++a) V[tid][a] = v[a];
+  __syncthreads();
+  if (!WITH_K) {
+    lds_to_rows(V, i0, n, r, Out);
+    return;
+  }
+  if (i0 + tid < n)
+    for (int a = 0; a < r; ++a) Zt[a * n + i0 + tid] = V[tid][a];
+#pragma unroll
+  for (int b = kR - 1; b >= 0; --b) {
+    v[b] *= dinv[b];
+#pragma unroll
+    for (int a = 0; a < b; ++a) v[a] = __builtin_fma(-C[b * (b + 1) / 2 + a], v[b], v[a]);
   }
   __syncthreads();
-  const int ti = tid & 15, tj = tid >> 4;
-  double acc[4][4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t i = i0 + 4 * ti + u;
+  for (int a = 0; a < kR; ++a) V[tid][a] = v[a];
+  __syncthreads();
+  lds_to_rows(V, i0, n, r, Out);
+}
+
+// H_L[i][j] = (float)(H[i][j] - sum_a Z[i][a] Z[j][a]) on the matrix cores.
+// Only tiles on or above the diagonal are computed; each off-diagonal tile is
+// also written mirrored, so H_L is exactly symmetric (H must be symmetric: the
+// upper tiles of H are read).  Four waves of 32 x 32 per 64 x 64 tile, K = r
+// in STEPS 4-deep MFMA steps, operands read coalesced from Z transposed
+// (Zt, r x n, L2-resident); the tile goes through LDS for coalesced row and
+// column stores.
+template <int STEPS>
+__global__ __launch_bounds__(kThreads) void downdate_kernel(const float* __restrict__ H, int64_t ldh,
+                                                            const double* __restrict__ Zt, int64_t n, int r,
+                                                            float* __restrict__ HL, int64_t ldhl, int tiles) {
+  __shared__ float T[kTP][kTP + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int kl = lane >> 4, cl = lane & 15;
+  int t = static_cast<int>(blockIdx.x), bi = 0;
+  while (t >= tiles - bi) {
+    t -= tiles - bi;
+    ++bi;
+  }
+  const int bj = bi + t;
+  const int64_t i0 = static_cast<int64_t>(bi) * kTP, j0 = static_cast<int64_t>(bj) * kTP;
+  const int wr = wave >> 1, wc = wave & 1;
+  double a[STEPS][2], b[STEPS][2];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t j = j0 + 4 * tj + v;
-      acc[u][v] = (i < n && j < n) ? static_cast<double>(H[i * ldh + j]) : 0.0;
+  for (int s = 0; s < STEPS; ++s) {
+    const int k = 4 * s + kl;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int64_t i = i0 + 32 * wr + 16 * u + cl, j = j0 + 32 * wc + 16 * u + cl;
+      a[s][u] = (k < r && i < n) ? Zt[k * n + i] : 0.0;
+      b[s][u] = (k < r && j < n) ? Zt[k * n + j] : 0.0;
     }
   }
-  for (int a = 0; a < r; ++a) {
-    double zi[4], zj[4];
+  doublex4 acc[2][2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      zi[u] = Zi[a][4 * ti + u];
-      zj[u] = Zj[a][4 * tj + u];
-    }
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
+    for (int v = 0; v < 2; ++v) acc[u][v] = doublex4{0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) acc[u][v] = __builtin_fma(-zi[u], zj[v], acc[u][v]);
-  }
+  for (int s = 0; s < STEPS; ++s)
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int64_t i = i0 + 4 * ti + u;
-    if (i >= n) continue;
+    for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t j = j0 + 4 * tj + v;
-      if (j < n) HL[i * ldhl + j] = static_cast<float>(acc[u][v]);
+      for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[s][u], b[s][v], acc[u][v], 0, 0, 0);
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = 32 * wr + 16 * u + kl + 4 * q, col = 32 * wc + 16 * v + cl;
+        const int64_t i = i0 + row, j = j0 + col;
+        const double h = (i < n && j < n) ? static_cast<double>(H[i * ldh + j]) : 0.0;
+        T[row][col] = static_cast<float>(h - acc[u][v][q]);
+      }
+  __syncthreads();
+  for (int e = tid; e < kTP * kTP; e += kThreads) {
+    const int row = e / kTP, col = e % kTP;
+    const int64_t i = i0 + row, j = j0 + col;
+    if (i < n && j < n) HL[i * ldhl + j] = T[row][col];
+    if (bi != bj) {
+      const int64_t i2 = j0 + row, j2 = i0 + col;
+      if (i2 < n && j2 < n) HL[i2 * ldhl + j2] = T[col][row];
     }
   }
 }
@@ -348,26 +468,40 @@ Split choose_split(int64_t P, int64_t K) {
   return s;
 }
 
-size_t part_bytes(int64_t P, int64_t K) {
-  const Split s = choose_split(P, K);
+// Splits of the matrix-core product: K in multiples of kMChunk, enough
+// workgroups of kMP rows to cover the chip twice over.
+Split choose_split_mfma(int64_t P, int64_t K, int64_t max_splits) {
+  Split s;
+  s.tiles = ceil_div(P, kMP);
+  const int64_t stages = ceil_div(K, kMChunk);
+  const int64_t want =
+      std::max<int64_t>(1, std::min({ceil_div(kTargetBlocks, s.tiles), stages, max_splits}));
+  s.kchunk = ceil_div(stages, want) * kMChunk;
+  s.splits = ceil_div(K, s.kchunk);
+  return s;
+}
+
+size_t part_bytes(const Split& s, int64_t P) {
   return static_cast<size_t>(s.splits) * static_cast<size_t>(P) * kR * sizeof(double);
 }
 
 struct Layout {
-  size_t off_part, off_y, off_q, off_c, off_cinv, off_flag, total;
+  size_t off_part, off_y, off_q, off_g, off_c, off_dinv, off_flag, total;
 };
 
 Layout lowrank_layout(int64_t m, int64_t n, int64_t r) {
   Layout L;
-  size_t part = std::max(part_bytes(n, n), part_bytes(r, n));
-  if (m > 0) part = std::max(part, part_bytes(m, n));
+  size_t part = std::max(part_bytes(choose_split_mfma(n, n, kTargetBlocks), n),
+                         part_bytes(choose_split_mfma(r, n, kMaxGramSplits), r));
+  if (m > 0) part = std::max(part, part_bytes(choose_split(m, n), m));
   const size_t nr = static_cast<size_t>(n) * static_cast<size_t>(r) * sizeof(double);
   L.off_part = 0;
   L.off_y = align256(part);
   L.off_q = align256(L.off_y + nr);
-  L.off_c = align256(L.off_q + nr);
-  L.off_cinv = align256(L.off_c + kR * kR * sizeof(double));
-  L.off_flag = align256(L.off_cinv + kR * kR * sizeof(double));
+  L.off_g = align256(L.off_q + nr);
+  L.off_c = align256(L.off_g + kR * kR * sizeof(double));
+  L.off_dinv = align256(L.off_c + kR * kR * sizeof(double));
+  L.off_flag = align256(L.off_dinv + kR * sizeof(double));
   L.total = align256(L.off_flag + sizeof(int32_t));
   return L;
 }
@@ -377,8 +511,9 @@ struct Ctx {
   double* part;
   double* Y;
   double* Q;
+  double* G;
   double* C;
-  double* Cinv;
+  double* dinv;
   int32_t* flag;
 };
 
@@ -389,58 +524,65 @@ Ctx make_ctx(const Layout& L, void* ws, void* stream) {
   c.part = reinterpret_cast<double*>(base + L.off_part);
   c.Y = reinterpret_cast<double*>(base + L.off_y);
   c.Q = reinterpret_cast<double*>(base + L.off_q);
+  c.G = reinterpret_cast<double*>(base + L.off_g);
   c.C = reinterpret_cast<double*>(base + L.off_c);
-  c.Cinv = reinterpret_cast<double*>(base + L.off_cinv);
+  c.dinv = reinterpret_cast<double*>(base + L.off_dinv);
   c.flag = reinterpret_cast<int32_t*>(base + L.off_flag);
   return c;
 }
 
-template <int MODE, int DT>
-gptq_status launch_tall(TallArgs a, const Ctx& c, Split* used) {
+template <int DT>
+gptq_status launch_compensation(TallArgs a, const Ctx& c, Split* used) {
   const Split s = choose_split(a.P, a.K);
   a.kchunk = s.kchunk;
   a.part = c.part;
-  tall_product_kernel<MODE, DT><<<dim3(static_cast<unsigned>(s.tiles), static_cast<unsigned>(s.splits)),
-                                  kThreads, 0, c.st>>>(a);
+  compensation_kernel<DT><<<dim3(static_cast<unsigned>(s.tiles), static_cast<unsigned>(s.splits)), kThreads, 0,
+                            c.st>>>(a);
   GPTQ_TRY_LAUNCH();
   *used = s;
   return GPTQ_OK;
 }
 
-// Out (n x r, float64) = H X for X n x r.
+// part = the split partials of S^T B for S K x P (float32 or float64,
+// leading dimension lds) and B K x r.
+template <typename ST>
+Split partial_t(const ST* S, int64_t lds, const double* B, int64_t P, int64_t K, int64_t r, int64_t max_splits,
+                const Ctx& c) {
+  const Split s = choose_split_mfma(P, K, max_splits);
+  tall_mfma_kernel<ST><<<dim3(static_cast<unsigned>(s.tiles), static_cast<unsigned>(s.splits)), kThreads, 0,
+                         c.st>>>(S, lds, B, r, P, K, static_cast<int>(r), s.kchunk, c.part);
+  return s;
+}
+
+// Out (n x r, float64) = H X for X n x r (H symmetric: A(p, k) = H[k][p]).
 gptq_status product_h(const float* H, int64_t ldh, const double* X, int64_t n, int64_t r, double* Out,
                       const Ctx& c) {
-  TallArgs a = {};
-  a.A = H; a.lda = ldh; a.B = X; a.ldb = r; a.P = n; a.K = n; a.r = r;
-  Split s;
-  gptq_status rc = launch_tall<kHessianT, GPTQ_F32>(a, c, &s);
-  if (rc != GPTQ_OK) return rc;
+  const Split s = partial_t<float>(H, ldh, X, n, n, r, kTargetBlocks, c);
+  GPTQ_TRY_LAUNCH();
   reduce_splits_kernel<false><<<static_cast<unsigned>(ceil_div(n * r, kThreads)), kThreads, 0, c.st>>>(
       c.part, static_cast<int>(s.splits), n, r, Out, r);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
 
-// C, Cinv from the Cholesky factor of A^T B (A, B n x r).
+// C (and 1 / diag C) from the Cholesky factor of A^T B (A, B n x r).
 gptq_status factor_gram(const double* A, const double* B, int64_t n, int64_t r, const Ctx& c, int reset) {
-  TallArgs a = {};
-  a.A = A; a.lda = r; a.B = B; a.ldb = r; a.P = r; a.K = n; a.r = r;
-  Split s;
-  gptq_status rc = launch_tall<kMatT, GPTQ_F32>(a, c, &s);
-  if (rc != GPTQ_OK) return rc;
-  small_cholesky_kernel<<<1, kThreads, 0, c.st>>>(c.part, static_cast<int>(s.splits), static_cast<int>(r), c.C,
-                                                  c.Cinv, c.flag, reset);
+  const Split s = partial_t<double>(A, r, B, r, n, r, kMaxGramSplits, c);
+  GPTQ_TRY_LAUNCH();
+  reduce_splits_kernel<false><<<static_cast<unsigned>(ceil_div(r * r, kThreads)), kThreads, 0, c.st>>>(
+      c.part, static_cast<int>(s.splits), r, r, c.G, r);
+  GPTQ_TRY_LAUNCH();
+  small_cholesky_kernel<<<1, 64, 0, c.st>>>(c.G, static_cast<int>(r), c.C, c.dinv, c.flag, reset);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
 
-// Out = Y C^{-T} with C from the last factor_gram (orthonormal columns when
-// C came from Y^T Y).
+// Out = Y C^{-T} with C C^T = Y^T Y: orthonormal columns spanning Y's.
 gptq_status orthonormalize(const double* Y, int64_t n, int64_t r, double* Out, const Ctx& c, int reset) {
   gptq_status rc = factor_gram(Y, Y, n, r, c, reset);
   if (rc != GPTQ_OK) return rc;
-  right_multiply_kernel<true><<<static_cast<unsigned>(ceil_div(n, 16)), kThreads, 0, c.st>>>(
-      Y, c.Cinv, n, static_cast<int>(r), Out);
+  solve_rows_kernel<false><<<static_cast<unsigned>(ceil_div(n, 64)), 64, 0, c.st>>>(
+      c.C, c.dinv, Y, n, static_cast<int>(r), Out, nullptr);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
@@ -496,14 +638,16 @@ extern "C" gptq_status gptq_lowrank_hessian(const float* H, int64_t n, int64_t l
   gptq_status rc = product_h(H, ldh, L, n, r, c.Y, c);                    // Y = H L
   if (rc == GPTQ_OK) rc = factor_gram(L, c.Y, n, r, c, 1);                 // L^T H L = C C^T
   if (rc != GPTQ_OK) return rc;
-  right_multiply_kernel<true><<<static_cast<unsigned>(ceil_div(n, 16)), kThreads, 0, c.st>>>(
-      c.Y, c.Cinv, n, static_cast<int>(r), c.Q);                          // Z = Y C^{-T}
+  solve_rows_kernel<true><<<static_cast<unsigned>(ceil_div(n, 64)), 64, 0, c.st>>>(
+      c.C, c.dinv, c.Y, n, static_cast<int>(r), K, c.Q);                 // Zt = (Y C^{-T})^T, K = Z C^{-1}
   GPTQ_TRY_LAUNCH();
-  right_multiply_kernel<false><<<static_cast<unsigned>(ceil_div(n, 16)), kThreads, 0, c.st>>>(
-      c.Q, c.Cinv, n, static_cast<int>(r), K);                            // K = Z C^{-1}
-  GPTQ_TRY_LAUNCH();
-  const unsigned t = static_cast<unsigned>(ceil_div(n, kTP));
-  downdate_kernel<<<dim3(t, t), kThreads, 0, c.st>>>(H, ldh, c.Q, n, static_cast<int>(r), H_L, ldhl);
+  const int t = static_cast<int>(ceil_div(n, kTP));
+  const unsigned blocks = static_cast<unsigned>(static_cast<int64_t>(t) * (t + 1) / 2);
+  const int ri = static_cast<int>(r);
+  if (r <= 8) downdate_kernel<2><<<blocks, kThreads, 0, c.st>>>(H, ldh, c.Q, n, ri, H_L, ldhl, t);
+  else if (r <= 16) downdate_kernel<4><<<blocks, kThreads, 0, c.st>>>(H, ldh, c.Q, n, ri, H_L, ldhl, t);
+  else if (r <= 32) downdate_kernel<8><<<blocks, kThreads, 0, c.st>>>(H, ldh, c.Q, n, ri, H_L, ldhl, t);
+  else downdate_kernel<16><<<blocks, kThreads, 0, c.st>>>(H, ldh, c.Q, n, ri, H_L, ldhl, t);
   GPTQ_TRY_LAUNCH();
   return read_flag(c);
 }
@@ -518,13 +662,13 @@ extern "C" gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int
   if (!ws || ws_bytes < lay.total) return GPTQ_ERR_WORKSPACE;
   const Ctx c = make_ctx(lay, ws, stream);
   TallArgs a = {};
-  a.A = W; a.lda = ldw; a.w_dtype = w_dtype; a.codes = codes; a.scales = scales; a.zeros = zeros;
+  a.A = W; a.lda = ldw; a.codes = codes; a.scales = scales; a.zeros = zeros;
   a.group = group_size; a.G = group_size ? ceil_div(n, group_size) : 1; a.perm = perm;
   a.B = K; a.ldb = r; a.P = m; a.K = n; a.r = r;
   Split s;
-  gptq_status rc = w_dtype == GPTQ_F32  ? launch_tall<kDelta, GPTQ_F32>(a, c, &s)
-                   : w_dtype == GPTQ_F16 ? launch_tall<kDelta, GPTQ_F16>(a, c, &s)
-                                         : launch_tall<kDelta, GPTQ_BF16>(a, c, &s);
+  gptq_status rc = w_dtype == GPTQ_F32  ? launch_compensation<GPTQ_F32>(a, c, &s)
+                   : w_dtype == GPTQ_F16 ? launch_compensation<GPTQ_F16>(a, c, &s)
+                                         : launch_compensation<GPTQ_BF16>(a, c, &s);
   if (rc != GPTQ_OK) return rc;
   reduce_splits_kernel<true><<<static_cast<unsigned>(ceil_div(m * r, kThreads)), kThreads, 0, c.st>>>(
       c.part, static_cast<int>(s.splits), m, r, R, ldr);
