@@ -635,13 +635,22 @@ void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int
                        const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx,
                        float* Y, int64_t ldy, int vec_w, int vec_x) {
   // Decode-sized batches: one 16-column tile, 16 or 64 rows per workgroup
-  // (more workgroups for short layers); larger batches: 128 x 128 tiles with
-  // X staged in LDS.
-  if (batch <= 16) {
-    if (m <= 16384)
-      launch_mfma<BITS, 1, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
-    else
-      launch_mfma<BITS, 4, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, vec_w, vec_x);
+  // (more workgroups for short layers); up to 64 rows of X: that kernel once
+  // per 16 rows (it streams the weights at near-HBM rate, the 128-wide tile
+  // below would spend most of its work on padding); larger batches: 128 x 128
+  // tiles with X staged in LDS.
+  if (batch <= 64) {
+    for (int b0 = 0; b0 < batch; b0 += 16) {
+      const int cb = std::min(16, batch - b0);
+      const uint16_t* Xc = X + (int64_t)b0 * ldx;
+      float* Yc = Y + (int64_t)b0 * ldy;
+      if (m <= 16384)
+        launch_mfma<BITS, 1, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, Xc, cb, ldx, Yc, ldy, vec_w,
+                                vec_x);
+      else
+        launch_mfma<BITS, 4, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, Xc, cb, ldx, Yc, ldy, vec_w,
+                                vec_x);
+    }
   } else {
     const dim3 grid((unsigned)ceil_div(m, (int64_t)kPM), (unsigned)ceil_div(batch, (int64_t)kPN));
     dequant_gemm_lds_kernel<BITS><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, group_size, X,

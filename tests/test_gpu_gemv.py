@@ -176,7 +176,8 @@ GEMM_CASES = [
     (70, 1000, 4, 0, 1),        # ragged m and n, per-row
     (64, 1024, 4, 128, 5),      # contiguous groups, batch inside one tile
     (40, 1000, 3, 128, 16),     # 3-bit, partial last group, full tile
-    (33, 500, 2, 256, 17),      # 2-bit, two column tiles
+    (33, 500, 2, 256, 17),      # 2-bit, batch past one 16-row chunk
+    (64, 768, 4, 128, 40),      # three 16-row chunks, the last one ragged
     (20000, 384, 4, 0, 2),      # many rows (32 rows per wave)
     (96, 640, 4, 128, 100),     # prefill-sized batch (128 x 128 tiles, X staged in LDS)
     (300, 1000, 3, 0, 257),     # prefill, ragged rows, columns and batch, 3-bit
