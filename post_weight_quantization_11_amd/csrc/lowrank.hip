@@ -250,10 +250,11 @@ __global__ __launch_bounds__(kThreads) void reduce_splits_kernel(const double* _
 // i keeps row i in registers; rows and columns past r are those of the
 // identity, so every loop runs the full kR steps with compile-time indices.
 // Step k takes C[k][k] from lane k (readlane), scales column k and publishes
-// it through LDS for the trailing update.  Writes C
-// (kR x kR, zero above the diagonal and past r) and dinv[a] = 1 / C[a][a]
-// (0 past r).  A pivot that is not a positive finite number sets *flag to 1
-// (reset clears the flag first).
+// it through LDS for the trailing update.  Writes C (kR x kR, zero above the
+// diagonal and past r) and Dinv, the inverses of C's four 16 x 16 diagonal
+// blocks (identity past r; lane 16 b + c builds column c of block b by
+// forward substitution).  A pivot that is not a positive finite number sets
+// *flag to 1 (reset clears the flag first).
 constexpr int kMaxGramSplits = 8;   // K splits of the r x r Gram products
 
 __device__ __forceinline__ double lane_value(double v, int lane) {
@@ -261,6 +262,9 @@ __device__ __forceinline__ double lane_value(double v, int lane) {
   const int hi = __builtin_amdgcn_readlane(static_cast<int>(__double2hiint(v)), lane);
   return __hiloint2double(hi, lo);
 }
+
+constexpr int kBlk = 16;                 // diagonal block size of the blocked solves
+constexpr int kNBlk = kR / kBlk;
 
 // Step K of the register-resident Cholesky (lane i holds row i in g); the
 // steps are chained at compile time so every register index is static.
@@ -282,7 +286,7 @@ __device__ __forceinline__ void cholesky_step(double (&g)[kR], double* col, int 
 }
 
 __global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __restrict__ G, int r,
-                                                            double* __restrict__ C, double* __restrict__ dinv,
+                                                            double* __restrict__ C, double* __restrict__ Dinv,
                                                             int32_t* __restrict__ flag, int reset) {
   __shared__ double Gs[kR][kR + 1];
   __shared__ double col[kR];
@@ -300,7 +304,24 @@ __global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __rest
   cholesky_step<0>(g, col, i, bad, diag);
 #pragma unroll
   for (int j = 0; j < kR; ++j) C[i * kR + j] = (i < r && j <= i) ? g[j] : 0.0;
-  dinv[i] = i < r ? 1.0 / diag : 0.0;
+  // The factor (identity past r) back into LDS for the diagonal-block inverses.
+#pragma unroll
+  for (int j = 0; j < kR; ++j) Gs[i][j] = j < i ? g[j] : 0.0;
+  Gs[i][i] = diag;
+  __syncthreads();
+  {
+    const int b0 = (i / kBlk) * kBlk, c = i % kBlk;
+    double x[kBlk];
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) {
+      double acc = t == c ? 1.0 : 0.0;
+#pragma unroll
+      for (int u = 0; u < t; ++u) acc = __builtin_fma(-Gs[b0 + t][b0 + u], x[u], acc);
+      x[t] = acc / Gs[b0 + t][b0 + t];
+    }
+#pragma unroll
+    for (int t = 0; t < kBlk; ++t) Dinv[(b0 + t) * kBlk + c] = x[t];
+  }
   if (i == 0) {
     const int32_t prev = reset ? 0 : *flag;
     *flag = prev | bad;
@@ -308,77 +329,101 @@ __global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __rest
 }
 
 // Row-wise triangular solves with the factor C (lower, kR x kR, zero past r)
-// and dinv of the last small_cholesky_kernel, one lane per row of Y (n x r),
-// 64 rows per workgroup.  C's lower triangle and dinv sit in LDS (every lane
-// reads the same entry); the rows go HBM -> LDS -> registers and back through
-// LDS, so the solves themselves are straight-line code on registers.
-//   Z row:  z C^T = y  (forward substitution; Z = Y C^{-T})
-//   K row:  k C = z    (back substitution;   K = Z C^{-1})
-// Both run column by column (each finished entry is subtracted from all later
-// ones at once).  Entries past r stay 0 because dinv is 0 there.
+// of the last small_cholesky_kernel, blocked by 16 columns on the float64
+// matrix cores (MFMA 16x16x4: A element (row l%16, k l/16), B element
+// (k l/16, column l%16), accumulator register q of lane l at row l/16 + 4q,
+// column l%16).  Each wave owns 16 rows:
+//   Z = Y C^{-T}:  Z_b = (Y_b - sum_{c<b} Z_c C_bc^T) D_b^T   (b = 0 .. 3)
+//   K = Z C^{-1}:  K_b = (Z_b - sum_{c>b} K_c C_cb) D_b       (b = 3 .. 0)
+// with D_b the inverse of diagonal block b.  Results go through the wave's
+// LDS tiles to become A operands of the later blocks.  Columns past r are 0
+// (Y is 0 there, C's blocks are 0 and D_b is the identity).
 // WITH_K = false writes Z (n x r) to Out; WITH_K = true writes Z transposed
 // (r x n) to Zt and K (n x r) to Out.
-constexpr int kTri = kR * (kR + 1) / 2;
-
-__device__ __forceinline__ void rows_to_lds(const double* __restrict__ Y, int64_t i0, int64_t n, int r,
-                                            double (*V)[kR + 1]) {
-  for (int rr = 0; rr < 64; ++rr) {
-    const int64_t i = i0 + rr;
-    V[rr][threadIdx.x] = (i < n && static_cast<int>(threadIdx.x) < r) ? Y[i * r + threadIdx.x] : 0.0;
-  }
-}
-
-__device__ __forceinline__ void lds_to_rows(const double (*V)[kR + 1], int64_t i0, int64_t n, int r,
-                                            double* __restrict__ Out) {
-  for (int rr = 0; rr < 64; ++rr) {
-    const int64_t i = i0 + rr;
-    if (i < n && static_cast<int>(threadIdx.x) < r) Out[i * r + threadIdx.x] = V[rr][threadIdx.x];
-  }
-}
-
 template <bool WITH_K>
-__global__ __launch_bounds__(64) void solve_rows_kernel(const double* __restrict__ Cg, const double* __restrict__ dg,
-                                                        const double* __restrict__ Y, int64_t n, int r,
-                                                        double* __restrict__ Out, double* __restrict__ Zt) {
-  __shared__ double C[kTri];             // row a of the lower triangle at a (a + 1) / 2
-  __shared__ double dinv[kR];
-  __shared__ double V[64][kR + 1];
-  const int tid = threadIdx.x;
-  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64;
-  for (int a = 0; a < kR; ++a)
-    if (tid <= a) C[a * (a + 1) / 2 + tid] = Cg[a * kR + tid];
-  dinv[tid] = dg[tid];
-  rows_to_lds(Y, i0, n, r, V);
-  __syncthreads();
-  double v[kR];
+__global__ __launch_bounds__(kThreads) void solve_rows_kernel(const double* __restrict__ C,
+                                                              const double* __restrict__ Dinv,
+                                                              const double* __restrict__ Y, int64_t n, int r,
+                                                              double* __restrict__ Out, double* __restrict__ Zt) {
+  __shared__ double W[kThreads / 64][kNBlk + 1][kBlk][kBlk + 1];   // per wave: 4 result blocks + staging
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lq = lane >> 4;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64 + 16 * wave;
+  double (*T)[kBlk + 1] = W[wave][kNBlk];
+  const doublex4 zero4 = {0.0, 0.0, 0.0, 0.0};
+
 #pragma unroll
-  for (int a = 0; a < kR; ++a) v[a] = V[tid][a];
+  for (int b = 0; b < kNBlk; ++b) {
+    doublex4 acc;
 #pragma unroll
-  for (int b = 0; b < kR; ++b) {
-    v[b] *= dinv[b];
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = i0 + lq + 4 * q;
+      const int col = kBlk * b + lr;
+      acc[q] = (row < n && col < r) ? Y[row * r + col] : 0.0;
+    }
 #pragma unroll
-    for (int a = b + 1; a < kR; ++a) v[a] = __builtin_fma(-C[a * (a + 1) / 2 + b], v[b], v[a]);
+    for (int c = 0; c < b; ++c)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const double av = -W[wave][c][lr][4 * s4 + lq];
+        const double bv = C[(kBlk * b + lr) * kR + kBlk * c + 4 * s4 + lq];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[lq + 4 * q][lr] = acc[q];
+    __syncthreads();
+    doublex4 z = zero4;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      z = __builtin_amdgcn_mfma_f64_16x16x4f64(T[lr][4 * s4 + lq], Dinv[(kBlk * b + lr) * kBlk + 4 * s4 + lq], z,
+                                              0, 0, 0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[wave][b][lq + 4 * q][lr] = z[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = i0 + lq + 4 * q;
+      const int col = kBlk * b + lr;
+      if (row < n && col < r) {
+        if (WITH_K) Zt[col * n + row] = z[q];
+        else Out[row * r + col] = z[q];
+      }
+    }
   }
+  if (!WITH_K) return;
 #pragma unroll
-  for (int a = 0; a < kR; ++a) V[tid][a] = v[a];
-  __syncthreads();
-  if (!WITH_K) {
-    lds_to_rows(V, i0, n, r, Out);
-    return;
+  for (int b = kNBlk - 1; b >= 0; --b) {
+    doublex4 acc;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = W[wave][b][lq + 4 * q][lr];
+#pragma unroll
+    for (int c = b + 1; c < kNBlk; ++c)
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const double av = -W[wave][c][lr][4 * s4 + lq];
+        const double bv = C[(kBlk * c + 4 * s4 + lq) * kR + kBlk * b + lr];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) T[lq + 4 * q][lr] = acc[q];
+    __syncthreads();
+    doublex4 k = zero4;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      k = __builtin_amdgcn_mfma_f64_16x16x4f64(T[lr][4 * s4 + lq], Dinv[(kBlk * b + 4 * s4 + lq) * kBlk + lr], k,
+                                              0, 0, 0);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) W[wave][b][lq + 4 * q][lr] = k[q];
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t row = i0 + lq + 4 * q;
+      const int col = kBlk * b + lr;
+      if (row < n && col < r) Out[row * r + col] = k[q];
+    }
   }
-  if (i0 + tid < n)
-    for (int a = 0; a < r; ++a) Zt[a * n + i0 + tid] = V[tid][a];
-#pragma unroll
-  for (int b = kR - 1; b >= 0; --b) {
-    v[b] *= dinv[b];
-#pragma unroll
-    for (int a = 0; a < b; ++a) v[a] = __builtin_fma(-C[b * (b + 1) / 2 + a], v[b], v[a]);
-  }
-  __syncthreads();
-#pragma unroll
-  for (int a = 0; a < kR; ++a) V[tid][a] = v[a];
-  __syncthreads();
-  lds_to_rows(V, i0, n, r, Out);
 }
 
 // H_L[i][j] = (float)(H[i][j] - sum_a Z[i][a] Z[j][a]) on the matrix cores.
@@ -501,7 +546,7 @@ Layout lowrank_layout(int64_t m, int64_t n, int64_t r) {
   L.off_g = align256(L.off_q + nr);
   L.off_c = align256(L.off_g + kR * kR * sizeof(double));
   L.off_dinv = align256(L.off_c + kR * kR * sizeof(double));
-  L.off_flag = align256(L.off_dinv + kR * sizeof(double));
+  L.off_flag = align256(L.off_dinv + kR * kBlk * sizeof(double));
   L.total = align256(L.off_flag + sizeof(int32_t));
   return L;
 }
@@ -581,7 +626,7 @@ gptq_status factor_gram(const double* A, const double* B, int64_t n, int64_t r, 
 gptq_status orthonormalize(const double* Y, int64_t n, int64_t r, double* Out, const Ctx& c, int reset) {
   gptq_status rc = factor_gram(Y, Y, n, r, c, reset);
   if (rc != GPTQ_OK) return rc;
-  solve_rows_kernel<false><<<static_cast<unsigned>(ceil_div(n, 64)), 64, 0, c.st>>>(
+  solve_rows_kernel<false><<<static_cast<unsigned>(ceil_div(n, 64)), kThreads, 0, c.st>>>(
       c.C, c.dinv, Y, n, static_cast<int>(r), Out, nullptr);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
@@ -638,7 +683,7 @@ extern "C" gptq_status gptq_lowrank_hessian(const float* H, int64_t n, int64_t l
   gptq_status rc = product_h(H, ldh, L, n, r, c.Y, c);                    // Y = H L
   if (rc == GPTQ_OK) rc = factor_gram(L, c.Y, n, r, c, 1);                 // L^T H L = C C^T
   if (rc != GPTQ_OK) return rc;
-  solve_rows_kernel<true><<<static_cast<unsigned>(ceil_div(n, 64)), 64, 0, c.st>>>(
+  solve_rows_kernel<true><<<static_cast<unsigned>(ceil_div(n, 64)), kThreads, 0, c.st>>>(
       c.C, c.dinv, c.Y, n, static_cast<int>(r), K, c.Q);                 // Zt = (Y C^{-T})^T, K = Z C^{-1}
   GPTQ_TRY_LAUNCH();
   const int t = static_cast<int>(ceil_div(n, kTP));
