@@ -29,7 +29,8 @@ constexpr int kThreads = 256;
 constexpr int kTP = 64;                    // output rows per workgroup
 constexpr int kTK = 32;                    // K per LDS stage
 constexpr int kPitch = kTP + 4;            // doubles per LDS row (32-byte aligned rows)
-constexpr int kTargetBlocks = 512;
+constexpr int kTargetBlocks = 512;         // workgroups the matrix-core products aim for
+constexpr int kCompensationBlocks = 1024;  // and the compensation product
 
 static_assert(kR == 64, "the tile shapes assume a 64-column rank tile");
 
@@ -144,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void compensation_kernel(TallArgs a) {
 // kDepth steps of operands in flight, and are summed through LDS in wave
 // order at the end.
 constexpr int kMP = 32;                   // rows per workgroup
-constexpr int kDepth = 8;                 // K steps in flight per wave
+constexpr int kDepth = 4;                 // K steps in flight per wave
 constexpr int kMChunk = 16 * kDepth;      // K granularity of a split
 
 template <typename ST>
@@ -505,7 +506,7 @@ Split choose_split(int64_t P, int64_t K) {
   s.tiles = ceil_div(P, kTP);
   const int64_t stages = ceil_div(K, kTK);
   // Enough workgroups to cover the chip, at least four K stages per split.
-  int64_t want = ceil_div(kTargetBlocks, s.tiles);
+  int64_t want = ceil_div(kCompensationBlocks, s.tiles);
   const int64_t cap = std::max<int64_t>(1, stages / 4);
   want = std::max<int64_t>(1, std::min(want, cap));
   s.kchunk = ceil_div(stages, want) * kTK;
