@@ -246,17 +246,22 @@ __global__ __launch_bounds__(kThreads) void reduce_splits_kernel(const double* _
   else static_cast<double*>(out)[p * ldo + c] = s;
 }
 
-// One wave: G (r x r, leading dimension r, lower triangle used) = C C^T
-// (Cholesky, lower).  G is staged through LDS with coalesced loads, then lane
-// i keeps row i in registers; rows and columns past r are those of the
-// identity, so every loop runs the full kR steps with compile-time indices.
-// Step k takes C[k][k] from lane k (readlane), scales column k and publishes
-// it through LDS for the trailing update.  Writes C (kR x kR, zero above the
-// diagonal and past r) and Dinv, the inverses of C's four 16 x 16 diagonal
-// blocks (identity past r; lane 16 b + c builds column c of block b by
-// forward substitution).  A pivot that is not a positive finite number sets
-// *flag to 1 (reset clears the flag first).
+// One workgroup of four waves: G (r x r, leading dimension r, lower triangle
+// used) = C C^T (Cholesky, lower), blocked by 16-column panels with the
+// matrix in LDS (rows and columns past r are those of the identity).  Panel
+// p: wave 0 factors columns 16p .. 16p+15 of every row (lane i = row i,
+// the panel in registers; the pivot and the entries of the finished column
+// come from their lanes by readlane); then the four waves subtract the panel
+// product from the trailing lower 16 x 16 blocks on the float64 matrix cores
+// (MFMA 16x16x4: A element (row l%16, k l/16), B element (k l/16, column
+// l%16), accumulator register q of lane l at row l/16 + 4q, column l%16).
+// Writes C (kR x kR, zero above the diagonal and past r) and Dinv, the
+// inverses of C's four 16 x 16 diagonal blocks (identity past r; thread
+// 16 b + c builds column c of block b by forward substitution).  A pivot that
+// is not a positive finite number sets *flag to 1 (reset clears it first).
 constexpr int kMaxGramSplits = 8;   // K splits of the r x r Gram products
+constexpr int kBlk = 16;            // panel and diagonal block size
+constexpr int kNBlk = kR / kBlk;
 
 __device__ __forceinline__ double lane_value(double v, int lane) {
   const int lo = __builtin_amdgcn_readlane(static_cast<int>(__double2loint(v)), lane);
@@ -264,54 +269,88 @@ __device__ __forceinline__ double lane_value(double v, int lane) {
   return __hiloint2double(hi, lo);
 }
 
-constexpr int kBlk = 16;                 // diagonal block size of the blocked solves
-constexpr int kNBlk = kR / kBlk;
-
-// Step K of the register-resident Cholesky (lane i holds row i in g); the
-// steps are chained at compile time so every register index is static.
-template <int K>
-__device__ __forceinline__ void cholesky_step(double (&g)[kR], double* col, int i, int& bad, double& diag) {
-  const double d = lane_value(g[K], K);              // current G[K][K], held by lane K
-  double c = 1.0;
-  if (d > 0.0 && d < INFINITY) c = sqrt(d);
-  else bad = 1;
-  const double lik = i == K ? c : (i > K ? g[K] / c : 0.0);
-  if (i == K) diag = c;
-  g[K] = lik;
-  col[i] = lik;
-  __syncthreads();
+// Panel P of the factorization, run by one wave (lane i = row i).
+template <int P>
+__device__ __forceinline__ void factor_panel(double (*Gs)[kR + 1], int i, int& bad) {
+  constexpr int c0 = P * kBlk;
+  double g[kBlk];
 #pragma unroll
-  for (int j = K + 1; j < kR; ++j) g[j] = __builtin_fma(-lik, col[j], g[j]);
-  __syncthreads();
-  if constexpr (K + 1 < kR) cholesky_step<K + 1>(g, col, i, bad, diag);
+  for (int k = 0; k < kBlk; ++k) g[k] = Gs[i][c0 + k];
+#pragma unroll
+  for (int k = 0; k < kBlk; ++k) {
+    const double d = lane_value(g[k], c0 + k);
+    double c = 1.0;
+    if (d > 0.0 && d < INFINITY) c = sqrt(d);
+    else bad = 1;
+    const double lik = i == c0 + k ? c : (i > c0 + k ? g[k] / c : 0.0);
+    g[k] = lik;
+#pragma unroll
+    for (int j = k + 1; j < kBlk; ++j) g[j] = __builtin_fma(-lik, lane_value(lik, c0 + j), g[j]);
+  }
+#pragma unroll
+  for (int k = 0; k < kBlk; ++k)
+    if (c0 + k <= i) Gs[i][c0 + k] = g[k];
 }
 
-__global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __restrict__ G, int r,
-                                                            double* __restrict__ C, double* __restrict__ Dinv,
-                                                            int32_t* __restrict__ flag, int reset) {
+// Trailing update after panel P: every lower 16 x 16 block (bi, bj) with
+// bi >= bj > P loses panel(bi) panel(bj)^T; block t of the list goes to wave
+// t mod 4.
+template <int P>
+__device__ __forceinline__ void trailing_update(double (*Gs)[kR + 1], int wave, int lane) {
+  constexpr int c0 = P * kBlk;
+  constexpr int T = kNBlk - 1 - P;
+  const int lr = lane & 15, lq = lane >> 4;
+  int t = 0;
+#pragma unroll
+  for (int bi = P + 1; bi < kNBlk; ++bi)
+#pragma unroll
+    for (int bj = P + 1; bj <= bi; ++bj, ++t) {
+      if (t % 4 != wave) continue;
+      doublex4 acc;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = Gs[kBlk * bi + lq + 4 * q][kBlk * bj + lr];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const double av = -Gs[kBlk * bi + lr][c0 + 4 * s4 + lq];
+        const double bv = Gs[kBlk * bj + lr][c0 + 4 * s4 + lq];
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) Gs[kBlk * bi + lq + 4 * q][kBlk * bj + lr] = acc[q];
+    }
+  (void)T;
+}
+
+template <int P>
+__device__ __forceinline__ void cholesky_panels(double (*Gs)[kR + 1], int tid, int& bad) {
+  const int wave = tid >> 6, lane = tid & 63;
+  if (wave == 0) factor_panel<P>(Gs, lane, bad);
+  __syncthreads();
+  if constexpr (P + 1 < kNBlk) {
+    trailing_update<P>(Gs, wave, lane);
+    __syncthreads();
+    cholesky_panels<P + 1>(Gs, tid, bad);
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void small_cholesky_kernel(const double* __restrict__ G, int r,
+                                                                  double* __restrict__ C, double* __restrict__ Dinv,
+                                                                  int32_t* __restrict__ flag, int reset) {
   __shared__ double Gs[kR][kR + 1];
-  __shared__ double col[kR];
-  const int i = threadIdx.x;
-  for (int e = i; e < kR * kR; e += 64) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < kR * kR; e += kThreads) {
     const int a = e / kR, b = e % kR;
     Gs[a][b] = a < r ? (b <= a ? G[a * r + b] : 0.0) : (a == b ? 1.0 : 0.0);
   }
   __syncthreads();
-  double g[kR];
-#pragma unroll
-  for (int j = 0; j < kR; ++j) g[j] = Gs[i][j];
-  int bad = 0;
-  double diag = 1.0;
-  cholesky_step<0>(g, col, i, bad, diag);
-#pragma unroll
-  for (int j = 0; j < kR; ++j) C[i * kR + j] = (i < r && j <= i) ? g[j] : 0.0;
-  // The factor (identity past r) back into LDS for the diagonal-block inverses.
-#pragma unroll
-  for (int j = 0; j < kR; ++j) Gs[i][j] = j < i ? g[j] : 0.0;
-  Gs[i][i] = diag;
-  __syncthreads();
-  {
-    const int b0 = (i / kBlk) * kBlk, c = i % kBlk;
+  int bad = 0;  // meaningful in wave 0 (every lane of it sees the same pivots)
+  cholesky_panels<0>(Gs, tid, bad);
+  for (int e = tid; e < kR * kR; e += kThreads) {
+    const int i = e / kR, j = e % kR;
+    C[e] = (i < r && j <= i) ? Gs[i][j] : 0.0;
+  }
+  if (tid < kR) {
+    const int b0 = (tid / kBlk) * kBlk, c = tid % kBlk;
     double x[kBlk];
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) {
@@ -323,7 +362,7 @@ __global__ __launch_bounds__(64) void small_cholesky_kernel(const double* __rest
 #pragma unroll
     for (int t = 0; t < kBlk; ++t) Dinv[(b0 + t) * kBlk + c] = x[t];
   }
-  if (i == 0) {
+  if (tid == 0) {
     const int32_t prev = reset ? 0 : *flag;
     *flag = prev | bad;
   }
@@ -618,7 +657,7 @@ gptq_status factor_gram(const double* A, const double* B, int64_t n, int64_t r, 
   reduce_splits_kernel<false><<<static_cast<unsigned>(ceil_div(r * r, kThreads)), kThreads, 0, c.st>>>(
       c.part, static_cast<int>(s.splits), r, r, c.G, r);
   GPTQ_TRY_LAUNCH();
-  small_cholesky_kernel<<<1, 64, 0, c.st>>>(c.G, static_cast<int>(r), c.C, c.dinv, c.flag, reset);
+  small_cholesky_kernel<<<1, kThreads, 0, c.st>>>(c.G, static_cast<int>(r), c.C, c.dinv, c.flag, reset);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
