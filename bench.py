@@ -236,7 +236,7 @@ def bench_gptaq(args):
     def step(ev=None):
         mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
         mark(0)
-        g.gptq_hessian_accumulate(H2, Xcat, 2.0, True)
+        g.gptq_hessian_pair_accumulate(H2, Xcat, 2.0, True)
         mark(1)
         H = H2[:n, :n].contiguous()
         U, perm = g.gptq_prepare_hinv(H, cfg.damp_rel, False)

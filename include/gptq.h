@@ -74,6 +74,22 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dt
                                     int64_t tokens, int64_t ldx, float alpha, int reset,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* The two blocks asymmetric calibration needs (GPTAQ / GPTQv2 abstract, see
+ * gptq_asym_target) from one pass over Xcat = [Xq | Xf] (tokens x 2n, Xq in
+ * columns 0..n-1, Xf in n..2n-1): H2 (2n x 2n, row-major) receives
+ * alpha Xq^T Xq (rows and columns 0..n-1) and alpha Xq^T Xf (rows 0..n-1,
+ * columns n..2n-1), with their mirror images below the diagonal, as
+ * gptq_hessian_accumulate on Xcat would (up to the float32 accumulation
+ * order: the token splits may differ).  The block
+ * alpha Xf^T Xf (rows and columns n..2n-1) is unspecified on return: when n
+ * is a multiple of 2048 its tiles are not computed (a third of the work).
+ * Arguments as for gptq_hessian_accumulate with 2n columns (ldx >= 2n,
+ * workspace of gptq_hessian_ws_bytes(2n, tokens, x_dtype) bytes);
+ * n <= 32768. */
+gptq_status gptq_hessian_pair_accumulate(float* H2, int64_t n, const void* Xcat, int x_dtype,
+                                         int64_t tokens, int64_t ldx, float alpha, int reset,
+                                         void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------------
  * Stage 2: damping, act-order and the inverse-Hessian factor.
  * GPTQ knowledge note, "How It Works": a damped Cholesky formulation

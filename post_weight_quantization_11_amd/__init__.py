@@ -11,6 +11,7 @@ from ._lib import (  # noqa: F401
     gptq_dequant_gemm,
     gptq_dequant_gemv,
     gptq_hessian_accumulate,
+    gptq_hessian_pair_accumulate,
     gptq_lora_quantize_linear,
     gptq_lowrank_basis,
     gptq_lowrank_compensation,

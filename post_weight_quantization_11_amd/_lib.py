@@ -26,6 +26,7 @@ EXPORTS = (
     "gptq_status_string",
     "gptq_hessian_ws_bytes",
     "gptq_hessian_accumulate",
+    "gptq_hessian_pair_accumulate",
     "gptq_prepare_ws_bytes",
     "gptq_prepare_hinv",
     "gptq_quantize_ws_bytes",
@@ -72,6 +73,8 @@ def load(path: str = LIB_PATH):
     lib.gptq_hessian_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_hessian_accumulate.restype = C
     lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
+    lib.gptq_hessian_pair_accumulate.restype = C
+    lib.gptq_hessian_pair_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
     lib.gptq_prepare_ws_bytes.restype = sz
     lib.gptq_prepare_ws_bytes.argtypes = [i64]
     lib.gptq_prepare_hinv.restype = C
@@ -165,6 +168,26 @@ def gptq_hessian_accumulate(H, X, alpha: float = 2.0, reset: bool = False, ws=No
                                      0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "gptq_hessian_accumulate")
     return H
+
+
+def gptq_hessian_pair_accumulate(H2, Xcat, alpha: float = 2.0, reset: bool = False, ws=None, stream=None):
+    """H2 (2n x 2n float32): the Xq^T Xq and Xq^T Xf blocks of alpha Xcat^T Xcat
+    for Xcat = [Xq | Xf] (tokens x 2n); the Xf^T Xf block is unspecified."""
+    lib = load()
+    _device_check(H2)
+    _rows_check(Xcat)
+    n2 = H2.shape[0]
+    if n2 % 2 or Xcat.shape[1] != n2 or tuple(H2.shape) != (n2, n2):
+        raise ValueError("H2 must be 2n x 2n and Xcat tokens x 2n")
+    tokens = Xcat.shape[0]
+    dt = _dtype_code(Xcat)
+    if ws is None:
+        ws = _workspace(lib.gptq_hessian_ws_bytes(n2, tokens, dt), H2.device)
+    rc = lib.gptq_hessian_pair_accumulate(_ptr(H2), n2 // 2, _ptr(Xcat), dt, tokens,
+                                          Xcat.stride(0) if tokens else n2, float(alpha), int(bool(reset)),
+                                          _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_hessian_pair_accumulate")
+    return H2
 
 
 def gptq_prepare_hinv(H, damp_rel: float = 0.01, act_order: bool = False, U=None, perm=None,
@@ -314,13 +337,13 @@ def gptq_asym_target(W, Hc, U, perm=None, Wt=None, ws=None, stream=None):
 
 def gptaq_quantize_linear(W, Xq, Xf, levels: int = 16, group_size: int = 0, damp_rel: float = 0.01,
                           act_order: bool = False, block_size: int = 128, stream=None):
-    """Asymmetric calibration for one layer: one Hessian call over [Xq | Xf],
+    """Asymmetric calibration for one layer: one paired Hessian call over [Xq | Xf],
     prepare on the Xq block, the target W', then the usual sweep and pack."""
     torch = _torch()
     n = W.shape[1]
     Xcat = torch.cat([Xq, Xf], dim=1)
     H2 = torch.empty((2 * n, 2 * n), dtype=torch.float32, device=W.device)
-    gptq_hessian_accumulate(H2, Xcat, 2.0, True, stream=stream)
+    gptq_hessian_pair_accumulate(H2, Xcat, 2.0, True, stream=stream)
     H = H2[:n, :n].contiguous()
     U, perm = gptq_prepare_hinv(H, damp_rel, act_order, stream=stream)
     p = perm if act_order else None

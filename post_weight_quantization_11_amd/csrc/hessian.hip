@@ -614,10 +614,11 @@ struct SyrkPlan {
 // that tiles x splits fills the 256 CUs in whole rounds: minimises rounds x
 // tokens-per-split, preferring fewer splits (less reduction traffic) within
 // 2% of the best.
-SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype) {
+// skip_last drops that many tiles from the end of the band-blocked order.
+SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype, int skip_last = 0) {
   SyrkPlan p;
   p.nb = (int)ceil_div(n, kTile);
-  p.ntiles = p.nb * (p.nb + 1) / 2;
+  p.ntiles = p.nb * (p.nb + 1) / 2 - skip_last;
   const int64_t kt = dtype == GPTQ_F32 ? kKt32 : kKt16;
   const int64_t cus = 256;
   double best = 1e300;
@@ -657,9 +658,10 @@ extern "C" size_t gptq_hessian_ws_bytes(int64_t n, int64_t tokens, int x_dtype) 
   return (size_t)p.nsplit * (size_t)p.ntiles * (size_t)kTileElems * sizeof(float);
 }
 
-extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
-                                               int64_t tokens, int64_t ldx, float alpha, int reset,
-                                               void* ws, size_t ws_bytes, void* stream) {
+namespace {
+
+gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_t tokens, int64_t ldx, float alpha,
+                         int reset, void* ws, size_t ws_bytes, void* stream, int skip_last) {
   if (n < 0 || tokens < 0 || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
   if (n > (int64_t)1 << 16) return GPTQ_ERR_UNSUPPORTED;
   if (n == 0) return GPTQ_OK;
@@ -673,7 +675,7 @@ extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* 
     }
     return GPTQ_OK;
   }
-  const SyrkPlan p = plan_syrk(n, tokens, x_dtype);
+  const SyrkPlan p = plan_syrk(n, tokens, x_dtype, skip_last);
   const size_t need = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)kTileElems * sizeof(float);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
   float* partial = static_cast<float*>(ws);
@@ -715,4 +717,26 @@ extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* 
                                                                    partial, (double)alpha, reset);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
+                                               int64_t tokens, int64_t ldx, float alpha, int reset,
+                                               void* ws, size_t ws_bytes, void* stream) {
+  return hessian_impl(H, n, X, x_dtype, tokens, ldx, alpha, reset, ws, ws_bytes, stream, 0);
+}
+
+extern "C" gptq_status gptq_hessian_pair_accumulate(float* H2, int64_t n, const void* Xcat, int x_dtype,
+                                                    int64_t tokens, int64_t ldx, float alpha, int reset,
+                                                    void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0) return GPTQ_ERR_INVALID_ARG;
+  if (n > ((int64_t)1 << 15)) return GPTQ_ERR_UNSUPPORTED;
+  // The tiles with both bands in the second half (the Xf^T Xf block) come
+  // last in the band-blocked order when the half is a whole number of
+  // kGroup-band super-blocks; then they are left out.
+  const int64_t half_bands = ceil_div(n, kTile);
+  const bool aligned = n % kTile == 0 && half_bands % kGroup == 0;
+  const int skip = aligned ? (int)(half_bands * (half_bands + 1) / 2) : 0;
+  return hessian_impl(H2, 2 * n, Xcat, x_dtype, tokens, ldx, alpha, reset, ws, ws_bytes, stream, skip);
 }

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import certify_ties, dev, host, log
+from tests.gpu_util import certify_ties, dev, host, log, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,27 @@ def test_gptaq_layer_parity(g, levels, group, act, xdt):
     lo = np.sum((Xq64 @ oracle.dequantize(ro).T - Xf64 @ W.T.astype(np.float64)) ** 2)
     log(f"  asymmetric loss gpu {lg:.6e} oracle {lo:.6e}")
     assert abs(lg - lo) <= 1e-3 * lo
+
+
+@pytest.mark.parametrize("n,tokens,skipped", [(2048, 640, True), (300, 500, False)])
+def test_hessian_pair_blocks(g, n, tokens, skipped):
+    # gptq_hessian_pair_accumulate writes the Xq^T Xq and Xq^T Xf blocks (and
+    # their mirrors) as the full call would; for n a multiple of 2048 the
+    # Xf^T Xf block's tiles are skipped, which the untouched sentinel shows.
+    import torch
+    log(f"hessian pair n={n} tokens={tokens}")
+    W, Xq, Xf = _inputs(tokens, n, 8, seed=n + 7)
+    Xcat = np.concatenate([Xq, Xf], axis=1)
+    H2 = torch.full((2 * n, 2 * n), 12345.0, dtype=torch.float32, device="cuda")
+    g.gptq_hessian_pair_accumulate(H2, dev(Xcat), 2.0, reset=True)
+    Hg = host(H2).astype(np.float64)
+    Ho = oracle.hessian(Xcat.astype(np.float64))
+    top = slice(0, n)
+    assert rel_fro(Hg[top, top], Ho[top, top]) <= 1e-5
+    assert rel_fro(Hg[top, n:], Ho[top, n:]) <= 1e-5
+    np.testing.assert_array_equal(Hg[n:, top], Hg[top, n:].T)
+    np.testing.assert_array_equal(Hg[top, top], Hg[top, top].T)
+    if skipped:
+        assert np.all(Hg[n:, n:] == 12345.0)
+    else:
+        assert rel_fro(Hg[n:, n:], Ho[n:, n:]) <= 1e-5
