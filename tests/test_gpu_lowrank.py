@@ -211,3 +211,23 @@ def test_lowrank_hessian_full_size(g):
     log(f"  max err/tol {float(np.max(err / tol)):.3e}")
     assert np.all(err <= tol)
     assert np.all(np.abs(host(K) - Ko) <= f64 * np.max(np.abs(Ko)))
+
+
+def test_lowrank_basis_full_size(g):
+    # The bench shape: 4096-wide H, rank 64, 12 iterations.  Properties that
+    # hold at any size: orthonormal columns, and the span an invariant
+    # subspace of H (residual of H L - L (L^T H L) tiny, since the 64 spikes
+    # separate the top eigenvalues from the rest).
+    import torch
+    n, r, T = 4096, 64, 6144
+    log(f"lowrank basis full size n={n} r={r}")
+    X, rng = _spiked_x(T, n, _spikes(r), seed=91)
+    H32 = oracle.hessian(X.astype(np.float64)).astype(np.float32)
+    L = host(g.gptq_lowrank_basis(dev(H32), _d64(rng.standard_normal((n, r))), 12))
+    torch.cuda.synchronize()
+    H = H32.astype(np.float64)
+    HL = H @ L
+    res = np.linalg.norm(HL - L @ (L.T @ HL)) / np.linalg.norm(HL)
+    log(f"  |L^T L - I| {np.max(np.abs(L.T @ L - np.eye(r))):.2e}, invariant-subspace residual {res:.2e}")
+    assert np.max(np.abs(L.T @ L - np.eye(r))) <= 1e-12
+    assert res <= 1e-8
