@@ -19,8 +19,9 @@
  *    the call).  The library keeps no device allocation between calls.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls are asynchronous and stream-ordered, except
- *    gptq_prepare_hinv, which synchronises `stream` once to report whether
- *    the damped Hessian was positive definite.
+ *    gptq_prepare_hinv, gptq_lowrank_basis and gptq_lowrank_hessian, which
+ *    synchronise `stream` once to report whether a matrix they factor was
+ *    positive definite.
  *  - Row-major storage; `ld*` are leading dimensions in elements.
  *  - Every argument is validated on the host before anything is launched; a
  *    failed check returns an error and touches no memory.  Device data is
