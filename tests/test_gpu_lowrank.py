@@ -191,12 +191,14 @@ def test_lowrank_edges(g):
     assert ei.value.status == Lb.GPTQ_ERR_INVALID_ARG
 
 
-def test_lowrank_hessian_full_size(g):
-    # The 4096-wide attention-projection Hessian with the largest rank (64),
-    # whole-matrix comparison against the oracle on the same float32 H.
+@pytest.mark.parametrize("n,r,T", [(4096, 64, 6144), (11008, 48, 2048)])
+def test_lowrank_hessian_full_size(g, n, r, T):
+    # The 4096-wide attention-projection Hessian with the largest rank (64)
+    # and the 11008-wide down-projection one (rank 48, fewer tokens than
+    # columns: H is singular, L^T H L is not), whole-matrix comparison against
+    # the oracle on the same float32 H.
     import torch
-    n, r, T = 4096, 64, 6144
-    log(f"lowrank hessian full size n={n} r={r}")
+    log(f"lowrank hessian full size n={n} r={r} tokens={T}")
     X, rng = _spiked_x(T, n, _spikes(16), seed=77)
     H32 = oracle.hessian(X.astype(np.float64)).astype(np.float32)
     L = np.linalg.qr(rng.standard_normal((n, r)))[0]
