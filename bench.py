@@ -25,7 +25,8 @@ forward (HIP events on the stream).
 
 `--gptaq` instead times the asymmetric-calibration variant on the 4096 x 4096
 layer (Xq = the quantized model's inputs, here X plus 5% noise; Xf = X):
-one Hessian call over [Xq | Xf], prepare, the target W' (three float32
+one paired Hessian call over [Xq | Xf] (the Xf^T Xf tiles skipped), prepare,
+the target W' (three float32
 matrix products), sweep, pack; one JSON line with the per-stage times.
 
 `--lora` instead times GPTQ with the low-rank correction (GPTQ-intrinsic

@@ -167,3 +167,13 @@ def test_lowrank_argument_errors(lib):
     assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
     bad = list(args); bad[15] = 16                                 # workspace
     assert f(*bad) == _lib.GPTQ_ERR_WORKSPACE
+
+
+def test_hessian_pair_argument_errors(lib):
+    f = lib.gptq_hessian_pair_accumulate
+    assert f(_fake(), -1, _fake(), 2, 10, 10, 2.0, 1, _fake(), 10, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 1 << 16, _fake(), 2, 10, 1 << 17, 2.0, 1, _fake(), 10, _null()) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert f(_fake(), 10, _fake(), 9, 10, 20, 2.0, 1, _fake(), 10, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 10, _fake(), 2, 10, 19, 2.0, 1, _fake(), 1 << 30, _null()) == _lib.GPTQ_ERR_INVALID_ARG  # ldx < 2n
+    assert f(_fake(), 10, _fake(), 2, 10, 20, 2.0, 1, _fake(), 16, _null()) == _lib.GPTQ_ERR_WORKSPACE
+    assert f(_null(), 0, _null(), 2, 10, 0, 2.0, 1, _null(), 0, _null()) == _lib.GPTQ_OK  # n = 0
