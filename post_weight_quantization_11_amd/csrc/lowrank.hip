@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kThreads) void reduce_splits_kernel(const double* _
 // inverses of C's four 16 x 16 diagonal blocks (identity past r; thread
 // 16 b + c builds column c of block b by forward substitution).  A pivot that
 // is not a positive finite number sets *flag to 1 (reset clears it first).
-constexpr int kMaxGramSplits = 8;   // K splits of the r x r Gram products
+constexpr int kMaxGramSplits = 32;  // K splits of the r x r Gram products
 constexpr int kBlk = 16;            // panel and diagonal block size
 constexpr int kNBlk = kR / kBlk;
 
