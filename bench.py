@@ -5,16 +5,19 @@ A step runs the whole path on inputs already resident in HBM:
   gptq_prepare_hinv       (damping, act-order, U)
   gptq_quantize_layer     (column sweep + lazy block updates)
   gptq_pack               (un-permute + pack, g_idx)
-Default workload: Llama-7B-shaped attention projection, W 4096 x 4096 bf16,
-262144 calibration tokens (128 x 2048) bf16 with Student-t(4) channel
-scales, 4-bit asymmetric, group size 128, block 128, damping 1%.
+Default workload: the 175B-class fc1 layer, W 49152 x 12288 fp16
+~N(0, 0.01^2), 262144 calibration tokens (128 x 2048) fp16 with 0.5% of the
+channels scaled x50, 4-bit asymmetric per-row grid, block 128, damping 1%
+(the largest layer that is quantized on one GPU; `--config 4 --layer 0`
+takes the 12288 x 12288 layer of the same model, `--config 2` the Llama-7B
+4096 x 4096 attention projection, 4-bit g128).
 
 Prints one JSON line: columns/s of the whole step, per-stage times and
 roofline fractions, the dominant kernel's roofline record and the CPU
 oracle's time on a bounded sample of the same workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2]
-                       [--no-cpu] [--copy-calibration]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
+                       [--layer L] [--no-cpu] [--copy-calibration]
 
 `--decoder` instead times the sequential whole-decoder pass (post_weight_
 quantization_11_amd.decoder): 32 Llama-7B-shaped blocks of random bf16
@@ -79,25 +82,36 @@ def to_device(st):
     return torch.from_numpy(st.raw).cuda()
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hessian_attn_proj_4096_traffic.md")
-TRAFFIC_SOURCES = [os.path.join(ROOT, "post_weight_quantization_11_amd", "csrc", f) for f in ("hessian.hip", "common.h")]
+# Committed FETCH_SIZE / WRITE_SIZE summaries: (kernel, config, layer) ->
+# (profile file, the sources the kernel is built from).
+CSRC = os.path.join(ROOT, "post_weight_quantization_11_amd", "csrc")
+TRAFFIC_PROFILES = {
+    ("hessian", 2, 0): ("hessian_attn_proj_4096_traffic.md", ("hessian.hip", "common.h")),
+    ("hessian", 4, 1): ("hessian_fc1_12288_traffic.md", ("hessian.hip", "common.h")),
+    ("quant_block", 4, 1): ("quant_block_fc1_49152x12288_traffic.md", ("quantize.hip", "common.h")),
+}
 
 
-def measured_traffic(config):
-    """HBM bytes per Hessian call from the committed FETCH_SIZE/WRITE_SIZE
-    profile of the 4096-wide workload, or None when that profile was taken on
-    other kernel sources than the ones built here (or for other workloads)."""
+def measured_traffic(kernel, config, layer):
+    """HBM bytes per launch of `kernel` from its committed FETCH_SIZE /
+    WRITE_SIZE profile for this workload, or None when there is none or it
+    was taken on other kernel sources than the ones built here."""
     import hashlib
-    if config != 2 or not os.path.exists(TRAFFIC_PROFILE):
+    key = (kernel, config, layer)
+    if key not in TRAFFIC_PROFILES:
+        return None
+    name, sources = TRAFFIC_PROFILES[key]
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
         return None
     fields = {}
-    for line in open(TRAFFIC_PROFILE):
+    for line in open(path):
         if ":" in line and line.split(":")[0].strip() in ("traffic_bytes_per_launch", "sources_sha256"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
-        with open(f, "rb") as fh:
+    for f in sources:
+        with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     if fields.get("sources_sha256") != h.hexdigest() or "traffic_bytes_per_launch" not in fields:
         return None
@@ -108,9 +122,23 @@ def bits_of(levels):
     return {3: 2, 4: 2, 8: 3, 16: 4}[levels]
 
 
-def cpu_baseline(L, X, cfg, n, m, tokens_total):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return platform.processor() or platform.machine()
+
+
+def cpu_baseline(L, X, cfg, n, m, tokens_total, h_tokens=None, q_rows=1024):
     """Times the CPU oracle on a bounded sample of the same workload and
-    scales each stage to the full workload.  Returns the record."""
+    scales each stage to the full workload: the Hessian on the first
+    ``h_tokens`` tokens (scaled by tokens), damping/act-order/U at full n,
+    the sweep and the pack on ``q_rows`` rows with the full U (rows are
+    independent given U, so those rows' results are exact; scaled by rows).
+    Returns the record."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -118,17 +146,23 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total):
         blas = ",".join(sorted({i.get("internal_api", "?") for i in threadpool_info()}))
     except Exception:  # pragma: no cover
         threads, blas = os.cpu_count() or 1, "unknown"
-    t_sample = min(tokens_total, 32768)
-    m_sample = min(m, 1024)
+    if h_tokens is None:
+        # about 2.5e12 flop of float64 BLAS, whatever the width
+        h_tokens = int(min(tokens_total, max(2048, 2.5e12 / (2.0 * n * n) // 2048 * 2048)))
+    t_sample = min(tokens_total, h_tokens)
+    m_sample = min(m, q_rows)
     Xs = wl.Stored(X.raw[:t_sample], X.dtype).f32 if X is not None else L.x_all(t_sample).f32
     t0 = time.perf_counter()
     H = oracle.hessian(Xs)
     t_h = (time.perf_counter() - t0) * (tokens_total / t_sample)
+    del Xs
     H = H * (tokens_total / t_sample)          # same scale as the full Hessian
     t0 = time.perf_counter()
     perm = oracle.act_order_perm(H) if cfg.act_order else np.arange(n)
     Hd, _ = oracle.damp_and_permute(H, perm, cfg.damp_rel)
+    del H
     U = oracle.inverse_cholesky_upper(Hd)
+    del Hd
     t_p = time.perf_counter() - t0
     W64 = L.W.f32[:m_sample].astype(np.float64)
     t0 = time.perf_counter()
@@ -148,7 +182,7 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total):
                    f"full U (x{m / m_sample:g}, rows are independent); numpy float64, BLAS={blas}"),
         "stage_s": {"hessian": t_h, "prepare": t_p, "quantize": t_q, "pack": t_k},
         "ms_per_layer": total * 1e3,
-        "host": platform.processor() or platform.machine(),
+        "host": cpu_model(),
         "os_cpu_count": os.cpu_count(),
     }
 
@@ -448,7 +482,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=4)
+    ap.add_argument("--layer", type=int, default=None,
+                    help="layer of the workload (default: fc1 for config 4, else the first)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
@@ -489,11 +525,12 @@ def main():
         bench_lora(args)
         return
     cfg = wl.WORKLOADS[args.config]
-    layer = cfg.layers[0]
+    li = (len(cfg.layers) - 1 if args.config == 4 else 0) if args.layer is None else args.layer
+    layer = cfg.layers[li]
     m, n, N = layer.m, layer.n, cfg.tokens
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    L = wl.workload_layer(args.config, 0)
+    L = wl.workload_layer(args.config, li)
     X = L.x_all()
     log(f"inputs generated in {time.perf_counter() - t0:.1f}s: W {m}x{n} {cfg.dtype}, X {N}x{n}")
     Wd = to_device(L.W)
@@ -538,9 +575,10 @@ def main():
         if ev:
             ev[4].record(stream)
 
-    for _ in range(args.warmup):
+    for i in range(args.warmup):
         step()
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{args.warmup} done")
 
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
@@ -549,6 +587,7 @@ def main():
         step(events[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    log(f"{args.steps} timed steps done in {wall:.2f}s")
     stage_names = ["hessian", "prepare", "quantize", "pack"]
     st_ms = {k: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
              for i, k in enumerate(stage_names)}
@@ -566,6 +605,7 @@ def main():
     codes_ok = bool(int(out["codes"].max().item()) <= cfg.levels - 1)
     finite = bool(torch.isfinite(out["scales"]).all().item() and torch.isfinite(out["row_loss"]).all().item())
 
+    nblocks = -(-n // cfg.block_size)
     flops_h = float(n) * (n + 1) * N
     flops_p = 2.0 / 3.0 * float(n) ** 3
     flops_u = float(m) * n * (n - cfg.block_size)
@@ -574,15 +614,51 @@ def main():
     bytes_pack = float(m) * n * (1 + bits / 8) + 8 * n
     stages = {
         "hessian": {"ms": st_ms["hessian"], "tflops": flops_h / st_ms["hessian"] / 1e9,
-                    "frac_peak": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS, "peak": "bf16 MFMA 2500 TF"},
+                    "frac_peak": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
+                    "peak": f"{'bf16' if cfg.dtype == 'bf16' else 'fp16' if cfg.dtype == 'f16' else 'fp32'} MFMA"},
         "prepare": {"ms": st_ms["prepare"], "tflops": flops_p / st_ms["prepare"] / 1e9,
                     "frac_peak": flops_p / st_ms["prepare"] / 1e9 / PEAK_F64_TFLOPS, "peak": "f64 78.6 TF"},
-        "quantize": {"ms": st_ms["quantize"], "update_tflops": flops_u / st_ms["quantize"] / 1e9,
+        "quantize": {"ms": st_ms["quantize"], "launches": nblocks,
+                     "update_tflops": flops_u / st_ms["quantize"] / 1e9,
                      "update_frac_f32_peak": flops_u / st_ms["quantize"] / 1e9 / PEAK_F32_TFLOPS,
-                     "sweep_GBps": bytes_sweep / st_ms["quantize"] / 1e6},
+                     "update_budget_ms_at_60pct": flops_u / (0.6 * PEAK_F32_TFLOPS * 1e9),
+                     "sweep_GBps": bytes_sweep / st_ms["quantize"] / 1e6,
+                     "sweep_frac_hbm": bytes_sweep / st_ms["quantize"] / 1e6 / PEAK_HBM_GBS,
+                     "sweep_budget_ms_at_50pct": bytes_sweep / (0.5 * PEAK_HBM_GBS * 1e6)},
         "pack": {"ms": st_ms["pack"], "GBps": bytes_pack / st_ms["pack"] / 1e6,
-                 "frac_hbm": bytes_pack / st_ms["pack"] / 1e6 / PEAK_HBM_GBS},
+                 "frac_hbm": bytes_pack / st_ms["pack"] / 1e6 / PEAK_HBM_GBS,
+                 "budget_ms_at_50pct": bytes_pack / (0.5 * PEAK_HBM_GBS * 1e6)},
     }
+    # Dominant kernel's roofline record.  The quantize call is one launch of
+    # quant_block_kernel per 128-column block (plus a per-row grid kernel of a
+    # few microseconds), so its per-launch figures are the call's divided by
+    # the block count.
+    if st_ms["quantize"] >= st_ms["hessian"]:
+        roof = {
+            "kernel": (f"quant_block_kernel ({nblocks} launches per gptq_quantize_layer call: sweep + "
+                       "fp32 MFMA deferred update), HIP events around the call"),
+            "bound": "mfma",
+            "achieved": flops_u / st_ms["quantize"] / 1e9,
+            "peak": PEAK_F32_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_u / st_ms["quantize"] / 1e9 / PEAK_F32_TFLOPS,
+            "avg_launch_us": st_ms["quantize"] * 1e3 / nblocks,
+            "traffic": measured_traffic("quant_block", args.config, li),
+            "algorithmic": (f"m n (n - 128) / {nblocks} = {flops_u / nblocks:.4g} flop per launch "
+                            f"({flops_u:.4g} per call)"),
+        }
+    else:
+        roof = {
+            "kernel": "gptq_hessian_accumulate (syrk16 MFMA + split reduce), HIP events around the call",
+            "bound": "mfma",
+            "achieved": flops_h / st_ms["hessian"] / 1e9,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
+            "traffic": measured_traffic("hessian", args.config, li),
+            "algorithmic": f"n(n+1)N = {flops_h:.4g} flop per launch",
+        }
+    roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)"
     ms_layer = sum(st_ms.values())
     rec = {
         "metric": METRIC,
@@ -595,28 +671,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": {"bf16": "bf16", "f16": "fp16", "f32": "fp32"}[cfg.dtype],
         "data": "synthetic",
-        "config": {"workload": cfg.name, "m": m, "n": n, "tokens": N, "x_dtype": cfg.dtype,
-                   "levels": cfg.levels, "group_size": cfg.group_size, "block_size": cfg.block_size,
-                   "damp_rel": cfg.damp_rel, "act_order": cfg.act_order, "parallelism": "1 GPU"},
+        "config": {"workload": f"{cfg.name}: {layer.name} {m}x{n}", "m": m, "n": n, "tokens": N,
+                   "x_dtype": cfg.dtype, "levels": cfg.levels, "group_size": cfg.group_size,
+                   "block_size": cfg.block_size, "damp_rel": cfg.damp_rel, "act_order": cfg.act_order,
+                   "parallelism": "1 GPU"},
         "ms_per_layer_events": ms_layer,
         "weights_per_s": m * n / (ms_per_step / 1e3),
         "stages": stages,
-        "roofline": {
-            "kernel": "gptq_hessian_accumulate (syrk16 MFMA + split reduce), HIP events around the call",
-            "bound": "mfma",
-            "achieved": flops_h / st_ms["hessian"] / 1e9,
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
-            "traffic": measured_traffic(args.config),
-            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0, copy-calibrated)",
-            "algorithmic": f"n(n+1)N = {flops_h:.4g} flop per launch",
-        },
+        "roofline": roof,
         "sanity": {"codes_in_range": codes_ok, "finite": finite},
     }
     if not args.no_cpu:
+        del Xd
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(L, X, cfg, n, m, N)
     print(json.dumps(rec), flush=True)

@@ -66,9 +66,14 @@ const char* gptq_status_string(int status);
  *   tokens  >= 0 (0 with reset = 0 leaves H unchanged).
  *   ws      device workspace of at least gptq_hessian_ws_bytes(n, tokens,
  *           x_dtype) bytes (NULL allowed when that is 0).
- * Products of 16-bit inputs are exact in float32; sums are float32 over
- * chunks of at most 2048 tokens, then over chunks, then across token
- * splits in float64.
+ * Arithmetic: products of 16-bit inputs are exact in float32.  The tokens
+ * are cut into splits of at most 32768 tokens; within a split every entry of
+ * the upper triangle is summed in one float32 matrix-core accumulator (16
+ * tokens per instruction), and the splits' sums are added in float64 (with alpha and the
+ * incoming H when reset = 0) before the one rounding to float32.  The
+ * workspace holds the split sums: splits x upper 256 x 256 tiles x 256 KB
+ * (about 2.4 GB for n = 12288 over 262144 tokens); it is written and read
+ * back within the call.
  * ---------------------------------------------------------------------- */
 size_t gptq_hessian_ws_bytes(int64_t n, int64_t tokens, int x_dtype);
 gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
@@ -84,9 +89,11 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dt
  * order: the token splits may differ).  The block
  * alpha Xf^T Xf (rows and columns n..2n-1) is unspecified on return: when n
  * is a multiple of 2048 its tiles are not computed (a third of the work).
- * Arguments as for gptq_hessian_accumulate with 2n columns (ldx >= 2n,
- * workspace of gptq_hessian_ws_bytes(2n, tokens, x_dtype) bytes);
- * n <= 32768. */
+ * Arguments as for gptq_hessian_accumulate with 2n columns (ldx >= 2n);
+ * n <= 32768.  Workspace: gptq_hessian_pair_ws_bytes(n, tokens, x_dtype)
+ * bytes, which never exceeds gptq_hessian_ws_bytes(2n, tokens, x_dtype)
+ * (0 for invalid arguments). */
+size_t gptq_hessian_pair_ws_bytes(int64_t n, int64_t tokens, int x_dtype);
 gptq_status gptq_hessian_pair_accumulate(float* H2, int64_t n, const void* Xcat, int x_dtype,
                                          int64_t tokens, int64_t ldx, float alpha, int reset,
                                          void* ws, size_t ws_bytes, void* stream);

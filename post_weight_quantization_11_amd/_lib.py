@@ -26,6 +26,7 @@ EXPORTS = (
     "gptq_status_string",
     "gptq_hessian_ws_bytes",
     "gptq_hessian_accumulate",
+    "gptq_hessian_pair_ws_bytes",
     "gptq_hessian_pair_accumulate",
     "gptq_prepare_ws_bytes",
     "gptq_prepare_hinv",
@@ -73,6 +74,8 @@ def load(path: str = LIB_PATH):
     lib.gptq_hessian_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_hessian_accumulate.restype = C
     lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
+    lib.gptq_hessian_pair_ws_bytes.restype = sz
+    lib.gptq_hessian_pair_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_hessian_pair_accumulate.restype = C
     lib.gptq_hessian_pair_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
     lib.gptq_prepare_ws_bytes.restype = sz
@@ -182,7 +185,7 @@ def gptq_hessian_pair_accumulate(H2, Xcat, alpha: float = 2.0, reset: bool = Fal
     tokens = Xcat.shape[0]
     dt = _dtype_code(Xcat)
     if ws is None:
-        ws = _workspace(lib.gptq_hessian_ws_bytes(n2, tokens, dt), H2.device)
+        ws = _workspace(lib.gptq_hessian_pair_ws_bytes(n2 // 2, tokens, dt), H2.device)
     rc = lib.gptq_hessian_pair_accumulate(_ptr(H2), n2 // 2, _ptr(Xcat), dt, tokens,
                                           Xcat.stride(0) if tokens else n2, float(alpha), int(bool(reset)),
                                           _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))

@@ -21,6 +21,7 @@
 // mirrors the upper triangle.
 #include "common.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace gptq {
@@ -647,6 +648,49 @@ SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype, int skip_last = 0) {
   return p;
 }
 
+// The plan of a call that leaves out the last skip_last tiles: the token
+// splits are those of the full tile set, so the workspace it needs never
+// exceeds gptq_hessian_ws_bytes of the full width.
+SyrkPlan plan_syrk_skipping(int64_t n, int64_t tokens, int dtype, int skip_last) {
+  SyrkPlan p = plan_syrk(n, tokens, dtype);
+  if (skip_last > 0) {
+    p.ntiles -= skip_last;
+    p.launched = (int64_t)kXcds * ceil_div(p.ntiles, kXcds) * p.nsplit;
+  }
+  return p;
+}
+
+size_t plan_ws_bytes(const SyrkPlan& p) {
+  return (size_t)p.nsplit * (size_t)p.ntiles * (size_t)kTileElems * sizeof(float);
+}
+
+// Tiles of the X_f^T X_f block that a paired call leaves out (0 when they do
+// not form the tail of the band-blocked order): with n a multiple of the tile
+// and the half a whole number of kGroup-band super-blocks, the tiles with
+// both bands in the second half come last.
+int pair_skipped_tiles(int64_t n) {
+  const int64_t half_bands = ceil_div(n, kTile);
+  const bool aligned = n % kTile == 0 && half_bands % kGroup == 0;
+  return aligned ? (int)(half_bands * (half_bands + 1) / 2) : 0;
+}
+
+// hipFuncSetAttribute once per device and kernel; concurrent first calls may
+// both set it (the call is idempotent), none skips it.
+std::atomic<uint64_t> g_direct_attr_done[2];
+
+gptq_status ensure_direct_lds_attr(int x_dtype) {
+  int dev = 0;
+  GPTQ_TRY_HIP(hipGetDevice(&dev));
+  const int which = x_dtype == GPTQ_BF16 ? 0 : 1;
+  const uint64_t bit = dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit != 0 && (g_direct_attr_done[which].load(std::memory_order_acquire) & bit)) return GPTQ_OK;
+  const void* fn = x_dtype == GPTQ_BF16 ? reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_BF16>)
+                                        : reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_F16>);
+  GPTQ_TRY_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDirectLdsBytes));
+  g_direct_attr_done[which].fetch_or(bit, std::memory_order_release);
+  return GPTQ_OK;
+}
+
 }  // namespace
 }  // namespace gptq
 
@@ -654,8 +698,12 @@ using namespace gptq;
 
 extern "C" size_t gptq_hessian_ws_bytes(int64_t n, int64_t tokens, int x_dtype) {
   if (n <= 0 || tokens <= 0 || !valid_dtype(x_dtype)) return 0;
-  const SyrkPlan p = plan_syrk(n, tokens, x_dtype);
-  return (size_t)p.nsplit * (size_t)p.ntiles * (size_t)kTileElems * sizeof(float);
+  return plan_ws_bytes(plan_syrk(n, tokens, x_dtype));
+}
+
+extern "C" size_t gptq_hessian_pair_ws_bytes(int64_t n, int64_t tokens, int x_dtype) {
+  if (n <= 0 || n > ((int64_t)1 << 15) || tokens <= 0 || !valid_dtype(x_dtype)) return 0;
+  return plan_ws_bytes(plan_syrk_skipping(2 * n, tokens, x_dtype, pair_skipped_tiles(n)));
 }
 
 namespace {
@@ -675,8 +723,8 @@ gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_
     }
     return GPTQ_OK;
   }
-  const SyrkPlan p = plan_syrk(n, tokens, x_dtype, skip_last);
-  const size_t need = (size_t)p.nsplit * (size_t)p.ntiles * (size_t)kTileElems * sizeof(float);
+  const SyrkPlan p = plan_syrk_skipping(n, tokens, x_dtype, skip_last);
+  const size_t need = plan_ws_bytes(p);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
   float* partial = static_cast<float*>(ws);
   if (x_dtype == GPTQ_F32) {
@@ -687,14 +735,8 @@ gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_
     const int vec_ok = (ldx % 8 == 0) && ((reinterpret_cast<uintptr_t>(X) & 15) == 0);
     const bool direct = vec_ok && (n % 8 == 0);
     if (direct) {
-      static bool attr_done[2] = {false, false};
-      const int which = x_dtype == GPTQ_BF16 ? 0 : 1;
-      if (!attr_done[which]) {
-        const void* fn = x_dtype == GPTQ_BF16 ? reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_BF16>)
-                                              : reinterpret_cast<const void*>(&syrk16_direct_kernel<GPTQ_F16>);
-        GPTQ_TRY_HIP(hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kDirectLdsBytes));
-        attr_done[which] = true;
-      }
+      const gptq_status rc = ensure_direct_lds_attr(x_dtype);
+      if (rc != GPTQ_OK) return rc;
       if (x_dtype == GPTQ_BF16)
         syrk16_direct_kernel<GPTQ_BF16><<<(unsigned)p.launched, kThreads, kDirectLdsBytes, st>>>(
             static_cast<const uint16_t*>(X), ldx, (int)n, tokens, p.nb, p.ntiles, p.nsplit, p.tok_per_split,
@@ -732,11 +774,6 @@ extern "C" gptq_status gptq_hessian_pair_accumulate(float* H2, int64_t n, const 
                                                     void* ws, size_t ws_bytes, void* stream) {
   if (n < 0) return GPTQ_ERR_INVALID_ARG;
   if (n > ((int64_t)1 << 15)) return GPTQ_ERR_UNSUPPORTED;
-  // The tiles with both bands in the second half (the Xf^T Xf block) come
-  // last in the band-blocked order when the half is a whole number of
-  // kGroup-band super-blocks; then they are left out.
-  const int64_t half_bands = ceil_div(n, kTile);
-  const bool aligned = n % kTile == 0 && half_bands % kGroup == 0;
-  const int skip = aligned ? (int)(half_bands * (half_bands + 1) / 2) : 0;
-  return hessian_impl(H2, 2 * n, Xcat, x_dtype, tokens, ldx, alpha, reset, ws, ws_bytes, stream, skip);
+  return hessian_impl(H2, 2 * n, Xcat, x_dtype, tokens, ldx, alpha, reset, ws, ws_bytes, stream,
+                      pair_skipped_tiles(n));
 }

@@ -59,6 +59,22 @@ def test_workspace_queries(lib):
     assert lib.gptq_quantize_ws_bytes(4096, 4096, 2, 1, 128) >= q + 4096 * 4096 * 4
 
 
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_pair_workspace_never_exceeds_the_full_width_query(lib, dt):
+    # The paired Hessian call documents gptq_hessian_ws_bytes(2n, ...) as an
+    # upper bound of what it needs; its own query must respect that bound on
+    # every shape (no launch happens here).
+    assert lib.gptq_hessian_pair_ws_bytes(0, 100, dt) == 0
+    assert lib.gptq_hessian_pair_ws_bytes(64, 0, dt) == 0
+    assert lib.gptq_hessian_pair_ws_bytes((1 << 15) + 1, 100, dt) == 0
+    for n in (8, 256, 1000, 2048, 4096, 8192, 11008, 12288):
+        for tokens in (1, 640, 2048, 8192, 32768, 65536, 262144):
+            pair = lib.gptq_hessian_pair_ws_bytes(n, tokens, dt)
+            full = lib.gptq_hessian_ws_bytes(2 * n, tokens, dt)
+            assert 0 < pair <= full, (n, tokens, pair, full)
+            assert pair % (256 * 256 * 4) == 0
+
+
 def _null():
     return ctypes.c_void_p(0)
 
