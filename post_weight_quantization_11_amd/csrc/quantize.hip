@@ -112,7 +112,25 @@ __global__ __launch_bounds__(256) void row_grid_kernel(const void* __restrict__ 
   const int lane = threadIdx.x & 63;
   if (r >= m) return;
   float mn = INFINITY, mx = -INFINITY;
-  for (int j = lane; j < n; j += 64) {
+  int j0 = 0;
+  // Aligned rows: four elements per lane per load, four loads in flight.
+  const int64_t align = DT == GPTQ_F32 ? 16 : 8;
+  if ((reinterpret_cast<uintptr_t>(W) % align) == 0 && (ldw & 3) == 0) {
+    const int n4 = n & ~3;
+    for (; j0 + 4 * 4 * 64 <= n4; j0 += 4 * 4 * 64) {
+      floatx4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = load4_as_f32<DT>(W, r * ldw + j0 + 4 * (lane + 64 * u));
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          mn = fminf(mn, v[u][k]);
+          mx = fmaxf(mx, v[u][k]);
+        }
+    }
+  }
+  for (int j = j0 + lane; j < n; j += 64) {
     const float v = load_as_f32<DT>(W, r * ldw + j);
     mn = fminf(mn, v);
     mx = fmaxf(mx, v);
@@ -710,15 +728,54 @@ struct QuantLayout {
   size_t off_E = 0, off_Wp = 0, off_P = 0, off_Plast = 0, pstride = 0, total = 0;
 };
 
+// Number of K splits of block kb+1's update (over `stages` 32-column stages)
+// that finishes the launch soonest.  One workgroup of either role occupies a
+// CU (the LDS of the sweep role); the nsw sweep workgroups are dispatched
+// first and take about kSweepUs each; an update workgroup takes kStageUs per
+// stage plus kItemUs.  Greedy list scheduling of identical items on 256 CUs
+// gives the launch time in closed form; the fewest splits within 1% of the
+// best are taken (fewer partial products for the sweep to read).
+constexpr double kSweepUs = 35.0, kStageUs = 2.5, kItemUs = 3.0;
+constexpr int kMaxSplits = 16;
+
+int choose_splits(int nsw, int mtiles, int stages) {
+  if (stages <= 0) return 0;
+  const int cus = 256;
+  const int q = nsw / cus, a = nsw % cus;           // sweeps per CU: q, or q + 1 on a CUs
+  double best = 1e300;
+  double cost[kMaxSplits + 1];
+  const int smax = std::min(stages, kMaxSplits);
+  for (int S = 1; S <= smax; ++S) {
+    const int sps = (int)ceil_div(stages, S);
+    const int items = (int)ceil_div(stages, sps) * mtiles;
+    const double d = sps * kStageUs + kItemUs;
+    const int full = items / cus, rem = items % cus;
+    // CUs free at q * kSweepUs (256 - a of them) take the remainder first.
+    const int early = cus - a;
+    double t = q * kSweepUs + (full + (rem > 0 ? 1 : 0)) * d;
+    if (a > 0) t = std::max(t, (q + 1) * kSweepUs + (full + (rem > early ? 1 : 0)) * d);
+    if (items == 0) t = (q + (a > 0)) * kSweepUs;
+    cost[S] = t;
+    best = std::min(best, t);
+  }
+  for (int S = 1; S <= smax; ++S)
+    if (cost[S] <= best * 1.01) return S;
+  return 1;
+}
+
 QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
   QuantLayout L;
   L.nblocks = (int)ceil_div(n, kBS);
   L.mtiles = (int)ceil_div(m, 128);
   L.nsw = (int)ceil_div(m, kRowsPerWG);
-  // K splits of the update so that sweep and update workgroups together
-  // about fill the 256 CUs (at least one split).
-  L.smax = (int)std::max<int64_t>(1, std::min<int64_t>(std::max(L.nblocks - 1, 1),
-                                                       (256 - std::min<int64_t>(L.nsw, 255)) / L.mtiles));
+  // The most partial products any launch writes (at least one buffer row).
+  L.smax = 1;
+  for (int kb = 1; kb + 1 < L.nblocks; ++kb) {
+    const int stages = kb * (kBS / kUK);
+    const int S = choose_splits(L.nsw, L.mtiles, stages);
+    const int sps = (int)ceil_div(stages, S);
+    L.smax = std::max(L.smax, (int)ceil_div(stages, sps));
+  }
   const size_t mn = (size_t)m * (size_t)n * sizeof(float);
   L.pstride = (size_t)L.smax * (size_t)m * kBS;   // floats per partial-product buffer
   L.off_E = 0;
@@ -807,7 +864,7 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m
     if (make_next && kb >= 1) {
       // Block kb+1's update over columns [0, 128 kb) in ranges of whole 32-column stages.
       const int stages = kb * (kBS / kUK);
-      const int s_target = std::min(stages, L.smax);
+      const int s_target = choose_splits(L.nsw, L.mtiles, stages);
       sps = (int)ceil_div(stages, s_target);
       ns_next = (int)ceil_div(stages, sps);
     }

@@ -15,6 +15,19 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: long-running case")
 
 
+# Lines that parity tests want in the run's own log (tie counts, measured
+# errors): printed in the terminal summary, so they appear with -q and with
+# output capture on.
+REPORT_LINES = []
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    if REPORT_LINES:
+        terminalreporter.section("parity measurements")
+        for line in REPORT_LINES:
+            terminalreporter.write_line(line)
+
+
 def read_golden(name):
     """Non-comment, non-empty lines of a golden fixture."""
     with open(os.path.join(GOLDEN, name)) as f:

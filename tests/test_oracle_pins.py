@@ -520,6 +520,71 @@ def test_decoder_pieces_closed_forms():
     np.testing.assert_allclose(out[1], 0.5 * (h[0] + h[1]), rtol=1e-15)
 
 
+def test_silu_closed_forms():
+    # silu(x) = x * sigmoid(x): odd part x / 2, silu(x) - silu(-x) = x, value
+    # 0 and slope 1/2 at 0, e/(1 + e) at 1, x for large x, 0 for very negative x.
+    D = oracle.decoder_oracle
+    x = np.linspace(-6.0, 6.0, 49)
+    y = D.silu(x)
+    np.testing.assert_allclose(y - D.silu(-x), x, rtol=0, atol=1e-14)
+    assert D.silu(np.array(0.0)) == 0.0
+    h = 1e-6
+    np.testing.assert_allclose((D.silu(np.array(h)) - D.silu(np.array(-h))) / (2 * h), 0.5, rtol=1e-9)
+    np.testing.assert_allclose(D.silu(np.array([1.0, -1.0, 2.0])),
+                               [np.e / (1 + np.e), -1 / (1 + np.e), 2 * np.e ** 2 / (1 + np.e ** 2)], rtol=1e-15)
+    np.testing.assert_allclose(D.silu(np.array(40.0)), 40.0, rtol=1e-15)
+    assert abs(float(D.silu(np.array(-40.0)))) < 1e-15
+    # gating below the threshold: silu is below the identity for x > 0 and negative for x < 0
+    assert np.all(y[x > 0] < x[x > 0]) and np.all(y[x < 0] < 0)
+
+
+def test_attention_against_explicit_rotations_and_softmax():
+    # The oracle's attention against a second formulation: RoPE as explicit
+    # 2 x 2 rotation matrices on the pairs (i, i + D/2) with angle
+    # p * 10000^(-2i/D), softmax from scipy, causal mask as a loop bound.
+    from scipy.special import softmax
+    D = oracle.decoder_oracle
+    rng = np.random.default_rng(17)
+    d, heads, seqs, S = 16, 2, 2, 5
+    hd = d // heads
+    h = rng.standard_normal((seqs * S, d))
+    Wq, Wk, Wv = (rng.standard_normal((d, d)) * 0.3 for _ in range(3))
+
+    def rot(vec, p):
+        out = vec.copy()
+        for i in range(hd // 2):
+            th = p * 10000.0 ** (-2.0 * i / hd)
+            R = np.array([[np.cos(th), -np.sin(th)], [np.sin(th), np.cos(th)]])
+            out[[i, i + hd // 2]] = R @ vec[[i, i + hd // 2]]
+        return out
+
+    ref = np.zeros((seqs * S, d))
+    for s in range(seqs):
+        for t in range(S):
+            x_t = h[s * S + t]
+            for hh in range(heads):
+                sl = slice(hh * hd, (hh + 1) * hd)
+                q = rot((Wq @ x_t)[sl], t)
+                ks = [rot((Wk @ h[s * S + u])[sl], u) for u in range(t + 1)]
+                vs = [(Wv @ h[s * S + u])[sl] for u in range(t + 1)]
+                p_ = softmax(np.array([q @ k for k in ks]) / np.sqrt(hd))
+                ref[s * S + t, sl] = sum(pi * v for pi, v in zip(p_, vs))
+    np.testing.assert_allclose(D.attention(h, Wq, Wk, Wv, heads, seqs, S), ref, rtol=1e-12, atol=1e-13)
+
+
+def test_rms_norm_by_hand():
+    D = oracle.decoder_oracle
+    x = np.array([[3.0, 4.0], [1.0, -1.0]])
+    # mean squares 12.5 and 1
+    np.testing.assert_allclose(D.rms_norm(x, eps=0.0), [[3 / np.sqrt(12.5), 4 / np.sqrt(12.5)], [1.0, -1.0]],
+                               rtol=1e-15)
+
+
+def _silu_ref(x):
+    from scipy.special import expit
+    return x * expit(x)
+
+
 def _forward_inputs(blocks_what, X, n_heads, seqs, seq_len):
     """Layer inputs of every block recomputed token-block by token-block from
     the final (dequantized) weights -- a second, independent formulation of
@@ -533,7 +598,7 @@ def _forward_inputs(blocks_what, X, n_heads, seqs, seq_len):
         a = np.concatenate(parts, axis=0)
         X = X + a @ W["o"].T
         h2 = D.rms_norm(X)
-        mm = D.silu(h2 @ W["gate"].T) * (h2 @ W["up"].T)
+        mm = _silu_ref(h2 @ W["gate"].T) * (h2 @ W["up"].T)
         X = X + mm @ W["down"].T
         inputs.append(dict(q=h, k=h, v=h, o=a, gate=h2, up=h2, down=mm))
     return X, inputs
@@ -706,6 +771,49 @@ def test_lowrank_planted_mistakes_are_caught(name, monkeypatch):
     caught = []
     for check in (test_lowrank_hessian_is_the_joint_optimum_over_r, test_lowrank_basis_is_the_truncated_svd,
                   test_lowrank_depends_on_the_span_only):
+        try:
+            check()
+        except AssertionError:
+            caught.append(check)
+    assert caught, f"mutation '{name}' was not caught by any pin"
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes in the whole-decoder oracle: each plausible slip in its
+# pieces or its wiring must fail at least one decoder pin.
+# ---------------------------------------------------------------------------
+DECODER_MUTATIONS = {
+    "silu with sigmoid(-x)": ("silu", "return x / (1.0 + np.exp(-x))", "return x / (1.0 + np.exp(x))"),
+    "silu without x": ("silu", "return x / (1.0 + np.exp(-x))", "return 1.0 / (1.0 + np.exp(-x))"),
+    "swiglu without gate": ("quantize_decoder",
+                            'mm = silu(h2 @ res["gate"]["What"].T) * (h2 @ res["up"]["What"].T)',
+                            'mm = h2 @ res["up"]["What"].T'),
+    "swiglu gate and up swapped": ("quantize_decoder",
+                                   'mm = silu(h2 @ res["gate"]["What"].T) * (h2 @ res["up"]["What"].T)',
+                                   'mm = silu(h2 @ res["up"]["What"].T) * (h2 @ res["gate"]["What"].T)'),
+    "rope sign": ("rope", "x1 * cos - x2 * sin, x1 * sin + x2 * cos", "x1 * cos + x2 * sin, x1 * sin + x2 * cos"),
+    "no causal mask": ("attention", "sc = np.where(np.tril(np.ones((seq_len, seq_len), dtype=bool)), sc, -np.inf)",
+                       "pass"),
+    "rms without root": ("rms_norm", "return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)",
+                         "return x / (np.mean(x * x, axis=-1, keepdims=True) + eps)"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(DECODER_MUTATIONS))
+def test_decoder_planted_mistakes_are_caught(name, monkeypatch):
+    D = oracle.decoder_oracle
+    fn, old, new = DECODER_MUTATIONS[name]
+    src = textwrap.dedent(inspect.getsource(getattr(D, fn)))
+    assert old in src
+    ns = dict(D.__dict__)
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), ns)
+    # the module attribute is the entry of the module's globals, which the
+    # other decoder functions look the mutant up in
+    monkeypatch.setitem(D.__dict__, fn, ns[fn])
+    caught = []
+    for check in (test_decoder_pieces_closed_forms, test_silu_closed_forms,
+                  test_attention_against_explicit_rotations_and_softmax, test_rms_norm_by_hand,
+                  lambda: test_decoder_pass_feeds_each_layer_the_quantized_predecessors(4, 32, False)):
         try:
             check()
         except AssertionError:

@@ -53,12 +53,86 @@ def test_certify_rejects_a_flip_away_from_a_tie():
         gu.certify_ties(W, U, None, 16, 0, 16, branch["codes"], res["codes"])
 
 
+def _adjacent(res, r, j):
+    """The other code adjacent to the oracle's w/s at (r, j)."""
+    g = res["group_size"]
+    gi = 0 if g == 0 else j // g
+    s, z = np.float32(res["scales"][r, gi]), int(res["zeros"][r, gi])
+    q = np.float32(np.float32(res["qin"][r, j]) / s)
+    lo, hi = int(np.floor(q)) + z, int(np.floor(q)) + 1 + z
+    c = int(res["codes"][r, j])
+    return hi if c == lo else lo
+
+
+def test_certify_rejects_a_code_not_adjacent_to_the_tie(monkeypatch):
+    W, U, _, res = _case(group=8)
+    res = oracle.gptq_quantize(W, U, None, 16, 8, block_size=16, record_inputs=True)
+    c = int(res["codes"][2, 9])
+    branch = oracle.gptq_quantize(W, U, None, 16, 8, block_size=16, forced={(2, 9): (c + 3) % 16})
+    monkeypatch.setattr(gu, "K_SIGMA", 1e12)
+    with pytest.raises(AssertionError, match="not adjacent"):
+        gu.certify_ties(W, U, None, 16, 8, 16, branch["codes"], res["codes"])
+
+
+def _fp32_sweep(W, U, levels, group):
+    """The unblocked sweep with every operation rounded to float32 (values
+    recorded when quantized): a float32 computation of the same decisions."""
+    f = np.float32
+    W = np.asarray(W, dtype=f)
+    U = np.asarray(U, dtype=f)
+    m, n = W.shape
+    maxq = levels - 1
+    V = W.copy()
+    qin = np.zeros((m, n), dtype=f)
+    codes = np.zeros((m, n), dtype=f)
+    if group == 0:
+        s, z = oracle.grid_params(V, maxq)
+    for j in range(n):
+        if group and j % group == 0:
+            s, z = oracle.grid_params(V[:, j:j + group], maxq)
+        v = V[:, j].copy()
+        qin[:, j] = v
+        c = oracle.quantize_values(v, s, z, maxq)
+        what = (s * (c - z)).astype(f)
+        e = ((v - what).astype(f) * f(f(1) / U[j, j])).astype(f)
+        codes[:, j] = c
+        V[:, j + 1:] = (V[:, j + 1:] - (e[:, None] * U[j, j + 1:][None, :]).astype(f)).astype(f)
+    return codes, qin
+
+
+@pytest.mark.parametrize("group", [0, 16])
+def test_fp32_sweep_deviation_within_the_derived_sigma(group):
+    # The tolerance model must not be optimistic: a float32 sweep's values
+    # deviate from the float64 oracle's by less than K_SIGMA sigma_j at every
+    # column before the first code difference of a row (and by far less in rms).
+    rng = np.random.default_rng(31)
+    n, m = 384, 48
+    X = rng.standard_normal((4 * n, n)) @ (np.eye(n) + rng.standard_normal((n, n)) / np.sqrt(n))
+    X *= np.exp(rng.normal(0, 1, n))
+    H = oracle.hessian(X)
+    Hd, _ = oracle.damp_and_permute(H, None, 0.01)
+    U = oracle.inverse_cholesky_upper(Hd).astype(np.float32).astype(np.float64)
+    W = (rng.standard_normal((m, n)) * 0.02).astype(np.float32).astype(np.float64)
+    res = oracle.gptq_quantize(W, U, None, 16, group, block_size=1, record_inputs=True)
+    sigma = gu.sweep_sigma(W, U, None, res)
+    c32, q32 = _fp32_sweep(W, U, 16, group)
+    ratios = []
+    for r in range(m):
+        d = np.nonzero(c32[r] != res["codes"][r])[0]
+        upto = d[0] if d.size else n
+        dev = np.abs(q32[r, :upto].astype(np.float64) - res["qin"][r, :upto])
+        assert np.all(dev <= gu.K_SIGMA * sigma[r, :upto] + 1e-30), r
+        ratios.append(dev / np.maximum(sigma[r, :upto], 1e-300))
+    ratios = np.concatenate(ratios)
+    assert np.sqrt(np.mean(ratios ** 2)) < 1.0
+
+
 def test_certify_accepts_a_branch_at_admitted_ties(monkeypatch):
     W, U, _, res = _case(group=8)
     res = oracle.gptq_quantize(W, U, None, 16, 8, block_size=16, record_inputs=True)
-    forced = {(0, 3): (int(res["codes"][0, 3]) + 1) % 16, (4, 17): (int(res["codes"][4, 17]) + 3) % 16}
+    forced = {(0, 3): _adjacent(res, 0, 3), (4, 17): _adjacent(res, 4, 17)}
     branch = oracle.gptq_quantize(W, U, None, 16, 8, block_size=16, forced=forced)
-    monkeypatch.setattr(gu, "TIE_TOL", 0.5)   # every decision counts as a tie here
+    monkeypatch.setattr(gu, "K_SIGMA", 1e12)   # every decision counts as a tie here
     rows, ties = gu.certify_ties(W, U, None, 16, 8, 16, branch["codes"], res["codes"])
     assert rows == 2 and ties == 2
     # identical codes: nothing to certify
