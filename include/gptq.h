@@ -80,6 +80,24 @@ gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dt
                                     int64_t tokens, int64_t ldx, float alpha, int reset,
                                     void* ws, size_t ws_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * H as gptq_hessian_accumulate (up to the float32 accumulation order), with
+ * no workspace argument and no allocation.  The token-split partial sums
+ * live in a static device array of GPTQ_HESSIAN_NOALLOC_SCRATCH_BYTES bytes
+ * that the library holds on every device it runs on until the process ends.
+ * When one split's partial tiles fill more than that (n > 12800) the call
+ * returns GPTQ_ERR_UNSUPPORTED; otherwise the tokens are taken in passes of
+ * as many splits as the array holds, each pass adding its float64 sum into H.
+ * Calls on one device share the array: calls that overlap on one device
+ * (concurrent streams or threads) race and give undefined results.  A failed
+ * lookup of the array's device address returns GPTQ_ERR_HIP.  Arguments as
+ * for gptq_hessian_accumulate. */
+#define GPTQ_HESSIAN_NOALLOC_SCRATCH_BYTES (320u * 1024u * 1024u)
+gptq_status gptq_hessian_accumulate_noalloc(float* H, int64_t n, const void* X, int x_dtype,
+                                            int64_t tokens, int64_t ldx, float alpha, int reset,
+                                            void* stream);
+
 /* The two blocks asymmetric calibration needs (GPTAQ / GPTQv2 abstract, see
  * gptq_asym_target) from one pass over Xcat = [Xq | Xf] (tokens x 2n, Xq in
  * columns 0..n-1, Xf in n..2n-1): H2 (2n x 2n, row-major) receives

@@ -26,6 +26,7 @@ EXPORTS = (
     "gptq_status_string",
     "gptq_hessian_ws_bytes",
     "gptq_hessian_accumulate",
+    "gptq_hessian_accumulate_noalloc",
     "gptq_hessian_pair_ws_bytes",
     "gptq_hessian_pair_accumulate",
     "gptq_prepare_ws_bytes",
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH):
     lib.gptq_hessian_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_hessian_accumulate.restype = C
     lib.gptq_hessian_accumulate.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp, sz, vp]
+    lib.gptq_hessian_accumulate_noalloc.restype = C
+    lib.gptq_hessian_accumulate_noalloc.argtypes = [vp, i64, vp, C, i64, i64, ctypes.c_float, C, vp]
     lib.gptq_hessian_pair_ws_bytes.restype = sz
     lib.gptq_hessian_pair_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_hessian_pair_accumulate.restype = C
@@ -170,6 +173,23 @@ def gptq_hessian_accumulate(H, X, alpha: float = 2.0, reset: bool = False, ws=No
                                      float(alpha), int(bool(reset)), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "gptq_hessian_accumulate")
+    return H
+
+
+def gptq_hessian_accumulate_noalloc(H, X, alpha: float = 2.0, reset: bool = False, stream=None):
+    """As gptq_hessian_accumulate, with the library's static device scratch
+    instead of a workspace (no allocation anywhere in the call)."""
+    lib = load()
+    _device_check(H)
+    _rows_check(X)
+    n = H.shape[0]
+    if X.shape[1] != n or tuple(H.shape) != (n, n):
+        raise ValueError("H must be n x n and X tokens x n")
+    tokens = X.shape[0]
+    rc = lib.gptq_hessian_accumulate_noalloc(_ptr(H), n, _ptr(X), _dtype_code(X), tokens,
+                                             X.stride(0) if tokens else n, float(alpha), int(bool(reset)),
+                                             _stream(stream))
+    _check(rc, "gptq_hessian_accumulate_noalloc")
     return H
 
 

@@ -20,6 +20,7 @@
 // kernel sums the splits in float64, scales by alpha, adds the old H and
 // mirrors the upper triangle.
 #include "common.h"
+#include "hessian_internal.h"
 
 #include <atomic>
 #include <type_traits>
@@ -616,7 +617,7 @@ struct SyrkPlan {
 // tokens-per-split, preferring fewer splits (less reduction traffic) within
 // 2% of the best.
 // skip_last drops that many tiles from the end of the band-blocked order.
-SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype, int skip_last = 0) {
+SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype, int skip_last = 0, int max_splits = 1 << 30) {
   SyrkPlan p;
   p.nb = (int)ceil_div(n, kTile);
   p.ntiles = p.nb * (p.nb + 1) / 2 - skip_last;
@@ -628,6 +629,7 @@ SyrkPlan plan_syrk(int64_t n, int64_t tokens, int dtype, int skip_last = 0) {
   int nc = 0;
   const int s_min = (int)ceil_div(tokens, kMaxSplitTokens);
   for (int s = s_min; s <= s_min + 64; ++s) {
+    if (s > s_min && s > max_splits) break;
     const int64_t tps = round_up(ceil_div(tokens, s), kt);
     if (s > s_min && tps * (s - 1) >= tokens) break;  // a split would be empty
     if (s > s_min && tps < 4 * kt) break;
@@ -709,7 +711,8 @@ extern "C" size_t gptq_hessian_pair_ws_bytes(int64_t n, int64_t tokens, int x_dt
 namespace {
 
 gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_t tokens, int64_t ldx, float alpha,
-                         int reset, void* ws, size_t ws_bytes, void* stream, int skip_last) {
+                         int reset, void* ws, size_t ws_bytes, void* stream, int skip_last,
+                         int max_splits = 1 << 30) {
   if (n < 0 || tokens < 0 || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
   if (n > (int64_t)1 << 16) return GPTQ_ERR_UNSUPPORTED;
   if (n == 0) return GPTQ_OK;
@@ -723,7 +726,8 @@ gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_
     }
     return GPTQ_OK;
   }
-  const SyrkPlan p = plan_syrk_skipping(n, tokens, x_dtype, skip_last);
+  const SyrkPlan p = skip_last > 0 ? plan_syrk_skipping(n, tokens, x_dtype, skip_last)
+                                   : plan_syrk(n, tokens, x_dtype, 0, max_splits);
   const size_t need = plan_ws_bytes(p);
   if (ws == nullptr || ws_bytes < need) return GPTQ_ERR_WORKSPACE;
   float* partial = static_cast<float*>(ws);
@@ -762,6 +766,40 @@ gptq_status hessian_impl(float* H, int64_t n, const void* X, int x_dtype, int64_
 }
 
 }  // namespace
+
+namespace gptq {
+
+int64_t hessian_split_bytes(int64_t n) {
+  const int64_t nb = ceil_div(n, kTile);
+  return nb * (nb + 1) / 2 * (int64_t)kTileElems * (int64_t)sizeof(float);
+}
+
+gptq_status hessian_accumulate_bounded(float* H, int64_t n, const void* X, int x_dtype, int64_t tokens,
+                                       int64_t ldx, float alpha, int reset, void* ws, size_t ws_bytes,
+                                       void* stream) {
+  if (n < 0 || tokens < 0 || !valid_dtype(x_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (n > (int64_t)1 << 16) return GPTQ_ERR_UNSUPPORTED;
+  if (n == 0) return GPTQ_OK;
+  if (H == nullptr) return GPTQ_ERR_INVALID_ARG;
+  if (tokens > 0 && (X == nullptr || ldx < n)) return GPTQ_ERR_INVALID_ARG;
+  const int64_t per_split = hessian_split_bytes(n);
+  const int64_t max_splits = (int64_t)ws_bytes / per_split;
+  if (ws == nullptr || max_splits < 1) return GPTQ_ERR_WORKSPACE;
+  if (tokens == 0) return hessian_impl(H, n, X, x_dtype, 0, ldx, alpha, reset, ws, ws_bytes, stream, 0);
+  // Passes of at most max_splits splits of kMaxSplitTokens tokens; each pass
+  // adds its float64 split sum to H (the first pass honours reset).
+  const int64_t pass_tokens = max_splits * kMaxSplitTokens;
+  const char* xb = static_cast<const char*>(X);
+  for (int64_t t0 = 0; t0 < tokens; t0 += pass_tokens) {
+    const int64_t tt = std::min(pass_tokens, tokens - t0);
+    const gptq_status rc = hessian_impl(H, n, xb + t0 * ldx * (int64_t)elem_bytes(x_dtype), x_dtype, tt, ldx,
+                                        alpha, t0 == 0 ? reset : 0, ws, ws_bytes, stream, 0, (int)max_splits);
+    if (rc != GPTQ_OK) return rc;
+  }
+  return GPTQ_OK;
+}
+
+}  // namespace gptq
 
 extern "C" gptq_status gptq_hessian_accumulate(float* H, int64_t n, const void* X, int x_dtype,
                                                int64_t tokens, int64_t ldx, float alpha, int reset,

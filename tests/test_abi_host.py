@@ -75,6 +75,21 @@ def test_pair_workspace_never_exceeds_the_full_width_query(lib, dt):
             assert pair % (256 * 256 * 4) == 0
 
 
+def test_noalloc_hessian_rejects_before_any_launch(lib):
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    # widths whose one token split does not fit the static scratch
+    assert lib.gptq_hessian_accumulate_noalloc(vp(0x1000), i64(13056), vp(0x1000), 1, i64(16), i64(13056),
+                                               ctypes.c_float(2.0), 1, vp(0)) == _lib.GPTQ_ERR_UNSUPPORTED
+    assert lib.gptq_hessian_accumulate_noalloc(vp(0), i64(64), vp(0x1000), 1, i64(16), i64(64),
+                                               ctypes.c_float(2.0), 1, vp(0)) == _lib.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_hessian_accumulate_noalloc(vp(0x1000), i64(64), vp(0x1000), 9, i64(16), i64(64),
+                                               ctypes.c_float(2.0), 1, vp(0)) == _lib.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_hessian_accumulate_noalloc(vp(0x1000), i64(64), vp(0x1000), 1, i64(16), i64(32),
+                                               ctypes.c_float(2.0), 1, vp(0)) == _lib.GPTQ_ERR_INVALID_ARG
+    assert lib.gptq_hessian_accumulate_noalloc(vp(0), i64(0), vp(0), 1, i64(0), i64(0),
+                                               ctypes.c_float(2.0), 1, vp(0)) == _lib.GPTQ_OK
+
+
 def _null():
     return ctypes.c_void_p(0)
 
