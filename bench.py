@@ -3,8 +3,9 @@
 A step runs the whole path on inputs already resident in HBM:
   gptq_hessian_accumulate (all calibration tokens, reset)
   gptq_prepare_hinv       (damping, act-order, U)
-  gptq_quantize_layer     (column sweep + lazy block updates)
-  gptq_pack               (un-permute + pack, g_idx)
+  gptq_quantize_layer     (column sweep + lazy block updates, codes in
+                           original column order, g_idx)
+  gptq_pack               (pack)
 Default workload: the 175B-class fc1 layer, W 49152 x 12288 fp16
 ~N(0, 0.01^2), 262144 calibration tokens (128 x 2048) fp16 with 0.5% of the
 channels scaled x50, 4-bit asymmetric per-row grid, block 128, damping 1%
@@ -280,7 +281,7 @@ def bench_gptaq(args):
         mark(3)
         q = g.gptq_quantize_layer(Wt, U, None, cfg.levels, cfg.group_size, cfg.block_size)
         mark(4)
-        g.gptq_pack(q["codes"], None, bits_of(cfg.levels), cfg.group_size)
+        g.gptq_pack(q["codes"], bits_of(cfg.levels))
         mark(5)
 
     for _ in range(args.warmup):
@@ -348,9 +349,9 @@ def bench_lora(args):
         mark(4)
         q = g.gptq_quantize_layer(Wd, U, None, cfg.levels, cfg.group_size, cfg.block_size)
         mark(5)
-        g.gptq_pack(q["codes"], None, bits_of(cfg.levels), cfg.group_size)
+        g.gptq_pack(q["codes"], bits_of(cfg.levels))
         mark(6)
-        R = g.gptq_lowrank_compensation(Wd, q, K, None, cfg.group_size)
+        R = g.gptq_lowrank_compensation(Wd, q, K, cfg.group_size)
         mark(7)
         out.update(q=q, R=R, L=Lb)
 
@@ -546,15 +547,14 @@ def main():
     out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=dev),
                scales=torch.empty((m, G), dtype=torch.float32, device=dev),
                zeros=torch.empty((m, G), dtype=torch.uint8, device=dev),
-               row_loss=torch.empty((m,), dtype=torch.float32, device=dev))
+               g_idx=torch.empty((n,), dtype=torch.int32, device=dev),
+               row_loss=torch.empty((m,), dtype=torch.float32, device=dev), Wq=None)
     bits = bits_of(cfg.levels)
     packed = torch.empty((m, g.packed_words(n, bits)), dtype=torch.int32, device=dev)
-    gidx = torch.empty((n,), dtype=torch.int32, device=dev)
     xdt = _lib._dtype_code(Xd)
     ws_h = torch.empty(max(1, lib.gptq_hessian_ws_bytes(n, N, xdt)), dtype=torch.uint8, device=dev)
     ws_p = torch.empty(max(1, lib.gptq_prepare_ws_bytes(n)), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(max(1, lib.gptq_quantize_ws_bytes(m, n, _lib._dtype_code(Wd), int(cfg.act_order),
-                                                         cfg.block_size)), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(1, lib.gptq_quantize_ws_bytes(m, n, cfg.block_size)), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -570,8 +570,7 @@ def main():
                               cfg.block_size, out=out, ws=ws_q)
         if ev:
             ev[3].record(stream)
-        g.gptq_pack(out["codes"], perm if cfg.act_order else None, bits, cfg.group_size,
-                    packed=packed, g_idx=gidx)
+        g.gptq_pack(out["codes"], bits, packed=packed)
         if ev:
             ev[4].record(stream)
 

@@ -160,51 +160,56 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_rel, int act
  *   e = (w_rj - s*(c - z)) / U_jj
  *   w_rk -= e * U_jk for the later columns k of the block; the later blocks
  *   receive the block's corrections as one matrix product.
- * maxq = levels - 1.
+ * maxq = levels - 1.  Groups are group_size consecutive processing
+ * positions; "current values" at a group start include every correction of
+ * the columns before it (also for groups wider than a block).
  *   W          device, m x n, element type w_dtype, leading dimension ldw
- *              >= n; read only (the float32 working copy is in ws).
+ *              >= n; read only.
  *   U          device, n x n float32 from gptq_prepare_hinv (processing order).
- *   perm       device, n int32 processing order, or NULL for the identity.
+ *   perm       device, n int32 processing order (a permutation of 0..n-1),
+ *              or NULL for the identity.
  *   levels     3 (ternary), 4 (2-bit), 8 (3-bit) or 16 (4-bit).
- *   group_size 0 (one grid per row) or one of 16, 32, 64, 128.
+ *   group_size 0 (one grid per row), 16, 32, 64, or a multiple of 128.
  *   block_size 128.
- *   codes      device, m x n uint8 output in PROCESSING order
- *              (codes[r*n + j] belongs to original column perm[j]).
+ * Outputs (original column order unless noted):
+ *   codes      device, m x n uint8 (leading dimension n): codes[r*n + k] is the
+ *              code of original column k.
  *   scales     device, m x G float32, G = 1 if group_size = 0 else
  *              ceil(n / group_size); group g covers processing positions
  *              [g*group_size, (g+1)*group_size).
  *   zeros      device, m x G uint8.
+ *   g_idx      device, n int32 or NULL: the group of original column k,
+ *              g_idx[perm[j]] = j / group_size (all 0 when group_size = 0).
  *   row_loss   device, m float32 = sum_j e_rj^2 / 2 per row, or NULL.
- *   ws         device workspace of gptq_quantize_ws_bytes(m, n, w_dtype,
- *              perm != NULL, block_size) bytes.
+ *   Wq         device, m x n (leading dimension n) dequantized weights in
+ *              w_dtype, or NULL: Wq[r][k] = fl_w(fl32(s (c - z))) with the
+ *              scale and zero of column k's group, rounded to nearest even.
+ *   ws         device workspace of gptq_quantize_ws_bytes(m, n, block_size)
+ *              bytes (0 for invalid arguments).
  * Every row is independent: running a subset of rows gives those rows'
- * results exactly.
+ * results exactly.  With m = 0 only g_idx is written.
  * ---------------------------------------------------------------------- */
-size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int w_dtype, int permuted, int block_size);
+size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int block_size);
 gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
                                 const float* U, const int32_t* perm,
                                 int levels, int group_size, int block_size,
-                                uint8_t* codes, float* scales, uint8_t* zeros,
-                                float* row_loss, void* ws, size_t ws_bytes, void* stream);
+                                uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
+                                float* row_loss, void* Wq, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Stage 4: un-permute and pack (GPTQ knowledge note, "Tradeoffs": packed
- * weights; Wiki "GPTQ", "Performance and Accuracy": 4 bits per weight).
- *   codes      device, m x n uint8 in processing order (from
- *              gptq_quantize_layer), values < 2^bits.
- *   perm       device, n int32 or NULL (identity).
+ * Stage 4: pack (GPTQ knowledge note, "Tradeoffs": packed weights; Wiki
+ * "GPTQ", "Performance and Accuracy": 4 bits per weight).
+ *   codes      device, m x n uint8 in original column order (as
+ *              gptq_quantize_layer writes them), values < 2^bits.
  *   bits       2, 3 or 4.
  *   packed     device, m x ld_packed uint32 output; ld_packed >=
- *              ceil(n*bits/32).  Row r's codes in ORIGINAL column order form
- *              a little-endian bit stream: code of column k occupies bits
- *              [k*bits, (k+1)*bits) of the row; unused tail bits are 0;
- *              words beyond ceil(n*bits/32) are not written.
- *   g_idx      device, n int32 output or NULL: g_idx[perm[j]] = j / group_size
- *              (all 0 when group_size = 0).
+ *              ceil(n*bits/32).  Row r's codes form a little-endian bit
+ *              stream: code of column k occupies bits [k*bits, (k+1)*bits)
+ *              of the row; unused tail bits are 0; words beyond
+ *              ceil(n*bits/32) are not written.
  * ---------------------------------------------------------------------- */
-gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t* perm,
-                      int bits, int group_size, uint32_t* packed, int64_t ld_packed,
-                      int32_t* g_idx, void* stream);
+gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uint32_t* packed,
+                      int64_t ld_packed, void* stream);
 
 /* ------------------------------------------------------------------------
  * Asymmetric calibration (GPTAQ / GPTQv2 abstract, Daily Papers and mlsanity
@@ -285,17 +290,20 @@ gptq_status gptq_lowrank_hessian(const float* H, int64_t n, int64_t ldh, const d
                                  void* stream);
 
 /* R[a][i] = sum_c K[c][a] (W[i][c] - W^[i][c]): the least-squares R for the
- * quantized weights W^[i][perm[j]] = scales[i][g(j)] (codes[i][j] -
- * zeros[i][g(j)]), g(j) = j / group_size (0 when group_size = 0).
+ * quantized weights W^[i][c] = scales[i][g(c)] (codes[i][c] -
+ * zeros[i][g(c)]), g(c) = g_idx[c], or c / group_size when g_idx is NULL
+ * (0 when group_size = 0).
  *   W, w_dtype, m, n, ldw   the layer as given to gptq_quantize_layer.
- *   codes, scales, zeros    gptq_quantize_layer's outputs (processing order).
- *   group_size, perm        as given to gptq_quantize_layer (perm may be NULL).
+ *   codes, scales, zeros    gptq_quantize_layer's outputs (codes in original
+ *                           column order), group_size as given to it.
+ *   g_idx                   gptq_quantize_layer's g_idx output (needed with
+ *                           act-order), or NULL.
  *   K      device, n x r float64 from gptq_lowrank_hessian.
  *   R      device, r x m float32 output (ldr >= m).
  * Does not synchronise. */
 gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
                                       const uint8_t* codes, const float* scales, const uint8_t* zeros,
-                                      int group_size, const int32_t* perm, const double* K, int64_t r,
+                                      int group_size, const int32_t* g_idx, const double* K, int64_t r,
                                       float* R, int64_t ldr, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
@@ -310,8 +318,9 @@ gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int64_t m, int
  *              (bits 2, 3 or 4; ld_packed >= ceil(n*bits/32)).
  *   scales     device, m x G float32; zeros device, m x G uint8 (G >= 1).
  *   g_idx      device, n int32 (the group of each column, < G) or NULL: then
- *              g(k) = k / group_size, or 0 when group_size = 0.  gptq_pack's
- *              g_idx output (act-order) can be passed as is.
+ *              g(k) = k / group_size, or 0 when group_size = 0.
+ *              gptq_quantize_layer's g_idx output (act-order) can be passed
+ *              as is.
  *   X          device, batch x ldx IEEE binary16 (ldx >= n).
  *   Y          device, batch x ldy float32 output (ldy >= m), overwritten.
  *   batch      1 .. GPTQ_GEMV_MAX_BATCH (else GPTQ_ERR_UNSUPPORTED).

@@ -230,8 +230,8 @@ def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
     if g < 0:
         raise ValueError("group_size must be >= 0")
     B = max(1, int(block_size))
-    if B > 1 and g > 0 and B % g != 0:
-        raise ValueError("blocked sweep needs block_size % group_size == 0")
+    if B > 1 and g > 0 and B % g != 0 and g % B != 0:
+        raise ValueError("blocked sweep needs block_size % group_size == 0 or group_size % block_size == 0")
     if order not in ("right", "left"):
         raise ValueError("order must be 'right' or 'left'")
     G = 1 if g == 0 else -(-n // g)
@@ -250,10 +250,19 @@ def gptq_quantize(W, U, perm=None, levels: int = 16, group_size: int = 0,
     s_cur = scales[:, 0].copy()
     z_cur = zeros[:, 0].copy()
 
+    # Left-looking order: applied[k] = how many leading columns' errors column
+    # k has received.  A group wider than the block takes its statistics from
+    # the current values of all its columns, so at its first block every
+    # column of the group is brought up to date (right-looking order keeps
+    # every later column up to date at each block boundary anyway).
+    applied = np.zeros(n, dtype=np.int64)
     for b0 in range(0, n, B):
         b1 = min(n, b0 + B)
         if order == "left" and b0 > 0:
-            V[:, b0:b1] -= E[:, :b0] @ U[:b0, b0:b1]
+            hi = min(n, b0 + g) if (g > B and b0 % g == 0) else b1
+            k0 = int(applied[b0])
+            V[:, b0:hi] -= E[:, k0:b0] @ U[k0:b0, b0:hi]
+            applied[b0:hi] = b0
         for j in range(b0, b1):
             if g > 0 and j % g == 0:
                 gi = j // g

@@ -86,11 +86,11 @@ def load(path: str = LIB_PATH):
     lib.gptq_prepare_hinv.restype = C
     lib.gptq_prepare_hinv.argtypes = [vp, i64, ctypes.c_float, C, vp, vp, i32p, vp, sz, vp]
     lib.gptq_quantize_ws_bytes.restype = sz
-    lib.gptq_quantize_ws_bytes.argtypes = [i64, i64, C, C, C]
+    lib.gptq_quantize_ws_bytes.argtypes = [i64, i64, C]
     lib.gptq_quantize_layer.restype = C
-    lib.gptq_quantize_layer.argtypes = [vp, C, i64, i64, i64, vp, vp, C, C, C, vp, vp, vp, vp, vp, sz, vp]
+    lib.gptq_quantize_layer.argtypes = [vp, C, i64, i64, i64, vp, vp, C, C, C, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.gptq_pack.restype = C
-    lib.gptq_pack.argtypes = [vp, i64, i64, vp, C, C, vp, i64, vp, vp]
+    lib.gptq_pack.argtypes = [vp, i64, i64, C, vp, i64, vp]
     lib.gptq_dequant_gemv.restype = C
     lib.gptq_dequant_gemv.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, vp, i64, i64, vp, i64, vp]
     lib.gptq_asym_target_ws_bytes.restype = sz
@@ -234,9 +234,11 @@ def gptq_prepare_hinv(H, damp_rel: float = 0.01, act_order: bool = False, U=None
 
 
 def gptq_quantize_layer(W, U, perm=None, levels: int = 16, group_size: int = 0, block_size: int = 128,
-                        want_row_loss: bool = True, out=None, ws=None, stream=None):
-    """Returns dict(codes (m x n uint8, processing order), scales (m x G), zeros (m x G uint8),
-    row_loss (m) or None)."""
+                        want_row_loss: bool = True, want_g_idx: bool = True, want_wq: bool = False,
+                        out=None, ws=None, stream=None):
+    """Returns dict(codes (m x n uint8, original column order), scales (m x G),
+    zeros (m x G uint8), g_idx (n int32) or None, row_loss (m) or None,
+    Wq (m x n, W's dtype, dequantized) or None)."""
     torch = _torch()
     lib = load()
     _device_check(U, perm)
@@ -245,18 +247,25 @@ def gptq_quantize_layer(W, U, perm=None, levels: int = 16, group_size: int = 0, 
     if tuple(U.shape) != (n, n) or (perm is not None and perm.numel() != n):
         raise ValueError("U must be n x n and perm n long")
     G = 1 if group_size == 0 else -(-n // group_size)
+    dev = W.device
     if out is None:
-        out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=W.device),
-                   scales=torch.empty((m, G), dtype=torch.float32, device=W.device),
-                   zeros=torch.empty((m, G), dtype=torch.uint8, device=W.device),
-                   row_loss=torch.empty((m,), dtype=torch.float32, device=W.device) if want_row_loss else None)
+        out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=dev),
+                   scales=torch.empty((m, G), dtype=torch.float32, device=dev),
+                   zeros=torch.empty((m, G), dtype=torch.uint8, device=dev),
+                   g_idx=torch.empty((n,), dtype=torch.int32, device=dev) if want_g_idx else None,
+                   row_loss=torch.empty((m,), dtype=torch.float32, device=dev) if want_row_loss else None,
+                   Wq=torch.empty((m, n), dtype=W.dtype, device=dev) if want_wq else None)
+    for key in ("g_idx", "row_loss", "Wq"):
+        out.setdefault(key, None)
+    if out["Wq"] is not None and (out["Wq"].dtype != W.dtype or not out["Wq"].is_contiguous()):
+        raise ValueError("Wq must be a contiguous m x n tensor of W's dtype")
     if ws is None:
-        ws = _workspace(lib.gptq_quantize_ws_bytes(m, n, _dtype_code(W), int(perm is not None), block_size),
-                        W.device)
+        ws = _workspace(lib.gptq_quantize_ws_bytes(m, n, block_size), dev)
     rc = lib.gptq_quantize_layer(_ptr(W), _dtype_code(W), m, n, W.stride(0) if m else n, _ptr(U), _ptr(perm),
                                  int(levels), int(group_size), int(block_size), _ptr(out["codes"]),
-                                 _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out.get("row_loss")),
-                                 _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+                                 _ptr(out["scales"]), _ptr(out["zeros"]), _ptr(out["g_idx"]),
+                                 _ptr(out["row_loss"]), _ptr(out["Wq"]), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream))
     _check(rc, "gptq_quantize_layer")
     return out
 
@@ -265,21 +274,19 @@ def packed_words(n: int, bits: int) -> int:
     return -(-(n * bits) // 32)
 
 
-def gptq_pack(codes, perm=None, bits: int = 4, group_size: int = 0, want_g_idx: bool = True,
-              packed=None, g_idx=None, stream=None):
-    """Returns (packed m x ceil(n*bits/32) int32 words (bit patterns of uint32), g_idx or None)."""
+def gptq_pack(codes, bits: int = 4, packed=None, stream=None):
+    """packed (m x ceil(n*bits/32) int32 words: bit patterns of uint32) of
+    codes in original column order."""
     torch = _torch()
     lib = load()
-    _device_check(codes, perm)
+    _device_check(codes)
     m, n = codes.shape
     if packed is None:
         packed = torch.empty((m, packed_words(n, bits)), dtype=torch.int32, device=codes.device)
-    if want_g_idx and g_idx is None:
-        g_idx = torch.empty((n,), dtype=torch.int32, device=codes.device)
-    rc = lib.gptq_pack(_ptr(codes), m, n, _ptr(perm), int(bits), int(group_size), _ptr(packed),
-                       packed.stride(0) if m else packed_words(n, bits), _ptr(g_idx), _stream(stream))
+    rc = lib.gptq_pack(_ptr(codes), m, n, int(bits), _ptr(packed),
+                       packed.stride(0) if m else packed_words(n, bits), _stream(stream))
     _check(rc, "gptq_pack")
-    return packed, g_idx
+    return packed
 
 
 def gptq_dequant_gemv(packed, scales, zeros, X, n: int, bits: int, group_size: int = 0, g_idx=None,
@@ -372,8 +379,8 @@ def gptaq_quantize_linear(W, Xq, Xf, levels: int = 16, group_size: int = 0, damp
     p = perm if act_order else None
     Wt = gptq_asym_target(W, H2[:n, n:], U, p, stream=stream)
     q = gptq_quantize_layer(Wt, U, p, levels, group_size, block_size, stream=stream)
-    packed, g_idx = gptq_pack(q["codes"], p, bits_for_levels(levels), group_size, stream=stream)
-    q.update(H=H, Hc=H2[:n, n:], U=U, perm=perm, Wt=Wt, packed=packed, g_idx=g_idx)
+    packed = gptq_pack(q["codes"], bits_for_levels(levels), stream=stream)
+    q.update(H=H, Hc=H2[:n, n:], U=U, perm=perm, Wt=Wt, packed=packed)
     return q
 
 
@@ -415,12 +422,14 @@ def gptq_lowrank_hessian(H, L, H_L=None, K=None, ws=None, stream=None):
     return H_L, K
 
 
-def gptq_lowrank_compensation(W, q, K, perm=None, group_size: int = 0, R=None, ws=None, stream=None):
-    """R (r x m float32) = K^T (W - W^)^T for gptq_quantize_layer's output q."""
+def gptq_lowrank_compensation(W, q, K, group_size: int = 0, R=None, ws=None, stream=None):
+    """R (r x m float32) = K^T (W - W^)^T for gptq_quantize_layer's output q
+    (codes in original column order; q["g_idx"] is used when present)."""
     torch = _torch()
     lib = load()
     _rows_check(W)
-    _device_check(K, perm, q["codes"], q["scales"], q["zeros"])
+    g_idx = q.get("g_idx")
+    _device_check(K, g_idx, q["codes"], q["scales"], q["zeros"])
     m, n = W.shape
     r = K.shape[1]
     if R is None:
@@ -428,7 +437,7 @@ def gptq_lowrank_compensation(W, q, K, perm=None, group_size: int = 0, R=None, w
     if ws is None:
         ws = _workspace(lib.gptq_lowrank_ws_bytes(m, n, r), W.device)
     rc = lib.gptq_lowrank_compensation(_ptr(W), _dtype_code(W), m, n, W.stride(0), _ptr(q["codes"]),
-                                       _ptr(q["scales"]), _ptr(q["zeros"]), int(group_size), _ptr(perm), _ptr(K),
+                                       _ptr(q["scales"]), _ptr(q["zeros"]), int(group_size), _ptr(g_idx), _ptr(K),
                                        r, _ptr(R), R.stride(0), _ptr(ws), 0 if ws is None else ws.numel(),
                                        _stream(stream))
     _check(rc, "gptq_lowrank_compensation")
@@ -454,9 +463,9 @@ def gptq_lora_quantize_linear(W, X=None, H=None, rank: int = 16, levels: int = 1
     U, perm = gptq_prepare_hinv(H_L, damp_rel, act_order, stream=stream)
     p = perm if act_order else None
     q = gptq_quantize_layer(W, U, p, levels, group_size, block_size, stream=stream)
-    packed, g_idx = gptq_pack(q["codes"], p, bits_for_levels(levels), group_size, stream=stream)
-    R = gptq_lowrank_compensation(W, q, K, p, group_size, stream=stream)
-    q.update(H=H, L=L, H_L=H_L, K=K, U=U, perm=perm, packed=packed, g_idx=g_idx, R=R)
+    packed = gptq_pack(q["codes"], bits_for_levels(levels), stream=stream)
+    R = gptq_lowrank_compensation(W, q, K, group_size, stream=stream)
+    q.update(H=H, L=L, H_L=H_L, K=K, U=U, perm=perm, packed=packed, R=R)
     return q
 
 
@@ -476,7 +485,6 @@ def gptq_quantize_linear(W, X=None, H=None, levels: int = 16, group_size: int = 
     U, perm = gptq_prepare_hinv(H, damp_rel, act_order, stream=stream)
     q = gptq_quantize_layer(W, U, perm if act_order else None, levels, group_size, block_size,
                             stream=stream)
-    packed, g_idx = gptq_pack(q["codes"], perm if act_order else None, bits_for_levels(levels),
-                              group_size, stream=stream)
-    q.update(H=H, U=U, perm=perm, packed=packed, g_idx=g_idx)
+    packed = gptq_pack(q["codes"], bits_for_levels(levels), stream=stream)
+    q.update(H=H, U=U, perm=perm, packed=packed)
     return q

@@ -34,16 +34,17 @@ constexpr int kCompensationBlocks = 1024;  // and the compensation product
 
 static_assert(kR == 64, "the tile shapes assume a 64-column rank tile");
 
-// The compensation product Out(p, a) = sum_k D(p, k) B(k, a): D = W - W^ in
-// processing order (formed on the fly), B = K with rows gathered through perm.
+// The compensation product Out(p, a) = sum_k D(p, k) B(k, a): D = W - W^
+// (formed on the fly from the codes in original column order and the group
+// of each column), B = K.
 struct TallArgs {
   const void* A;          // W (m x n, leading dimension lda)
   int64_t lda;
-  const uint8_t* codes;   // m x n, processing order
+  const uint8_t* codes;   // m x n, original column order
   const float* scales;    // m x G
   const uint8_t* zeros;   // m x G
   int64_t G, group;
-  const int32_t* perm;    // D's column k is W's column perm[k], B's row k is perm[k]; may be NULL
+  const int32_t* gidx;    // group of column k (< G), or NULL: k / group (0 when group is 0)
   const double* B;        // K x r float64, row-major (leading dimension ldb)
   int64_t ldb;
   int64_t P, K, r;
@@ -56,7 +57,7 @@ __device__ inline double w_elem(const void* W, int64_t i) {
   return static_cast<double>(load_as_f32<DT>(W, i));
 }
 
-// As[kk][pp] = D(p0 + pp, k0 + kk) = W[p][perm[k]] - s (c - z): exactly the
+// As[kk][pp] = D(p0 + pp, k0 + kk) = W[p][k] - s_g(k) (c - z_g(k)): exactly the
 // float64 difference of the stored weight and its dequantized value (s is
 // float32 and c - z a small integer, so s (c - z) is exact); 0 outside.
 template <int DT>
@@ -68,12 +69,11 @@ __device__ inline void load_a_stage(const TallArgs& a, double (*As)[kPitch], int
     const int64_t p = p0 + pp, k = k0 + kk;
     double v = 0.0;
     if (p < a.P && k < a.K) {
-      const int64_t col = a.perm ? static_cast<int64_t>(a.perm[k]) : k;
-      const int64_t g = a.group ? k / a.group : 0;
+      const int64_t g = a.gidx ? static_cast<int64_t>(a.gidx[k]) : (a.group ? k / a.group : 0);
       const double s = static_cast<double>(a.scales[p * a.G + g]);
       const double c = static_cast<double>(a.codes[p * a.K + k]);
       const double z = static_cast<double>(a.zeros[p * a.G + g]);
-      v = w_elem<DT>(a.A, p * a.lda + col) - s * (c - z);
+      v = w_elem<DT>(a.A, p * a.lda + k) - s * (c - z);
     }
     As[kk][pp] = v;
   }
@@ -106,10 +106,7 @@ __global__ __launch_bounds__(kThreads) void compensation_kernel(TallArgs a) {
         const int kk = (tid >> 6) + 4 * it;
         const int64_t k = k0 + kk;
         double v = 0.0;
-        if (k < kend && col < a.r) {
-          const int64_t row = a.perm ? static_cast<int64_t>(a.perm[k]) : k;
-          v = a.B[row * a.ldb + col];
-        }
+        if (k < kend && col < a.r) v = a.B[k * a.ldb + col];
         Bs[kk][col] = v;
       }
     }
@@ -739,7 +736,7 @@ extern "C" gptq_status gptq_lowrank_hessian(const float* H, int64_t n, int64_t l
 
 extern "C" gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
                                                  const uint8_t* codes, const float* scales, const uint8_t* zeros,
-                                                 int group_size, const int32_t* perm, const double* K, int64_t r,
+                                                 int group_size, const int32_t* g_idx, const double* K, int64_t r,
                                                  float* R, int64_t ldr, void* ws, size_t ws_bytes, void* stream) {
   if (!W || !codes || !scales || !zeros || !K || !R || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
   if (m < 1 || !rank_ok(n, r) || ldw < n || ldr < m || group_size < 0) return GPTQ_ERR_INVALID_ARG;
@@ -748,7 +745,7 @@ extern "C" gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int
   const Ctx c = make_ctx(lay, ws, stream);
   TallArgs a = {};
   a.A = W; a.lda = ldw; a.codes = codes; a.scales = scales; a.zeros = zeros;
-  a.group = group_size; a.G = group_size ? ceil_div(n, group_size) : 1; a.perm = perm;
+  a.group = group_size; a.G = group_size ? ceil_div(n, group_size) : 1; a.gidx = g_idx;
   a.B = K; a.ldb = r; a.P = m; a.K = n; a.r = r;
   Split s;
   gptq_status rc = w_dtype == GPTQ_F32  ? launch_compensation<GPTQ_F32>(a, c, &s)

@@ -1,10 +1,10 @@
-// Stage 4: un-permute and pack the codes (GPTQ knowledge note, "Tradeoffs":
-// deployment runs on packed weights; Wiki "GPTQ", "Performance and
-// Accuracy": 4 bits per weight).  Row-wise little-endian bit stream in
-// 32-bit words: the code of original column k occupies bits
-// [k*b, (k+1)*b).  One thread packs 32 codes into b whole words, so reads
-// and writes of neighbouring threads are contiguous.  With a permutation the
-// row is first scattered into LDS in original column order.
+// Stage 4: pack the codes (GPTQ knowledge note, "Tradeoffs": deployment runs
+// on packed weights; Wiki "GPTQ", "Performance and Accuracy": 4 bits per
+// weight).  Row-wise little-endian bit stream in 32-bit words: the code of
+// column k occupies bits [k*b, (k+1)*b).  One thread packs 32 codes into b
+// whole words (read as two 16-byte loads, 4- and 2-bit words written as one
+// 16- or 8-byte store), so reads and writes of neighbouring threads are
+// contiguous.
 #include "common.h"
 
 namespace gptq {
@@ -45,33 +45,31 @@ __device__ inline void pack32(const uint8_t* src, int count, uint32_t (&out)[BIT
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void pack_kernel(const uint8_t* __restrict__ codes, int n,
-                                                        const int32_t* __restrict__ perm,
                                                         uint32_t* __restrict__ packed, int64_t ldp) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t row_s[];
   const int64_t r = blockIdx.x;
   const uint8_t* src = codes + r * n;
-  if (perm != nullptr) {
-    for (int j = threadIdx.x; j < n; j += kThreads) row_s[min(max(perm[j], 0), n - 1)] = src[j];
-    __syncthreads();
-    src = row_s;
-  }
+  uint32_t* dst = packed + r * ldp;
   const int nseg = (n + 31) / 32;
   const int nwords = (int)(((int64_t)n * BITS + 31) / 32);
+  // Whole segments of an aligned row go out in one store of BITS words (4-
+  // and 2-bit codes; 3-bit words go out one by one).
+  const bool vec = BITS != 3 && (reinterpret_cast<uintptr_t>(dst) & (4 * BITS - 1)) == 0;
   for (int sg = threadIdx.x; sg < nseg; sg += kThreads) {
     uint32_t out[BITS];
     pack32<BITS>(src + sg * 32, min(32, n - sg * 32), out);
+    if (vec && sg * BITS + BITS <= nwords) {
+      if constexpr (BITS == 4) {
+        *reinterpret_cast<uint4*>(dst + sg * 4) = uint4{out[0], out[1], out[2], out[3]};
+      } else if constexpr (BITS == 2) {
+        *reinterpret_cast<uint2*>(dst + sg * 2) = uint2{out[0], out[1]};
+      }
+    } else {
 #pragma unroll
-    for (int w = 0; w < BITS; ++w) {
-      const int wi = sg * BITS + w;
-      if (wi < nwords) packed[r * ldp + wi] = out[w];
+      for (int w = 0; w < BITS; ++w) {
+        const int wi = sg * BITS + w;
+        if (wi < nwords) dst[wi] = out[w];
+      }
     }
-  }
-}
-
-__global__ void gidx_kernel(int n, const int32_t* __restrict__ perm, int group, int32_t* __restrict__ gidx) {
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
-    const int col = perm ? min(max(perm[j], 0), n - 1) : j;
-    gidx[col] = group > 0 ? j / group : 0;
   }
 }
 
@@ -80,29 +78,22 @@ __global__ void gidx_kernel(int n, const int32_t* __restrict__ perm, int group, 
 
 using namespace gptq;
 
-extern "C" gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, const int32_t* perm, int bits,
-                                 int group_size, uint32_t* packed, int64_t ld_packed, int32_t* g_idx,
-                                 void* stream) {
-  if (m < 0 || n < 0 || group_size < 0) return GPTQ_ERR_INVALID_ARG;
+extern "C" gptq_status gptq_pack(const uint8_t* codes, int64_t m, int64_t n, int bits, uint32_t* packed,
+                                 int64_t ld_packed, void* stream) {
+  if (m < 0 || n < 0) return GPTQ_ERR_INVALID_ARG;
   if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
   if (n > (int64_t)1 << 16 || m > ((int64_t)1 << 31) - 1) return GPTQ_ERR_UNSUPPORTED;
-  if (n == 0) return GPTQ_OK;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (g_idx != nullptr) {
-    gidx_kernel<<<(unsigned)ceil_div(n, kThreads), kThreads, 0, st>>>((int)n, perm, group_size, g_idx);
-    GPTQ_TRY_LAUNCH();
-  }
-  if (m == 0) return GPTQ_OK;
+  if (n == 0 || m == 0) return GPTQ_OK;
   if (codes == nullptr || packed == nullptr) return GPTQ_ERR_INVALID_ARG;
   if (ld_packed < ceil_div(n * bits, 32)) return GPTQ_ERR_INVALID_ARG;
-  const size_t shm = perm ? (size_t)n : 0;
+  hipStream_t st = static_cast<hipStream_t>(stream);
   const unsigned grid = (unsigned)m;
   if (bits == 2)
-    pack_kernel<2><<<grid, kThreads, shm, st>>>(codes, (int)n, perm, packed, ld_packed);
+    pack_kernel<2><<<grid, kThreads, 0, st>>>(codes, (int)n, packed, ld_packed);
   else if (bits == 3)
-    pack_kernel<3><<<grid, kThreads, shm, st>>>(codes, (int)n, perm, packed, ld_packed);
+    pack_kernel<3><<<grid, kThreads, 0, st>>>(codes, (int)n, packed, ld_packed);
   else
-    pack_kernel<4><<<grid, kThreads, shm, st>>>(codes, (int)n, perm, packed, ld_packed);
+    pack_kernel<4><<<grid, kThreads, 0, st>>>(codes, (int)n, packed, ld_packed);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }

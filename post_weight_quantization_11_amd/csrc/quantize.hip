@@ -74,15 +74,57 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl<0, N>(f);
 }
 
-// Wp[r][j] = W[r][perm[j]] as float32 (processing order).
+// pinv[perm[j]] = j and g_idx[perm[j]] = j / g (0 when g = 0); identity
+// when perm is NULL.  Out-of-range perm entries are clamped, never followed.
+__global__ void index_kernel(int n, const int32_t* __restrict__ perm, int g, int32_t* __restrict__ pinv,
+                             int32_t* __restrict__ gidx) {
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < n; j += gridDim.x * blockDim.x) {
+    const int col = perm != nullptr ? min(max(perm[j], 0), n - 1) : j;
+    if (pinv != nullptr) pinv[col] = j;
+    if (gidx != nullptr) gidx[col] = g > 0 ? j / g : 0;
+  }
+}
+
+// Rounds a float32 value to the storage type (round to nearest even).
+template <int DT> __device__ inline void store_from_f32(void* p, int64_t i, float v);
+template <> __device__ inline void store_from_f32<GPTQ_F32>(void* p, int64_t i, float v) {
+  static_cast<float*>(p)[i] = v;
+}
+template <> __device__ inline void store_from_f32<GPTQ_F16>(void* p, int64_t i, float v) {
+  static_cast<_Float16*>(p)[i] = (_Float16)v;
+}
+template <> __device__ inline void store_from_f32<GPTQ_BF16>(void* p, int64_t i, float v) {
+  const uint32_t u = __float_as_uint(v);
+  static_cast<uint16_t*>(p)[i] = (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Row r of the sweep's codes (processing order) into original column order,
+// in place (the row is staged in LDS first; pinv NULL: already in order), and
+// the dequantized weights Wq[r][k] = fl_w(fl32(s_g (c - z_g))) of original
+// column k, g = pinv[k] / group (Wq may be NULL).
 template <int DT>
-__global__ __launch_bounds__(256) void permute_w_kernel(const void* __restrict__ W, int64_t ldw, int n,
-                                                        const int32_t* __restrict__ perm,
-                                                        float* __restrict__ Wp) {
+__global__ __launch_bounds__(256) void finalize_kernel(uint8_t* __restrict__ codes, int n,
+                                                       const int32_t* __restrict__ pinv,
+                                                       const float* __restrict__ scales,
+                                                       const uint8_t* __restrict__ zeros, int g, int G,
+                                                       void* __restrict__ Wq, int64_t ldq) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t row_s[];
   const int64_t r = blockIdx.x;
-  for (int j = threadIdx.x; j < n; j += 256) {
-    const int pj = min(max(perm[j], 0), n - 1);   // out-of-range entries are clamped, never followed
-    Wp[r * n + j] = load_as_f32<DT>(W, r * ldw + pj);
+  uint8_t* row = codes + r * n;
+  if (pinv != nullptr) {
+    for (int j = threadIdx.x; j < n; j += 256) row_s[j] = row[j];
+    __syncthreads();
+  }
+  for (int k = threadIdx.x; k < n; k += 256) {
+    const int j = pinv != nullptr ? min(max(pinv[k], 0), n - 1) : k;
+    const uint8_t c = pinv != nullptr ? row_s[j] : row[k];
+    if (pinv != nullptr) row[k] = c;
+    if (Wq != nullptr) {
+      const int gi = g > 0 ? j / g : 0;
+      const float sc = scales[r * G + gi];
+      const float zc = (float)zeros[r * G + gi];
+      store_from_f32<DT>(Wq, r * ldq + k, sc * ((float)c - zc));
+    }
   }
 }
 
@@ -271,6 +313,54 @@ __device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, co
       }
 }
 
+// Groups wider than one block (g a multiple of 128): at the group's first
+// block c0 the range is taken over the current values of all its columns.
+// For a later block b of the group those are W[:, b] - E[:, <c0] U[<c0, b];
+// range_gemm_kernel forms the product's split partials (the deferred-update
+// GEMM with its K range cut at c0) and range_reduce_kernel folds each row's
+// min / max over block b into grange (first = 1 starts it afresh).
+__global__ __launch_bounds__(kThreads) void range_gemm_kernel(const float* __restrict__ E,
+                                                              const float* __restrict__ U, int m, int n, int b,
+                                                              int c0, int sps, int mtiles, float* __restrict__ P) {
+  __shared__ GemmLds lds;
+  const int gid = (int)blockIdx.x;
+  update_gemm_body(E, U, m, n, b, c0, sps, P, gid % mtiles, gid / mtiles, lds);
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void range_reduce_kernel(const void* __restrict__ W, int64_t ldw,
+                                                           const int32_t* __restrict__ perm, int m, int n, int b,
+                                                           const float* __restrict__ P, int nsplit, int first,
+                                                           float* __restrict__ grange) {
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (r >= m) return;
+  const int c0 = b * kBS;
+  const int bw = min(kBS, n - c0);
+  float mn = INFINITY, mx = -INFINITY;
+  for (int c = lane; c < bw; c += 64) {
+    const int col = c0 + c;
+    const int src = perm != nullptr ? min(max(perm[col], 0), n - 1) : col;
+    float v = load_as_f32<DT>(W, r * ldw + src);
+    for (int sp = 0; sp < nsplit; ++sp) v -= P[((int64_t)sp * m + r) * kBS + c];
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, off));
+    mx = fmaxf(mx, __shfl_xor(mx, off));
+  }
+  if (lane == 0) {
+    if (!first) {
+      mn = fminf(mn, grange[2 * r]);
+      mx = fmaxf(mx, grange[2 * r + 1]);
+    }
+    grange[2 * r] = mn;
+    grange[2 * r + 1] = mx;
+  }
+}
+
 // The in-block sweep of block kb for 64 rows (4 waves x 16 rows; within a
 // wave, lane r < 16 owns row r for the sequential part and all 64 lanes run
 // the MFMA part).
@@ -293,7 +383,8 @@ __device__ __forceinline__ void sweep_body(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
     const float* __restrict__ P, int nsplit, float* __restrict__ Plast, int use_last, int make_next, float maxq,
     int g, int G, uint8_t* __restrict__ codes, float* __restrict__ E, float* __restrict__ scales,
-    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, int wg, SweepLds& S) {
+    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, const int32_t* __restrict__ perm,
+    const float* __restrict__ grange, int wg, SweepLds& S) {
   auto& Ud = S.Ud;
   auto& invd = S.invd;
   auto& T = S.T;
@@ -322,7 +413,7 @@ __device__ __forceinline__ void sweep_body(
     // one 16-byte (or, for 16-bit W, 8-byte) load per W slot, with no
     // per-element tests; the lower triangle of the diagonal block is loaded
     // and masked when it is stored to LDS.
-    const bool fast = bw == kBS && vecu && (ldw & 3) == 0 &&
+    const bool fast = bw == kBS && vecu && perm == nullptr && (ldw & 3) == 0 &&
                       (reinterpret_cast<uintptr_t>(Wsrc) & (DT == GPTQ_F32 ? 15 : 7)) == 0;
     floatx4 uv[kUSlots];
     if (fast) {
@@ -365,7 +456,11 @@ __device__ __forceinline__ void sweep_body(
         if (row < m) {
 #pragma unroll
           for (int k = 0; k < 4; ++k)
-            if (c + k < bw) v[k] = load_as_f32<DT>(Wsrc, row * ldw + c0 + c + k);
+            if (c + k < bw) {
+              // processing position c0 + c + k is original column perm[c0 + c + k]
+              const int col = perm != nullptr ? min(max(perm[c0 + c + k], 0), n - 1) : c0 + c + k;
+              v[k] = load_as_f32<DT>(Wsrc, row * ldw + col);
+            }
         }
         t[q] = v;
       }
@@ -445,9 +540,12 @@ __device__ __forceinline__ void sweep_body(
   const bool owner = lane < kRowsPerWave;
   const bool active = owner && row < m;
   float s = 1.f, z = 0.f, inv_s = 1.f;
-  if (g == 0 && active) {
-    s = scales[row * G];
-    z = (float)zeros[row * G];
+  // A per-row grid, or a group that began in an earlier block: its grid was
+  // stored when the group started.
+  if ((g == 0 || (g > kBS && (c0 % g) != 0)) && active) {
+    const int gi = g == 0 ? 0 : c0 / g;
+    s = scales[row * G + gi];
+    z = (float)zeros[row * G + gi];
     inv_s = 1.f / s;
   }
   float loss = 0.f;
@@ -517,7 +615,13 @@ __device__ __forceinline__ void sweep_body(
       uoff_load(j0, uf[sb & 1]);   // all zero (and no access) when there is no next block
     }
     if (block_group && sb == 0) {
-      grid_from_range(Gs[wave][r][0], Gs[wave][r][1], maxq, s, z, inv_s);
+      float gmn = Gs[wave][r][0], gmx = Gs[wave][r][1];
+      if (g > kBS && c0 + kBS < n && active) {
+        // the group goes on past this block: fold in its later blocks' range
+        gmn = fminf(gmn, grange[2 * row]);
+        gmx = fmaxf(gmx, grange[2 * row + 1]);
+      }
+      grid_from_range(gmn, gmx, maxq, s, z, inv_s);
       if (active) {
         const int gi = c0 / g;
         scales[row * G + gi] = s;
@@ -707,8 +811,8 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
     const float* __restrict__ Pcur, int nsplit, float* __restrict__ Plast, int use_last, int make_next,
     float maxq, int g, int G, uint8_t* __restrict__ codes, float* __restrict__ E, float* __restrict__ scales,
-    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, int nsw, int mtiles, int sps,
-    float* __restrict__ Pnext) {
+    uint8_t* __restrict__ zeros, float* __restrict__ row_loss, int codes_aligned, const int32_t* __restrict__ perm,
+    const float* __restrict__ grange, int nsw, int mtiles, int sps, float* __restrict__ Pnext) {
   __shared__ union {
     SweepLds s;
     GemmLds g;
@@ -716,7 +820,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
   const int wg = (int)blockIdx.x;
   if (wg < nsw) {
     sweep_body<DT>(Wsrc, ldw, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales,
-                   zeros, row_loss, codes_aligned, wg, lds.s);
+                   zeros, row_loss, codes_aligned, perm, grange, wg, lds.s);
   } else {
     const int gid = wg - nsw;
     update_gemm_body(E, U, m, n, kb + 1, kb * kBS, sps, Pnext, gid % mtiles, gid / mtiles, lds.g);
@@ -725,7 +829,7 @@ __global__ __launch_bounds__(kThreads) void quant_block_kernel(
 
 struct QuantLayout {
   int nblocks = 0, mtiles = 0, nsw = 0, smax = 0;
-  size_t off_E = 0, off_Wp = 0, off_P = 0, off_Plast = 0, pstride = 0, total = 0;
+  size_t off_E = 0, off_P = 0, off_Plast = 0, off_pinv = 0, off_grange = 0, pstride = 0, total = 0;
 };
 
 // Number of K splits of block kb+1's update (over `stages` 32-column stages)
@@ -754,7 +858,6 @@ int choose_splits(int nsw, int mtiles, int stages) {
     const int early = cus - a;
     double t = q * kSweepUs + (full + (rem > 0 ? 1 : 0)) * d;
     if (a > 0) t = std::max(t, (q + 1) * kSweepUs + (full + (rem > early ? 1 : 0)) * d);
-    if (items == 0) t = (q + (a > 0)) * kSweepUs;
     cost[S] = t;
     best = std::min(best, t);
   }
@@ -763,12 +866,17 @@ int choose_splits(int nsw, int mtiles, int stages) {
   return 1;
 }
 
-QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
+// Workspace: E (m x n float32 scaled errors), two buffers of split-K partial
+// products (smax x m x 128 float32 each), Plast (m x 128), the inverse
+// permutation (n int32) and the per-row ranges of wide groups (m x 2 float32).
+QuantLayout quant_layout(int64_t m, int64_t n) {
   QuantLayout L;
   L.nblocks = (int)ceil_div(n, kBS);
   L.mtiles = (int)ceil_div(m, 128);
   L.nsw = (int)ceil_div(m, kRowsPerWG);
-  // The most partial products any launch writes (at least one buffer row).
+  // The most partial products any launch writes (at least one buffer row);
+  // the group-range products of wide groups use a single split per K range
+  // of the same size, so they fit as well.
   L.smax = 1;
   for (int kb = 1; kb + 1 < L.nblocks; ++kb) {
     const int stages = kb * (kBS / kUK);
@@ -779,87 +887,96 @@ QuantLayout quant_layout(int64_t m, int64_t n, int permuted) {
   const size_t mn = (size_t)m * (size_t)n * sizeof(float);
   L.pstride = (size_t)L.smax * (size_t)m * kBS;   // floats per partial-product buffer
   L.off_E = 0;
-  L.off_Wp = align256(L.off_E + mn);
-  L.off_P = align256(L.off_Wp + (permuted ? mn : 0));
+  L.off_P = align256(L.off_E + mn);
   L.off_Plast = align256(L.off_P + 2 * L.pstride * sizeof(float));
-  L.total = align256(L.off_Plast + (size_t)m * kBS * sizeof(float));
+  L.off_pinv = align256(L.off_Plast + (size_t)m * kBS * sizeof(float));
+  L.off_grange = align256(L.off_pinv + (size_t)n * sizeof(int32_t));
+  L.total = align256(L.off_grange + (size_t)m * 2 * sizeof(float));
   return L;
 }
 
 template <int DT>
 gptq_status launch_block(const void* src, int64_t ld, int m, int n, int kb, const float* U, const float* Pcur,
                          int nsplit, float* Plast, int use_last, int make_next, float maxq, int g, int G,
-                         uint8_t* codes, float* E, float* scales, uint8_t* zeros, float* row_loss, int nsw,
-                         int mtiles, int ngemm, int sps, float* Pnext, hipStream_t st) {
+                         uint8_t* codes, float* E, float* scales, uint8_t* zeros, float* row_loss,
+                         const int32_t* perm, const float* grange, int nsw, int mtiles, int ngemm, int sps,
+                         float* Pnext, hipStream_t st) {
   const int codes_aligned = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
   quant_block_kernel<DT><<<(unsigned)(nsw + ngemm), kThreads, 0, st>>>(
       src, ld, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales, zeros,
-      row_loss, codes_aligned, nsw, mtiles, sps, Pnext);
+      row_loss, codes_aligned, perm, grange, nsw, mtiles, sps, Pnext);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
 
-}  // namespace
-}  // namespace gptq
-
-using namespace gptq;
-
-extern "C" size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int w_dtype, int permuted, int block_size) {
-  (void)w_dtype;
-  (void)block_size;
-  if (m <= 0 || n <= 0) return 0;
-  return quant_layout(m, n, permuted).total;
+// The range of the later blocks of a group that starts at block kb and spans
+// gb blocks, over their values at the group start (into grange).
+template <int DT>
+gptq_status launch_group_range(const void* W, int64_t ldw, const int32_t* perm, int m, int n, int kb, int gb,
+                               const float* E, const float* U, float* Ptmp, int mtiles, int smax, float* grange,
+                               hipStream_t st) {
+  const int c0 = kb * kBS;
+  const int nblocks = (int)ceil_div(n, kBS);
+  bool first = true;
+  for (int b = kb + 1; b < std::min(nblocks, kb + gb); ++b) {
+    const int stages = c0 / kUK;
+    int nsplit = 0;
+    if (stages > 0) {
+      // at most smax splits: Ptmp holds smax partial products
+      const int S = std::min(smax, std::max(1, choose_splits(0, mtiles, stages)));
+      const int sps = (int)ceil_div(stages, S);
+      nsplit = (int)ceil_div(stages, sps);
+      range_gemm_kernel<<<(unsigned)(mtiles * nsplit), kThreads, 0, st>>>(E, U, m, n, b, c0, sps, mtiles, Ptmp);
+      GPTQ_TRY_LAUNCH();
+    }
+    range_reduce_kernel<DT><<<(unsigned)ceil_div(m, 4), 256, 0, st>>>(W, ldw, perm, m, n, b, Ptmp, nsplit,
+                                                                      first ? 1 : 0, grange);
+    GPTQ_TRY_LAUNCH();
+    first = false;
+  }
+  return GPTQ_OK;
 }
 
-extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
-                                           const float* U, const int32_t* perm, int levels, int group_size,
-                                           int block_size, uint8_t* codes, float* scales, uint8_t* zeros,
-                                           float* row_loss, void* ws, size_t ws_bytes, void* stream) {
-  if (m < 0 || n < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
-  if (!(levels == 3 || levels == 4 || levels == 8 || levels == 16)) return GPTQ_ERR_INVALID_ARG;
-  if (group_size < 0 || block_size <= 0) return GPTQ_ERR_INVALID_ARG;
-  if (block_size != kBS) return GPTQ_ERR_UNSUPPORTED;
-  if (!(group_size == 0 || group_size == 16 || group_size == 32 || group_size == 64 || group_size == 128))
-    return GPTQ_ERR_UNSUPPORTED;
-  if (n > (int64_t)1 << 16 || m > ((int64_t)1 << 31) - 1) return GPTQ_ERR_UNSUPPORTED;
-  if (m == 0 || n == 0) return GPTQ_OK;
-  if (W == nullptr || U == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr || ldw < n)
-    return GPTQ_ERR_INVALID_ARG;
-  const QuantLayout L = quant_layout(m, n, perm != nullptr);
-  if (ws == nullptr || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  char* base = static_cast<char*>(ws);
-  float* E = reinterpret_cast<float*>(base + L.off_E);
-  float* Wp = reinterpret_cast<float*>(base + L.off_Wp);
-  float* P = reinterpret_cast<float*>(base + L.off_P);
-  const int mi = (int)m, ni = (int)n;
-  const float maxq = (float)(levels - 1);
-  const int G = group_size == 0 ? 1 : (int)ceil_div(n, group_size);
+template <int DT>
+gptq_status launch_row_grid(const void* W, int64_t ldw, int m, int n, float maxq, float* scales, uint8_t* zeros,
+                            hipStream_t st) {
+  row_grid_kernel<DT><<<(unsigned)ceil_div(m, 4), 256, 0, st>>>(W, ldw, m, n, maxq, scales, zeros);
+  GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}
 
-  const void* src = W;
-  int64_t ld = ldw;
-  int sdt = w_dtype;
-  if (perm != nullptr) {
-    if (w_dtype == GPTQ_F32) permute_w_kernel<GPTQ_F32><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
-    else if (w_dtype == GPTQ_F16) permute_w_kernel<GPTQ_F16><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
-    else permute_w_kernel<GPTQ_BF16><<<(unsigned)m, 256, 0, st>>>(W, ldw, ni, perm, Wp);
-    GPTQ_TRY_LAUNCH();
-    src = Wp;
-    ld = n;
-    sdt = GPTQ_F32;
-  }
-  if (group_size == 0) {
-    const unsigned grid = (unsigned)ceil_div(m, 4);
-    if (w_dtype == GPTQ_F32) row_grid_kernel<GPTQ_F32><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
-    else if (w_dtype == GPTQ_F16) row_grid_kernel<GPTQ_F16><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
-    else row_grid_kernel<GPTQ_BF16><<<grid, 256, 0, st>>>(W, ldw, mi, ni, maxq, scales, zeros);
-    GPTQ_TRY_LAUNCH();
-  }
+template <int DT>
+gptq_status quantize_typed(const void* W, int64_t ldw, int m, int n, const float* U, const int32_t* perm,
+                           int levels, int g, uint8_t* codes, float* scales, uint8_t* zeros, int32_t* g_idx,
+                           float* row_loss, void* Wq, const QuantLayout& L, char* base, hipStream_t st) {
+  float* E = reinterpret_cast<float*>(base + L.off_E);
+  float* P = reinterpret_cast<float*>(base + L.off_P);
   float* Plast = reinterpret_cast<float*>(base + L.off_Plast);
+  int32_t* pinv = reinterpret_cast<int32_t*>(base + L.off_pinv);
+  float* grange = reinterpret_cast<float*>(base + L.off_grange);
+  const float maxq = (float)(levels - 1);
+  const int G = g == 0 ? 1 : (int)ceil_div(n, g);
+
+  if (perm != nullptr || g_idx != nullptr) {
+    index_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>(n, perm, g, perm != nullptr ? pinv : nullptr, g_idx);
+    GPTQ_TRY_LAUNCH();
+  }
+  if (g == 0) {
+    const gptq_status rc = launch_row_grid<DT>(W, ldw, m, n, maxq, scales, zeros, st);
+    if (rc != GPTQ_OK) return rc;
+  }
   int ns_cur = 0;   // partial products of block kb's update, from the previous launch
   for (int kb = 0; kb < L.nblocks; ++kb) {
     const int use_last = kb >= 1;
     const int make_next = kb + 1 < L.nblocks;
+    const float* Pcur = P + (size_t)(kb & 1) * L.pstride;
+    float* Pnext = P + (size_t)((kb + 1) & 1) * L.pstride;
+    if (g > kBS && (kb * kBS) % g == 0 && make_next) {
+      // Pnext is free until this block's launch writes it.
+      const gptq_status rc = launch_group_range<DT>(W, ldw, perm, m, n, kb, g / kBS, E, U, Pnext, L.mtiles,
+                                                    L.smax, grange, st);
+      if (rc != GPTQ_OK) return rc;
+    }
     int ns_next = 0, sps = 0;
     if (make_next && kb >= 1) {
       // Block kb+1's update over columns [0, 128 kb) in ranges of whole 32-column stages.
@@ -868,21 +985,64 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m
       sps = (int)ceil_div(stages, s_target);
       ns_next = (int)ceil_div(stages, sps);
     }
-    const float* Pcur = P + (size_t)(kb & 1) * L.pstride;
-    float* Pnext = P + (size_t)((kb + 1) & 1) * L.pstride;
     const int ngemm = L.mtiles * ns_next;
-    gptq_status rc;
-    if (sdt == GPTQ_F32)
-      rc = launch_block<GPTQ_F32>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size, G,
-                                  codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
-    else if (sdt == GPTQ_F16)
-      rc = launch_block<GPTQ_F16>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size, G,
-                                  codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
-    else
-      rc = launch_block<GPTQ_BF16>(src, ld, mi, ni, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, group_size,
-                                   G, codes, E, scales, zeros, row_loss, L.nsw, L.mtiles, ngemm, sps, Pnext, st);
+    const gptq_status rc = launch_block<DT>(W, ldw, m, n, kb, U, Pcur, ns_cur, Plast, use_last, make_next, maxq, g,
+                                            G, codes, E, scales, zeros, row_loss, perm, grange, L.nsw, L.mtiles,
+                                            ngemm, sps, Pnext, st);
     if (rc != GPTQ_OK) return rc;
     ns_cur = ns_next;
   }
+  if (perm != nullptr || Wq != nullptr) {
+    const size_t shm = perm != nullptr ? (size_t)n : 0;
+    finalize_kernel<DT><<<(unsigned)m, 256, shm, st>>>(codes, n, perm != nullptr ? pinv : nullptr, scales, zeros, g,
+                                                       G, Wq, n);
+    GPTQ_TRY_LAUNCH();
+  }
   return GPTQ_OK;
+}
+
+}  // namespace
+}  // namespace gptq
+
+using namespace gptq;
+
+extern "C" size_t gptq_quantize_ws_bytes(int64_t m, int64_t n, int block_size) {
+  if (m <= 0 || n <= 0 || block_size != kBS) return 0;
+  return quant_layout(m, n).total;
+}
+
+extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                           const float* U, const int32_t* perm, int levels, int group_size,
+                                           int block_size, uint8_t* codes, float* scales, uint8_t* zeros,
+                                           int32_t* g_idx, float* row_loss, void* Wq, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  if (m < 0 || n < 0 || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (!(levels == 3 || levels == 4 || levels == 8 || levels == 16)) return GPTQ_ERR_INVALID_ARG;
+  if (group_size < 0 || block_size <= 0) return GPTQ_ERR_INVALID_ARG;
+  if (block_size != kBS) return GPTQ_ERR_UNSUPPORTED;
+  if (!(group_size == 0 || group_size == 16 || group_size == 32 || group_size == 64 || group_size % kBS == 0))
+    return GPTQ_ERR_UNSUPPORTED;
+  if (n > (int64_t)1 << 16 || m > ((int64_t)1 << 31) - 1) return GPTQ_ERR_UNSUPPORTED;
+  if (n == 0) return GPTQ_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (m == 0) {
+    if (g_idx == nullptr) return GPTQ_OK;
+    index_kernel<<<(unsigned)ceil_div(n, 256), 256, 0, st>>>((int)n, perm, group_size, nullptr, g_idx);
+    GPTQ_TRY_LAUNCH();
+    return GPTQ_OK;
+  }
+  if (W == nullptr || U == nullptr || codes == nullptr || scales == nullptr || zeros == nullptr || ldw < n)
+    return GPTQ_ERR_INVALID_ARG;
+  const QuantLayout L = quant_layout(m, n);
+  if (ws == nullptr || ws_bytes < L.total) return GPTQ_ERR_WORKSPACE;
+  char* base = static_cast<char*>(ws);
+  const int mi = (int)m, ni = (int)n;
+  if (w_dtype == GPTQ_F32)
+    return quantize_typed<GPTQ_F32>(W, ldw, mi, ni, U, perm, levels, group_size, codes, scales, zeros, g_idx,
+                                    row_loss, Wq, L, base, st);
+  if (w_dtype == GPTQ_F16)
+    return quantize_typed<GPTQ_F16>(W, ldw, mi, ni, U, perm, levels, group_size, codes, scales, zeros, g_idx,
+                                    row_loss, Wq, L, base, st);
+  return quantize_typed<GPTQ_BF16>(W, ldw, mi, ni, U, perm, levels, group_size, codes, scales, zeros, g_idx,
+                                   row_loss, Wq, L, base, st);
 }

@@ -98,18 +98,18 @@ def attention(h, Wq, Wk, Wv, shape: DecoderShape, seqs: int, seq_len: int, chunk
     return out.permute(0, 2, 1, 3).reshape(seqs * seq_len, H * D).to(h.dtype)
 
 
-def dequantize(q, perm, group_size: int, dtype):
-    """W^ in the original column order: s_g (c - z_g), formed in float64."""
+def dequantize(q, group_size: int, dtype):
+    """W^ = s_g (c - z_g) in original column order, formed in float64 (exact:
+    a float32 scale times a small integer) from the codes and g_idx."""
     torch = _lib._torch()
     codes = q["codes"].to(torch.float64)
     n = codes.shape[1]
-    gi = torch.zeros(n, dtype=torch.long, device=codes.device) if group_size == 0 else \
-        torch.arange(n, device=codes.device) // group_size
+    if q.get("g_idx") is not None:
+        gi = q["g_idx"].long()
+    else:
+        gi = torch.zeros(n, dtype=torch.long, device=codes.device) if group_size == 0 else \
+            torch.arange(n, device=codes.device) // group_size
     w = q["scales"].to(torch.float64)[:, gi] * (codes - q["zeros"].to(torch.float64)[:, gi])
-    if perm is not None:
-        out = torch.empty_like(w)
-        out[:, perm.long()] = w
-        w = out
     return w.to(dtype)
 
 
@@ -126,8 +126,9 @@ def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, le
     gptq_hessian_accumulate (float32, float16 or bfloat16; default: X's dtype,
     float32 if X is float64).  timer(stage) -> context manager, optional.
 
-    Returns (X_out, results): results[b][name] = dict(codes, scales, zeros,
-    row_loss, perm, packed, g_idx) for block b.
+    Returns (X_out, results): results[b][name] = dict(codes (original column
+    order), scales, zeros, g_idx, row_loss, Wq (or None), perm, packed) for
+    block b.
     """
     torch = _lib._torch()
     if h_dtype is None:
@@ -155,14 +156,18 @@ def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, le
             U, perm = _lib.gptq_prepare_hinv(H, damp_rel, act_order)
         return U, (perm if act_order else None)
 
+    # The forward runs on the library's dequantized weights (Wq, in W's dtype)
+    # when it runs in that dtype; a float64 forward (validation) forms them
+    # exactly from the codes.
     def quant(W, U, perm):
+        exact = cdt != W.dtype
         with stage("quantize"):
-            q = _lib.gptq_quantize_layer(W, U, perm, levels, group_size, 128)
+            q = _lib.gptq_quantize_layer(W, U, perm, levels, group_size, 128, want_wq=not exact)
         with stage("pack"):
-            packed, g_idx = _lib.gptq_pack(q["codes"], perm, bits, group_size)
-        q.update(perm=perm, packed=packed, g_idx=g_idx)
+            packed = _lib.gptq_pack(q["codes"], bits)
+        q.update(perm=perm, packed=packed)
         with stage("forward"):
-            What = dequantize(q, perm, group_size, cdt)
+            What = dequantize(q, group_size, cdt) if exact else q["Wq"]
         return q, What
 
     results = []

@@ -31,6 +31,24 @@ def host(t):
     return t.cpu().numpy()
 
 
+def processing_order(codes, perm):
+    """Codes in original column order (as gptq_quantize_layer returns them)
+    re-indexed by processing position: column j is original column perm[j]."""
+    codes = np.asarray(codes)
+    return codes if perm is None else codes[:, np.asarray(perm, dtype=np.int64)]
+
+
+def expected_wq(codes_orig, scales, zeros, g_idx, dtype):
+    """fl_w(fl32(s (c - z))) of each original column, in storage bit patterns
+    (bf16 as uint16), from a result's own codes, scales, zeros and g_idx."""
+    import workloads as wl
+    gi = np.asarray(g_idx, dtype=np.int64)
+    s = np.asarray(scales, dtype=np.float32)[:, gi]
+    cz = (np.asarray(codes_orig, dtype=np.float32) - np.asarray(zeros, dtype=np.float32)[:, gi])
+    v = (s * cz).astype(np.float32)
+    return wl.to_storage(v, dtype).raw
+
+
 def rel_fro(a, b):
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)

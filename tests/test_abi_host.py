@@ -54,9 +54,12 @@ def test_workspace_queries(lib):
     assert ws % (136 * 256 * 256 * 4) == 0 and ws // (136 * 256 * 256 * 4) >= 8
     assert lib.gptq_prepare_ws_bytes(0) == 0
     assert lib.gptq_prepare_ws_bytes(100) >= 2 * 128 * 128 * 8
-    q = lib.gptq_quantize_ws_bytes(4096, 4096, 2, 0, 128)
-    assert q >= 4096 * 4096 * 4
-    assert lib.gptq_quantize_ws_bytes(4096, 4096, 2, 1, 128) >= q + 4096 * 4096 * 4
+    q = lib.gptq_quantize_ws_bytes(4096, 4096, 128)
+    assert q >= 4096 * 4096 * 4                       # the scaled errors E
+    assert lib.gptq_quantize_ws_bytes(4096, 4096, 64) == 0
+    assert lib.gptq_quantize_ws_bytes(0, 4096, 128) == 0
+    # no permuted copy of W: the workspace stays within E plus O(m + n) x 128 terms
+    assert lib.gptq_quantize_ws_bytes(49152, 12288, 128) < 49152 * 12288 * 4 * 1.1
 
 
 @pytest.mark.parametrize("dt", [0, 1, 2])
@@ -132,18 +135,22 @@ def test_quantize_argument_errors(lib):
 
     def call(**kw):
         a = dict(W=_fake(), dt=2, m=64, n=256, ldw=256, U=_fake(), perm=_null(), levels=16, group=128,
-                 block=128, codes=_fake(), scales=_fake(), zeros=_fake(), loss=_null(), ws=_fake(),
-                 wsb=1 << 40)
+                 block=128, codes=_fake(), scales=_fake(), zeros=_fake(), gidx=_null(), loss=_null(), wq=_null(),
+                 ws=_fake(), wsb=1 << 40)
         a.update(kw)
         return f(a["W"], a["dt"], a["m"], a["n"], a["ldw"], a["U"], a["perm"], a["levels"], a["group"],
-                 a["block"], a["codes"], a["scales"], a["zeros"], a["loss"], a["ws"], a["wsb"], _null())
+                 a["block"], a["codes"], a["scales"], a["zeros"], a["gidx"], a["loss"], a["wq"], a["ws"], a["wsb"],
+                 _null())
 
     for lv in (0, 1, 2, 5, 15, 17, 32):
         assert call(levels=lv) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(dt=5) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(group=-1) == _lib.GPTQ_ERR_INVALID_ARG
-    for g in (8, 24, 48, 256):
+    for g in (8, 24, 48, 96, 200, 320):
         assert call(group=g) == _lib.GPTQ_ERR_UNSUPPORTED
+    # groups that are multiples of the block pass validation (workspace checked next)
+    for g in (256, 384, 1024):
+        assert call(group=g, wsb=16) == _lib.GPTQ_ERR_WORKSPACE
     assert call(block=64) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ldw=255) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(W=_null()) == _lib.GPTQ_ERR_INVALID_ARG
@@ -158,11 +165,13 @@ def test_quantize_argument_errors(lib):
 def test_pack_argument_errors(lib):
     f = lib.gptq_pack
     for b in (0, 1, 5, 8):
-        assert f(_fake(), 4, 64, _null(), b, 0, _fake(), 64, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
-    assert f(_fake(), 4, 64, _null(), 4, -1, _fake(), 64, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
-    assert f(_fake(), 4, 64, _null(), 4, 0, _fake(), 7, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
-    assert f(_null(), 4, 64, _null(), 4, 0, _fake(), 8, _null(), _null()) == _lib.GPTQ_ERR_INVALID_ARG
-    assert f(_fake(), 4, 0, _null(), 4, 0, _fake(), 8, _null(), _null()) == _lib.GPTQ_OK
+        assert f(_fake(), 4, 64, b, _fake(), 64, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), -4, 64, 4, _fake(), 64, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 4, 64, 4, _fake(), 7, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_null(), 4, 64, 4, _fake(), 8, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 4, 64, 4, _null(), 8, _null()) == _lib.GPTQ_ERR_INVALID_ARG
+    assert f(_fake(), 4, 0, 4, _fake(), 8, _null()) == _lib.GPTQ_OK
+    assert f(_fake(), 0, 64, 4, _fake(), 8, _null()) == _lib.GPTQ_OK
 
 
 def test_lowrank_argument_errors(lib):

@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import certify_ties, host, log, rel_fro
+from tests.gpu_util import certify_ties, host, log, processing_order, rel_fro
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def test_decoder_pass_parity(g, levels, group, act):
             qg, qo = rg[b][name], ro[b][name]
             if act:
                 np.testing.assert_array_equal(host(qg["perm"]), qo["perm"])
-            cg = host(qg["codes"]).astype(np.int64)
+            cg = processing_order(host(qg["codes"]), qo["perm"]).astype(np.int64)
             co = qo["codes"].astype(np.int64)
             rows, ties = certify_ties(qo["W"], qo["U"], qo["perm"], levels, group, 128, cg, co)
             ties_total += ties

@@ -23,7 +23,7 @@ def g(gpu_lib):
 
 
 def _layer(m, n, bits, group, act, seed, ld_extra=0):
-    """Seeded packed layer: codes, per-group scales/zeros, g_idx as gptq_pack gives it."""
+    """Seeded packed layer: codes, per-group scales/zeros, g_idx as gptq_quantize_layer gives it."""
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, 31])))
     maxq = (1 << bits) - 1
     codes = rng.integers(0, maxq + 1, size=(m, n), dtype=np.int64)

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import oracle
-from tests.gpu_util import certify_ties, dev, host, log
+from tests.gpu_util import certify_ties, dev, host, log, processing_order
 
 pytestmark = pytest.mark.gpu
 
@@ -107,9 +107,11 @@ def test_lowrank_compensation_parity(g, m, n, r, levels, group, act, wdt):
     L = np.linalg.qr(rng.standard_normal((n, r)))[0]
     _, K = oracle.lowrank_hessian(H, L)
     res = _quantized(W.f32, H, levels, group, act)
-    q = {"codes": dev(res["codes"], "u8"), "scales": dev(res["scales"]), "zeros": dev(res["zeros"], "u8")}
-    perm = dev(res["perm"], "i32") if act else None
-    R = host(g.gptq_lowrank_compensation(stored_to_dev(W), q, _d64(K), perm, group))
+    # codes in original column order with each column's group, as gptq_quantize_layer returns them
+    q = {"codes": dev(oracle.unpermute_codes(res["codes"], res["perm"]), "u8"), "scales": dev(res["scales"]),
+         "zeros": dev(res["zeros"], "u8"),
+         "g_idx": dev(oracle.group_index(res["perm"], group), "i32") if act else None}
+    R = host(g.gptq_lowrank_compensation(stored_to_dev(W), q, _d64(K), group))
     torch.cuda.synchronize()
     Ro = oracle.lowrank_compensation(W.f32.astype(np.float64), res["What"], K)
     D = np.abs(W.f32.astype(np.float64) - res["What"])
@@ -148,7 +150,7 @@ def test_lora_layer_parity(g, levels, group, act, rank, via):
     torch.cuda.synchronize()
     if act:
         np.testing.assert_array_equal(host(q["perm"]), ro["perm"])
-    cg = host(q["codes"]).astype(np.int64)
+    cg = processing_order(host(q["codes"]), ro["perm"]).astype(np.int64)
     rows, ties = certify_ties(W.astype(np.float64), ro["U"], ro["perm"], levels, group, 128, cg, ro["codes"])
     log(f"  rows differing {rows}, ties {ties}")
     Wh = oracle.dequantize(dict(codes=cg.astype(np.float32), scales=host(q["scales"]), zeros=host(q["zeros"]),

@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.gpu_util import certify_ties, code_mismatch, dev, host, log, rel_fro, stored_to_dev
+from tests.gpu_util import expected_wq, processing_order, certify_ties, code_mismatch, dev, host, log, rel_fro, stored_to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -143,9 +143,16 @@ def _quant_case(m, n, dtype, levels, group, act, seed, law="correlated"):
     return W, H, perm, U32
 
 
-def _check_quant(q, res, W64, H, label, allow_frac=1e-4, U64=None, perm=None):
-    codes_g = host(q["codes"]).astype(np.int64)
+def _check_quant(q, res, W64, H, label, allow_frac=1e-4, U64=None, perm=None, w_dtype=None):
+    codes_orig = host(q["codes"])
+    codes_g = processing_order(codes_orig, res["perm"]).astype(np.int64)
     codes_o = res["codes"].astype(np.int64)
+    gidx_o = oracle.group_index(res["perm"], res["group_size"])
+    if q.get("g_idx") is not None:
+        np.testing.assert_array_equal(host(q["g_idx"]), gidx_o)
+    if q.get("Wq") is not None:
+        np.testing.assert_array_equal(host(q["Wq"]), expected_wq(codes_orig, host(q["scales"]), host(q["zeros"]),
+                                                                 gidx_o, w_dtype))
     mism, total = code_mismatch(codes_g, codes_o)
     if mism > allow_frac * total and U64 is not None:
         # every split must be a certified rounding tie (see certify_ties)
@@ -183,6 +190,12 @@ QUANT_CASES = [
     (1, 128, "bf16", 16, 0, False),
     (1024, 1024, "bf16", 16, 128, False),
     (512, 1536, "bf16", 8, 128, True),
+    # groups wider than the 128-column block: their range is taken over the
+    # current values of all their columns at the group start
+    (300, 640, "bf16", 16, 256, True),
+    (129, 1000, "f32", 8, 512, False),
+    (64, 384, "f16", 4, 384, False),
+    (70, 520, "bf16", 3, 256, False),
 ]
 
 
@@ -191,10 +204,10 @@ def test_quantize_parity(g, m, n, dtype, levels, group, act):
     log(f"quantize m={m} n={n} {dtype} levels={levels} g={group} act={act}")
     W, H, perm, U32 = _quant_case(m, n, dtype, levels, group, act, seed=300 + m + n)
     q = g.gptq_quantize_layer(stored_to_dev(W), dev(U32), dev(perm, "i32") if act else None,
-                              levels, group)
+                              levels, group, want_wq=True)
     W64 = W.f32.astype(np.float64)
     res = oracle.gptq_quantize(W64, U32.astype(np.float64), perm, levels, group, block_size=128)
-    _check_quant(q, res, W64, H, "codes", U64=U32.astype(np.float64), perm=perm)
+    _check_quant(q, res, W64, H, "codes", U64=U32.astype(np.float64), perm=perm, w_dtype=dtype)
 
 
 @pytest.mark.parametrize("levels,group,act,dtype", [(16, 0, False, "f32"), (16, 128, True, "bf16"),
@@ -213,9 +226,12 @@ def test_diagonal_hessian_is_rtn_bit_exact(g, levels, group, act, dtype):
     g.gptq_hessian_accumulate(H, stored_to_dev(X), 2.0, reset=True)
     U, perm = g.gptq_prepare_hinv(H, 0.01, act)
     np.testing.assert_array_equal(host(perm), np.arange(n))
-    q = g.gptq_quantize_layer(stored_to_dev(W), U, perm if act else None, levels, group)
+    q = g.gptq_quantize_layer(stored_to_dev(W), U, perm if act else None, levels, group, want_wq=True)
     rtn = oracle.rtn_quantize(W.f32.astype(np.float64), levels, group)
     np.testing.assert_array_equal(host(q["codes"]), rtn["codes"].astype(np.uint8))
+    np.testing.assert_array_equal(host(q["g_idx"]), oracle.group_index(np.arange(n), group))
+    np.testing.assert_array_equal(host(q["Wq"]), expected_wq(rtn["codes"], rtn["scales"], rtn["zeros"],
+                                                             oracle.group_index(np.arange(n), group), dtype))
     np.testing.assert_array_equal(host(q["scales"]), rtn["scales"])
     np.testing.assert_array_equal(host(q["zeros"]), rtn["zeros"].astype(np.uint8))
     # Non-constant diagonal with act-order: RTN in processing-order groups.
@@ -225,24 +241,34 @@ def test_diagonal_hessian_is_rtn_bit_exact(g, levels, group, act, dtype):
     np.testing.assert_array_equal(host(perm2), po)
     q2 = g.gptq_quantize_layer(stored_to_dev(W), U2, perm2, levels, group)
     rtn2 = oracle.rtn_quantize(W.f32.astype(np.float64), levels, group, perm=po)
-    np.testing.assert_array_equal(host(q2["codes"]), rtn2["codes"].astype(np.uint8))
+    np.testing.assert_array_equal(host(q2["codes"]), oracle.unpermute_codes(rtn2["codes"], po).astype(np.uint8))
     np.testing.assert_array_equal(host(q2["scales"]), rtn2["scales"])
+    np.testing.assert_array_equal(host(q2["g_idx"]), oracle.group_index(po, group))
 
 
 # ---------------------------------------------------------------------------
 # Stage 4: pack
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("bits,n,act,group", [(4, 256, False, 0), (3, 300, True, 32), (2, 97, True, 16),
-                                              (4, 1000, True, 128), (2, 64, False, 64)])
-def test_pack_parity(g, bits, n, act, group):
+@pytest.mark.parametrize("bits,n,m", [(4, 256, 37), (3, 300, 37), (2, 97, 37), (4, 1000, 5), (2, 64, 1),
+                                      (4, 4096, 300), (3, 96, 3)])
+def test_pack_parity(g, bits, n, m):
     rng = np.random.default_rng(bits * 1000 + n)
-    m = 37
     codes = rng.integers(0, 1 << bits, size=(m, n)).astype(np.uint8)
-    perm = rng.permutation(n) if act else np.arange(n)
-    packed, gidx = g.gptq_pack(dev(codes, "u8"), dev(perm, "i32") if act else None, bits, group)
-    ref = oracle.pack_codes(oracle.unpermute_codes(codes, perm), bits)
-    np.testing.assert_array_equal(host(packed).view(np.uint32), ref)
-    np.testing.assert_array_equal(host(gidx), oracle.group_index(perm, group))
+    packed = g.gptq_pack(dev(codes, "u8"), bits)
+    np.testing.assert_array_equal(host(packed).view(np.uint32), oracle.pack_codes(codes, bits))
+
+
+def test_pack_padded_rows(g):
+    import torch
+    rng = np.random.default_rng(8)
+    m, n, bits = 9, 200, 4
+    codes = rng.integers(0, 16, size=(m, n)).astype(np.uint8)
+    nw = g.packed_words(n, bits)
+    buf = torch.full((m, nw + 3), -1, dtype=torch.int32, device="cuda")   # ld_packed > words per row
+    g.gptq_pack(dev(codes, "u8"), bits, packed=buf[:, :nw])
+    out = host(buf).view(np.uint32)
+    np.testing.assert_array_equal(out[:, :nw], oracle.pack_codes(codes, bits))
+    assert np.all(out[:, nw:] == 0xFFFFFFFF)          # words beyond the row are not written
 
 
 # ---------------------------------------------------------------------------
@@ -262,7 +288,7 @@ def test_end_to_end_single_linear_256(g):
                             damp_rel=cfg.damp_rel, act_order=cfg.act_order)
     assert rel_fro(host(q["H"]), res["H"]) <= 1e-5
     _check_quant(q, res, W64, res["H"], "e2e")
-    same = ~np.any(host(q["codes"]).astype(np.int64) != res["codes"], axis=1)
+    same = ~np.any(processing_order(host(q["codes"]), res["perm"]).astype(np.int64) != res["codes"], axis=1)
     np.testing.assert_array_equal(host(q["packed"]).view(np.uint32)[same], res["packed"][same])
 
 
@@ -285,12 +311,14 @@ def test_results_do_not_depend_on_workspace_contents(g):
         wsp = torch.full((int(lib.gptq_prepare_ws_bytes(n)),), fill, dtype=torch.uint8, device="cuda")
         U, perm = g.gptq_prepare_hinv(H, 0.01, True, ws=wsp)
         W = stored_to_dev(wl.gaussian_w(m, n, 77, 0.02, "bf16"))
-        wsq = torch.full((int(lib.gptq_quantize_ws_bytes(m, n, 2, 1, 128)),), fill, dtype=torch.uint8,
+        wsq = torch.full((int(lib.gptq_quantize_ws_bytes(m, n, 128)),), fill, dtype=torch.uint8,
                          device="cuda")
-        q = g.gptq_quantize_layer(W, U, perm, 16, 32, 128, ws=wsq)
+        q = g.gptq_quantize_layer(W, U, perm, 16, 32, 128, want_wq=True, ws=wsq)
+        q256 = g.gptq_quantize_layer(W, U, perm, 16, 256, 128, ws=wsq)
         torch.cuda.synchronize()
         runs.append([host(H), host(U), host(perm), host(q["codes"]), host(q["scales"]), host(q["zeros"]),
-                     host(q["row_loss"])])
+                     host(q["row_loss"]), host(q["Wq"]), host(q["g_idx"]), host(q256["codes"]),
+                     host(q256["scales"])])
     for a, b in zip(*runs):
         np.testing.assert_array_equal(a, b)
     assert np.all(np.isfinite(runs[0][1])) and np.all(np.isfinite(runs[0][6]))

@@ -1,19 +1,20 @@
 """Parity at the full sizes of the named workloads, in the launch
-configuration the benchmark times: the whole calibration set in one Hessian
-call, the whole layer in one prepare, quantize and pack call.
-
-The fp64 oracle cannot form a 12288-wide Hessian over 262144 tokens in
-seconds, so each stage is checked on outputs it can compute one by one:
+configuration the benchmark times (the whole calibration set in one Hessian
+call, the whole layer in one prepare, quantize and pack call), with the GPU
+stages chained: GPU H -> GPU prepare -> GPU sweep -> GPU pack.  Each stage
+is compared with the oracle run on the GPU's own upstream output, on what the
+float64 oracle can compute in seconds:
 
 * Hessian over all tokens: sampled rows of H, fp64, streamed over tokens.
-* prepare: H_s, the oracle Hessian of the first 16384 tokens rounded to fp32,
-  is fed to both sides; U is compared whole, the permutation exactly.
-* quantize: both sides take the oracle's U (fp32) and permutation; the GPU
-  quantizes every row, the oracle a seeded sample of rows (rows are
-  independent given U, so the sample's results are exactly the full
-  layer's results for those rows).
-* pack: sampled rows whose codes equal the oracle's are compared with the
-  oracle's packing of its own codes; g_idx whole.
+* prepare: the oracle factors the GPU's float32 H; U is compared whole, the
+  permutation exactly.
+* quantize: the GPU quantizes every row with its own U; the oracle runs its
+  sweep on a seeded sample of rows with its own U from the same H (rows are
+  independent given U, so the sample's results are exactly the full layer's
+  results for those rows).  Rows that split from the oracle are certified as
+  rounding ties against the oracle's sweep on the GPU's U (whose distance to
+  the oracle's U is checked above).
+* outputs: g_idx whole; Wq and the packed words on the sampled rows.
 """
 import time
 
@@ -22,14 +23,14 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.gpu_util import certify_ties, code_mismatch, dev, host, log, rel_fro, stored_to_dev
+from tests.gpu_util import (certify_ties, code_mismatch, dev, expected_wq, host, log, processing_order,
+                             rel_fro, stored_to_dev)
 
 pytestmark = pytest.mark.gpu
 
 F32 = np.float32
 H_ROWS = 48            # sampled rows of H
 Q_ROWS = 48            # sampled rows of W for the oracle sweep
-SUB_TOKENS = 16384     # tokens of the oracle Hessian fed to prepare/quantize
 
 LAYERS = [(2, 0), (3, 0), (3, 1), (4, 0), (4, 1)]
 
@@ -78,39 +79,37 @@ def test_full_size_layer(g, config, layer):
     err_h = rel_fro(Hg_rows, Ho_rows)
     log(f"  H rows rel_fro={err_h:.3e} ({time.perf_counter() - t_start:.0f}s)")
     assert err_h <= 1e-5
-    del H
 
-    # --- prepare on the oracle's Hessian of a token prefix ---------------------
-    Hs32 = oracle.hessian(wl.Stored(X.raw[:SUB_TOKENS], X.dtype).f32).astype(F32)
+    # --- prepare on the GPU's Hessian (both sides) -----------------------------
+    Hg32 = host(H)
     del X
-    Hs = Hs32.astype(np.float64)
+    Hs = Hg32.astype(np.float64)
     perm_o = oracle.act_order_perm(Hs) if cfg.act_order else np.arange(n)
     Hd, _ = oracle.damp_and_permute(Hs, perm_o, cfg.damp_rel)
     U_o = oracle.inverse_cholesky_upper(Hd)
     del Hd
-    U_g, perm_g = g.gptq_prepare_hinv(dev(Hs32), cfg.damp_rel, cfg.act_order)
+    U_g, perm_g = g.gptq_prepare_hinv(H, cfg.damp_rel, cfg.act_order)
+    del H
     np.testing.assert_array_equal(host(perm_g), perm_o)
-    Ug = host(U_g).astype(np.float64)
-    del U_g
-    assert np.all(np.tril(Ug, -1) == 0)
-    err_u = rel_fro(Ug, U_o)
-    log(f"  U rel_fro={err_u:.3e} ({time.perf_counter() - t_start:.0f}s)")
+    Ug64 = host(U_g).astype(np.float64)
+    assert np.all(np.tril(Ug64, -1) == 0)
+    err_u = rel_fro(Ug64, U_o)
+    log(f"  U (from the GPU's H) rel_fro={err_u:.3e} ({time.perf_counter() - t_start:.0f}s)")
     assert err_u <= 1e-5
-    del Ug
 
-    # --- quantize every row with the oracle's U; oracle on sampled rows --------
-    U32 = U_o.astype(F32)
-    del U_o
+    # --- quantize every row with the GPU's U; oracle chain on sampled rows -----
     act = cfg.act_order
-    perm_d = dev(perm_o, "i32") if act else None
-    q = g.gptq_quantize_layer(stored_to_dev(L.W), dev(U32), perm_d, cfg.levels, cfg.group_size,
-                              cfg.block_size)
+    perm_d = perm_g if act else None
+    q = g.gptq_quantize_layer(stored_to_dev(L.W), U_g, perm_d, cfg.levels, cfg.group_size, cfg.block_size,
+                              want_wq=True)
+    torch.cuda.synchronize()
+    del U_g
     qrows = np.sort(rng.choice(m, Q_ROWS, replace=False))
     W64 = L.W.f32[qrows].astype(np.float64)
-    res = oracle.gptq_quantize(W64, U32.astype(np.float64), perm_o, cfg.levels, cfg.group_size,
-                               block_size=cfg.block_size)
+    res = oracle.gptq_quantize(W64, U_o, perm_o, cfg.levels, cfg.group_size, block_size=cfg.block_size)
     qr = torch.from_numpy(qrows).cuda()
-    codes_g = host(q["codes"][qr]).astype(np.int64)
+    codes_orig = host(q["codes"][qr])
+    codes_g = processing_order(codes_orig, perm_o).astype(np.int64)
     codes_o = res["codes"].astype(np.int64)
     mism, total = code_mismatch(codes_g, codes_o)
     same = ~np.any(codes_g != codes_o, axis=1)
@@ -123,15 +122,15 @@ def test_full_size_layer(g, config, layer):
     lo = oracle.layer_loss(W64, oracle.dequantize(res), Hs)
     rlg = host(q["row_loss"][qr])
     rl_err = float(np.max(np.abs(rlg[same] - res["row_loss"][same]) / res["row_loss"][same])) if same.any() else 0.0
-    log(f"  codes mismatch {mism}/{total} (rows {int((~same).sum())}) scale_err {s_err:.2e} "
+    log(f"  codes mismatch vs the oracle chain {mism}/{total} (rows {int((~same).sum())}) scale_err {s_err:.2e} "
         f"loss gpu/oracle {lg / lo:.6f} row_loss_err {rl_err:.2e} ({time.perf_counter() - t_start:.0f}s)")
     if mism > 1e-4 * total:
-        # every split must be a certified rounding tie (see certify_ties)
-        nrows, ties = certify_ties(W64, U32.astype(np.float64), perm_o, cfg.levels, cfg.group_size,
-                                   cfg.block_size, codes_g, codes_o)
-        log(f"  {mism} codes in {nrows} rows follow {ties} certified rounding ties")
+        # every split must be a certified rounding tie of the sweep on the GPU's U
+        nrows, ties = certify_ties(W64, Ug64, perm_o, cfg.levels, cfg.group_size, cfg.block_size, codes_g, codes_o)
+        log(f"  {mism} codes in {nrows} rows: {ties} certified rounding ties of the sweep on the GPU's U")
     else:
         assert mism <= 1e-4 * total
+    del Ug64
     assert s_err <= 1e-5
     assert np.array_equal(zg[same], zo[same])
     assert abs(lg / lo - 1) <= 1e-3
@@ -139,12 +138,16 @@ def test_full_size_layer(g, config, layer):
     # every row of the GPU result is in range and finite
     assert int(q["codes"].max().item()) <= cfg.levels - 1
     assert bool(torch.isfinite(q["scales"]).all().item()) and bool(torch.isfinite(q["row_loss"]).all().item())
+    # g_idx whole; Wq from the sampled rows' own codes, scales and zeros
+    gidx_o = oracle.group_index(perm_o, cfg.group_size)
+    np.testing.assert_array_equal(host(q["g_idx"]), gidx_o)
+    np.testing.assert_array_equal(host(q["Wq"][qr]), expected_wq(codes_orig, sg, zg, gidx_o, cfg.dtype))
 
     # --- pack the whole layer --------------------------------------------------
     bits = _bits(cfg.levels)
-    packed, gidx = g.gptq_pack(q["codes"], perm_d, bits, cfg.group_size)
-    np.testing.assert_array_equal(host(gidx), oracle.group_index(perm_o, cfg.group_size))
+    packed = g.gptq_pack(q["codes"], bits)
     ref = oracle.pack_codes(oracle.unpermute_codes(res["codes"], perm_o), bits)
     pk = host(packed[qr]).view(np.uint32)
     np.testing.assert_array_equal(pk[same], ref[same])
+    np.testing.assert_array_equal(pk, oracle.pack_codes(codes_orig, bits))
     log(f"  done in {time.perf_counter() - t_start:.0f}s")

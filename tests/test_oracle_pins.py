@@ -348,6 +348,34 @@ def test_block_size_and_update_order_invariance(levels, group, act):
         np.testing.assert_allclose(r["E"], r1["E"], rtol=1e-9, atol=1e-12)
 
 
+@pytest.mark.parametrize("levels,group,act", [(16, 64, False), (8, 96, True), (4, 64, True)])
+def test_groups_wider_than_the_block(levels, group, act):
+    """Groups spanning several blocks take their range from the current values
+    of all their columns at the group start: B = 1 (the unblocked definition),
+    right-looking B = 32 and left-looking B = 32 agree."""
+    rng = _rng(44)
+    n, m = 200, 25
+    X = rng.standard_normal((4 * n, n)) @ (np.eye(n) + 0.3 * rng.standard_normal((n, n)))
+    W = rng.standard_normal((m, n)) * 0.05
+    H = oracle.hessian(X)
+    perm = oracle.act_order_perm(H) if act else np.arange(n)
+    Hd, _ = oracle.damp_and_permute(H, perm, 0.01)
+    U = oracle.inverse_cholesky_upper(Hd)
+    r1 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=1)
+    r2 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=32, order="right")
+    r3 = oracle.gptq_quantize(W, U, perm, levels, group, block_size=32, order="left")
+    assert r1["scales"].shape[1] == -(-n // group)
+    for r in (r2, r3):
+        np.testing.assert_array_equal(r["codes"], r1["codes"])
+        np.testing.assert_array_equal(r["scales"], r1["scales"])
+        np.testing.assert_allclose(r["E"], r1["E"], rtol=1e-9, atol=1e-12)
+    # A group statistic taken before the earlier corrections reach the group's
+    # later columns would differ: with U diagonal the range of a whole group
+    # is that of the original weights (RTN), here it is not.
+    rtn = oracle.rtn_quantize(W, levels, group, perm=perm)
+    assert not np.array_equal(rtn["scales"][:, 1:], r1["scales"][:, 1:])
+
+
 def test_hessian_scale_invariance_and_row_independence():
     rng = _rng(41)
     n, m = 48, 20
