@@ -118,7 +118,7 @@ def dequantize(q, group_size: int, dtype):
 # ---------------------------------------------------------------------------
 def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, levels: int = 4,
                      group_size: int = 64, act_order: bool = False, damp_rel: float = 0.01,
-                     h_dtype=None, timer=None):
+                     h_dtype=None, timer=None, keep_inputs: bool = False):
     """Quantizes every linear layer of every block in order.
 
     X: tokens x d_model calibration inputs of the first block (the dtype the
@@ -128,7 +128,8 @@ def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, le
 
     Returns (X_out, results): results[b][name] = dict(codes (original column
     order), scales, zeros, g_idx, row_loss, Wq (or None), perm, packed) for
-    block b.
+    block b; with keep_inputs also the layer input as handed to the Hessian
+    call ("X_in"), the Hessian ("H") and the factor ("U").
     """
     torch = _lib._torch()
     if h_dtype is None:
@@ -147,13 +148,18 @@ def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, le
     def stage(name):
         return timer(name) if timer is not None else _Null()
 
+    kept = {}
+
     def factor(inp):
         n = inp.shape[1]
         H = torch.empty((n, n), dtype=torch.float32, device=dev)
+        X_in = inp.to(h_dtype).contiguous()
         with stage("hessian"):
-            _lib.gptq_hessian_accumulate(H, inp.to(h_dtype).contiguous(), 2.0, True)
+            _lib.gptq_hessian_accumulate(H, X_in, 2.0, True)
         with stage("prepare"):
             U, perm = _lib.gptq_prepare_hinv(H, damp_rel, act_order)
+        if keep_inputs:
+            kept.update(X_in=X_in, H=H, U=U)
         return U, (perm if act_order else None)
 
     # The forward runs on the library's dequantized weights (Wq, in W's dtype)
@@ -165,7 +171,7 @@ def quantize_decoder(blocks, X, shape: DecoderShape, seqs: int, seq_len: int, le
             q = _lib.gptq_quantize_layer(W, U, perm, levels, group_size, 128, want_wq=not exact)
         with stage("pack"):
             packed = _lib.gptq_pack(q["codes"], bits)
-        q.update(perm=perm, packed=packed)
+        q.update(perm=perm, packed=packed, **kept)
         with stage("forward"):
             What = dequantize(q, group_size, cdt) if exact else q["Wq"]
         return q, What

@@ -130,11 +130,12 @@ def sweep_sigma(W64, U64, perm, res):
     return np.sqrt(np.maximum(var.T, 0.0))
 
 
-def certify_ties(W64, U64, perm, levels, group, block, codes_gpu, codes_oracle, max_rows=16):
+def certify_ties(W64, U64, perm, levels, group, block, codes_gpu, codes_oracle, max_rows=16, branches=None):
     """Returns (rows_checked, ties) for the rows where codes differ; raises
     AssertionError when a split is not at a near-tie, when the GPU's code is
     not adjacent to the tie, or when the forced oracle does not converge to
-    the GPU's row."""
+    the GPU's row.  With a dict `branches`, branches[r] receives the oracle's
+    result for row r on the GPU's branch (its codes equal the GPU's row)."""
     import oracle
     codes_gpu = np.asarray(codes_gpu).astype(np.int64)
     codes_oracle = np.asarray(codes_oracle).astype(np.int64)
@@ -153,6 +154,8 @@ def certify_ties(W64, U64, perm, levels, group, block, codes_gpu, codes_oracle, 
                                        record_inputs=True, forced=forced)
             diff = np.nonzero(res["codes"][0].astype(np.int64) != codes_gpu[r])[0]
             if diff.size == 0:
+                if branches is not None:
+                    branches[int(r)] = res
                 break
             j = int(diff[0])
             gi = 0 if group == 0 else j // group
@@ -172,3 +175,13 @@ def certify_ties(W64, U64, perm, levels, group, block, codes_gpu, codes_oracle, 
         else:
             raise AssertionError(f"row {r}: more than {MAX_TIES_PER_ROW} ties")
     return int(rows.size), ties
+
+
+def on_gpu_branches(res, branches):
+    """The oracle result `res` (rows x n, processing order) with each row r in
+    `branches` replaced by the oracle's result on the GPU's branch."""
+    out = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in res.items()}
+    for r, b in branches.items():
+        for key in ("codes", "scales", "zeros", "E", "row_loss"):
+            out[key][r] = b[key][0]
+    return out

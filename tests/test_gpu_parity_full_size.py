@@ -23,8 +23,8 @@ import pytest
 
 import oracle
 import workloads as wl
-from tests.gpu_util import (certify_ties, code_mismatch, dev, expected_wq, host, log, processing_order,
-                             rel_fro, stored_to_dev)
+from tests.gpu_util import (certify_ties, code_mismatch, dev, expected_wq, host, log, on_gpu_branches,
+                             processing_order, rel_fro, stored_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -112,6 +112,24 @@ def test_full_size_layer(g, config, layer):
     codes_g = processing_order(codes_orig, perm_o).astype(np.int64)
     codes_o = res["codes"].astype(np.int64)
     mism, total = code_mismatch(codes_g, codes_o)
+    log(f"  codes mismatch vs the oracle chain {mism}/{total} (rows {int(np.any(codes_g != codes_o, axis=1).sum())})")
+    # Rows that split: every split must be a certified rounding tie of the
+    # sweep on the GPU's U (above the 1e-4 share the certificate is required
+    # for the bar to hold); scales, zeros, losses are then compared with the
+    # oracle on the GPU's branch.
+    branches = {}
+    try:
+        nrows, ties = certify_ties(W64, Ug64, perm_o, cfg.levels, cfg.group_size, cfg.block_size, codes_g,
+                                   codes_o, branches=branches)
+        if nrows:
+            log(f"  {mism} codes in {nrows} rows: {ties} certified rounding ties of the sweep on the GPU's U")
+    except AssertionError as e:
+        # within the mismatch bar an uncertified split is allowed (and logged)
+        log(f"  uncertified split within the 1e-4 bar: {e}")
+        assert mism <= 1e-4 * total
+        branches = {}
+    res = on_gpu_branches(res, branches)
+    codes_o = res["codes"].astype(np.int64)
     same = ~np.any(codes_g != codes_o, axis=1)
     sg, so = host(q["scales"][qr]), res["scales"]
     zg, zo = host(q["zeros"][qr]).astype(np.int64), res["zeros"].astype(np.int64)
@@ -122,14 +140,9 @@ def test_full_size_layer(g, config, layer):
     lo = oracle.layer_loss(W64, oracle.dequantize(res), Hs)
     rlg = host(q["row_loss"][qr])
     rl_err = float(np.max(np.abs(rlg[same] - res["row_loss"][same]) / res["row_loss"][same])) if same.any() else 0.0
-    log(f"  codes mismatch vs the oracle chain {mism}/{total} (rows {int((~same).sum())}) scale_err {s_err:.2e} "
+    log(f"  on the GPU's branches: rows differing {int((~same).sum())} scale_err {s_err:.2e} "
         f"loss gpu/oracle {lg / lo:.6f} row_loss_err {rl_err:.2e} ({time.perf_counter() - t_start:.0f}s)")
-    if mism > 1e-4 * total:
-        # every split must be a certified rounding tie of the sweep on the GPU's U
-        nrows, ties = certify_ties(W64, Ug64, perm_o, cfg.levels, cfg.group_size, cfg.block_size, codes_g, codes_o)
-        log(f"  {mism} codes in {nrows} rows: {ties} certified rounding ties of the sweep on the GPU's U")
-    else:
-        assert mism <= 1e-4 * total
+    assert np.all(same) or mism <= 1e-4 * total
     del Ug64
     assert s_err <= 1e-5
     assert np.array_equal(zg[same], zo[same])

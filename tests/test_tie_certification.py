@@ -133,7 +133,14 @@ def test_certify_accepts_a_branch_at_admitted_ties(monkeypatch):
     forced = {(0, 3): _adjacent(res, 0, 3), (4, 17): _adjacent(res, 4, 17)}
     branch = oracle.gptq_quantize(W, U, None, 16, 8, block_size=16, forced=forced)
     monkeypatch.setattr(gu, "K_SIGMA", 1e12)   # every decision counts as a tie here
-    rows, ties = gu.certify_ties(W, U, None, 16, 8, 16, branch["codes"], res["codes"])
+    branches = {}
+    rows, ties = gu.certify_ties(W, U, None, 16, 8, 16, branch["codes"], res["codes"], branches=branches)
     assert rows == 2 and ties == 2
+    # the oracle on the GPU's branches reproduces the branch exactly (losses included)
+    on = gu.on_gpu_branches(res, branches)
+    np.testing.assert_array_equal(on["codes"], branch["codes"])
+    np.testing.assert_array_equal(on["scales"], branch["scales"])
+    np.testing.assert_allclose(on["row_loss"], branch["row_loss"], rtol=1e-12)
+    assert sorted(branches) == [0, 4]
     # identical codes: nothing to certify
     assert gu.certify_ties(W, U, None, 16, 8, 16, res["codes"], res["codes"]) == (0, 0)
