@@ -364,8 +364,14 @@ __global__ __launch_bounds__(256) void range_reduce_kernel(const void* __restric
 // The in-block sweep of block kb for 64 rows (4 waves x 16 rows; within a
 // wave, lane r < 16 owns row r for the sequential part and all 64 lanes run
 // the MFMA part).
+// U's diagonal block, upper triangle with the diagonal, packed by rows: row i
+// holds columns i .. 127 from offset i (257 - i) / 2 (every read of the sweep
+// is on or above the diagonal; half the LDS of a square tile).
+constexpr int kUdPacked = kBS * (kBS + 1) / 2;
+__device__ __forceinline__ int ud_index(int i, int j) { return i * (2 * kBS + 1 - i) / 2 + (j - i); }
+
 struct SweepLds {
-  float Ud[kBS][kBS + 1];
+  float Ud[kUdPacked];
   float invd[kBS];
   __attribute__((aligned(16))) float T[kWaves][kRowsPerWave][kTP];
   float Eb[kWaves][kRowsPerWave][kSB + 1];
@@ -404,7 +410,7 @@ __device__ __forceinline__ void sweep_body(
   // Slot q of lane l of the slab is row (l + 64q) / 32, columns
   // 4*((l + 64q) % 32) .. +3.
   constexpr int kSlots = kRowsPerWave * kBS / 4 / 64;
-  constexpr int kPIn = 4;
+  constexpr int kPIn = 2;
   floatx4 t[kSlots];
   {
     const bool vecu = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
@@ -415,14 +421,7 @@ __device__ __forceinline__ void sweep_body(
     // and masked when it is stored to LDS.
     const bool fast = bw == kBS && vecu && perm == nullptr && (ldw & 3) == 0 &&
                       (reinterpret_cast<uintptr_t>(Wsrc) & (DT == GPTQ_F32 ? 15 : 7)) == 0;
-    floatx4 uv[kUSlots];
     if (fast) {
-#pragma unroll
-      for (int q = 0; q < kUSlots; ++q) {
-        const int e = tid + kThreads * q;
-        const int i = e >> 5, j = (e & 31) * 4;
-        uv[q] = *reinterpret_cast<const floatx4*>(U + (int64_t)(c0 + i) * n + c0 + j);
-      }
 #pragma unroll
       for (int q = 0; q < kSlots; ++q) {
         const int e = lane + 64 * q;
@@ -431,22 +430,6 @@ __device__ __forceinline__ void sweep_body(
         t[q] = row < m ? load4_as_f32<DT>(Wsrc, row * ldw + c0 + c) : floatx4{0.f, 0.f, 0.f, 0.f};
       }
     } else {
-#pragma unroll
-      for (int q = 0; q < kUSlots; ++q) {
-        const int e = tid + kThreads * q;
-        const int i = e >> 5, j = (e & 31) * 4;
-        floatx4 v = {0.f, 0.f, 0.f, 0.f};
-        if (i < bw && j + 3 >= i) {
-          const float* p = U + (int64_t)(c0 + i) * n + c0 + j;
-          if (vecu && j + 4 <= bw) {
-            v = *reinterpret_cast<const floatx4*>(p);
-          } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) v[k] = j + k < bw ? p[k] : 0.f;
-          }
-        }
-        uv[q] = v;
-      }
 #pragma unroll
       for (int q = 0; q < kSlots; ++q) {
         const int e = lane + 64 * q;
@@ -481,12 +464,40 @@ __device__ __forceinline__ void sweep_body(
 #pragma unroll
     for (int u = 0; u < kPIn; ++u) load_split(u, pv[u]);
     const float dj = tid < bw ? U[(int64_t)(c0 + tid) * n + c0 + tid] : 1.f;   // kThreads >= kBS
+    // U's diagonal block into LDS in two halves of 8 slots (register budget of
+    // two workgroups per CU); slots wholly below the diagonal are skipped.
+    const bool fullu = bw == kBS && vecu;
 #pragma unroll
-    for (int q = 0; q < kUSlots; ++q) {
-      const int e = tid + kThreads * q;
-      const int i = e >> 5, j = (e & 31) * 4;
+    for (int h = 0; h < 2; ++h) {
+      floatx4 uv[kUSlots / 2];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) Ud[i][j + k] = j + k >= i ? uv[q][k] : 0.f;
+      for (int q2 = 0; q2 < kUSlots / 2; ++q2) {
+        const int e = tid + kThreads * (q2 + h * (kUSlots / 2));
+        const int i = e >> 5, j = (e & 31) * 4;
+        floatx4 v = {0.f, 0.f, 0.f, 0.f};
+        if (j + 3 >= i) {
+          const float* p = U + (int64_t)(c0 + i) * n + c0 + j;
+          if (fullu) {
+            v = *reinterpret_cast<const floatx4*>(p);
+          } else if (i < bw) {
+            if (vecu && j + 4 <= bw) {
+              v = *reinterpret_cast<const floatx4*>(p);
+            } else {
+#pragma unroll
+              for (int k = 0; k < 4; ++k) v[k] = j + k < bw ? p[k] : 0.f;
+            }
+          }
+        }
+        uv[q2] = v;
+      }
+#pragma unroll
+      for (int q2 = 0; q2 < kUSlots / 2; ++q2) {
+        const int e = tid + kThreads * (q2 + h * (kUSlots / 2));
+        const int i = e >> 5, j = (e & 31) * 4;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (j + k >= i) Ud[ud_index(i, j + k)] = uv[q2][k];
+      }
     }
     if (tid < kBS) invd[tid] = tid < bw ? 1.f / dj : 0.f;
     for (int sp = 0; sp < nsub; sp += kPIn) {
@@ -578,7 +589,7 @@ __device__ __forceinline__ void sweep_body(
   const bool vec_uo = (n & 3) == 0 && (reinterpret_cast<uintptr_t>(U) & 15) == 0;
   // uf[k4][h][t]: B element (k = 4*k4 + lane/16) of tile ct = 4*h + t, i.e.
   // U_off[k, 64*h + 4*(lane%16) + t].
-  floatx4 uf[2][kSB / 4][2];
+  floatx4 uf[kSB / 4][2];
   auto uoff_load = [&](int j0, floatx4 (&f)[kSB / 4][2]) {
 #pragma unroll
     for (int k4 = 0; k4 < kSB / 4; ++k4) {
@@ -612,7 +623,9 @@ __device__ __forceinline__ void sweep_body(
     const int sb = sbc;
     const int j0 = sb * kSB;
     if constexpr (FULL) {
-      uoff_load(j0, uf[sb & 1]);   // all zero (and no access) when there is no next block
+      // the fragments of the previous sub-block's slice (all zero, and no
+      // access, when there is no next block); consumed from column 8 on
+      if (sb > 0) uoff_load(j0 - kSB, uf);
     }
     if (block_group && sb == 0) {
       float gmn = Gs[wave][r][0], gmx = Gs[wave][r][1];
@@ -661,10 +674,11 @@ __device__ __forceinline__ void sweep_body(
       float un[kSB];
       float idn = invd[j0];
 #pragma unroll
-      for (int kk = 0; kk < kSB; ++kk) un[kk] = Ud[j0][j0 + kk];
+      for (int kk = 0; kk < kSB; ++kk) un[kk] = Ud[ud_index(j0, j0 + kk)];
       // The previous sub-block's Plast slice (independent of this chain) is
-      // spread over the columns, two MFMAs per column, so that the matrix
-      // core works while the column chain waits on its own latencies.
+      // spread over the second half of the columns, four MFMAs per column,
+      // so that the matrix core works while the column chain waits on its
+      // own latencies and the fragments' loads have eight columns to land.
       constexpr bool kSlice = decltype(sbc)::value > 0;
       float pa[kSB / 4];
       if constexpr (kSlice) {
@@ -674,11 +688,12 @@ __device__ __forceinline__ void sweep_body(
 #pragma unroll
       for (int jj = 0; jj < kSB; ++jj) {
         if constexpr (kSlice) {
-          const int k4 = jj >> 2, ct = 2 * (jj & 3);
-          const auto& f = uf[(decltype(sbc)::value - 1) & 1];
-          pacc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][ct >> 2][ct & 3], pacc[ct], 0, 0, 0);
-          pacc[ct + 1] =
-              __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], f[k4][(ct + 1) >> 2][(ct + 1) & 3], pacc[ct + 1], 0, 0, 0);
+          if (jj >= kSB / 2) {
+            const int k4 = (jj - kSB / 2) >> 1, h = (jj - kSB / 2) & 1;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+              pacc[4 * h + t] = __builtin_amdgcn_mfma_f32_16x16x4f32(pa[k4], uf[k4][h][t], pacc[4 * h + t], 0, 0, 0);
+          }
         }
         float uc[kSB];
 #pragma unroll
@@ -687,7 +702,7 @@ __device__ __forceinline__ void sweep_body(
         if (jj + 1 < kSB) {
           idn = invd[j0 + jj + 1];
 #pragma unroll
-          for (int kk = jj + 2; kk < kSB; ++kk) un[kk] = Ud[j0 + jj + 1][j0 + kk];
+          for (int kk = jj + 2; kk < kSB; ++kk) un[kk] = Ud[ud_index(j0 + jj + 1, j0 + kk)];
         }
         const float c = quant_code(w[jj], s, inv_s, z, maxq);
         const float what = s * (c - z);
@@ -709,7 +724,7 @@ __device__ __forceinline__ void sweep_body(
           loss = __builtin_fmaf(e, e, loss);
           cw[jj >> 2] |= (uint32_t)c << (8 * (jj & 3));
 #pragma unroll
-          for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, Ud[j0 + jj][j0 + kk], w[kk]);
+          for (int kk = jj + 1; kk < kSB; ++kk) w[kk] = __builtin_fmaf(-e, Ud[ud_index(j0 + jj, j0 + kk)], w[kk]);
         } else {
           eb[jj] = 0.f;
         }
@@ -749,7 +764,7 @@ __device__ __forceinline__ void sweep_body(
       for (int k4 = 0; k4 < 4; ++k4) {
         const int k = k4 * 4 + (lane >> 4);
         const float a = -Eb[wave][lane & 15][k];
-        const float b = Ud[j0 + k][ct * kSB + (lane & 15)];
+        const float b = Ud[ud_index(j0 + k, ct * kSB + (lane & 15))];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc, 0, 0, 0);
       }
 #pragma unroll
@@ -779,7 +794,8 @@ __device__ __forceinline__ void sweep_body(
   if (active && row_loss != nullptr) row_loss[row] = (kb == 0 ? 0.f : row_loss[row]) + 0.5f * loss;
   if (make_next) {
     // Last slice, then Plast[rows] = E[rows, block kb] U[block kb, block kb+1].
-    uoff_accumulate(kBS - kSB, uf[(kBS / kSB - 1) & 1]);
+    uoff_load(kBS - kSB, uf);
+    uoff_accumulate(kBS - kSB, uf);
     // 16x16x4 accumulator: register i of lane l is row 4*(l/16) + i, MFMA
     // column l%16, so tiles 4h .. 4h+3 hold block columns 64h + 4*(l%16) + 0..3.
     const bool vec_pl = (reinterpret_cast<uintptr_t>(Plast) & 15) == 0;
@@ -807,7 +823,7 @@ __device__ __forceinline__ void sweep_body(
 // deferred update over the columns before block kb (the last block's share
 // comes from the sweep itself), split over K in ranges of sps stages.
 template <int DT>
-__global__ __launch_bounds__(kThreads) void quant_block_kernel(
+__global__ __launch_bounds__(kThreads, 2) void quant_block_kernel(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
     const float* __restrict__ Pcur, int nsplit, float* __restrict__ Plast, int use_last, int make_next,
     float maxq, int g, int G, uint8_t* __restrict__ codes, float* __restrict__ E, float* __restrict__ scales,
