@@ -8,17 +8,21 @@
 //   U = R^{-1} = J L^{-1} J       (upper, U^T U = H_d^{-1})
 // so one Cholesky and one triangular inverse (2/3 n^3 flops in all) give U
 // directly; H_d^{-1} is never formed.  Both run in float64, right-looking
-// with 64 x 64 blocks, interleaved in one loop over block columns kb with two
-// launches per step:
+// with 64 x 64 blocks, in one loop over block columns kb:
 //   panel(kb)   L[i, kb] = A[i, kb] inv(L_kk)^T                   (MFMA f64)
 //               X[kb, j] = inv(L_kk) T[kb, j], j < kb             (MFMA f64)
-//   update(kb)  A[i, j] -= L[i, kb] L[j, kb]^T, kb < j <= i       (MFMA f64)
-//               T[i, j] -= L[i, kb] X[kb, j], i > kb, j <= kb     (MFMA f64)
-//               + the workgroup that updates block (kb+1, kb+1) then factors
-//                 and inverts it (16-column leaves, float64 MFMA between
-//                 them), overlapping the rest of the trailing update
+//   update      A[i, j] -= sum_p L[i, p] L[j, p]^T                (MFMA f64)
+//               T[i, j] -= sum_p L[i, p] X[p, j]                  (MFMA f64)
+//               + the workgroup that updates the next diagonal block then
+//                 factors and inverts it (16-column leaves, float64 MFMA
+//                 between them), overlapping the rest of the trailing update
 // where X = L^{-1} is built in place of T (forward substitution by block
-// rows).  Matrices are padded to a multiple of 64 with an identity block.
+// rows).  For large n block columns are taken in pairs (p0, p1 = p0 + 1):
+// panel(p0); a narrow update of block column p1 and inverse row p1 alone with
+// panel p0; panel(p1); then one trailing update with both panels (K = 128) --
+// the float64 trailing matrix is read and written once per pair instead of
+// once per block column, which halves the HBM traffic that bounds large n.
+// Matrices are padded to a multiple of 64 with an identity block.
 #include "common.h"
 
 namespace gptq {
@@ -422,8 +426,8 @@ __device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, co
 }
 
 // Step kb, first launch: panel L[i, kb] = A[i, kb] inv(L_kk)^T for i > kb
-// (tiles 0 .. T-1; also written transposed to Lt[k][i], the row-major B
-// operand of the trailing update) and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
+// (tiles 0 .. T-1; also written transposed to Lt[lt_row0 + k][i], the
+// row-major B operand of the trailing update) and row kb of the inverse X[kb, j] = inv(L_kk) T[kb, j]
 // for j < kb (tiles T .. T+kb-1), four workgroups per 64 x 64 tile.  A
 // workgroup owns 16 output rows of a panel tile (which read only those rows)
 // or 16 output columns of an inverse-row tile (which read only those
@@ -431,7 +435,8 @@ __device__ inline void gemm_tile64(TileLds& t, const double* Ap, int64_t lda, co
 // one 16 x 16 block with 16 float64 MFMAs.
 __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict__ A, double* __restrict__ X,
                                                               const double* __restrict__ Linv,
-                                                              double* __restrict__ Lt, int np, int nbk, int kb) {
+                                                              double* __restrict__ Lt, int np, int nbk, int kb,
+                                                              int lt_row0) {
   __shared__ double Ls[kB][kP];      // inv(L_kk)
   __shared__ double Ps[kB][17];      // the tile's 16 rows (transposed) or 16 columns, [k][16]
   const int T = nbk - kb - 1;
@@ -472,74 +477,96 @@ __global__ __launch_bounds__(kThreads) void chol_panel_kernel(double* __restrict
     const int row = (lane >> 4) + 4 * r, col = lane & 15;
     if (panel) {
       p[(int64_t)row * np + wave * 16 + col] = acc[r];
-      Lt[(int64_t)(wave * 16 + col) * np + (kb + 1 + tile) * kB + part * 16 + row] = acc[r];
+      Lt[(int64_t)(lt_row0 + wave * 16 + col) * np + (kb + 1 + tile) * kB + part * 16 + row] = acc[r];
     } else
       p[(int64_t)(wave * 16 + row) * np + col] = acc[r];
   }
 }
 
-// Step kb, second launch: trailing update A[i, j] -= L[i, kb] L[j, kb]^T for
-// kb < j <= i ("SYRK" tiles) and T[i, j] -= L[i, kb] X[kb, j] for i > kb,
-// j <= kb ("inverse" tiles).  Tile 0 is the next diagonal block; workgroup 0
-// updates it and then factors and inverts it with factor_diag.  Every wave of
-// the other workgroups owns a contiguous range of half tiles (32 rows x 64
-// columns) and runs each on its own: operands go from global memory (mostly
-// L2) straight into MFMA registers in 16-column-deep chunks, the next chunk
-// in flight while the current one multiplies, so no wave waits for another
-// and loads, stores and MFMAs of one wave overlap.  No tile reads what another
-// tile of the launch writes.
-__device__ inline void update_tile_ref(int t, int S, int kb, int np, double* A, double* X, const double*& pa,
-                                       const double*& pb, double*& pc, bool& transB, int& bi_out) {
-  if (t < S) {
-    int ii, jj;
-    tri_decode(t, ii, jj);
-    const int bi = kb + 1 + ii, bj = kb + 1 + jj;
-    bi_out = bi;
-    pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-    pb = A + (int64_t)bj * kB * np + (int64_t)kb * kB;
-    pc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
-    transB = true;
+// The trailing update with panels p0 .. kl = p0 + P - 1 (P = 1 or 2), next =
+// kl + 1.  Full mode: "SYRK" tiles A[i, j] -= sum_p L[i, p] L[j, p]^T for
+// next <= j <= i and "inverse" tiles T[i, j] -= sum_p L[i, p] X[p, j] for
+// i >= next, j <= kl (only panels p >= j: X is lower triangular).  Narrow
+// mode (P = 1): only block column next (SYRK tiles (i, next), i >= next) and
+// inverse row next (tiles (next, j), j <= kl) -- what panel(next) reads.
+// Tile 0 is the diagonal block (next, next); workgroup 0 updates it and then
+// factors and inverts it with factor_diag.  Every wave of the other
+// workgroups owns a contiguous range of half tiles (32 rows x 64 columns) and
+// runs each on its own: operands go from global memory (mostly L2) straight
+// into MFMA registers in 16-column-deep chunks, the next chunk in flight
+// while the current one multiplies, so no wave waits for another and loads,
+// stores and MFMAs of one wave overlap.  No tile reads what another tile of
+// the launch writes.  An inverse tile T[i, j] with j >= p0 is touched for the
+// first time by this launch (it starts from zero).
+struct UpdPlan {
+  int p0, P, next, T, S, total;
+  bool narrow;
+};
+
+__host__ __device__ inline UpdPlan upd_plan(int nbk, int p0, int P, bool narrow) {
+  UpdPlan u;
+  u.p0 = p0;
+  u.P = P;
+  u.next = p0 + P;
+  u.narrow = narrow;
+  u.T = nbk - u.next;
+  u.S = narrow ? u.T : u.T * (u.T + 1) / 2;
+  u.total = u.S + (narrow ? u.next : u.T * u.next);
+  return u;
+}
+
+// Tile t of the plan: block row / column, SYRK or inverse.
+__device__ inline void upd_tile(const UpdPlan& u, int t, int& bi, int& bj, bool& syrk) {
+  syrk = t < u.S;
+  if (syrk) {
+    if (u.narrow) {
+      bi = u.next + t;
+      bj = u.next;
+    } else {
+      int ii, jj;
+      tri_decode(t, ii, jj);
+      bi = u.next + ii;
+      bj = u.next + jj;
+    }
   } else {
-    const int e = t - S;
-    const int bi = kb + 1 + e / (kb + 1), bj = e % (kb + 1);
-    bi_out = bi;
-    pa = A + (int64_t)bi * kB * np + (int64_t)kb * kB;
-    pb = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
-    pc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
-    transB = false;
+    const int e = t - u.S;
+    if (u.narrow) {
+      bi = u.next;
+      bj = e;
+    } else {
+      bi = u.next + e / u.next;
+      bj = e % u.next;
+    }
   }
 }
 
 // Half tiles per workgroup of the trailing update (one per wave at a time).
 constexpr int kUpdWaves = kThreads / 64;
 
-// Workgroups for step kb's update launch: workgroup 0 plus enough for about
-// one half tile per wave, at most one workgroup per CU.
-inline int update_grid(int nbk, int kb) {
-  const int T = nbk - kb - 1;
-  const int total = T * (T + 1) / 2 + T * (kb + 1);
-  const int units = 2 * (total - 1);
+// Workgroups for an update launch: workgroup 0 plus enough for about one half
+// tile per wave, at most one workgroup per CU.
+inline int update_grid(const UpdPlan& u) {
+  const int units = 2 * (u.total - 1);
   return 1 + std::min((units + kUpdWaves - 1) / kUpdWaves, kUpdateBlocks - 1);
 }
 
 __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restrict__ A, double* __restrict__ X,
                                                                double* __restrict__ Linv,
                                                                const double* __restrict__ Lt, int np, int n, int nbk,
-                                                               int kb, int32_t* __restrict__ info) {
+                                                               int p0, int P, int narrow, int32_t* __restrict__ info) {
   __shared__ TileLds tl;
   __shared__ FactorLds fx;
-  const int T = nbk - kb - 1;
-  const int S = T * (T + 1) / 2;
-  const int total = S + T * (kb + 1);
+  const UpdPlan up = upd_plan(nbk, p0, P, narrow != 0);
   if (blockIdx.x == 0) {
-    const double *pa, *pb;
-    double* pc;
-    bool tb;
-    int bi;
-    update_tile_ref(0, S, kb, np, A, X, pa, pb, pc, tb, bi);
-    gemm_tile64(tl, pa, np, pb, np, tb, pc, np, true, &tl.As[0][0]);
+    // Diagonal block (next, next) -= sum_p L[next, p] L[next, p]^T, then factor.
+    double* pc = A + (int64_t)up.next * kB * np + (int64_t)up.next * kB;
+    for (int p = 0; p < P; ++p) {
+      const double* pa = A + (int64_t)up.next * kB * np + (int64_t)(p0 + p) * kB;
+      if (p > 0) __syncthreads();   // the previous product's LDS reads are done
+      gemm_tile64(tl, pa, np, pa, np, true, pc, np, true, p + 1 == P ? &tl.As[0][0] : nullptr);
+    }
     __syncthreads();
-    factor_diag(&tl.As[0][0], &tl.Bs[0][0], fx, X, Linv, np, n, kb + 1, info);
+    factor_diag(&tl.As[0][0], &tl.Bs[0][0], fx, X, Linv, np, n, up.next, info);
     return;
   }
   // Half tile u covers tile u/2 (tiles 1 .. total-1), rows 32*(u%2) .. +31.
@@ -554,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   const int worker = before + slot - (xcd == 0 ? 1 : 0);
   const int gw = worker * kUpdWaves + __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nw = ((int)gridDim.x - 1) * kUpdWaves;
-  const int units = 2 * (total - 1);
+  const int units = 2 * (up.total - 1);
   const int per = (units + nw - 1) / nw;
   const int u_lo = 2 + gw * per;
   const int u_hi = min(2 + units, u_lo + per);
@@ -562,16 +589,15 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   // float64 MFMA 16x16x4: A element (row l%16, k l/16), B element (k l/16,
   // column l%16), accumulator register r of lane l: row l/16 + 4r, column
   // l%16.  The contraction index and the output columns are permuted so that
-  // every load and store is 16 bytes wide: MFMA step s (0..15) with lane
-  // quarter q = l/16 stands for k = 8*(s/2) + 2q + s%2 (a lane's two steps
-  // 2j, 2j+1 read one adjacent pair of k of its A row), and column block cb
-  // (0..3) with MFMA column c stands for tile column 32*(cb/2) + 2c + cb%2
-  // (blocks 2p and 2p+1 read one adjacent pair of columns of a B row and of
-  // a C row).  B is row-major over k for both kinds of tile: Lt[k][j] for a
-  // SYRK tile, X[kb rows k][j] for an inverse tile.
+  // every load and store is 16 bytes wide: MFMA step s (0..15) of a 64-deep
+  // panel with lane quarter q = l/16 stands for k = 8*(s/2) + 2q + s%2 (a
+  // lane's two steps 2j, 2j+1 read one adjacent pair of k of its A row), and
+  // column block cb (0..3) with MFMA column c stands for tile column
+  // 32*(cb/2) + 2c + cb%2 (blocks 2p and 2p+1 read one adjacent pair of
+  // columns of a B row and of a C row).  B is row-major over k for both kinds
+  // of tile: Lt[k][j] for a SYRK tile, X[p0 rows + k][j] for an inverse tile.
   const int q = lane >> 4, c16 = lane & 15;
   constexpr int kChunk = 4;                    // MFMA steps per chunk (16 of k)
-  constexpr int kChunks = kB / 4 / kChunk;
   // One chunk: a[rb][jj] = A row rb*16 + c16 at the k pair of steps 2jj,
   // 2jj+1; b[ss][pp] = B row of step ss at columns 32pp + 2*c16 + 0..1.
   struct Chunk {
@@ -595,40 +621,38 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
         ck.b[ss][pp] = *reinterpret_cast<const double2*>(ub + (int64_t)k * np + 32 * pp + 2 * c16);
       }
   };
-  // Unit u's operands: A rows of the half tile, the B block (row-major over
-  // k, leading dimension np), the C rows.
-  auto unit_ref = [&](int u, const double*& ua, const double*& ub, double*& uc) {
-    const int t = u >> 1;
+  // Unit u's operands from its first usable panel on: A rows of the half
+  // tile, the B block (row-major over k, leading dimension np), the C rows,
+  // the number of 16-deep chunks, and whether C starts from zero.
+  auto unit_ref = [&](int u, const double*& ua, const double*& ub, double*& uc, int& nch, bool& first) {
     int bi, bj;
-    if (t < S) {
-      int ii, jj;
-      tri_decode(t, ii, jj);
-      bi = kb + 1 + ii;
-      bj = kb + 1 + jj;
-      ub = Lt + (int64_t)bj * kB;
+    bool syrk;
+    upd_tile(up, u >> 1, bi, bj, syrk);
+    const int pstart = syrk ? 0 : max(0, bj - p0);   // X[p, bj] = 0 for panels p < bj
+    if (syrk) {
+      ub = Lt + (int64_t)pstart * kB * np + (int64_t)bj * kB;
       uc = A + (int64_t)bi * kB * np + (int64_t)bj * kB;
     } else {
-      const int e = t - S;
-      bi = kb + 1 + e / (kb + 1);
-      bj = e % (kb + 1);
-      ub = X + (int64_t)kb * kB * np + (int64_t)bj * kB;
+      ub = X + (int64_t)(p0 + pstart) * kB * np + (int64_t)bj * kB;
       uc = X + (int64_t)bi * kB * np + (int64_t)bj * kB;
     }
-    ua = A + ((int64_t)bi * kB + (u & 1) * 32) * np + (int64_t)kb * kB;
+    ua = A + ((int64_t)bi * kB + (u & 1) * 32) * np + (int64_t)(p0 + pstart) * kB;
     uc += (int64_t)(u & 1) * 32 * np;
+    nch = (P - pstart) * (kB / (4 * kChunk));
+    first = !syrk && bj >= p0;
   };
   Chunk ck[2];
   const double *pa, *pb;
   double* pc;
-  unit_ref(u_lo, pa, pb, pc);
+  int nch;
+  bool first;
+  unit_ref(u_lo, pa, pb, pc, nch, first);
   load_chunk(ck[0], pa, pb, 0);
   for (int u = u_lo; u < u_hi; ++u) {
-    const int t = u >> 1;
     // C in the accumulator layout: cv[rb][pp][r] = row rb*16 + q + 4r,
     // columns 32pp + 2*c16 + 0..1 (column blocks 2pp, 2pp+1).  An inverse
-    // tile T[i, kb] is touched here for the first time: its old contents
-    // (X is never cleared as a whole) are read but replaced by zero.
-    const bool first = t >= S && (t - S) % (kb + 1) == kb;
+    // tile first touched here has its old contents (X is never cleared as a
+    // whole) read but replaced by zero.
     double2 cv[2][2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -647,12 +671,11 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     // last unit loads its own first chunk again, which is never used).
     const double *na, *nb;
     double* nc;
-    unit_ref(u + 1 < u_hi ? u + 1 : u, na, nb, nc);
-#pragma unroll
-    for (int ch = 0; ch < kChunks; ++ch) {
-      Chunk& cur = ck[ch & 1];
-      Chunk& nxt = ck[(ch + 1) & 1];
-      if (ch + 1 < kChunks)
+    int nnch;
+    bool nfirst;
+    unit_ref(u + 1 < u_hi ? u + 1 : u, na, nb, nc, nnch, nfirst);
+    auto step = [&](Chunk& cur, Chunk& nxt, int ch) {
+      if (ch + 1 < nch)
         load_chunk(nxt, pa, pb, ch + 1);
       else
         load_chunk(nxt, na, nb, 0);
@@ -667,6 +690,12 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
             acc[rb][cb] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, bv, acc[rb][cb], 0, 0, 0);
           }
         }
+    };
+    // nch is even (4 per panel): chunks alternate between the two named
+    // buffers, so no register array is indexed at run time.
+    for (int ch = 0; ch < nch; ch += 2) {
+      step(ck[0], ck[1], ch);
+      step(ck[1], ck[0], ch + 1);
     }
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -682,6 +711,8 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
     pa = na;
     pb = nb;
     pc = nc;
+    nch = nnch;
+    first = nfirst;
   }
 }
 
@@ -707,7 +738,7 @@ PrepLayout prep_layout(int64_t n) {
   L.off_X = align256(L.off_A + mat);
   L.off_Linv = align256(L.off_X + mat);
   L.off_Lt = align256(L.off_Linv + (size_t)kB * kB * sizeof(double));
-  L.off_lam = align256(L.off_Lt + (size_t)kB * (size_t)L.np * sizeof(double));
+  L.off_lam = align256(L.off_Lt + (size_t)2 * kB * (size_t)L.np * sizeof(double));
   L.off_info = align256(L.off_lam + sizeof(double));
   L.total = align256(L.off_info + sizeof(int32_t));
   return L;
@@ -749,11 +780,36 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
   build_reversed_kernel<<<(unsigned)np, kThreads, 0, st>>>(H, ni, np, perm, lam, A);
   GPTQ_TRY_LAUNCH();
   potrf_diag_kernel<<<1, kThreads, 0, st>>>(A, X, Linv, np, ni, 0, info);
-  for (int kb = 0; kb < nbk; ++kb) {
+  auto panel = [&](int kb, int lt_row0) {
     const int T = nbk - kb - 1;
-    if (T + kb > 0) chol_panel_kernel<<<(unsigned)(4 * (T + kb)), kThreads, 0, st>>>(A, X, Linv, Lt, np, nbk, kb);
-    if (T > 0)
-      chol_update_kernel<<<(unsigned)update_grid(nbk, kb), kThreads, 0, st>>>(A, X, Linv, Lt, np, ni, nbk, kb, info);
+    if (T + kb > 0)
+      chol_panel_kernel<<<(unsigned)(4 * (T + kb)), kThreads, 0, st>>>(A, X, Linv, Lt, np, nbk, kb, lt_row0);
+  };
+  auto update = [&](int p0, int P, bool narrow) {
+    const UpdPlan u = upd_plan(nbk, p0, P, narrow);
+    chol_update_kernel<<<(unsigned)update_grid(u), kThreads, 0, st>>>(A, X, Linv, Lt, np, ni, nbk, p0, P,
+                                                                      narrow ? 1 : 0, info);
+  };
+  // Pairs pay once the float64 trailing matrix outgrows the 256 MB last-level
+  // cache (padded n >= 6144, measured: 12288 wide 42.4 -> 34.9 ms); below
+  // that the update is latency-bound and the narrow launch only adds a step
+  // (4096 wide 2.57 -> 2.77 ms), so every block column is its own step.
+  const bool pairs = np >= 6144;
+  for (int kb = 0; kb < nbk;) {
+    if (!pairs) {
+      panel(kb, 0);
+      if (kb + 1 < nbk) update(kb, 1, false);
+      kb += 1;
+    } else if (kb + 1 < nbk) {
+      panel(kb, 0);
+      update(kb, 1, true);            // block column and inverse row kb + 1
+      panel(kb + 1, kB);
+      if (kb + 2 < nbk) update(kb, 2, false);
+      kb += 2;
+    } else {
+      panel(kb, 0);                   // the last block column: no trailing matrix
+      kb += 1;
+    }
     GPTQ_TRY_LAUNCH();
   }
   write_u_kernel<<<(unsigned)n, kThreads, 0, st>>>(X, ni, np, U);
