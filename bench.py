@@ -157,6 +157,7 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total, h_tokens=None, q_rows=1024):
     H = oracle.hessian(Xs)
     t_h = (time.perf_counter() - t0) * (tokens_total / t_sample)
     del Xs
+    log(f"  oracle Hessian on {t_sample} tokens: {t_h * t_sample / tokens_total:.1f}s")
     H = H * (tokens_total / t_sample)          # same scale as the full Hessian
     t0 = time.perf_counter()
     perm = oracle.act_order_perm(H) if cfg.act_order else np.arange(n)
@@ -165,10 +166,12 @@ def cpu_baseline(L, X, cfg, n, m, tokens_total, h_tokens=None, q_rows=1024):
     U = oracle.inverse_cholesky_upper(Hd)
     del Hd
     t_p = time.perf_counter() - t0
+    log(f"  oracle prepare at n={n}: {t_p:.1f}s")
     W64 = L.W.f32[:m_sample].astype(np.float64)
     t0 = time.perf_counter()
     res = oracle.gptq_quantize(W64, U, perm, cfg.levels, cfg.group_size, cfg.block_size)
     t_q = (time.perf_counter() - t0) * (m / m_sample)
+    log(f"  oracle sweep on {m_sample} rows: {t_q * m_sample / m:.1f}s")
     t0 = time.perf_counter()
     oracle.pack_codes(oracle.unpermute_codes(res["codes"], perm).astype(np.int64), bits_of(cfg.levels))
     t_k = (time.perf_counter() - t0) * (m / m_sample)
