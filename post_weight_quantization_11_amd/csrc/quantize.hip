@@ -226,8 +226,11 @@ __device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, co
     for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = floatx16{};
 
   // Stage slabs: E 128 x 32 and U 32 x 128, 1024 float4 each, 4 per thread.
-  floatx4 ea[4], ub[4];
-  auto gload = [&](int k0) {
+  // Two register sets: the slabs of stage s + 2 are loaded while stage s is
+  // multiplied and stage s + 1's (loaded a stage earlier) go to LDS, so each
+  // HBM read of E has two stages of matrix-core work to arrive.
+  floatx4 ea0[4], ub0[4], ea1[4], ub1[4];
+  auto gload = [&](int k0, floatx4 (&ea)[4], floatx4 (&ub)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 256 * i;
@@ -256,7 +259,7 @@ __device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, co
       ub[i] = v;
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, const floatx4 (&ea)[4], const floatx4 (&ub)[4]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int e = tid + 256 * i;
@@ -271,17 +274,7 @@ __device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, co
       *reinterpret_cast<floatx4*>(&Bs[buf][kk][c]) = ub[i];
     }
   };
-
-  const int nst = (k_end - k_begin) / kUK;
-  if (nst > 0) {
-    gload(k_begin);
-    lstore(0);
-  }
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int buf = s & 1;
-    const bool next = s + 1 < nst;
-    if (next) gload(k_begin + (s + 1) * kUK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int k2 = 0; k2 < kUK / 2; ++k2) {
       const int k = k2 * 2 + (lane >> 5);
@@ -296,8 +289,26 @@ __device__ __forceinline__ void update_gemm_body(const float* __restrict__ E, co
         for (int cb = 0; cb < 2; ++cb)
           acc[rb][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[rb], b[cb], acc[rb][cb], 0, 0, 0);
     }
-    // Buffer buf ^ 1 was last read in stage s - 1, before the previous barrier.
-    if (next) lstore(buf ^ 1);
+  };
+
+  const int nst = (k_end - k_begin) / kUK;
+  if (nst > 0) {
+    gload(k_begin, ea0, ub0);
+    lstore(0, ea0, ub0);
+  }
+  if (nst > 1) gload(k_begin + kUK, ea1, ub1);
+  __syncthreads();
+  // Stage s is read from buffer s & 1.  A buffer is written only after the
+  // barrier that follows its last read.
+  for (int s = 0; s < nst; s += 2) {
+    if (s + 2 < nst) gload(k_begin + (s + 2) * kUK, ea0, ub0);
+    compute(0);
+    if (s + 1 < nst) lstore(1, ea1, ub1);
+    __syncthreads();
+    if (s + 1 >= nst) break;
+    if (s + 3 < nst) gload(k_begin + (s + 3) * kUK, ea1, ub1);
+    compute(1);
+    if (s + 2 < nst) lstore(0, ea0, ub0);
     __syncthreads();
   }
   // 32x32 accumulator: register r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32.
