@@ -17,11 +17,12 @@
 //                 factors and inverts it (16-column leaves, float64 MFMA
 //                 between them), overlapping the rest of the trailing update
 // where X = L^{-1} is built in place of T (forward substitution by block
-// rows).  For large n block columns are taken in pairs (p0, p1 = p0 + 1):
-// panel(p0); a narrow update of block column p1 and inverse row p1 alone with
-// panel p0; panel(p1); then one trailing update with both panels (K = 128) --
-// the float64 trailing matrix is read and written once per pair instead of
-// once per block column, which halves the HBM traffic that bounds large n.
+// rows).  For large n block columns are taken in groups of four p0 .. p0+3:
+// panel(p0 + t), each but the last followed by a narrow update of block
+// column and inverse row p0+t+1 alone with panels p0 .. p0+t, then one
+// trailing update with all four panels (K = 256) -- the float64 trailing
+// matrix is read and written once per group instead of once per block
+// column, which cuts the memory traffic that bounds large n.
 // Matrices are padded to a multiple of 64 with an identity block.
 #include "common.h"
 
@@ -31,6 +32,7 @@ namespace {
 constexpr int kB = 64;        // Cholesky block
 constexpr int kThreads = 256;
 constexpr int kUpdateBlocks = 256;  // workgroups of the trailing-update launch (one per CU)
+constexpr int kGroupWide = 4;       // block columns per trailing update for large n
 
 __global__ void init_scalars_kernel(int32_t* info) {
   if (threadIdx.x == 0 && blockIdx.x == 0) *info = 0;
@@ -738,7 +740,7 @@ PrepLayout prep_layout(int64_t n) {
   L.off_X = align256(L.off_A + mat);
   L.off_Linv = align256(L.off_X + mat);
   L.off_Lt = align256(L.off_Linv + (size_t)kB * kB * sizeof(double));
-  L.off_lam = align256(L.off_Lt + (size_t)2 * kB * (size_t)L.np * sizeof(double));
+  L.off_lam = align256(L.off_Lt + (size_t)kGroupWide * kB * (size_t)L.np * sizeof(double));
   L.off_info = align256(L.off_lam + sizeof(double));
   L.total = align256(L.off_info + sizeof(int32_t));
   return L;
@@ -790,26 +792,22 @@ extern "C" gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_r
     chol_update_kernel<<<(unsigned)update_grid(u), kThreads, 0, st>>>(A, X, Linv, Lt, np, ni, nbk, p0, P,
                                                                       narrow ? 1 : 0, info);
   };
-  // Pairs pay once the float64 trailing matrix outgrows the 256 MB last-level
-  // cache (padded n >= 6144, measured: 12288 wide 42.4 -> 34.9 ms); below
-  // that the update is latency-bound and the narrow launch only adds a step
-  // (4096 wide 2.57 -> 2.77 ms), so every block column is its own step.
-  const bool pairs = np >= 6144;
-  for (int kb = 0; kb < nbk;) {
-    if (!pairs) {
-      panel(kb, 0);
-      if (kb + 1 < nbk) update(kb, 1, false);
-      kb += 1;
-    } else if (kb + 1 < nbk) {
-      panel(kb, 0);
-      update(kb, 1, true);            // block column and inverse row kb + 1
-      panel(kb + 1, kB);
-      if (kb + 2 < nbk) update(kb, 2, false);
-      kb += 2;
-    } else {
-      panel(kb, 0);                   // the last block column: no trailing matrix
-      kb += 1;
+  // Groups of block columns pay once the float64 trailing matrix outgrows the
+  // 256 MB last-level cache (padded n >= 6144); below that the update is
+  // latency-bound and each narrow launch only adds a step (4096 wide, pairs:
+  // 2.57 -> 2.77 ms), so every block column is its own step.  A group of g
+  // columns p0 .. p0+g-1: panel(p0 + t) for t = 0 .. g-1, each but the last
+  // followed by the narrow update of block column and inverse row p0+t+1
+  // with the panels p0 .. p0+t, then one trailing update with all g panels.
+  const int group = np >= 6144 ? kGroupWide : 1;
+  for (int p0 = 0; p0 < nbk;) {
+    const int gsz = std::min(group, nbk - p0);
+    for (int t = 0; t < gsz; ++t) {
+      panel(p0 + t, t * kB);
+      if (t + 1 < gsz) update(p0, t + 1, true);
     }
+    if (p0 + gsz < nbk) update(p0, gsz, false);
+    p0 += gsz;
     GPTQ_TRY_LAUNCH();
   }
   write_u_kernel<<<(unsigned)n, kThreads, 0, st>>>(X, ni, np, U);

@@ -84,8 +84,8 @@ def _h32(n, seed, tokens=None, law="lognormal1"):
     return oracle.hessian(X.f32).astype(F32)
 
 
-# 6200 and 8192 take the paired block-column schedule (padded n >= 6144),
-# 6200 with an odd number of 64-wide block columns (97).
+# 6200 and 8192 take the grouped block-column schedule (padded n >= 6144,
+# groups of four), 6200 with 97 block columns (a last group of one).
 @pytest.mark.parametrize("n,act", [(100, False), (256, True), (520, True), (64, False), (1, True), (6200, True),
                                    (8192, False)])
 def test_prepare_parity(g, n, act):
