@@ -235,3 +235,60 @@ def test_lowrank_basis_full_size(g):
     log(f"  |L^T L - I| {np.max(np.abs(L.T @ L - np.eye(r))):.2e}, invariant-subspace residual {res:.2e}")
     assert np.max(np.abs(L.T @ L - np.eye(r))) <= 1e-12
     assert res <= 1e-8
+
+
+@pytest.mark.parametrize("levels,group,rank", [(8, 64, 16), (16, 0, 4)])
+def test_lora_act_order_from_x_chain(g, levels, group, rank):
+    # The GPU's own chain under act-order, X -> H -> basis -> H_L -> perm ->
+    # U -> sweep -> R, each stage against the oracle fed the GPU's upstream
+    # result: H (from X, float32 accumulation) within 1e-5, the basis span
+    # within sin(theta) 1e-8 of the oracle's V_r of that H, H_L within its
+    # float32 bound, the act-order permutation identical on the GPU's float32
+    # H_L, U within 1e-5, codes equal except at certified ties, the joint loss
+    # within 1e-3 of the oracle's on the same permutation.  Whether that
+    # permutation also equals the one of the float64 H_L of the exact H is
+    # reported (near-equal diagonal entries may sort either way).
+    import torch
+    m, n, T = 96, 256, 2048
+    log(f"lora act-order chain from X m={m} n={n} tokens={T} rank={rank} levels={levels} group={group}")
+    X, rng = _spiked_x(T, n, _spikes(rank), seed=100 + levels + rank)
+    W = (rng.standard_normal((m, n)) * 0.02).astype(np.float32)
+    q = g.gptq_lora_quantize_linear(dev(W), X=dev(X), rank=rank, levels=levels, group_size=group,
+                                    act_order=True, iters=12, seed=rank)
+    torch.cuda.synchronize()
+    Ho = oracle.hessian(X.astype(np.float64))
+    Hg = host(q["H"]).astype(np.float64)
+    assert np.linalg.norm(Hg - Ho) <= 1e-5 * np.linalg.norm(Ho)
+    Lg = host(q["L"])
+    Vr = oracle.lowrank_basis(Hg, rank)
+    sin_theta = float(np.linalg.norm(Lg - Vr @ (Vr.T @ Lg), 2))
+    assert sin_theta <= 1e-8
+    HLo, Ko = oracle.lowrank_hessian(Hg, Lg)
+    HLg = host(q["H_L"]).astype(np.float64)
+    M = Lg.T @ Hg @ Lg
+    tol = 2.0 ** -24 * np.abs(HLo) + 32 * (n + rank) * np.linalg.cond(M) * 2.0 ** -52 * np.max(np.abs(Hg))
+    assert np.all(np.abs(HLg - HLo) <= tol)
+    perm_o = oracle.act_order_perm(HLg)
+    np.testing.assert_array_equal(host(q["perm"]), perm_o)
+    same_as_exact = bool(np.array_equal(perm_o, oracle.act_order_perm(oracle.lowrank_hessian(Ho, oracle.lowrank_basis(Ho, rank))[0])))
+    Hd, _ = oracle.damp_and_permute(HLg, perm_o, 0.01)
+    U_o = oracle.inverse_cholesky_upper(Hd)
+    Ug = host(q["U"]).astype(np.float64)
+    err_u = float(np.linalg.norm(Ug - U_o) / np.linalg.norm(U_o))
+    assert err_u <= 1e-5
+    W64 = W.astype(np.float64)
+    res = oracle.gptq_quantize(W64, U_o, perm_o, levels, group, block_size=128)
+    cg = processing_order(host(q["codes"]), perm_o).astype(np.int64)
+    rows, ties = certify_ties(W64, Ug, perm_o, levels, group, 128, cg, res["codes"])
+    Wh = oracle.dequantize(dict(codes=cg.astype(np.float32), scales=host(q["scales"]), zeros=host(q["zeros"]),
+                                group_size=group, perm=perm_o))
+    Rg = host(q["R"]).astype(np.float64)
+    Dg = W64 - Wh - Rg.T @ Lg.T
+    lg = 0.5 * float(np.sum((Dg @ Ho) * Dg))
+    Who = oracle.dequantize(res)
+    Ro = oracle.lowrank_compensation(W64, Who, Ko)
+    Do = W64 - Who - Ro.T @ Lg.T
+    lo = 0.5 * float(np.sum((Do @ Ho) * Do))
+    log(f"  H ok, sin(theta) {sin_theta:.1e}, U rel_fro {err_u:.1e}, rows differing {rows} (ties {ties}), "
+        f"joint loss gpu/oracle {lg / lo:.6f}, perm equals the exact H's: {same_as_exact}")
+    assert abs(lg / lo - 1) <= 1e-3
