@@ -44,7 +44,7 @@ EXPORTS = (
     "gptq_lowrank_compensation",
 )
 
-GEMV_MAX_BATCH = 8
+GEMV_MAX_BATCH = 8   # X rows per pass of the VALU product kernel
 LOWRANK_MAX_RANK = 64
 
 _lib = None
@@ -98,7 +98,7 @@ def load(path: str = LIB_PATH):
     lib.gptq_asym_target.restype = C
     lib.gptq_asym_target.argtypes = [vp, C, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, sz, vp]
     lib.gptq_dequant_gemm.restype = C
-    lib.gptq_dequant_gemm.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, i64, i64, vp, i64, vp]
+    lib.gptq_dequant_gemm.argtypes = [vp, i64, i64, i64, C, vp, vp, i64, C, vp, vp, i64, i64, vp, i64, vp]
     lib.gptq_lowrank_ws_bytes.restype = sz
     lib.gptq_lowrank_ws_bytes.argtypes = [i64, i64, i64]
     lib.gptq_lowrank_basis.restype = C
@@ -320,14 +320,16 @@ def gptq_dequant_gemv(packed, scales, zeros, X, n: int, bits: int, group_size: i
     return Y
 
 
-def gptq_dequant_gemm(packed, scales, zeros, X, n: int, bits: int, group_size: int = 0, Y=None, stream=None):
-    """Y (batch x m float32) = X W^T on the matrix cores, any batch; groups of
-    group_size columns (0 or a multiple of 128), no g_idx."""
+def gptq_dequant_gemm(packed, scales, zeros, X, n: int, bits: int, group_size: int = 0, g_idx=None, Y=None,
+                      stream=None):
+    """Y (batch x m float32) = X W^T, any batch: on the matrix cores for
+    groups of 0 or a multiple of 128 columns, else (act-order g_idx, narrower
+    groups) on the VALU kernel, eight rows of X per pass."""
     torch = _torch()
     lib = load()
     _rows_check(packed)
     _rows_check(X)
-    _device_check(scales, zeros)
+    _device_check(scales, zeros, g_idx)
     if X.dtype != torch.float16:
         raise ValueError("X must be float16")
     m = packed.shape[0]
@@ -340,8 +342,8 @@ def gptq_dequant_gemm(packed, scales, zeros, X, n: int, bits: int, group_size: i
         _rows_check(Y)
     G = scales.shape[1] if scales.dim() == 2 else 1
     rc = lib.gptq_dequant_gemm(_ptr(packed), m, int(n), packed.stride(0), int(bits), _ptr(scales), _ptr(zeros),
-                               int(G), int(group_size), _ptr(X), batch, X.stride(0), _ptr(Y), Y.stride(0),
-                               _stream(stream))
+                               int(G), int(group_size), _ptr(g_idx), _ptr(X), batch, X.stride(0), _ptr(Y),
+                               Y.stride(0), _stream(stream))
     _check(rc, "gptq_dequant_gemm")
     return Y
 

@@ -695,46 +695,22 @@ void launch_bits(size_t shm, hipStream_t st, const uint32_t* packed, int m, int 
 
 using namespace gptq;
 
-extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
-                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
-                                         const int32_t* g_idx, const uint16_t* X, int64_t batch, int64_t ldx,
-                                         float* Y, int64_t ldy, void* stream) {
-  if (m < 0 || n < 0 || group_size < 0 || G < 1) return GPTQ_ERR_INVALID_ARG;
-  if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
-  if (batch < 1 || batch > GPTQ_GEMV_MAX_BATCH) return GPTQ_ERR_UNSUPPORTED;
-  if (m > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 30) || G > ((int64_t)1 << 30)) return GPTQ_ERR_UNSUPPORTED;
-  if (m == 0) return GPTQ_OK;
-  if (ld_packed < ceil_div(n * bits, 32) || ldx < n || ldy < m) return GPTQ_ERR_INVALID_ARG;
-  if (g_idx == nullptr && group_size > 0 && G < ceil_div(n, group_size)) return GPTQ_ERR_INVALID_ARG;
-  if (Y == nullptr || (n > 0 && (packed == nullptr || scales == nullptr || zeros == nullptr || X == nullptr)))
-    return GPTQ_ERR_INVALID_ARG;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
-  const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
-  const bool per_code = g_idx != nullptr || (group_size > 0 && group_size % 32 != 0);
-  if (!per_code && group_size % 128 == 0 && batch >= 3) {
-    // From three rows of X on, the matrix-core kernel is faster (one dot2 per
-    // code pair per X row makes the VALU kernel compute-bound).
-    const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
-    if (bits == 2)
-      launch_mfma_shape<2>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-    else if (bits == 3)
-      launch_mfma_shape<3>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-    else
-      launch_mfma_shape<4>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-    GPTQ_TRY_LAUNCH();
-    return GPTQ_OK;
-  }
+namespace {
+
+// The VALU kernel over batch rows b0 .. b0+bn-1 (bn <= GPTQ_GEMV_MAX_BATCH).
+gptq_status launch_valu_rows(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ld_packed, int bits,
+                             const float* scales, const uint8_t* zeros, int G, int group_size, const int32_t* g_idx,
+                             const uint16_t* X, int bn, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x,
+                             bool per_code) {
   const size_t shm_per_row = (size_t)G * sizeof(float2);
-  const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
 #define GPTQ_GEMV_BITS(B)                                                                                      \
   do {                                                                                                         \
     if (per_code)                                                                                              \
-      launch_bits<B, true>(shm_per_row, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
+      launch_bits<B, true>(shm_per_row, st, packed, m, n, ld_packed, scales, zeros, G, group_size, g_idx, X, bn, \
                            ldx, Y, ldy, vec_w, vec_x);                                                         \
     else                                                                                                       \
-      launch_bits<B, false>(0, st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, g_idx, X, bi, \
-                            ldx, Y, ldy, vec_w, vec_x);                                                        \
+      launch_bits<B, false>(0, st, packed, m, n, ld_packed, scales, zeros, G, group_size, g_idx, X, bn, ldx, Y,  \
+                            ldy, vec_w, vec_x);                                                                \
   } while (0)
   if (bits == 2)
     GPTQ_GEMV_BITS(2);
@@ -747,31 +723,66 @@ extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int6
   return GPTQ_OK;
 }
 
-extern "C" gptq_status gptq_dequant_gemm(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
-                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
-                                         const uint16_t* X, int64_t batch, int64_t ldx, float* Y, int64_t ldy,
-                                         void* stream) {
+// Y = X W^T for any batch: the matrix-core kernel when the groups are
+// contiguous multiples of 128 columns (or one per row) and the batch is at
+// least min_mfma_batch, else the VALU kernel over chunks of
+// GPTQ_GEMV_MAX_BATCH rows of X (act-order g_idx, narrower groups).
+gptq_status dequant_product(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
+                            const float* scales, const uint8_t* zeros, int64_t G, int group_size,
+                            const int32_t* g_idx, const uint16_t* X, int64_t batch, int64_t ldx, float* Y,
+                            int64_t ldy, void* stream, int64_t min_mfma_batch) {
   if (m < 0 || n < 0 || group_size < 0 || G < 1 || batch < 0) return GPTQ_ERR_INVALID_ARG;
   if (!(bits == 2 || bits == 3 || bits == 4)) return GPTQ_ERR_INVALID_ARG;
-  if (group_size % 128 != 0) return GPTQ_ERR_UNSUPPORTED;
   if (m > ((int64_t)1 << 31) - 1 || n > ((int64_t)1 << 30) || G > ((int64_t)1 << 30) ||
       ceil_div(batch, 128) > 65535)
     return GPTQ_ERR_UNSUPPORTED;
   if (m == 0 || batch == 0) return GPTQ_OK;
   if (ld_packed < ceil_div(n * bits, 32) || ldx < n || ldy < m) return GPTQ_ERR_INVALID_ARG;
-  if (group_size > 0 && G < ceil_div(n, group_size)) return GPTQ_ERR_INVALID_ARG;
+  if (g_idx == nullptr && group_size > 0 && G < ceil_div(n, group_size)) return GPTQ_ERR_INVALID_ARG;
   if (Y == nullptr || (n > 0 && (packed == nullptr || scales == nullptr || zeros == nullptr || X == nullptr)))
     return GPTQ_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int vec_w = (reinterpret_cast<uintptr_t>(packed) % 16 == 0) && (ld_packed % 4 == 0);
   const int vec_x = (reinterpret_cast<uintptr_t>(X) % 16 == 0) && (ldx % 8 == 0);
-  const int mi = (int)m, ni = (int)n, Gi = (int)G, bi = (int)batch;
-  if (bits == 2)
-    launch_mfma_shape<2>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-  else if (bits == 3)
-    launch_mfma_shape<3>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-  else
-    launch_mfma_shape<4>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
-  GPTQ_TRY_LAUNCH();
+  const int mi = (int)m, ni = (int)n, Gi = (int)G;
+  const bool per_code = g_idx != nullptr || (group_size > 0 && group_size % 32 != 0);
+  if (!per_code && group_size % 128 == 0 && batch >= min_mfma_batch) {
+    const int bi = (int)batch;
+    if (bits == 2)
+      launch_mfma_shape<2>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    else if (bits == 3)
+      launch_mfma_shape<3>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    else
+      launch_mfma_shape<4>(st, packed, mi, ni, ld_packed, scales, zeros, Gi, group_size, X, bi, ldx, Y, ldy, vec_w, vec_x);
+    GPTQ_TRY_LAUNCH();
+    return GPTQ_OK;
+  }
+  for (int64_t b0 = 0; b0 < batch; b0 += GPTQ_GEMV_MAX_BATCH) {
+    const int bn = (int)std::min<int64_t>(GPTQ_GEMV_MAX_BATCH, batch - b0);
+    const gptq_status rc = launch_valu_rows(st, packed, mi, ni, ld_packed, bits, scales, zeros, Gi, group_size, g_idx,
+                                            X + b0 * ldx, bn, ldx, Y + b0 * ldy, ldy, vec_w, vec_x, per_code);
+    if (rc != GPTQ_OK) return rc;
+  }
   return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" gptq_status gptq_dequant_gemv(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
+                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
+                                         const int32_t* g_idx, const uint16_t* X, int64_t batch, int64_t ldx,
+                                         float* Y, int64_t ldy, void* stream) {
+  if (batch < 1) return GPTQ_ERR_INVALID_ARG;
+  // From three rows of X on, the matrix-core kernel is faster (one dot2 per
+  // code pair per X row makes the VALU kernel compute-bound).
+  return dequant_product(packed, m, n, ld_packed, bits, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                         stream, 3);
+}
+
+extern "C" gptq_status gptq_dequant_gemm(const uint32_t* packed, int64_t m, int64_t n, int64_t ld_packed, int bits,
+                                         const float* scales, const uint8_t* zeros, int64_t G, int group_size,
+                                         const int32_t* g_idx, const uint16_t* X, int64_t batch, int64_t ldx,
+                                         float* Y, int64_t ldy, void* stream) {
+  return dequant_product(packed, m, n, ld_packed, bits, scales, zeros, G, group_size, g_idx, X, batch, ldx, Y, ldy,
+                         stream, 1);
 }

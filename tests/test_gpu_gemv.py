@@ -110,10 +110,10 @@ def test_dequant_gemv_edges(g):
     L = _layer(8, 64, 4, 0, False, seed=1)
     packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
     s, z = dev(L["scales"]), dev(L["zeros"], "u8")
-    # batch above the limit
+    # batch 0 is an error for the decode call
     with pytest.raises(Lb.GptqError) as ei:
-        g.gptq_dequant_gemv(packed, s, z, torch.zeros((9, 64), dtype=torch.float16, device="cuda"), 64, 4)
-    assert ei.value.status == Lb.GPTQ_ERR_UNSUPPORTED
+        g.gptq_dequant_gemv(packed, s, z, torch.zeros((0, 64), dtype=torch.float16, device="cuda"), 64, 4)
+    assert ei.value.status == Lb.GPTQ_ERR_INVALID_ARG
     # unsupported bit width
     with pytest.raises(Lb.GptqError) as ei:
         g.gptq_dequant_gemv(packed, s, z, torch.zeros((1, 64), dtype=torch.float16, device="cuda"), 64, 5)
@@ -160,13 +160,14 @@ def test_dequant_gemv_full_size_layer(g):
 # ---------------------------------------------------------------------------
 # Matrix-core product (gptq_dequant_gemm), any batch.
 # ---------------------------------------------------------------------------
-def _run_gemm(g, L, Xbuf, n, bits, group):
+def _run_gemm(g, L, Xbuf, n, bits, group, pass_gidx=False):
     import torch
     packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
     xd = torch.from_numpy(Xbuf).cuda()
     if Xbuf.shape[1] != n:
         xd = xd[:, :n]
-    Y = g.gptq_dequant_gemm(packed, dev(L["scales"]), dev(L["zeros"], "u8"), xd, n, bits, group_size=group)
+    Y = g.gptq_dequant_gemm(packed, dev(L["scales"]), dev(L["zeros"], "u8"), xd, n, bits, group_size=group,
+                            g_idx=dev(L["g_idx"], "i32") if pass_gidx else None)
     torch.cuda.synchronize()
     return host(Y).astype(np.float64)
 
@@ -183,6 +184,34 @@ GEMM_CASES = [
     (300, 1000, 3, 0, 257),     # prefill, ragged rows, columns and batch, 3-bit
     (130, 512, 2, 256, 130),    # prefill, 2-bit groups of 256
 ]
+
+
+# Layouts the matrix-core kernel does not take: act-order groups through
+# g_idx and groups narrower than 128 columns, at batches above one VALU pass
+# (eight rows of X), through both entry points.
+VALU_BATCH_CASES = [
+    # m, n, bits, group, act, batch
+    (96, 1024, 3, 128, True, 19),      # act-order g128, three passes, the last one ragged
+    (70, 640, 4, 64, False, 40),       # g64, five passes
+    (33, 500, 2, 16, True, 9),         # act-order groups narrower than a segment
+    (257, 4096, 4, 128, True, 64),     # act-order prefill-sized batch
+]
+
+
+@pytest.mark.parametrize("m,n,bits,group,act,batch", VALU_BATCH_CASES)
+def test_dequant_products_any_layout_any_batch(g, m, n, bits, group, act, batch):
+    import torch
+    log(f"dequant product any layout m={m} n={n} bits={bits} group={group} act={act} batch={batch}")
+    L = _layer(m, n, bits, group, act, seed=m + n + batch)
+    X16, Xbuf = _x(batch, n, seed=3 * n + batch)
+    _check(_run_gemm(g, L, Xbuf, n, bits, group, pass_gidx=act), L, X16, n, bits)
+    _check(_run(g, L, X16, Xbuf, n, bits, group, pass_gidx=act), L, X16, n, bits)
+    if act:
+        # the same layer with contiguous groups through g_idx (a permutation
+        # that keeps the order) equals the one without g_idx
+        Lc = _layer(m, n, bits, group, False, seed=m + n + batch)
+        Yg = _run_gemm(g, Lc, Xbuf, n, bits, group, pass_gidx=True)
+        _check(Yg, Lc, X16, n, bits)
 
 
 @pytest.mark.parametrize("m,n,bits,group,batch", GEMM_CASES)
@@ -204,11 +233,6 @@ def test_dequant_gemm_padded_strides_and_edges(g):
     _check(_run_gemm(g, L, Xbuf, n, bits, group), L, X16, n, bits)
     packed = torch.from_numpy(L["packed"].view(np.int32)).cuda()
     s, z = dev(L["scales"]), dev(L["zeros"], "u8")
-    # groups that are not a multiple of 128 columns
-    with pytest.raises(Lb.GptqError) as ei:
-        g.gptq_dequant_gemm(packed, s, z, torch.zeros((2, n), dtype=torch.float16, device="cuda"), n, bits,
-                            group_size=64)
-    assert ei.value.status == Lb.GPTQ_ERR_UNSUPPORTED
     # batch 0 is a no-op
     Y = g.gptq_dequant_gemm(packed, s, z, torch.zeros((0, n), dtype=torch.float16, device="cuda"), n, bits,
                             group_size=group)
