@@ -33,6 +33,8 @@ from .gptq_oracle import (  # noqa: F401
     lowrank_hessian,
     lowrank_compensation,
     gptq_lora_layer,
+    refine_codes,
+    lora_refine,
     gptq_layer,
 )
 from . import decoder_oracle  # noqa: F401,E402

@@ -562,6 +562,104 @@ def gptq_lora_layer(W, X=None, H=None, rank: int = 16, levels: int = 16, group_s
 
 
 # ---------------------------------------------------------------------------
+# f4 refinement: the Daily Papers page's GPTQ-intrinsic LoRA abstract names
+# "Bid-Up", a refinement of the codes on a fixed grid that can alternate with
+# the optimal low-rank compensation and never increases the layer-wise
+# reconstruction error; it prints no algorithm.  Reading taken (the plainest
+# step with that guarantee): cyclic coordinate descent on the codes, with the
+# scales, zeros and the current correction C = (L R)^T held fixed.
+#
+# Row i's error is f(d) = 1/2 d H d^T = ||X d^T||^2 with d = W_i - C_i - W^_i
+# and H = 2 X^T X (the undamped calibration Hessian).  Moving the value of
+# column j by delta changes f by -delta g_j + delta^2 H_jj / 2 with g = H d,
+# so among the grid values s (c - z) of that column the best is the one
+# nearest to W^_ij + g_j / H_jj; a move is made only when it lowers f (a tie
+# keeps the current code, and a column with H_jj = 0 does not take part), so
+# f never increases.  Columns are visited in their original order, rows are
+# independent.  Float64 throughout, decisions included (the refinement has no
+# float32 interface to reproduce).
+# ---------------------------------------------------------------------------
+def _grid_of_columns(scales, zeros, g_idx, n):
+    """Per-element scale and zero (m x n float64) of the fixed grid."""
+    gi = np.zeros(n, dtype=np.int64) if g_idx is None else np.asarray(g_idx, dtype=np.int64)
+    S = np.asarray(scales, dtype=F32).astype(F64)
+    Z = np.asarray(zeros).astype(F64)
+    if S.ndim == 1:
+        S, Z = S[:, None], Z[:, None]
+    return S[:, gi], Z[:, gi]
+
+
+def refine_codes(W, H, codes, scales, zeros, g_idx, levels: int, sweeps: int = 1, L=None, R=None):
+    """Coordinate-descent refinement of the codes on their fixed grid.
+
+    W m x n, H n x n (undamped), codes m x n in original column order, scales
+    and zeros m x G, g_idx the group of each column (None: one group per
+    row).  L (n x r) and R (r x m) give the low-rank correction held fixed
+    (None: no correction).  Returns (codes as int64, moves made in each sweep).
+    """
+    W = np.asarray(W, dtype=F64)
+    H = np.asarray(H, dtype=F64)
+    m, n = W.shape
+    T = W.copy()
+    if L is not None and np.asarray(L).shape[1] > 0:
+        T = T - np.asarray(R, dtype=F64).T @ np.asarray(L, dtype=F64).T
+    c = np.asarray(codes, dtype=np.int64).copy()
+    S, Z = _grid_of_columns(scales, zeros, g_idx, n)
+    maxq = levels - 1
+    moves = []
+    for _ in range(sweeps):
+        count = 0
+        for i in range(m):
+            what = S[i] * (c[i] - Z[i])
+            d = T[i] - what
+            g = H @ d
+            for j in range(n):
+                hjj = H[j, j]
+                if not hjj > 0:
+                    continue
+                v = what[j] + g[j] / hjj
+                cj = int(min(max(np.rint(v / S[i, j]) + Z[i, j], 0.0), float(maxq)))
+                if cj == c[i, j]:
+                    continue
+                delta = S[i, j] * (cj - Z[i, j]) - what[j]
+                gain = delta * g[j] - 0.5 * delta * delta * hjj
+                if not gain > 0:
+                    continue
+                c[i, j] = cj
+                what[j] = S[i, j] * (cj - Z[i, j])
+                d[j] -= delta
+                g -= delta * H[:, j]
+                count += 1
+        moves.append(count)
+    return c, moves
+
+
+def lora_refine(W, H, L, K, codes, scales, zeros, g_idx, levels: int, rounds: int = 1, sweeps: int = 1):
+    """Alternates the refinement (current R held fixed) with R = R*(codes).
+
+    Starts from R*(codes).  Returns (codes, R, joint losses 1/2 tr(D H D^T),
+    D = W - W^ - R^T L^T, before the first round and after each round).
+    """
+    W = np.asarray(W, dtype=F64)
+    H = np.asarray(H, dtype=F64)
+    L = np.asarray(L, dtype=F64)
+    S, Z = _grid_of_columns(scales, zeros, g_idx, W.shape[1])
+    c = np.asarray(codes, dtype=np.int64).copy()
+
+    def joint(cc, R):
+        D = W - S * (cc - Z) - R.T @ L.T
+        return 0.5 * float(np.sum((D @ H) * D))
+
+    R = lowrank_compensation(W, S * (c - Z), K)
+    losses = [joint(c, R)]
+    for _ in range(rounds):
+        c, _ = refine_codes(W, H, c, scales, zeros, g_idx, levels, sweeps, L=L, R=R)
+        R = lowrank_compensation(W, S * (c - Z), K)
+        losses.append(joint(c, R))
+    return c, R, losses
+
+
+# ---------------------------------------------------------------------------
 # End to end for one layer.
 # ---------------------------------------------------------------------------
 def gptq_layer(W, X=None, H=None, levels: int = 16, group_size: int = 0,
