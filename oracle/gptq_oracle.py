@@ -578,6 +578,15 @@ def gptq_lora_layer(W, X=None, H=None, rank: int = 16, levels: int = 16, group_s
 # f never increases.  Columns are visited in their original order, rows are
 # independent.  Float64 throughout, decisions included (the refinement has no
 # float32 interface to reproduce).
+#
+# Two alternations are offered.  Literal: the refinement with the current R
+# fixed, then R = R*.  Joint: since min over R of the joint error is
+# 1/2 d H_L d^T with d = W - W^ (H_L = H - H L M^{-1} L^T H), the same
+# coordinate descent run on H_L with no correction makes every move optimal
+# over the code and R together; R = R* afterwards gives the R it implies.
+# Both never increase the joint error.  Where the correction removes strong
+# directions of X (H_jj >> (H_L)_jj), the literal step g_j / H_jj seldom
+# reaches half a grid step, and the joint one is the one that moves codes.
 # ---------------------------------------------------------------------------
 def _grid_of_columns(scales, zeros, g_idx, n):
     """Per-element scale and zero (m x n float64) of the fixed grid."""
@@ -634,28 +643,42 @@ def refine_codes(W, H, codes, scales, zeros, g_idx, levels: int, sweeps: int = 1
     return c, moves
 
 
-def lora_refine(W, H, L, K, codes, scales, zeros, g_idx, levels: int, rounds: int = 1, sweeps: int = 1):
-    """Alternates the refinement (current R held fixed) with R = R*(codes).
+def lora_refine(W, H, L, codes, scales, zeros, g_idx, levels: int, rounds: int = 1, sweeps: int = 1,
+                joint: bool = True, HL=None):
+    """Alternates the refinement with the compensation R = R*(codes).
 
-    Starts from R*(codes).  Returns (codes, R, joint losses 1/2 tr(D H D^T),
-    D = W - W^ - R^T L^T, before the first round and after each round).
+    joint=False: the refinement holds the current R fixed (error
+    1/2 d H d^T with d = W - W^ - R^T L^T), the literal alternation.
+    joint=True: the refinement lowers min over R of the joint error, which
+    is 1/2 d H_L d^T with d = W - W^ (the identity behind the low-rank
+    path), i.e. the same coordinate descent with H_L and no correction:
+    every move is then optimal over the code and R together.  HL overrides
+    the H_L formed here (e.g. the float32 H_L another side hands on).
+    Both never increase the joint error.  Starts from R*(codes).  Returns
+    (codes, R, joint errors 1/2 tr(D H D^T), D = W - W^ - R^T L^T, before
+    the first round and after each round).
     """
     W = np.asarray(W, dtype=F64)
     H = np.asarray(H, dtype=F64)
     L = np.asarray(L, dtype=F64)
+    HL_formed, K = lowrank_hessian(H, L)
+    HL = HL_formed if HL is None else np.asarray(HL, dtype=F64)
     S, Z = _grid_of_columns(scales, zeros, g_idx, W.shape[1])
     c = np.asarray(codes, dtype=np.int64).copy()
 
-    def joint(cc, R):
+    def joint_error(cc, R):
         D = W - S * (cc - Z) - R.T @ L.T
         return 0.5 * float(np.sum((D @ H) * D))
 
     R = lowrank_compensation(W, S * (c - Z), K)
-    losses = [joint(c, R)]
+    losses = [joint_error(c, R)]
     for _ in range(rounds):
-        c, _ = refine_codes(W, H, c, scales, zeros, g_idx, levels, sweeps, L=L, R=R)
+        if joint:
+            c, _ = refine_codes(W, HL, c, scales, zeros, g_idx, levels, sweeps)
+        else:
+            c, _ = refine_codes(W, H, c, scales, zeros, g_idx, levels, sweeps, L=L, R=R)
         R = lowrank_compensation(W, S * (c - Z), K)
-        losses.append(joint(c, R))
+        losses.append(joint_error(c, R))
     return c, R, losses
 
 

@@ -161,48 +161,72 @@ def test_dead_column_and_zero_sweeps():
 
 
 # ---------------------------------------------------------------------------
-# Alternation with the compensation: the joint error ||X (W - W^ - R^T L^T)^T||^2
-# (computed from X) never increases from round to round, the refinement with
-# R held fixed lowers exactly that error, and the final R is the least-squares
-# optimum for the final codes (a least-squares solve on X L, which does not
-# use the compensation's formula).
+# Alternation with the compensation, both forms: the joint error
+# ||X (W - W^ - R^T L^T)^T||^2 (computed from X) never increases from round
+# to round and the final R is the least-squares optimum for the final codes
+# (a least-squares solve on X L, which does not use the compensation's
+# formula).  Literal form: the refinement with R held fixed lowers exactly
+# that error with R fixed.  Joint form: once a round changes nothing, no
+# single change of a code lowers min over R of the joint error (brute force
+# over every single change, each with its own least-squares R).
 # ---------------------------------------------------------------------------
+def _min_over_r(W, What, X, L):
+    XL = X @ L
+    D = W - What
+    R = np.linalg.lstsq(XL, X @ D.T, rcond=None)[0]
+    return np.sum(((D - R.T @ L.T) @ X.T) ** 2, axis=1), R
+
+
+@pytest.mark.parametrize("joint", [False, True])
 @pytest.mark.parametrize("rank,levels,group", [(1, 3, 0), (2, 4, 2), (3, 16, 0)])
-def test_alternation_with_the_compensation(rank, levels, group):
+def test_alternation_with_the_compensation(rank, levels, group, joint):
     m, n = 4, 6
     W, X, scales, zeros, g_idx = _layer(20 + rank, m, n, 40, levels, group, spikes=(5.0, 3.0, 2.0)[:rank])
     H = 2.0 * X.T @ X
     L = oracle.lowrank_basis(H, rank)
-    HL, K = oracle.lowrank_hessian(H, L)
+    HL, _ = oracle.lowrank_hessian(H, L)
     res = oracle.gptq_layer(W, H=HL, levels=levels, group_size=group if group else 0, damp_rel=0.01)
+    sc, ze, gi = res["scales"], res["zeros"].astype(np.uint8), res["g_idx"]
     codes0 = res["codes_orig"]
-    codes, R, losses = oracle.lora_refine(W, H, L, K, codes0, res["scales"], res["zeros"].astype(np.uint8),
-                                          res["g_idx"], levels, rounds=3, sweeps=1)
-    What = _what(codes, res["scales"], res["zeros"].astype(np.uint8), res["g_idx"])
-    # the least-squares R for these codes, from X L directly
-    XL = X @ L
-    Rls = np.linalg.lstsq(XL, X @ (W - What).T, rcond=None)[0]
+    codes, R, losses = oracle.lora_refine(W, H, L, codes0, sc, ze, gi, levels, rounds=3, sweeps=1, joint=joint)
+    What = _what(codes, sc, ze, gi)
+    rows, Rls = _min_over_r(W, What, X, L)
     np.testing.assert_allclose(R, Rls, rtol=1e-8, atol=1e-10)
     direct = float(np.sum(((W - What - R.T @ L.T) @ X.T) ** 2))
     np.testing.assert_allclose(losses[-1], direct, rtol=1e-9)
+    np.testing.assert_allclose(direct, rows.sum(), rtol=1e-9)
     assert all(b <= a * (1 + 1e-12) for a, b in zip(losses, losses[1:]))
     if np.any(codes != codes0):
         assert losses[-1] < losses[0]
     # from arbitrary codes on the same grid the alternation must make progress
     start = np.random.default_rng(rank).integers(0, levels, codes0.shape)
-    _, _, lr = oracle.lora_refine(W, H, L, K, start, res["scales"], res["zeros"].astype(np.uint8), res["g_idx"],
-                                  levels, rounds=2, sweeps=1)
+    _, _, lr = oracle.lora_refine(W, H, L, start, sc, ze, gi, levels, rounds=2, sweeps=1, joint=joint)
     assert lr[0] > lr[1] >= lr[2] * (1 - 1e-12)
-    # the refinement step itself, R held at its value before the last round
-    c_prev, R_prev, _ = oracle.lora_refine(W, H, L, K, codes0, res["scales"], res["zeros"].astype(np.uint8),
-                                           res["g_idx"], levels, rounds=2, sweeps=1)
-    c_step, _ = oracle.refine_codes(W, H, c_prev, res["scales"], res["zeros"].astype(np.uint8), res["g_idx"],
-                                    levels, sweeps=1, L=L, R=R_prev)
-    T = W - R_prev.T @ L.T
-    before = np.sum(((T - _what(c_prev, res["scales"], res["zeros"].astype(np.uint8), res["g_idx"])) @ X.T) ** 2)
-    after = np.sum(((T - _what(c_step, res["scales"], res["zeros"].astype(np.uint8), res["g_idx"])) @ X.T) ** 2)
-    assert after <= before * (1 + 1e-12)
-    np.testing.assert_array_equal(c_step, codes)
+    if not joint:
+        # the refinement step itself, R held at its value before the last round
+        c_prev, R_prev, _ = oracle.lora_refine(W, H, L, codes0, sc, ze, gi, levels, rounds=2, sweeps=1, joint=False)
+        c_step, _ = oracle.refine_codes(W, H, c_prev, sc, ze, gi, levels, sweeps=1, L=L, R=R_prev)
+        T = W - R_prev.T @ L.T
+        before = np.sum(((T - _what(c_prev, sc, ze, gi)) @ X.T) ** 2)
+        after = np.sum(((T - _what(c_step, sc, ze, gi)) @ X.T) ** 2)
+        assert after <= before * (1 + 1e-12)
+        np.testing.assert_array_equal(c_step, codes)
+        return
+    # joint form, run to its fixed point from the arbitrary start
+    c = start
+    for _ in range(40):
+        c_new, _, _ = oracle.lora_refine(W, H, L, c, sc, ze, gi, levels, rounds=1, sweeps=1, joint=True)
+        if np.array_equal(c_new, c):
+            break
+        c = c_new
+    assert np.array_equal(c_new, c)
+    best, _ = _min_over_r(W, _what(c, sc, ze, gi), X, L)
+    for i, j in itertools.product(range(m), range(n)):
+        for cc in range(levels):
+            alt = c.copy()
+            alt[i, j] = cc
+            li, _ = _min_over_r(W, _what(alt, sc, ze, gi), X, L)
+            assert li[i] >= best[i] * (1 - 1e-9), (i, j, cc)
 
 
 # ---------------------------------------------------------------------------
@@ -232,7 +256,8 @@ def test_refine_planted_mistakes_are_caught(name, monkeypatch):
     for check in (lambda: test_diagonal_hessian_gives_the_nearest_grid_value(16, 0),
                   lambda: test_monotone_and_coordinatewise_optimal(1, 3, 0),
                   lambda: test_monotone_and_coordinatewise_optimal(3, 16, 0),
-                  lambda: test_alternation_with_the_compensation(2, 4, 2)):
+                  lambda: test_alternation_with_the_compensation(2, 4, 2, False),
+                  lambda: test_alternation_with_the_compensation(2, 4, 2, True)):
         try:
             check()
         except AssertionError:
