@@ -306,6 +306,47 @@ gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int64_t m, int
                                       int group_size, const int32_t* g_idx, const double* K, int64_t r,
                                       float* R, int64_t ldr, void* ws, size_t ws_bytes, void* stream);
 
+/* Fixed-grid refinement of the codes, to alternate with
+ * gptq_lowrank_compensation (Daily Papers page, GPTQ-intrinsic LoRA abstract:
+ * "Bid-Up", a refinement on the fixed grid that alternates with the optimal
+ * low-rank compensation and never increases the layer-wise error; the page
+ * prints no algorithm).  Reading implemented: cyclic coordinate descent.
+ * With the grid (scales, zeros) and the correction C = (L R)^T held fixed,
+ * row i's error 1/2 d H d^T, d = W_i - C_i - W^_i, is lowered one column at
+ * a time in original column order: column j's code becomes the one whose
+ * grid value s (c - z) is nearest to W^_ij + g_j / H_jj, g = H d, when that
+ * lowers the error (a tie keeps the code; columns with H_jj <= 0 keep
+ * theirs).  The error never increases.  Float64 throughout.
+ * Two uses with the compensation: H = 2 X^T X with the current (L, R) held
+ * fixed (the literal alternation), or H = H_L from gptq_lowrank_hessian
+ * with r = 0: min over R of the joint error is 1/2 d H_L d^T with
+ * d = W - W^, so every move is then optimal over the code and R together
+ * (recompute R with gptq_lowrank_compensation afterwards).
+ *   W, w_dtype, m, n, ldw   the layer (float32, float16 or bfloat16), m, n >= 1.
+ *   H      device, n x n float32 (ldh >= n), exactly symmetric: the
+ *          undamped calibration Hessian (as gptq_hessian_accumulate writes
+ *          it) or H_L (as gptq_lowrank_hessian writes it).
+ *   L, R   the correction: L device n x r float64 (leading dimension r), R
+ *          device r x m float32 (ldr >= m), as gptq_lowrank_basis and
+ *          gptq_lowrank_compensation write them; r = 0 for none (L, R may
+ *          then be NULL).  0 <= r <= GPTQ_LOWRANK_MAX_RANK, r <= n.
+ *   scales, zeros, group_size, g_idx   the fixed grid, as for
+ *          gptq_lowrank_compensation (m x G, G = ceil(n / group_size) or 1).
+ *   levels 2 .. 256 (codes stay in [0, levels - 1]).
+ *   sweeps >= 0 passes over all columns (0: nothing is launched).
+ *   codes  device, m x n uint8, original column order: read, and
+ *          overwritten with the refined codes.
+ *   moves  device int64[sweeps] output (the number of codes changed in each
+ *          pass), or NULL.
+ * Workspace gptq_refine_ws_bytes(m, n) (0 for sizes it does not take: m or n
+ * outside 1 .. 2^31 - 1, or m n > 2^48).  Does not synchronise. */
+size_t gptq_refine_ws_bytes(int64_t m, int64_t n);
+gptq_status gptq_refine_codes(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw, const float* H,
+                              int64_t ldh, const double* L, const float* R, int64_t r, int64_t ldr,
+                              const float* scales, const uint8_t* zeros, int group_size, const int32_t* g_idx,
+                              int levels, int sweeps, uint8_t* codes, int64_t* moves, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* ------------------------------------------------------------------------
  * Reading the packed weights back: matrix-vector product for decode
  * (GPTQ knowledge note, "Tradeoffs": the speed of a quantized model rests on

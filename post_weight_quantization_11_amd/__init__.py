@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     gptq_hessian_accumulate_noalloc,
     gptq_hessian_pair_accumulate,
     gptq_lora_quantize_linear,
+    gptq_lora_refine,
     gptq_lowrank_basis,
     gptq_lowrank_compensation,
     gptq_lowrank_hessian,
@@ -21,6 +22,7 @@ from ._lib import (  # noqa: F401
     gptq_prepare_hinv,
     gptq_quantize_layer,
     gptq_quantize_linear,
+    gptq_refine_codes,
     load,
     packed_words,
 )

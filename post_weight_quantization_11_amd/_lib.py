@@ -42,6 +42,8 @@ EXPORTS = (
     "gptq_lowrank_basis",
     "gptq_lowrank_hessian",
     "gptq_lowrank_compensation",
+    "gptq_refine_ws_bytes",
+    "gptq_refine_codes",
 )
 
 GEMV_MAX_BATCH = 8   # X rows per pass of the VALU product kernel
@@ -108,6 +110,11 @@ def load(path: str = LIB_PATH):
     lib.gptq_lowrank_compensation.restype = C
     lib.gptq_lowrank_compensation.argtypes = [vp, C, i64, i64, i64, vp, vp, vp, C, vp, vp, i64, vp, i64, vp, sz,
                                               vp]
+    lib.gptq_refine_ws_bytes.restype = sz
+    lib.gptq_refine_ws_bytes.argtypes = [i64, i64]
+    lib.gptq_refine_codes.restype = C
+    lib.gptq_refine_codes.argtypes = [vp, C, i64, i64, i64, vp, i64, vp, vp, i64, i64, vp, vp, C, vp, C, C, vp, vp,
+                                      vp, sz, vp]
     _lib = lib
     return lib
 
@@ -444,6 +451,60 @@ def gptq_lowrank_compensation(W, q, K, group_size: int = 0, R=None, ws=None, str
                                        _stream(stream))
     _check(rc, "gptq_lowrank_compensation")
     return R
+
+
+def gptq_refine_codes(W, H, q, levels: int, group_size: int = 0, sweeps: int = 1, L=None, R=None, codes=None,
+                      ws=None, stream=None):
+    """Fixed-grid refinement of q's codes (coordinate descent on the error
+    1/2 d H d^T, d = W - R^T L^T - W^, grid q["scales"] / q["zeros"] /
+    q["g_idx"] held fixed).  H is the undamped calibration Hessian.  The
+    refined codes go to `codes` (default: a copy of q["codes"]).  Returns
+    (codes, moves), moves an int64 device tensor with the number of codes
+    changed in each sweep."""
+    torch = _torch()
+    lib = load()
+    _rows_check(W)
+    _rows_check(H)
+    g_idx = q.get("g_idx")
+    _device_check(L, R, g_idx, q["codes"], q["scales"], q["zeros"], codes)
+    m, n = W.shape
+    r = 0 if L is None else L.shape[1]
+    if codes is None:
+        codes = q["codes"].clone()
+    moves = torch.zeros(max(1, int(sweeps)), dtype=torch.int64, device=W.device)
+    if ws is None:
+        ws = _workspace(lib.gptq_refine_ws_bytes(m, n), W.device)
+    rc = lib.gptq_refine_codes(_ptr(W), _dtype_code(W), m, n, W.stride(0), _ptr(H), H.stride(0), _ptr(L), _ptr(R),
+                               r, 0 if R is None else R.stride(0), _ptr(q["scales"]), _ptr(q["zeros"]),
+                               int(group_size), _ptr(g_idx), int(levels), int(sweeps), _ptr(codes), _ptr(moves),
+                               _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream))
+    _check(rc, "gptq_refine_codes")
+    return codes, moves[:int(sweeps)]
+
+
+def gptq_lora_refine(W, q, levels: int, group_size: int = 0, rounds: int = 1, sweeps: int = 1,
+                     joint: bool = True, stream=None):
+    """Alternates the fixed-grid refinement with R = R*(codes) for a layer
+    from gptq_lora_quantize_linear (q holds H, H_L, L, K, R, the grid and the
+    codes).  joint=True refines on H_L (every move optimal over the code and
+    R together); joint=False holds the current R fixed and refines on H.
+    Updates q["codes"], q["R"] and q["packed"]; returns the moves of each
+    round (int64 device tensor, rounds x sweeps)."""
+    torch = _torch()
+    ws = _workspace(load().gptq_refine_ws_bytes(W.shape[0], W.shape[1]), W.device)
+    per_round = []
+    for _ in range(int(rounds)):
+        if joint:
+            codes, moves = gptq_refine_codes(W, q["H_L"], q, levels, group_size, sweeps, codes=q["codes"], ws=ws,
+                                             stream=stream)
+        else:
+            codes, moves = gptq_refine_codes(W, q["H"], q, levels, group_size, sweeps, L=q["L"], R=q["R"],
+                                             codes=q["codes"], ws=ws, stream=stream)
+        q["codes"] = codes
+        q["R"] = gptq_lowrank_compensation(W, q, q["K"], group_size, R=q["R"], stream=stream)
+        per_round.append(moves)
+    q["packed"] = gptq_pack(q["codes"], bits_for_levels(levels), stream=stream)
+    return torch.stack(per_round) if per_round else torch.zeros((0, int(sweeps)), dtype=torch.int64)
 
 
 def gptq_lora_quantize_linear(W, X=None, H=None, rank: int = 16, levels: int = 16, group_size: int = 0,

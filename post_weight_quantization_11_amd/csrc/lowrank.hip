@@ -134,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void compensation_kernel(TallArgs a) {
   }
 }
 
-// The same product on the matrix cores for A(p, k) = S[k][p] (S float32 or
-// float64, widened exactly): float64 MFMA 16x16x4 (A element (row l%16,
+// The same product on the matrix cores for A(p, k) = S[k][p] (S and B float32
+// or float64, widened exactly): float64 MFMA 16x16x4 (A element (row l%16,
 // k l/16), B element (k l/16, column l%16), accumulator register i of lane l
 // at row l/16 + 4i, column l%16).  A workgroup owns kMP rows and all kR
 // columns; its four waves take every fourth 4-deep K step of the split, keep
@@ -145,9 +145,9 @@ constexpr int kMP = 32;                   // rows per workgroup
 constexpr int kDepth = 4;                 // K steps in flight per wave
 constexpr int kMChunk = 16 * kDepth;      // K granularity of a split
 
-template <typename ST>
+template <typename ST, typename BT = double>
 __global__ __launch_bounds__(kThreads) void tall_mfma_kernel(const ST* __restrict__ S, int64_t lds_,
-                                                             const double* __restrict__ B, int64_t ldb, int64_t P,
+                                                             const BT* __restrict__ B, int64_t ldb, int64_t P,
                                                              int64_t K, int r, int64_t kchunk,
                                                              double* __restrict__ part) {
   __shared__ double red[3][kMP][kR + 1];
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void tall_mfma_kernel(const ST* __restric
     a0[d] = (kin_ && pa_in) ? static_cast<double>(S[k_ * lds_ + pa]) : 0.0;        \
     a1[d] = (kin_ && pb_in) ? static_cast<double>(S[k_ * lds_ + pb]) : 0.0;        \
     _Pragma("unroll") for (int tj = 0; tj < 4; ++tj)                                \
-      b[d][tj] = (kin_ && c_in[tj]) ? B[k_ * ldb + 16 * tj + cl] : 0.0;             \
+      b[d][tj] = (kin_ && c_in[tj]) ? static_cast<double>(B[k_ * ldb + 16 * tj + cl]) : 0.0; \
   } while (0)
 
 #pragma unroll
@@ -531,6 +531,191 @@ __global__ __launch_bounds__(kThreads) void downdate_kernel(const float* __restr
 }
 
 // ---------------------------------------------------------------------------
+// Fixed-grid refinement of the codes (Daily Papers page, GPTQ-intrinsic LoRA
+// abstract: "Bid-Up", a refinement on the fixed grid that alternates with the
+// optimal low-rank compensation and never increases the layer-wise error; no
+// algorithm is printed).  Reading: cyclic coordinate descent.  Row i's error
+// is 1/2 d H d^T with d = W_i - C_i - W^_i (C = (L R)^T held fixed, H the
+// undamped H = 2 X^T X); moving column j's value by delta changes it by
+// -delta g_j + delta^2 H_jj / 2, g = H d, so the best grid value of that
+// column is the one nearest to W^_ij + g_j / H_jj, taken only when it lowers
+// the error (H_jj = 0 columns do not take part).  Columns in original order.
+//
+// The residual is kept transposed, Dt[j][i] = d_i[j] (float64, n x m), so
+// that one block's g for all rows is a tall product Dt^T H[:, block] on the
+// float64 matrix cores (tall_mfma_kernel, split over K), and the in-block
+// sequence runs one row per lane: per block of kRB columns, g from the
+// product, then each column's decision and the update g_k -= delta H_jk of
+// the block's later columns (the product of the next block sees every move
+// made so far).  In exact arithmetic this is the column-by-column sequence.
+// Float64 throughout; the decision arithmetic (v, rint, the gain) is written
+// without contraction, in the order the definition gives it.
+// ---------------------------------------------------------------------------
+constexpr int kRB = 64;   // columns per refinement block (= kR, the product's column tile)
+static_assert(kRB == kR, "one block is one column tile of the tall product");
+
+// Dt[j][i] = (W[i][j] - sum_a R[a][i] L[j][a]) - s_g(j) (c - z_g(j)) for a
+// 64 x 64 tile of (rows i, columns j); lane = row, wave = 16 columns.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void refine_residual_kernel(
+    const void* __restrict__ W, int64_t ldw, int64_t m, int64_t n, const double* __restrict__ L,
+    const float* __restrict__ R, int r, int64_t ldr, const uint8_t* __restrict__ codes,
+    const float* __restrict__ scales, const uint8_t* __restrict__ zeros, int64_t G, int64_t group,
+    const int32_t* __restrict__ gidx, double* __restrict__ Dt) {
+  __shared__ double Ls[64][kR + 1];
+  __shared__ double Rs[kR][64];
+  const int tid = threadIdx.x, li = tid & 63, jg = tid >> 6;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * 64, j0 = static_cast<int64_t>(blockIdx.y) * 64;
+  for (int e = tid; e < 64 * r; e += kThreads) {
+    const int jj = e / r, a = e % r;
+    Ls[jj][a] = j0 + jj < n ? L[(j0 + jj) * r + a] : 0.0;
+  }
+  for (int e = tid; e < 64 * r; e += kThreads) {
+    const int a = e >> 6, ii = e & 63;
+    Rs[a][ii] = i0 + ii < m ? static_cast<double>(R[a * ldr + i0 + ii]) : 0.0;
+  }
+  __syncthreads();
+  const int64_t i = i0 + li;
+  if (i >= m) return;
+  for (int jj = 16 * jg; jj < 16 * jg + 16; ++jj) {
+    const int64_t j = j0 + jj;
+    if (j >= n) break;
+    double corr = 0.0;
+    for (int a = 0; a < r; ++a) corr = __builtin_fma(Rs[a][li], Ls[jj][a], corr);
+    const int64_t g = gidx ? static_cast<int64_t>(gidx[j]) : (group ? j / group : 0);
+    const double s = static_cast<double>(scales[i * G + g]);
+    const double z = static_cast<double>(zeros[i * G + g]);
+    const double c = static_cast<double>(codes[i * n + j]);
+    Dt[j * m + i] = (w_elem<DT>(W, i * ldw + j) - corr) - s * (c - z);
+  }
+}
+
+__global__ void refine_clear_kernel(unsigned long long* __restrict__ p, int count) {
+  const int e = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (e < count) p[e] = 0ull;
+}
+
+// Block c0 .. c0+bw-1 for 64 rows (one wave; lane = row).  part holds the
+// block's split partials of Dt^T H[:, block] (kR columns per row, zero past
+// bw).  Writes the block's codes and residual columns; adds the number of
+// moves to *count (when not null).
+__global__ __launch_bounds__(64) void refine_sweep_kernel(
+    const double* __restrict__ part, int splits, int64_t m, int64_t n, int c0, int bw,
+    const float* __restrict__ H, int64_t ldh, const float* __restrict__ scales, const uint8_t* __restrict__ zeros,
+    int64_t G, int64_t group, const int32_t* __restrict__ gidx, double maxq, int codes_vec,
+    uint8_t* __restrict__ codes, double* __restrict__ Dt, unsigned long long* __restrict__ count) {
+#pragma clang fp contract(off)
+  __shared__ float2 grid[kRB][64];   // (s, z) of each column for each lane's row
+  const int lane = static_cast<int>(threadIdx.x);
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool active = i < m;
+  const int64_t ir = active ? i : m - 1;   // lanes past m follow row m-1 and write nothing
+  for (int j = 0; j < bw; ++j) {
+    const int64_t col = c0 + j;
+    const int64_t g = gidx ? static_cast<int64_t>(gidx[col]) : (group ? col / group : 0);
+    grid[j][lane] = float2{scales[ir * G + g], static_cast<float>(zeros[ir * G + g])};
+  }
+  double g[kRB];
+#pragma unroll
+  for (int j = 0; j < kRB; ++j) g[j] = 0.0;
+  for (int t = 0; t < splits; ++t) {
+    const double* p = part + (static_cast<int64_t>(t) * m + ir) * kR;
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) g[j] += p[j];
+  }
+  uint32_t cw[kRB / 4], c_old[kRB / 4];
+  uint8_t* crow = codes + ir * n + c0;
+  if (codes_vec && bw == kRB) {
+#pragma unroll
+    for (int q = 0; q < kRB / 16; ++q) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(crow)[q];
+      cw[4 * q] = v[0]; cw[4 * q + 1] = v[1]; cw[4 * q + 2] = v[2]; cw[4 * q + 3] = v[3];
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < kRB / 4; ++q) {
+      uint32_t v = 0u;
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (4 * q + t < bw) v |= static_cast<uint32_t>(crow[4 * q + t]) << (8 * t);
+      cw[q] = v;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kRB / 4; ++q) c_old[q] = cw[q];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  int moved = 0;
+  const float* hb = H + static_cast<int64_t>(c0) * ldh + c0;   // the block's diagonal block of H
+  // Every index into g and cw is a compile-time constant after unrolling
+  // (the bound bw is a uniform guard, not a trip count), so both stay in
+  // registers.
+#pragma unroll
+  for (int j = 0; j < kRB; ++j) {
+    if (j < bw) {
+    const double hjj = static_cast<double>(hb[static_cast<int64_t>(j) * ldh + j]);
+    const float2 sz = grid[j][lane];
+    const double s = static_cast<double>(sz.x), z = static_cast<double>(sz.y);
+    const int cold = static_cast<int>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
+    const double what = s * (static_cast<double>(cold) - z);
+    double delta = 0.0;
+    if (hjj > 0.0) {
+      const double v = what + g[j] / hjj;
+      const double q = fmin(fmax(rint(v / s) + z, 0.0), maxq);
+      const int cn = static_cast<int>(q);
+      if (cn != cold) {
+        const double d = s * (static_cast<double>(cn) - z) - what;
+        const double gain = d * g[j] - 0.5 * d * d * hjj;
+        if (gain > 0.0 && active) {
+          delta = d;
+          const int sh = 8 * (j & 3);
+          cw[j >> 2] = (cw[j >> 2] & ~(0xffu << sh)) | (static_cast<uint32_t>(cn) << sh);
+          ++moved;
+        }
+      }
+    }
+    if (__any(delta != 0.0)) {
+#pragma unroll
+      for (int k = j + 1; k < kRB; ++k)
+        if (k < bw) g[k] = g[k] - delta * static_cast<double>(hb[static_cast<int64_t>(j) * ldh + k]);
+    }
+    }
+  }
+
+  if (active) {
+    if (codes_vec && bw == kRB) {
+#pragma unroll
+      for (int q = 0; q < kRB / 16; ++q)
+        reinterpret_cast<u32x4*>(crow)[q] = u32x4{cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]};
+    } else {
+      for (int j = 0; j < bw; ++j) crow[j] = static_cast<uint8_t>(cw[j >> 2] >> (8 * (j & 3)));
+    }
+    // the residual of each moved column: d_j -= delta, delta recomputed from
+    // the old and new codes exactly as in the sequence above
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+      if (j >= bw) continue;
+      const int co = static_cast<int>((c_old[j >> 2] >> (8 * (j & 3))) & 0xffu);
+      const int cn = static_cast<int>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
+      if (co != cn) {
+        const float2 sz = grid[j][lane];
+        const double s = static_cast<double>(sz.x), z = static_cast<double>(sz.y);
+        const double d = s * (static_cast<double>(cn) - z) - s * (static_cast<double>(co) - z);
+        double* p = Dt + static_cast<int64_t>(c0 + j) * m + i;
+        *p = *p - d;
+      }
+    }
+  }
+  if (count != nullptr) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) moved += __shfl_xor(moved, off);
+    if (lane == 0 && moved > 0) atomicAdd(count, static_cast<unsigned long long>(moved));
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Host side.
 // ---------------------------------------------------------------------------
 struct Split {
@@ -678,6 +863,34 @@ gptq_status read_flag(const Ctx& c) {
 
 bool rank_ok(int64_t n, int64_t r) { return n >= 1 && r >= 1 && r <= kR && r <= n; }
 
+// Refinement workspace: the transposed residual Dt (n x m float64) and the
+// split partials of one block's product.
+struct RefineLayout {
+  Split split;
+  size_t off_dt, off_part, total;
+};
+
+RefineLayout refine_layout(int64_t m, int64_t n) {
+  RefineLayout L;
+  L.split = choose_split_mfma(m, n, kTargetBlocks);
+  L.off_dt = 0;
+  L.off_part = align256(static_cast<size_t>(n) * static_cast<size_t>(m) * sizeof(double));
+  L.total = align256(L.off_part + part_bytes(L.split, m));
+  return L;
+}
+
+template <int DT>
+gptq_status launch_refine_residual(const void* W, int64_t ldw, int64_t m, int64_t n, const double* L,
+                                   const float* R, int64_t r, int64_t ldr, const uint8_t* codes,
+                                   const float* scales, const uint8_t* zeros, int64_t G, int64_t group,
+                                   const int32_t* gidx, double* Dt, hipStream_t st) {
+  const dim3 grid(static_cast<unsigned>(ceil_div(m, 64)), static_cast<unsigned>(ceil_div(n, 64)));
+  refine_residual_kernel<DT><<<grid, kThreads, 0, st>>>(W, ldw, m, n, L, R, static_cast<int>(r), ldr, codes, scales,
+                                                        zeros, G, group, gidx, Dt);
+  GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}
+
 }  // namespace
 }  // namespace gptq
 
@@ -755,5 +968,68 @@ extern "C" gptq_status gptq_lowrank_compensation(const void* W, int w_dtype, int
   reduce_splits_kernel<true><<<static_cast<unsigned>(ceil_div(m * r, kThreads)), kThreads, 0, c.st>>>(
       c.part, static_cast<int>(s.splits), m, r, R, ldr);
   GPTQ_TRY_LAUNCH();
+  return GPTQ_OK;
+}
+
+// Sizes the refinement takes: rows and columns each below 2^31, at most 2^48
+// residual entries.
+static bool refine_size_ok(int64_t m, int64_t n) {
+  return m >= 1 && n >= 1 && m <= INT32_MAX && n <= INT32_MAX && m <= ((int64_t)1 << 48) / n;
+}
+
+extern "C" size_t gptq_refine_ws_bytes(int64_t m, int64_t n) {
+  if (!refine_size_ok(m, n)) return 0;
+  return refine_layout(m, n).total;
+}
+
+extern "C" gptq_status gptq_refine_codes(const void* W, int w_dtype, int64_t m, int64_t n, int64_t ldw,
+                                         const float* H, int64_t ldh, const double* L, const float* R, int64_t r,
+                                         int64_t ldr, const float* scales, const uint8_t* zeros, int group_size,
+                                         const int32_t* g_idx, int levels, int sweeps, uint8_t* codes,
+                                         int64_t* moves, void* ws, size_t ws_bytes, void* stream) {
+  if (!W || !H || !scales || !zeros || !codes || !valid_dtype(w_dtype)) return GPTQ_ERR_INVALID_ARG;
+  if (!refine_size_ok(m, n) || ldw < n || ldh < n) return GPTQ_ERR_INVALID_ARG;
+  if (levels < 2 || levels > 256 || sweeps < 0 || group_size < 0) return GPTQ_ERR_INVALID_ARG;
+  if (r < 0 || r > kR || r > n) return GPTQ_ERR_INVALID_ARG;
+  if (r > 0 && (!L || !R || ldr < m)) return GPTQ_ERR_INVALID_ARG;
+  const RefineLayout lay = refine_layout(m, n);
+  if (!ws || ws_bytes < lay.total) return GPTQ_ERR_WORKSPACE;
+  if (sweeps == 0) return GPTQ_OK;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  double* Dt = reinterpret_cast<double*>(base + lay.off_dt);
+  double* part = reinterpret_cast<double*>(base + lay.off_part);
+  const int64_t G = group_size ? ceil_div(n, group_size) : 1;
+  gptq_status rc = w_dtype == GPTQ_F32
+                       ? launch_refine_residual<GPTQ_F32>(W, ldw, m, n, L, R, r, ldr, codes, scales, zeros, G,
+                                                          group_size, g_idx, Dt, st)
+                   : w_dtype == GPTQ_F16
+                       ? launch_refine_residual<GPTQ_F16>(W, ldw, m, n, L, R, r, ldr, codes, scales, zeros, G,
+                                                          group_size, g_idx, Dt, st)
+                       : launch_refine_residual<GPTQ_BF16>(W, ldw, m, n, L, R, r, ldr, codes, scales, zeros, G,
+                                                           group_size, g_idx, Dt, st);
+  if (rc != GPTQ_OK) return rc;
+  unsigned long long* cnt = reinterpret_cast<unsigned long long*>(moves);
+  if (cnt != nullptr) {
+    refine_clear_kernel<<<static_cast<unsigned>(ceil_div(sweeps, 256)), 256, 0, st>>>(cnt, sweeps);
+    GPTQ_TRY_LAUNCH();
+  }
+  const int codes_vec = (reinterpret_cast<uintptr_t>(codes) & 15) == 0 && n % 16 == 0;
+  const Split& sp = lay.split;
+  const int nblk = static_cast<int>(ceil_div(n, kRB));
+  for (int sw = 0; sw < sweeps; ++sw) {
+    for (int b = 0; b < nblk; ++b) {
+      const int c0 = b * kRB;
+      const int bw = static_cast<int>(std::min<int64_t>(kRB, n - c0));
+      tall_mfma_kernel<double, float>
+          <<<dim3(static_cast<unsigned>(sp.tiles), static_cast<unsigned>(sp.splits)), kThreads, 0, st>>>(
+              Dt, m, H + c0, ldh, m, n, bw, sp.kchunk, part);
+      GPTQ_TRY_LAUNCH();
+      refine_sweep_kernel<<<static_cast<unsigned>(ceil_div(m, 64)), 64, 0, st>>>(
+          part, static_cast<int>(sp.splits), m, n, c0, bw, H, ldh, scales, zeros, G, group_size, g_idx,
+          static_cast<double>(levels - 1), codes_vec, codes, Dt, cnt ? cnt + sw : nullptr);
+      GPTQ_TRY_LAUNCH();
+    }
+  }
   return GPTQ_OK;
 }

@@ -209,6 +209,39 @@ def test_lowrank_argument_errors(lib):
     assert f(*bad) == _lib.GPTQ_ERR_WORKSPACE
 
 
+def test_refine_argument_errors(lib):
+    assert lib.gptq_refine_ws_bytes(0, 10) == 0
+    assert lib.gptq_refine_ws_bytes(10, 0) == 0
+    assert lib.gptq_refine_ws_bytes(1 << 31, 10) == 0
+    assert lib.gptq_refine_ws_bytes(1 << 30, 1 << 20) == 0        # m n > 2^48
+    ws = lib.gptq_refine_ws_bytes(4096, 4096)
+    assert ws >= 4096 * 4096 * 8                                   # the transposed float64 residual
+    big = 1 << 40
+    f = lib.gptq_refine_codes
+    # W, dtype, m, n, ldw, H, ldh, L, R, r, ldr, scales, zeros, group, g_idx, levels, sweeps, codes, moves, ws, bytes, stream
+    args = [_fake(), 2, 50, 100, 100, _fake(), 100, _null(), _null(), 0, 0, _fake(), _fake(), 0, _null(), 16, 0,
+            _fake(), _null(), _fake(), big, _null()]
+    assert f(*args) == _lib.GPTQ_OK                                # zero sweeps: validated, nothing launched
+    for idx, val, want in [(1, 7, "INVALID_ARG"), (2, 0, "INVALID_ARG"), (3, 0, "INVALID_ARG"),
+                           (4, 99, "INVALID_ARG"), (6, 99, "INVALID_ARG"), (15, 1, "INVALID_ARG"),
+                           (15, 257, "INVALID_ARG"), (16, -1, "INVALID_ARG"), (13, -2, "INVALID_ARG"),
+                           (9, 65, "INVALID_ARG"), (9, 4, "INVALID_ARG"),  # r > 0 needs L, R and ldr >= m
+                           (20, 16, "WORKSPACE")]:
+        bad = list(args)
+        bad[idx] = val
+        assert f(*bad) == getattr(_lib, "GPTQ_ERR_" + want), (idx, val)
+    for idx in (0, 5, 11, 12, 17):
+        bad = list(args)
+        bad[idx] = _null()
+        assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG, idx
+    ok = list(args); ok[7] = _fake(); ok[8] = _fake(); ok[9] = 4; ok[10] = 50
+    assert f(*ok) == _lib.GPTQ_OK
+    bad = list(ok); bad[10] = 49                                   # ldr < m
+    assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
+    bad = list(ok); bad[9] = 101                                   # r > n
+    assert f(*bad) == _lib.GPTQ_ERR_INVALID_ARG
+
+
 def test_hessian_pair_argument_errors(lib):
     f = lib.gptq_hessian_pair_accumulate
     assert f(_fake(), -1, _fake(), 2, 10, 10, 2.0, 1, _fake(), 10, _null()) == _lib.GPTQ_ERR_INVALID_ARG
