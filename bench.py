@@ -36,7 +36,9 @@ matrix products), sweep, pack; one JSON line with the per-stage times.
 `--lora` instead times GPTQ with the low-rank correction (GPTQ-intrinsic
 LoRA reading) on the same 4096 x 4096 layer: Hessian, the rank-`--rank`
 basis (subspace iteration, `--lora-iters` steps), the augmented Hessian H_L,
-prepare / sweep / pack on H_L and the compensation R; one JSON line with the
+prepare / sweep / pack on H_L and the compensation R, then `--refine-rounds`
+rounds (default 1) of the fixed-grid code refinement on H_L alternated with
+the compensation (one `--refine-sweeps` pass each); one JSON line with the
 per-stage times and their float64 roofline fractions.
 
 `--gemv` instead times the packed-weight decode product gptq_dequant_gemv
@@ -336,8 +338,11 @@ def bench_lora(args):
     Omega = torch.randn((n, r), generator=gen, device="cuda", dtype=torch.float64)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    names = ["hessian", "basis", "lowrank_hessian", "prepare", "quantize", "pack", "compensation"]
+    rounds, sweeps = max(0, args.refine_rounds), max(1, args.refine_sweeps)
+    names = ["hessian", "basis", "lowrank_hessian", "prepare", "quantize", "pack", "compensation", "refine"]
     out = {}
+    refine_ws = torch.empty(int(g.load().gptq_refine_ws_bytes(m, n)), dtype=torch.uint8, device="cuda")
+    moves = []
 
     def step(ev=None):
         mark = (lambda i: ev[i].record(stream)) if ev else (lambda i: None)
@@ -356,12 +361,22 @@ def bench_lora(args):
         mark(6)
         R = g.gptq_lowrank_compensation(Wd, q, K, cfg.group_size)
         mark(7)
+        for _ in range(rounds):
+            codes, mv = g.gptq_refine_codes(Wd, HL, q, cfg.levels, cfg.group_size, sweeps, codes=q["codes"],
+                                            ws=refine_ws)
+            q["codes"] = codes
+            R = g.gptq_lowrank_compensation(Wd, q, K, cfg.group_size, R=R)
+            moves.append(mv)
+        if rounds:
+            g.gptq_pack(q["codes"], bits_of(cfg.levels))
+        mark(8)
         out.update(q=q, R=R, L=Lb)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(9)] for _ in range(args.steps)]
+    moves.clear()
     t0 = time.perf_counter()
     for e in evs:
         step(e)
@@ -371,9 +386,13 @@ def bench_lora(args):
     # Algorithmic float64 flops: H Q per iteration (2 n^2 r) plus the Cholesky-QR
     # Gram and triangular products (4 n r^2 per pass, iters + 2 passes); H L and
     # the downdate (4 n^2 r) plus L^T H L, C^{-T} and C^{-1} (6 n r^2); R (2 m n r).
+    # The refinement: per sweep the gradient H d of every row, block by block
+    # (2 m n^2), plus one compensation per round (2 m n r).
     fl = {"basis": iters * 2.0 * n * n * r + (iters + 2) * 4.0 * n * r * r,
           "lowrank_hessian": 4.0 * n * n * r + 6.0 * n * r * r,
           "compensation": 2.0 * m * n * r}
+    if rounds:
+        fl["refine"] = rounds * (sweeps * 2.0 * m * n * n + 2.0 * m * n * r)
     roof = {k: {"ms": st[k], "tflops": fl[k] / (st[k] * 1e-3) / 1e12,
                 "frac": fl[k] / (st[k] * 1e-3) / 1e12 / PEAK_F64_TFLOPS} for k in fl}
     Lh = out["L"]
@@ -391,10 +410,14 @@ def bench_lora(args):
         "vs_baseline": None,
         "dtype": "bf16 inputs, f64 low-rank stages, f32/f64 quantizer",
         "data": "synthetic",
-        "config": {"workload": cfg.name + f", rank-{r} correction (L = V_r by {iters} subspace iterations)",
+        "config": {"workload": cfg.name + f", rank-{r} correction (L = V_r by {iters} subspace iterations)"
+                               + (f", {rounds} refinement round(s) of {sweeps} sweep(s) on H_L" if rounds else ""),
                    "m": m, "n": n, "tokens": N, "rank": r, "iters": iters, "levels": cfg.levels,
-                   "group_size": cfg.group_size, "parallelism": "1 GPU"},
+                   "group_size": cfg.group_size, "refine_rounds": rounds, "refine_sweeps": sweeps,
+                   "parallelism": "1 GPU"},
         "stage_ms": st,
+        "ms_without_refine": wall * 1e3 - st["refine"],
+        "refine_moves_per_step": int(sum(int(mv.sum()) for mv in moves)) // max(1, args.steps),
         "lowrank_roofline": {"bound": "f64 VALU", "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s", "stages": roof},
         "sanity": {"L_orthonormal_maxerr": orth, "R_finite": bool(torch.isfinite(out["R"]).all())},
     }
@@ -502,6 +525,8 @@ def main():
     ap.add_argument("--lora", action="store_true", help="time GPTQ with the low-rank correction instead")
     ap.add_argument("--rank", type=int, default=64)
     ap.add_argument("--lora-iters", type=int, default=10)
+    ap.add_argument("--refine-rounds", type=int, default=1)
+    ap.add_argument("--refine-sweeps", type=int, default=1)
     ap.add_argument("--levels", type=int, default=4)
     ap.add_argument("--group-size", type=int, default=64)
     args = ap.parse_args()
