@@ -31,6 +31,7 @@ constexpr int kTK = 32;                    // K per LDS stage
 constexpr int kPitch = kTP + 4;            // doubles per LDS row (32-byte aligned rows)
 constexpr int kTargetBlocks = 512;         // workgroups the matrix-core products aim for
 constexpr int kCompensationBlocks = 1024;  // and the compensation product
+constexpr int kRefineBlocks = 768;         // and the refinement's gradient product
 
 static_assert(kR == 64, "the tile shapes assume a 64-column rank tile");
 
@@ -599,31 +600,45 @@ __global__ void refine_clear_kernel(unsigned long long* __restrict__ p, int coun
 // block's split partials of Dt^T H[:, block] (kR columns per row, zero past
 // bw).  Writes the block's codes and residual columns; adds the number of
 // moves to *count (when not null).
+//
+// The block's diagonal block of H (widened to float64), each row's grid and
+// each row's gradient entries are staged in LDS (lane = row: gl[k][lane]),
+// so the column walk reads no global memory.  Columns go in sub-blocks of
+// kRSub: the sub-block's gradient entries are held in registers; a column's
+// decision is followed at once by the corrections of the sub-block's later
+// columns, and the block's columns after the sub-block take the sub-block's
+// corrections in one pass at its end.  For every column k the corrections
+// still arrive in increasing j, each as g_k = g_k - delta_j H_kj, so this is
+// the column-by-column sequence with the loop over k reordered only.
+constexpr int kRSub = 8;
+static_assert(kRSub == 8 && kRB % kRSub == 0, "whole sub-blocks of eight columns");
+
+template <bool FULL>
 __global__ __launch_bounds__(64) void refine_sweep_kernel(
-    const double* __restrict__ part, int splits, int64_t m, int64_t n, int c0, int bw,
+    const double* __restrict__ part, int splits, int64_t m, int64_t n, int c0, int bw_arg,
     const float* __restrict__ H, int64_t ldh, const float* __restrict__ scales, const uint8_t* __restrict__ zeros,
     int64_t G, int64_t group, const int32_t* __restrict__ gidx, double maxq, int codes_vec,
     uint8_t* __restrict__ codes, double* __restrict__ Dt, unsigned long long* __restrict__ count) {
 #pragma clang fp contract(off)
-  __shared__ float2 grid[kRB][64];   // (s, z) of each column for each lane's row
+  const int bw = FULL ? kRB : bw_arg;   // a whole block: every column test below is decided at compile time
+  __shared__ float2 grid[kRB][64];                              // (s, z) of each column for each lane's row
+  __shared__ __attribute__((aligned(16))) double hs[kRB][kRB];  // H[c0 + r][c0 + c] widened, zero past bw
+  __shared__ double gl[kRB][64];                                // gradient entry k of each lane's row
+  __shared__ int gcol[kRB];                                     // group of each column
   const int lane = static_cast<int>(threadIdx.x);
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 64 + lane;
   const bool active = i < m;
   const int64_t ir = active ? i : m - 1;   // lanes past m follow row m-1 and write nothing
-  for (int j = 0; j < bw; ++j) {
-    const int64_t col = c0 + j;
-    const int64_t g = gidx ? static_cast<int64_t>(gidx[col]) : (group ? col / group : 0);
-    grid[j][lane] = float2{scales[ir * G + g], static_cast<float>(zeros[ir * G + g])};
-  }
-  double g[kRB];
+  const float* hb = H + static_cast<int64_t>(c0) * ldh + c0;
+  // Every load that does not depend on another goes out first: column l of
+  // the H block, the group of column l, this row's codes, the first split's
+  // partials; then they are consumed.
+  float hv[kRB];
 #pragma unroll
-  for (int j = 0; j < kRB; ++j) g[j] = 0.0;
-  for (int t = 0; t < splits; ++t) {
-    const double* p = part + (static_cast<int64_t>(t) * m + ir) * kR;
-#pragma unroll
-    for (int j = 0; j < kRB; ++j) g[j] += p[j];
-  }
-  uint32_t cw[kRB / 4], c_old[kRB / 4];
+  for (int r = 0; r < kRB; ++r) hv[r] = (r < bw && lane < bw) ? hb[static_cast<int64_t>(r) * ldh + lane] : 0.f;
+  const int64_t col_l = c0 + lane;
+  const int gc = lane < bw ? (gidx ? static_cast<int>(gidx[col_l]) : (group ? static_cast<int>(col_l / group) : 0)) : 0;
+  uint32_t cw[kRB / 4];
   uint8_t* crow = codes + ir * n + c0;
   if (codes_vec && bw == kRB) {
 #pragma unroll
@@ -641,70 +656,149 @@ __global__ __launch_bounds__(64) void refine_sweep_kernel(
       cw[q] = v;
     }
   }
+  // The gradient entries: the split partials summed in split order into
+  // gl (0 + p_0 + p_1 + ...), one round trip per split.
+  for (int t = 0; t < splits; ++t) {
+    const doublex4* pp = reinterpret_cast<const doublex4*>(part + (static_cast<int64_t>(t) * m + ir) * kR);
+    doublex4 pv[kRB / 4];
 #pragma unroll
-  for (int q = 0; q < kRB / 4; ++q) c_old[q] = cw[q];
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  int moved = 0;
-  const float* hb = H + static_cast<int64_t>(c0) * ldh + c0;   // the block's diagonal block of H
-  // Every index into g and cw is a compile-time constant after unrolling
-  // (the bound bw is a uniform guard, not a trip count), so both stay in
-  // registers.
+    for (int v = 0; v < kRB / 4; ++v) pv[v] = pp[v];
+    if (t == 0) {
+      gcol[lane] = gc;
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) hs[r][lane] = static_cast<double>(hv[r]);
+    }
+#pragma unroll
+    for (int v = 0; v < kRB / 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[4 * v + e][lane] = (t == 0 ? 0.0 : gl[4 * v + e][lane]) + pv[v][e];
+  }
+  __syncthreads();
 #pragma unroll
   for (int j = 0; j < kRB; ++j) {
     if (j < bw) {
-    const double hjj = static_cast<double>(hb[static_cast<int64_t>(j) * ldh + j]);
-    const float2 sz = grid[j][lane];
-    const double s = static_cast<double>(sz.x), z = static_cast<double>(sz.y);
-    const int cold = static_cast<int>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
-    const double what = s * (static_cast<double>(cold) - z);
-    double delta = 0.0;
-    if (hjj > 0.0) {
-      const double v = what + g[j] / hjj;
+      const int64_t gg = gcol[j];
+      grid[j][lane] = float2{scales[ir * G + gg], static_cast<float>(zeros[ir * G + gg])};
+    }
+  }
+  __syncthreads();
+
+  int moved = 0;
+  // Every index into g, dl and cw is a compile-time constant after unrolling
+  // (bw is a uniform guard, not a trip count), so they stay in registers.
+#pragma unroll
+  for (int sb = 0; sb < kRB; sb += kRSub) {
+    // The sub-block's gradient entries, grid values and H triangle (H_kj
+    // for sb <= j <= k < sb + kRSub) go to registers in one batch.
+    double g[kRSub], dl[kRSub], ht[kRSub * (kRSub + 1) / 2];
+    float2 sz[kRSub];
+#pragma unroll
+    for (int jj = 0; jj < kRSub; ++jj) {
+      g[jj] = gl[sb + jj][lane];
+      sz[jj] = grid[sb + jj][lane];
+    }
+#pragma unroll
+    for (int kk = 0; kk < kRSub; ++kk)
+#pragma unroll
+      for (int jj = 0; jj <= kk; ++jj) ht[kk * (kk + 1) / 2 + jj] = hs[sb + kk][sb + jj];
+    // Branch-free decisions: every lane evaluates the candidate code, its
+    // step and its gain, and takes the step only if the walk would (a
+    // column past bw, a dead column, no change or no gain keeps the code).
+    // A step not taken is zero; subtracting zero times H leaves every
+    // gradient entry unchanged (up to the sign of a zero, which no decision
+    // depends on).
+#pragma unroll
+    for (int jj = 0; jj < kRSub; ++jj) {
+      const int j = sb + jj;
+      const double hjj = ht[jj * (jj + 1) / 2 + jj];
+      const double s = static_cast<double>(sz[jj].x), z = static_cast<double>(sz[jj].y);
+      const int sh = 8 * (j & 3);
+      const int cold = static_cast<int>((cw[j >> 2] >> sh) & 0xffu);
+      const double what = s * (static_cast<double>(cold) - z);
+      const double v = what + g[jj] / hjj;
       const double q = fmin(fmax(rint(v / s) + z, 0.0), maxq);
       const int cn = static_cast<int>(q);
-      if (cn != cold) {
-        const double d = s * (static_cast<double>(cn) - z) - what;
-        const double gain = d * g[j] - 0.5 * d * d * hjj;
-        if (gain > 0.0 && active) {
-          delta = d;
-          const int sh = 8 * (j & 3);
-          cw[j >> 2] = (cw[j >> 2] & ~(0xffu << sh)) | (static_cast<uint32_t>(cn) << sh);
-          ++moved;
-        }
-      }
-    }
-    if (__any(delta != 0.0)) {
+      const double d = s * (static_cast<double>(cn) - z) - what;
+      const double gain = d * g[jj] - 0.5 * d * d * hjj;
+      const bool take = j < bw && active && hjj > 0.0 && cn != cold && gain > 0.0;
+      const double delta = take ? d : 0.0;
+      cw[j >> 2] = take ? ((cw[j >> 2] & ~(0xffu << sh)) | (static_cast<uint32_t>(cn) << sh)) : cw[j >> 2];
+      moved += take ? 1 : 0;
+      dl[jj] = delta;
+      // the sub-block's later columns (H past bw is zero; g there is unused)
 #pragma unroll
-      for (int k = j + 1; k < kRB; ++k)
-        if (k < bw) g[k] = g[k] - delta * static_cast<double>(hb[static_cast<int64_t>(j) * ldh + k]);
+      for (int kk = jj + 1; kk < kRSub; ++kk) g[kk] = g[kk] - delta * ht[kk * (kk + 1) / 2 + jj];
     }
+    // The block's columns after the sub-block, eight at a time: H[k][sb ..
+    // sb+7] is one contiguous row piece (H_jk = H_kj, H being exactly
+    // symmetric).  All reads of a group are issued before its arithmetic.
+    for (int k0 = sb + kRSub; k0 < kRB; k0 += 8) {
+      doublex4 h0[8], h1[8];
+      double gk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        h0[u] = *reinterpret_cast<const doublex4*>(&hs[k0 + u][sb]);
+        h1[u] = *reinterpret_cast<const doublex4*>(&hs[k0 + u][sb + 4]);
+        gk[u] = gl[k0 + u][lane];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) gk[u] = gk[u] - dl[e] * h0[u][e];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) gk[u] = gk[u] - dl[4 + e] * h1[u][e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) gl[k0 + u][lane] = gk[u];
     }
   }
 
   if (active) {
+    // codes and the residual of each moved column: d_j -= delta, delta
+    // recomputed from the old and new codes exactly as in the walk
+    uint32_t c_old[kRB / 4];
     if (codes_vec && bw == kRB) {
+#pragma unroll
+      for (int q = 0; q < kRB / 16; ++q) {
+        const u32x4 v = reinterpret_cast<const u32x4*>(crow)[q];
+        c_old[4 * q] = v[0]; c_old[4 * q + 1] = v[1]; c_old[4 * q + 2] = v[2]; c_old[4 * q + 3] = v[3];
+      }
 #pragma unroll
       for (int q = 0; q < kRB / 16; ++q)
         reinterpret_cast<u32x4*>(crow)[q] = u32x4{cw[4 * q], cw[4 * q + 1], cw[4 * q + 2], cw[4 * q + 3]};
     } else {
+#pragma unroll
+      for (int q = 0; q < kRB / 4; ++q) {
+        uint32_t v = 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (4 * q + t < bw) v |= static_cast<uint32_t>(crow[4 * q + t]) << (8 * t);
+        c_old[q] = v;
+      }
       for (int j = 0; j < bw; ++j) crow[j] = static_cast<uint8_t>(cw[j >> 2] >> (8 * (j & 3)));
     }
-    // the residual of each moved column: d_j -= delta, delta recomputed from
-    // the old and new codes exactly as in the sequence above
+    // The residual entries of the block are read in one batch before any is
+    // written (one round trip instead of one per column: the compiler
+    // cannot tell the columns' addresses apart).
+    double* drow = Dt + static_cast<int64_t>(c0) * m + i;
 #pragma unroll
-    for (int j = 0; j < kRB; ++j) {
-      if (j >= bw) continue;
-      const int co = static_cast<int>((c_old[j >> 2] >> (8 * (j & 3))) & 0xffu);
-      const int cn = static_cast<int>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
-      if (co != cn) {
-        const float2 sz = grid[j][lane];
-        const double s = static_cast<double>(sz.x), z = static_cast<double>(sz.y);
-        const double d = s * (static_cast<double>(cn) - z) - s * (static_cast<double>(co) - z);
-        double* p = Dt + static_cast<int64_t>(c0 + j) * m + i;
-        *p = *p - d;
+    for (int h = 0; h < kRB; h += 32) {
+      double dold[32];
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) dold[jj] = h + jj < bw ? drow[static_cast<int64_t>(h + jj) * m] : 0.0;
+#pragma unroll
+      for (int jj = 0; jj < 32; ++jj) {
+        const int j = h + jj;
+        if (j >= bw) continue;
+        const int co = static_cast<int>((c_old[j >> 2] >> (8 * (j & 3))) & 0xffu);
+        const int cn = static_cast<int>((cw[j >> 2] >> (8 * (j & 3))) & 0xffu);
+        if (co != cn) {
+          const float2 sz = grid[j][lane];
+          const double s = static_cast<double>(sz.x), z = static_cast<double>(sz.y);
+          const double d = s * (static_cast<double>(cn) - z) - s * (static_cast<double>(co) - z);
+          drow[static_cast<int64_t>(j) * m] = dold[jj] - d;
+        }
       }
     }
   }
@@ -737,12 +831,12 @@ Split choose_split(int64_t P, int64_t K) {
 
 // Splits of the matrix-core product: K in multiples of kMChunk, enough
 // workgroups of kMP rows to cover the chip twice over.
-Split choose_split_mfma(int64_t P, int64_t K, int64_t max_splits) {
+Split choose_split_mfma(int64_t P, int64_t K, int64_t max_splits, int64_t target_blocks = kTargetBlocks) {
   Split s;
   s.tiles = ceil_div(P, kMP);
   const int64_t stages = ceil_div(K, kMChunk);
   const int64_t want =
-      std::max<int64_t>(1, std::min({ceil_div(kTargetBlocks, s.tiles), stages, max_splits}));
+      std::max<int64_t>(1, std::min({ceil_div(target_blocks, s.tiles), stages, max_splits}));
   s.kchunk = ceil_div(stages, want) * kMChunk;
   s.splits = ceil_div(K, s.kchunk);
   return s;
@@ -872,7 +966,8 @@ struct RefineLayout {
 
 RefineLayout refine_layout(int64_t m, int64_t n) {
   RefineLayout L;
-  L.split = choose_split_mfma(m, n, kTargetBlocks);
+  // three workgroups per CU (the product's registers and LDS allow three)
+  L.split = choose_split_mfma(m, n, kRefineBlocks, kRefineBlocks);
   L.off_dt = 0;
   L.off_part = align256(static_cast<size_t>(n) * static_cast<size_t>(m) * sizeof(double));
   L.total = align256(L.off_part + part_bytes(L.split, m));
@@ -1025,9 +1120,14 @@ extern "C" gptq_status gptq_refine_codes(const void* W, int w_dtype, int64_t m, 
           <<<dim3(static_cast<unsigned>(sp.tiles), static_cast<unsigned>(sp.splits)), kThreads, 0, st>>>(
               Dt, m, H + c0, ldh, m, n, bw, sp.kchunk, part);
       GPTQ_TRY_LAUNCH();
-      refine_sweep_kernel<<<static_cast<unsigned>(ceil_div(m, 64)), 64, 0, st>>>(
-          part, static_cast<int>(sp.splits), m, n, c0, bw, H, ldh, scales, zeros, G, group_size, g_idx,
-          static_cast<double>(levels - 1), codes_vec, codes, Dt, cnt ? cnt + sw : nullptr);
+      if (bw == kRB)
+        refine_sweep_kernel<true><<<static_cast<unsigned>(ceil_div(m, 64)), 64, 0, st>>>(
+            part, static_cast<int>(sp.splits), m, n, c0, bw, H, ldh, scales, zeros, G, group_size, g_idx,
+            static_cast<double>(levels - 1), codes_vec, codes, Dt, cnt ? cnt + sw : nullptr);
+      else
+        refine_sweep_kernel<false><<<static_cast<unsigned>(ceil_div(m, 64)), 64, 0, st>>>(
+            part, static_cast<int>(sp.splits), m, n, c0, bw, H, ldh, scales, zeros, G, group_size, g_idx,
+            static_cast<double>(levels - 1), codes_vec, codes, Dt, cnt ? cnt + sw : nullptr);
       GPTQ_TRY_LAUNCH();
     }
   }
