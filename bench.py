@@ -14,8 +14,12 @@ takes the 12288 x 12288 layer of the same model, `--config 2` the Llama-7B
 4096 x 4096 attention projection, 4-bit g128).
 
 Prints one JSON line: columns/s of the whole step, per-stage times and
-roofline fractions, the dominant kernel's roofline record and the CPU
-oracle's time on a bounded sample of the same workload.
+roofline fractions, the dominant kernel's roofline record, the CPU
+oracle's time on a bounded sample of the same workload, and under
+"next_rows" short measurements (3 steps each) of the rows built on top of
+the path: the packed decode product, asymmetric calibration, the low-rank
+correction with one refinement round, and a two-block decoder pass
+(`--no-next-rows` skips them).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
                        [--layer L] [--no-cpu] [--copy-calibration]
@@ -251,7 +255,7 @@ def bench_decoder(args):
         "quantizer_s": sum(v for k, v in split.items() if k != "forward"),
         "sanity": {"finite_output": finite},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def bench_gptaq(args):
@@ -320,7 +324,7 @@ def bench_gptaq(args):
                             "frac": tflops_t / PEAK_F32_TFLOPS,
                             "algorithmic": "3 m n^2 multiply-adds (W Hc^T, x U^T, x U)"},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def bench_lora(args):
@@ -421,7 +425,7 @@ def bench_lora(args):
         "lowrank_roofline": {"bound": "f64 VALU", "peak": PEAK_F64_TFLOPS, "unit": "TFLOP/s", "stages": roof},
         "sanity": {"L_orthonormal_maxerr": orth, "R_finite": bool(torch.isfinite(out["R"]).all())},
     }
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def dataclasses_replace(obj, **kw):
@@ -501,7 +505,7 @@ def bench_gemv(args):
         rec["cpu_baseline"] = {"value": cpu * (m / rows) * 1e6, "unit": "us per call", "cores": int(threads),
                                "kind": "oracle",
                                "sample": f"oracle.dequant_matmul on {rows} of the {m} rows, scaled by {m // rows}"}
-    print(json.dumps(rec), flush=True)
+    return rec
 
 
 def main():
@@ -529,6 +533,8 @@ def main():
     ap.add_argument("--refine-sweeps", type=int, default=1)
     ap.add_argument("--levels", type=int, default=4)
     ap.add_argument("--group-size", type=int, default=64)
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip the short measurements of the rows built on top of the path")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -542,16 +548,16 @@ def main():
 
     lib = g.load()
     if args.gemv:
-        bench_gemv(args)
+        print(json.dumps(bench_gemv(args)), flush=True)
         return
     if args.decoder:
-        bench_decoder(args)
+        print(json.dumps(bench_decoder(args)), flush=True)
         return
     if args.gptaq:
-        bench_gptaq(args)
+        print(json.dumps(bench_gptaq(args)), flush=True)
         return
     if args.lora:
-        bench_lora(args)
+        print(json.dumps(bench_lora(args)), flush=True)
         return
     cfg = wl.WORKLOADS[args.config]
     li = (len(cfg.layers) - 1 if args.config == 4 else 0) if args.layer is None else args.layer
@@ -710,11 +716,54 @@ def main():
         "roofline": roof,
         "sanity": {"codes_in_range": codes_ok, "finite": finite},
     }
+    del Xd, Wd, H, U, perm, out, packed, ws_h, ws_p, ws_q
+    torch.cuda.empty_cache()
     if not args.no_cpu:
-        del Xd
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(L, X, cfg, n, m, N)
+    del L, X
+    if not args.no_next_rows:
+        rec["next_rows"] = next_rows(args)
     print(json.dumps(rec), flush=True)
+
+
+def next_rows(args):
+    """Short measurements of the rows built on top of the path, each in its
+    own configuration (the full lines come from --gemv, --gptaq, --lora and
+    --decoder): the decode product on the fc1 layer at batch 1 (50 launches),
+    then three steps each of asymmetric
+    calibration and the rank-64 low-rank correction with one refinement
+    round on the 4096 x 4096 layer, and a two-block Llama-7B decoder pass."""
+    import argparse as _ap
+    import torch
+    short = _ap.Namespace(**vars(args))
+    short.steps, short.warmup, short.no_cpu = 3, 1, True
+    out = {}
+
+    def run(key, fn, pick):
+        t0 = time.perf_counter()
+        r = fn(short)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        out[key] = {k: r[k] for k in ("metric", "value", "unit", "config") if k in r}
+        out[key].update(pick(r))
+        log(f"next row {key}: {r['value']:.4g} {r['unit']} ({time.perf_counter() - t0:.1f}s)")
+
+    short.gemv_batch, short.steps, short.warmup = 1, 50, 5   # a 75 us kernel: more launches
+    run("f2_decode_product", bench_gemv,
+        lambda r: {"hbm_GBps": r["roofline"]["achieved"], "frac_hbm": r["roofline"]["frac"]})
+    short.steps, short.warmup = 3, 1
+    run("f3_asymmetric_calibration", bench_gptaq,
+        lambda r: {"stage_ms": r["stage_ms"], "target_frac_f32": r["target_roofline"]["frac"]})
+    short.refine_rounds, short.refine_sweeps = 1, 1
+    run("f4_lowrank_correction", bench_lora,
+        lambda r: {"stage_ms": r["stage_ms"], "ms_without_refine": r["ms_without_refine"],
+                   "refine_moves_per_step": r["refine_moves_per_step"],
+                   "frac_f64": {k: v["frac"] for k, v in r["lowrank_roofline"]["stages"].items()}})
+    short.decoder_blocks = 2
+    run("f1_decoder_pass", bench_decoder,
+        lambda r: {"layers": r["layers"], "quantizer_s": r["quantizer_s"], "stage_s": r["stage_s"]})
+    return out
 
 
 if __name__ == "__main__":
