@@ -36,6 +36,8 @@ constexpr int kSeg = 32;  // columns per lane segment
 constexpr float kTwo24 = 16777216.0f;
 constexpr int64_t kGridCap = 2048;            // workgroups at most (8 per CU)
 constexpr size_t kMaxStageBytes = 64 * 1024;  // LDS for staged (s, s*z) pairs
+constexpr int kXregMaxSpl = 6;                // decode kernel with X in registers: n <= 64 * 32 * 6
+constexpr int64_t kXregGrid = 768;             // its workgroups (three per CU), waves stream rows
 
 typedef __fp16 half2_t __attribute__((ext_vector_type(2)));
 
@@ -272,6 +274,116 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
   }
 }
 
+
+// Decode (one row of X), segments that share one group, aligned rows: lane
+// l owns the segments l, l + 64, ... of every row — the same columns of X
+// for all rows — so the X pairs of each segment (in decode order) and their
+// sums are formed once per workgroup into LDS (pair j of a segment at
+// [slot][j][lane]: a wave's reads are conflict-free) and the waves stream
+// rows, loading the
+// next row's words and grid values while the current row is multiplied.
+// Per lane the accumulation over its segments and the wave sum are those of
+// dequant_gemv_kernel, so Y is the same.  SPL = segments per lane
+// (n <= 64 * 32 * SPL); n a multiple of 32.
+template <int BITS, int SPL>
+__global__ __launch_bounds__(kThreads) void dequant_gemv_xreg_kernel(
+    const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int G, int group_size, const uint16_t* __restrict__ X,
+    float* __restrict__ Y) {
+  static_assert(BITS == 2 || BITS == 4, "whole-word segments");
+  using D = Decode<BITS>;
+  __shared__ uint32_t xq_lds[SPL][kSeg / 2][64];   // pair j of segment lane + 64 t
+  __shared__ float xs_lds[SPL][64];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nseg = (n + kSeg - 1) / kSeg;
+  const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in float16
+  // Wave w forms slots t = w, w + 4, ... (every lane its own segment).
+  for (int t = wave; t < SPL; t += kWaves) {
+    const int k0 = (lane + 64 * t) * kSeg;
+    uint32_t xn[kSeg / 2];
+    if (k0 + kSeg <= n) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(X + k0 + 8 * v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xn[4 * v + e] = q[e];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kSeg / 2; ++u) xn[u] = 0u;
+    }
+    float xs = 0.f;
+    uint32_t xq[kSeg / 2];
+#pragma unroll
+    for (int j = 0; j < kSeg / 2; ++j) {
+      xq[j] = x_pair(xn, D::first(j), D::H);
+      xs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xn[j]), __builtin_bit_cast(half2_t, ones), xs, false);
+    }
+#pragma unroll
+    for (int j = 0; j < kSeg / 2; ++j) xq_lds[t][j][lane] = xq[j];
+    xs_lds[t][lane] = xs;
+  }
+  __syncthreads();
+  int gs[SPL];
+#pragma unroll
+  for (int t = 0; t < SPL; ++t) gs[t] = group_size > 0 ? min(lane + 64 * t, nseg - 1) * kSeg / group_size : 0;
+  // A row's words and grid values for this lane's segments, with no branch
+  // (every segment is whole; a lane past the last segment reads the last one
+  // and row_out leaves it out), so the waits for one row's loads never wait
+  // for the next row's.
+  auto load_row = [&](int r, uint32_t (&w)[SPL][BITS], float (&sv)[SPL], float (&zv)[SPL]) {
+#pragma unroll
+    for (int t = 0; t < SPL; ++t) {
+      const int seg = min(lane + 64 * t, nseg - 1);
+      const uint32_t* wr = packed + (int64_t)r * ldp + (int64_t)seg * BITS;
+      if constexpr (BITS == 4) {
+        const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wr));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[t][e] = q[e];
+      } else {
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 q = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(wr));
+        w[t][0] = q[0];
+        w[t][1] = q[1];
+      }
+      sv[t] = scales[(int64_t)r * G + gs[t]];
+      zv[t] = (float)zeros[(int64_t)r * G + gs[t]];
+    }
+  };
+  auto row_out = [&](int r, const uint32_t (&w)[SPL][BITS], const float (&sv)[SPL], const float (&zv)[SPL]) {
+    float yacc = 0.f;
+#pragma unroll
+    for (int t = 0; t < SPL; ++t) {
+      if (lane + 64 * t < nseg) {
+        uint32_t pr[kSeg / 2];
+        D::pairs(w[t], pr);
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < kSeg / 2; ++j)
+          a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr[j]), __builtin_bit_cast(half2_t, xq_lds[t][j][lane]),
+                                     a, false);
+        yacc = __builtin_fmaf(sv[t], __builtin_fmaf(a, kTwo24, -zv[t] * xs_lds[t][lane]), yacc);
+      }
+    }
+    const float v = wave_sum(yacc);
+    if (lane == 0) Y[r] = v;
+  };
+  const int nwv = (int)gridDim.x * kWaves;
+  uint32_t w0[SPL][BITS], w1[SPL][BITS];
+  float s0[SPL], z0[SPL], s1[SPL], z1[SPL];
+  int r = (int)blockIdx.x * kWaves + wave;
+  if (r < m) load_row(r, w0, s0, z0);
+  for (; r < m; r += 2 * nwv) {
+    const int r1 = r + nwv;
+    if (r1 < m) load_row(r1, w1, s1, z1);
+    row_out(r, w0, s0, z0);
+    if (r1 < m) {
+      if (r1 + nwv < m) load_row(r1 + nwv, w0, s0, z0);
+      row_out(r1, w1, s1, z1);
+    }
+  }
+}
 
 // Matrix-core path (any batch, per-row grids or contiguous groups of a
 // multiple of 128 columns, no g_idx).  The same subnormal code pairs are the
@@ -702,6 +814,32 @@ gptq_status launch_valu_rows(hipStream_t st, const uint32_t* packed, int m, int 
                              const float* scales, const uint8_t* zeros, int G, int group_size, const int32_t* g_idx,
                              const uint16_t* X, int bn, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x,
                              bool per_code) {
+  const int spl = (int)ceil_div(ceil_div(n, kSeg), 64);
+  if (bn == 1 && !per_code && vec_w && vec_x && bits != 3 && n % kSeg == 0 && spl <= kXregMaxSpl) {
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(m, kWaves), kXregGrid);
+#define GPTQ_XREG(B, S)                                                                                   \
+  dequant_gemv_xreg_kernel<B, S><<<grid, kThreads, 0, st>>>(packed, m, n, ld_packed, scales, zeros, G, group_size, \
+                                                            X, Y)
+#define GPTQ_XREG_BITS(B)          \
+  do {                             \
+    switch (spl) {                 \
+      case 1: GPTQ_XREG(B, 1); break; \
+      case 2: GPTQ_XREG(B, 2); break; \
+      case 3: GPTQ_XREG(B, 3); break; \
+      case 4: GPTQ_XREG(B, 4); break; \
+      case 5: GPTQ_XREG(B, 5); break; \
+      default: GPTQ_XREG(B, 6); break; \
+    }                              \
+  } while (0)
+    if (bits == 2)
+      GPTQ_XREG_BITS(2);
+    else
+      GPTQ_XREG_BITS(4);
+#undef GPTQ_XREG_BITS
+#undef GPTQ_XREG
+    GPTQ_TRY_LAUNCH();
+    return GPTQ_OK;
+  }
   const size_t shm_per_row = (size_t)G * sizeof(float2);
 #define GPTQ_GEMV_BITS(B)                                                                                      \
   do {                                                                                                         \

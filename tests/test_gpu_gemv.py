@@ -80,6 +80,8 @@ CASES = [
     (1, 33, 4, 0, False, False, 1),         # one row, one column past a segment
     (77, 1000, 4, 128, False, False, 3),    # batch >= 3, contiguous groups: matrix-core kernel
     (50, 640, 2, 0, False, False, 8),       # per-row, full batch: matrix-core kernel
+    (3000, 1280, 4, 0, False, False, 1),    # decode kernel with X in LDS: lanes past the last segment
+    (200, 8192, 2, 64, False, False, 1),    # decode kernel with X in LDS: 2-bit, groups of 64
 ]
 
 
@@ -90,6 +92,22 @@ def test_dequant_gemv_parity(g, m, n, bits, group, act, pass_gidx, batch):
     X16, Xbuf = _x(batch, n, seed=n + batch)
     Y = _run(g, L, X16, Xbuf, n, bits, group, pass_gidx)
     _check(Y, L, X16, n, bits)
+
+
+@pytest.mark.parametrize("m,n,bits,group", [(64, 4096, 4, 128), (3000, 1280, 4, 0), (200, 8192, 2, 64),
+                                           (96, 12288, 4, 0)])
+def test_dequant_gemv_decode_kernel_matches_batched(g, m, n, bits, group):
+    # One row of X (aligned, n a multiple of 32, segments sharing a group) runs
+    # on the decode kernel that keeps X in LDS; two rows run on the batched
+    # VALU kernel.  Both sum each lane's segments in the same order and reduce
+    # over the wave the same way, so row 0 must agree bit for bit.
+    log(f"dequant_gemv decode kernel vs batched m={m} n={n} bits={bits} group={group}")
+    L = _layer(m, n, bits, group, False, seed=m + n + 3 * bits)
+    X16, Xbuf = _x(2, n, seed=n + 11)
+    Y1 = _run(g, L, X16[:1], Xbuf[:1], n, bits, group, False)
+    Y2 = _run(g, L, X16, Xbuf, n, bits, group, False)
+    _check(Y1, L, X16[:1], n, bits)
+    assert np.array_equal(Y1[0], Y2[0])
 
 
 def test_dequant_gemv_padded_strides(g):
