@@ -477,7 +477,9 @@ def bench_gemv(args):
         "config": {"workload": "175B-class fc1 decode product", "m": m, "n": n, "bits": bits, "group_size": 0,
                    "batch": batch, "parallelism": "1 GPU"},
         "roofline": {
-            "kernel": ("dequant_gemv_kernel<4> (VALU dot2)" if batch <= 2 else "dequant_mfma_kernel<4> (matrix cores)")
+            "kernel": ("dequant_gemv_xreg_kernel<4, 6> (VALU dot2, X in LDS)" if batch == 1
+                       else "dequant_gemv_kernel<4> (VALU dot2)" if batch == 2
+                       else "dequant_mfma_kernel<4> (matrix cores)")
                       + " via gptq_dequant_gemv, HIP events around each launch",
             "bound": "hbm",
             "achieved": nbytes / (us * 1e-6) / 1e9,
