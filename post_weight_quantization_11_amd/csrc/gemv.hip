@@ -275,54 +275,52 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_kernel(
 }
 
 
-// Decode (one row of X), segments that share one group, aligned rows: lane
-// l owns the segments l, l + 64, ... of every row — the same columns of X
-// for all rows — so the X pairs of each segment (in decode order) and their
-// sums are formed once per workgroup into LDS (pair j of a segment at
-// [slot][j][lane]: a wave's reads are conflict-free) and the waves stream
-// rows, loading the
-// next row's words and grid values while the current row is multiplied.
-// Per lane the accumulation over its segments and the wave sum are those of
-// dequant_gemv_kernel, so Y is the same.  SPL = segments per lane
-// (n <= 64 * 32 * SPL); n a multiple of 32.
-template <int BITS, int SPL>
+// Decode (NB = 1 or 2 rows of X), segments that share one group, aligned
+// rows: lane l owns the segments l, l + 64, ... of every row — the same
+// columns of X for all rows — so the X pairs of each segment (in decode
+// order) and their sums are formed once per workgroup into LDS (pair j of a
+// segment at [b][slot][j][lane]: a wave's reads are conflict-free) and the
+// waves stream rows, loading the next row's words and grid values while the
+// current row is multiplied.  Per lane and X row the accumulation over the
+// lane's segments and the wave sum are those of dequant_gemv_kernel, so Y is
+// the same.  SPL = segments per lane (n <= 64 * 32 * SPL); n a multiple of 32.
+template <int BITS, int SPL, int NB>
 __global__ __launch_bounds__(kThreads) void dequant_gemv_xreg_kernel(
     const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, int G, int group_size, const uint16_t* __restrict__ X,
-    float* __restrict__ Y) {
+    const uint8_t* __restrict__ zeros, int G, int group_size, const uint16_t* __restrict__ X, int64_t ldx,
+    float* __restrict__ Y, int64_t ldy) {
   static_assert(BITS == 2 || BITS == 4, "whole-word segments");
+  static_assert(NB == 1 || NB == 2, "one or two rows of X");
   using D = Decode<BITS>;
-  __shared__ uint32_t xq_lds[SPL][kSeg / 2][64];   // pair j of segment lane + 64 t
-  __shared__ float xs_lds[SPL][64];
+  __shared__ uint32_t xq_lds[NB][SPL][kSeg / 2][64];   // pair j of segment lane + 64 t, X row b
+  __shared__ float xs_lds[NB][SPL][64];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nseg = (n + kSeg - 1) / kSeg;
   const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in float16
-  // Wave w forms slots t = w, w + 4, ... (every lane its own segment).
-  for (int t = wave; t < SPL; t += kWaves) {
+  // Wave w forms slots u = w, w + 4, ... of (X row, segment slot) pairs.
+  for (int u = wave; u < NB * SPL; u += kWaves) {
+    const int b = u / SPL, t = u % SPL;
     const int k0 = (lane + 64 * t) * kSeg;
     uint32_t xn[kSeg / 2];
     if (k0 + kSeg <= n) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(X + k0 + 8 * v);
+        const u32x4 q = *reinterpret_cast<const u32x4*>(X + (int64_t)b * ldx + k0 + 8 * v);
 #pragma unroll
         for (int e = 0; e < 4; ++e) xn[4 * v + e] = q[e];
       }
     } else {
 #pragma unroll
-      for (int u = 0; u < kSeg / 2; ++u) xn[u] = 0u;
+      for (int v = 0; v < kSeg / 2; ++v) xn[v] = 0u;
     }
     float xs = 0.f;
-    uint32_t xq[kSeg / 2];
 #pragma unroll
     for (int j = 0; j < kSeg / 2; ++j) {
-      xq[j] = x_pair(xn, D::first(j), D::H);
+      xq_lds[b][t][j][lane] = x_pair(xn, D::first(j), D::H);
       xs = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xn[j]), __builtin_bit_cast(half2_t, ones), xs, false);
     }
-#pragma unroll
-    for (int j = 0; j < kSeg / 2; ++j) xq_lds[t][j][lane] = xq[j];
-    xs_lds[t][lane] = xs;
+    xs_lds[b][t][lane] = xs;
   }
   __syncthreads();
   int gs[SPL];
@@ -352,22 +350,30 @@ __global__ __launch_bounds__(kThreads) void dequant_gemv_xreg_kernel(
     }
   };
   auto row_out = [&](int r, const uint32_t (&w)[SPL][BITS], const float (&sv)[SPL], const float (&zv)[SPL]) {
-    float yacc = 0.f;
+    float yacc[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yacc[b] = 0.f;
 #pragma unroll
     for (int t = 0; t < SPL; ++t) {
       if (lane + 64 * t < nseg) {
         uint32_t pr[kSeg / 2];
         D::pairs(w[t], pr);
-        float a = 0.f;
 #pragma unroll
-        for (int j = 0; j < kSeg / 2; ++j)
-          a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr[j]), __builtin_bit_cast(half2_t, xq_lds[t][j][lane]),
-                                     a, false);
-        yacc = __builtin_fmaf(sv[t], __builtin_fmaf(a, kTwo24, -zv[t] * xs_lds[t][lane]), yacc);
+        for (int b = 0; b < NB; ++b) {
+          float a = 0.f;
+#pragma unroll
+          for (int j = 0; j < kSeg / 2; ++j)
+            a = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr[j]),
+                                       __builtin_bit_cast(half2_t, xq_lds[b][t][j][lane]), a, false);
+          yacc[b] = __builtin_fmaf(sv[t], __builtin_fmaf(a, kTwo24, -zv[t] * xs_lds[b][t][lane]), yacc[b]);
+        }
       }
     }
-    const float v = wave_sum(yacc);
-    if (lane == 0) Y[r] = v;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = wave_sum(yacc[b]);
+      if (lane == 0) Y[(int64_t)b * ldy + r] = v;
+    }
   };
   const int nwv = (int)gridDim.x * kWaves;
   uint32_t w0[SPL][BITS], w1[SPL][BITS];
@@ -815,11 +821,17 @@ gptq_status launch_valu_rows(hipStream_t st, const uint32_t* packed, int m, int 
                              const uint16_t* X, int bn, int64_t ldx, float* Y, int64_t ldy, int vec_w, int vec_x,
                              bool per_code) {
   const int spl = (int)ceil_div(ceil_div(n, kSeg), 64);
-  if (bn == 1 && !per_code && vec_w && vec_x && bits != 3 && n % kSeg == 0 && spl <= kXregMaxSpl) {
+  if (bn <= 2 && !per_code && vec_w && vec_x && bits != 3 && n % kSeg == 0 && spl <= kXregMaxSpl) {
     const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(m, kWaves), kXregGrid);
-#define GPTQ_XREG(B, S)                                                                                   \
-  dequant_gemv_xreg_kernel<B, S><<<grid, kThreads, 0, st>>>(packed, m, n, ld_packed, scales, zeros, G, group_size, \
-                                                            X, Y)
+#define GPTQ_XREG(B, S)                                                                                              \
+  do {                                                                                                               \
+    if (bn == 1)                                                                                                     \
+      dequant_gemv_xreg_kernel<B, S, 1><<<grid, kThreads, 0, st>>>(packed, m, n, ld_packed, scales, zeros, G,       \
+                                                                   group_size, X, ldx, Y, ldy);                     \
+    else                                                                                                             \
+      dequant_gemv_xreg_kernel<B, S, 2><<<grid, kThreads, 0, st>>>(packed, m, n, ld_packed, scales, zeros, G,       \
+                                                                   group_size, X, ldx, Y, ldy);                     \
+  } while (0)
 #define GPTQ_XREG_BITS(B)          \
   do {                             \
     switch (spl) {                 \

@@ -96,18 +96,22 @@ def test_dequant_gemv_parity(g, m, n, bits, group, act, pass_gidx, batch):
 
 @pytest.mark.parametrize("m,n,bits,group", [(64, 4096, 4, 128), (3000, 1280, 4, 0), (200, 8192, 2, 64),
                                            (96, 12288, 4, 0)])
-def test_dequant_gemv_decode_kernel_matches_batched(g, m, n, bits, group):
-    # One row of X (aligned, n a multiple of 32, segments sharing a group) runs
-    # on the decode kernel that keeps X in LDS; two rows run on the batched
-    # VALU kernel.  Both sum each lane's segments in the same order and reduce
-    # over the wave the same way, so row 0 must agree bit for bit.
-    log(f"dequant_gemv decode kernel vs batched m={m} n={n} bits={bits} group={group}")
+def test_dequant_gemv_decode_kernel_matches_row_group_kernel(g, m, n, bits, group):
+    # One or two rows of X with aligned rows (n a multiple of 32, segments
+    # sharing a group) run on the decode kernel that keeps X in LDS; the same
+    # two rows with a padded, unaligned row stride of X run on the row-group
+    # kernel.  Both sum each lane's segments in the same order and reduce over
+    # the wave the same way, so the results must agree bit for bit.
+    log(f"dequant_gemv decode kernel vs row-group kernel m={m} n={n} bits={bits} group={group}")
     L = _layer(m, n, bits, group, False, seed=m + n + 3 * bits)
     X16, Xbuf = _x(2, n, seed=n + 11)
+    _, Xpad = _x(2, n, seed=n + 11, ldx=n + 5)
     Y1 = _run(g, L, X16[:1], Xbuf[:1], n, bits, group, False)
     Y2 = _run(g, L, X16, Xbuf, n, bits, group, False)
-    _check(Y1, L, X16[:1], n, bits)
-    assert np.array_equal(Y1[0], Y2[0])
+    Yref = _run(g, L, X16, Xpad, n, bits, group, False)
+    _check(Y2, L, X16, n, bits)
+    assert np.array_equal(Y1[0], Yref[0])
+    assert np.array_equal(Y2, Yref)
 
 
 def test_dequant_gemv_padded_strides(g):
