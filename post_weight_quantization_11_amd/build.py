@@ -26,12 +26,15 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
-# Per-source additions: MFMA accumulators in VGPRs.  lowrank.hip: in the
-# AGPR form gfx950 issues its float64 MFMAs at about half the rate;
-# gemv.hip: the fold of the accumulators needs no AGPR -> VGPR copies
-# (prefill products ~4% faster, decode unchanged).
+# Per-source additions: MFMA accumulators in VGPRs.  lowrank.hip and
+# prepare.hip: in the AGPR form gfx950 issues float64 MFMAs at about half the
+# rate (independent 16x16x4 MFMAs: 36 TFLOP/s with one wave per SIMD, 48 with
+# two or more, against 77 in the VGPR form with one); gemv.hip: the fold of
+# the accumulators needs no AGPR -> VGPR copies (prefill products ~4% faster,
+# decode unchanged).
 EXTRA_FLAGS = {
     "lowrank.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prepare.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "gemv.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 

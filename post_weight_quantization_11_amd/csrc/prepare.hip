@@ -651,19 +651,6 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   unit_ref(u_lo, pa, pb, pc, nch, first);
   load_chunk(ck[0], pa, pb, 0);
   for (int u = u_lo; u < u_hi; ++u) {
-    // C in the accumulator layout: cv[rb][pp][r] = row rb*16 + q + 4r,
-    // columns 32pp + 2*c16 + 0..1 (column blocks 2pp, 2pp+1).  An inverse
-    // tile first touched here has its old contents (X is never cleared as a
-    // whole) read but replaced by zero.
-    double2 cv[2][2][4];
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          cv[rb][pp][r] =
-              *reinterpret_cast<const double2*>(pc + (int64_t)(rb * 16 + q + 4 * r) * np + 32 * pp + 2 * c16);
     doublex4 acc[2][4];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
@@ -699,6 +686,20 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
       step(ck[0], ck[1], ch);
       step(ck[1], ck[0], ch + 1);
     }
+    // C in the accumulator layout, read after the products (so that the
+    // operands, the accumulators and C never hold registers at once):
+    // cv[rb][pp][r] = row rb*16 + q + 4r, columns 32pp + 2*c16 + 0..1 (column
+    // blocks 2pp, 2pp+1).  An inverse tile first touched here has its old
+    // contents (X is never cleared as a whole) read but replaced by zero.
+    double2 cv[2][2][4];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          cv[rb][pp][r] =
+              *reinterpret_cast<const double2*>(pc + (int64_t)(rb * 16 + q + 4 * r) * np + 32 * pp + 2 * c16);
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
