@@ -433,6 +433,18 @@ def dataclasses_replace(obj, **kw):
     return dataclasses.replace(obj, **kw)
 
 
+def _gemv_kernel_name(batch):
+    """The kernel gptq_dequant_gemv runs on the 49152 x 12288 4-bit per-row layer."""
+    if batch == 1:
+        return "dequant_gemv_xreg_kernel<4, 6, 1> (VALU dot2, X in LDS)"
+    if batch == 2:
+        return "dequant_gemv_xreg_kernel<4, 6, 2> (VALU dot2, X in LDS)"
+    passes = f", {-(-batch // 16)} passes of 16 rows" if batch > 16 else ""
+    rows = min(batch, 16)
+    nb, tpw = (4, 1) if rows <= 4 else (8, 3) if rows <= 8 else (16, 3)
+    return f"dequant_mfma_stream_kernel<4, {nb}, {tpw}> (matrix cores, X staged in LDS panels{passes})"
+
+
 def bench_gemv(args):
     """Decode product on the 175B-class fc1 layer (49152 x 12288, 4-bit per-row)."""
     import torch
@@ -477,10 +489,7 @@ def bench_gemv(args):
         "config": {"workload": "175B-class fc1 decode product", "m": m, "n": n, "bits": bits, "group_size": 0,
                    "batch": batch, "parallelism": "1 GPU"},
         "roofline": {
-            "kernel": ("dequant_gemv_xreg_kernel<4, 6> (VALU dot2, X in LDS)" if batch == 1
-                       else "dequant_gemv_kernel<4> (VALU dot2)" if batch == 2
-                       else "dequant_mfma_kernel<4> (matrix cores)")
-                      + " via gptq_dequant_gemv, HIP events around each launch",
+            "kernel": _gemv_kernel_name(batch) + " via gptq_dequant_gemv, HIP events around each launch",
             "bound": "hbm",
             "achieved": nbytes / (us * 1e-6) / 1e9,
             "peak": PEAK_HBM_GBS,
@@ -732,7 +741,8 @@ def main():
 def next_rows(args):
     """Short measurements of the rows built on top of the path, each in its
     own configuration (the full lines come from --gemv, --gptaq, --lora and
-    --decoder): the decode product on the fc1 layer at batch 1 (50 launches),
+    --decoder): the decode product on the fc1 layer at batch 1 and 16 (50
+    launches each),
     then three steps each of asymmetric
     calibration and the rank-64 low-rank correction with one refinement
     round on the 4096 x 4096 layer, and a two-block Llama-7B decoder pass."""
@@ -751,8 +761,11 @@ def next_rows(args):
         out[key].update(pick(r))
         log(f"next row {key}: {r['value']:.4g} {r['unit']} ({time.perf_counter() - t0:.1f}s)")
 
-    short.gemv_batch, short.steps, short.warmup = 1, 50, 5   # a 75 us kernel: more launches
+    short.gemv_batch, short.steps, short.warmup = 1, 50, 5   # a 60 us kernel: more launches
     run("f2_decode_product", bench_gemv,
+        lambda r: {"hbm_GBps": r["roofline"]["achieved"], "frac_hbm": r["roofline"]["frac"]})
+    short.gemv_batch = 16
+    run("f2_decode_product_batch16", bench_gemv,
         lambda r: {"hbm_GBps": r["roofline"]["achieved"], "frac_hbm": r["roofline"]["frac"]})
     short.steps, short.warmup = 3, 1
     run("f3_asymmetric_calibration", bench_gptaq,

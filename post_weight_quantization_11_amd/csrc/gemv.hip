@@ -566,6 +566,170 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_kernel(
     }
 }
 
+// Decode batches of 3 to 16 rows of X on large layers (per-row grids, 2- or
+// 4-bit, n a multiple of 32): the kernel above reads X once per wave and
+// chunk, as many bytes as the weights it multiplies.  Here the workgroup
+// stages X once for all its rows, in panels of kStreamChunks chunks, already
+// in B-operand order (xs[chunk][j][q][b] = the 8 values MFMA j of lane
+// quarter q takes for X row b) with each segment's sum beside it, double
+// buffered so the next panel is staged while this one multiplies (one
+// barrier per panel).  Each wave owns TPW tiles of 16 rows for the whole of
+// n: per chunk it reads the B operands once from LDS and multiplies every
+// tile's decoded codes into that tile's accumulator; the words of the next
+// panel are loaded while the current one multiplies.  The z term uses the
+// staged segment sums (sum x over the row), so no all-ones MFMA is needed.
+constexpr int kStreamChunks = 4;  // chunks (128 columns each) per X panel
+constexpr int kStreamMaxTpw = 3;   // tiles of 16 rows per wave at most
+constexpr int kStreamMinTiles = 1024;  // 16-row tiles a layer needs for this kernel (a wave per SIMD)
+
+template <int BITS> struct SegWords;
+template <> struct SegWords<4> { typedef u32x4 type; };
+template <> struct SegWords<2> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
+
+template <int BITS, int NB, int TPW>
+__global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
+    const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
+    const uint8_t* __restrict__ zeros, int G, const uint16_t* __restrict__ X, int batch, int64_t ldx,
+    float* __restrict__ Y, int64_t ldy) {
+  static_assert(BITS == 2 || BITS == 4, "whole-word segments");
+  static_assert(NB == 4 || NB == 8 || NB == 16, "X rows staged");
+  using D = Decode<BITS>;
+  using WordT = typename SegWords<BITS>::type;
+  constexpr int PC = kStreamChunks;
+  constexpr int kUnits = NB * PC * 4;  // staged (X row, segment) pairs per panel
+  static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "whole waves stage");
+  __shared__ u32x4 xs[2][PC][4][4][NB];
+  __shared__ floatx4 xsum[2][PC][NB];
+  const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const int nseg = n / kSeg;
+  const int nchunk = (nseg + 3) / 4;
+  const int npanel = (nchunk + PC - 1) / PC;
+  const int bb = c16 < batch ? c16 : batch - 1;  // X row this lane's B operands come from
+  const int tile0 = (int)blockIdx.x * kWaves * TPW + wave;
+  const uint32_t* wrow[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int row = (tile0 + kWaves * i) * 16 + c16;
+    wrow[i] = packed + (int64_t)(row < m ? row : m - 1) * ldp;
+  }
+  // Staging: thread u < kUnits takes X row b = u / (4 PC) and panel segment
+  // u % (4 PC), so neighbouring threads read neighbouring 64-byte pieces.
+  const int su = threadIdx.x;
+  const int sb = su / (4 * PC), sseg = su % (4 * PC);
+  const uint16_t* xrow = X + (int64_t)(sb < batch ? sb : batch - 1) * ldx;
+  auto stage_load = [&](u32x4 (&xr)[4], int p) {
+    const int seg = p * 4 * PC + sseg;
+    const int s = seg < nseg ? seg : nseg - 1;
+    const u32x4* src = reinterpret_cast<const u32x4*>(xrow + (int64_t)s * kSeg);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) xr[v] = seg < nseg ? src[v] : u32x4{0u, 0u, 0u, 0u};
+  };
+  auto stage_store = [&](const u32x4 (&xr)[4], int buf) {
+    uint32_t xn[kSeg / 2];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xn[4 * v + e] = xr[v][e];
+    const int c = sseg >> 2, qs = sseg & 3;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      xs[buf][c][j][qs][sb] = u32x4{x_pair(xn, D::first(4 * j), D::H), x_pair(xn, D::first(4 * j + 1), D::H),
+                                    x_pair(xn, D::first(4 * j + 2), D::H), x_pair(xn, D::first(4 * j + 3), D::H)};
+    const uint32_t ones = 0x3C003C00u;  // (1.0, 1.0) in float16
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSeg / 2; ++j)
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xn[j]), __builtin_bit_cast(half2_t, ones), s, false);
+    xsum[buf][c][sb][qs] = s;
+  };
+  // A panel's words for the wave's tiles: segment 4 (p PC + c) + q of each
+  // tile row, clamped to the last segment (its X is staged as zeros).
+  struct Words {
+    WordT w[TPW][PC];
+  };
+  auto load_words = [&](Words& o, int p) {
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      const int seg = min(4 * (p * PC + c) + q, nseg - 1);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i)
+        o.w[i][c] = __builtin_nontemporal_load(reinterpret_cast<const WordT*>(wrow[i] + (int64_t)seg * BITS));
+    }
+  };
+  floatx4 acc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float sx = 0.f;
+  auto compute = [&](const Words& o, int buf) {
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      half8_t bop[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(half8_t, xs[buf][c][j][q][bb]);
+      const floatx4 s4 = xsum[buf][c][bb];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        uint32_t w[BITS];
+#pragma unroll
+        for (int e = 0; e < BITS; ++e) w[e] = o.w[i][c][e];
+        uint32_t pr[kSeg / 2];
+        D::pairs(w, pr);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]),
+                                                          bop[j], acc[i], 0, 0, 0);
+      }
+      sx += s4[0];
+      sx += s4[1];
+      sx += s4[2];
+      sx += s4[3];
+    }
+  };
+  // Panel 0 staged before the loop; panel p + 1's X and words load while
+  // panel p multiplies.  Two named word buffers (a runtime index into an
+  // array of them would put them in scratch memory).
+  Words wa, wb;
+  u32x4 xr[4];
+  if (su < kUnits) {
+    stage_load(xr, 0);
+    stage_store(xr, 0);
+  }
+  load_words(wa, 0);
+  __syncthreads();
+  for (int p = 0; p < npanel; p += 2) {
+    const bool more1 = p + 1 < npanel;
+    if (more1) {
+      if (su < kUnits) stage_load(xr, p + 1);
+      load_words(wb, p + 1);
+    }
+    compute(wa, 0);
+    if (more1 && su < kUnits) stage_store(xr, 1);
+    __syncthreads();
+    if (!more1) break;
+    const bool more2 = p + 2 < npanel;
+    if (more2) {
+      if (su < kUnits) stage_load(xr, p + 2);
+      load_words(wa, p + 2);
+    }
+    compute(wb, 1);
+    if (more2 && su < kUnits) stage_store(xr, 0);
+    __syncthreads();
+  }
+  // y = s (2^24 acc - z sum x); rows past m and X rows past the batch are not stored.
+  if (c16 >= batch) return;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = (tile0 + kWaves * i) * 16 + 4 * q + e;
+      if (row < m) {
+        const float sc = scales[(int64_t)row * G];
+        const float z = (float)zeros[(int64_t)row * G];
+        Y[(int64_t)c16 * ldy + row] = sc * __builtin_fmaf(acc[i][e], kTwo24, -z * sx);
+      }
+    }
+}
 
 // Prefill-sized batches: a workgroup owns 128 rows of W x 128 rows of X
 // (4 waves as 2 x 2, each 64 x 64 = 4 x 4 MFMA tiles).  Per 128-column chunk
@@ -748,6 +912,41 @@ void launch_mfma(hipStream_t st, const uint32_t* packed, int m, int n, int64_t l
                                                                batch, ldx, Y, ldy, vec_w, vec_x);
 }
 
+// Tiles per wave of the streaming kernel: the most (up to kStreamMaxTpw) that
+// still give every CU a workgroup.  With four staged rows of X, one tile per
+// wave (three times the workgroups, each staging X again) keeps more loads in
+// flight and is faster; with eight or sixteen the staging costs more than
+// that gains (49152 x 12288 4-bit: batch 3 73 vs 82 us, batch 16 92 vs 86 us).
+template <int BITS, int NB>
+void launch_stream_nb(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
+                      const uint8_t* zeros, int G, const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy,
+                      int64_t tiles) {
+  int tpw = NB == 4 ? 1 : kStreamMaxTpw;
+  while (tpw > 1 && ceil_div(tiles, (int64_t)kWaves * tpw) < kStreamMinTiles / kWaves) --tpw;
+  const unsigned grid = (unsigned)ceil_div(tiles, (int64_t)kWaves * tpw);
+  if (tpw >= 3)
+    dequant_mfma_stream_kernel<BITS, NB, 3><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
+                                                                      ldx, Y, ldy);
+  else if (tpw == 2)
+    dequant_mfma_stream_kernel<BITS, NB, 2><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
+                                                                      ldx, Y, ldy);
+  else
+    dequant_mfma_stream_kernel<BITS, NB, 1><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
+                                                                      ldx, Y, ldy);
+}
+
+template <int BITS>
+void launch_stream(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
+                   const uint8_t* zeros, int G, const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy,
+                   int64_t tiles) {
+  if (batch <= 4)
+    launch_stream_nb<BITS, 4>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+  else if (batch <= 8)
+    launch_stream_nb<BITS, 8>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+  else
+    launch_stream_nb<BITS, 16>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+}
+
 template <int BITS>
 void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
                        const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx,
@@ -758,10 +957,24 @@ void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int
   // below would spend most of its work on padding); larger batches: 128 x 128
   // tiles with X staged in LDS.
   if (batch <= 64) {
+    // The streaming kernel on layers of at least kStreamMinTiles tiles; on
+    // layers of 3/4 of that only for more than eight rows of X (12288 x
+    // 49152: batch 3-8 102-123 us on the kernel below against 142-152 us,
+    // batch 12-16 160-203 us against 149 us).
+    const int64_t tiles = ceil_div(m, (int64_t)16);
+    const bool stream_layout = BITS != 3 && group_size == 0 && n >= kSeg && n % kSeg == 0 && vec_w && vec_x;
     for (int b0 = 0; b0 < batch; b0 += 16) {
       const int cb = std::min(16, batch - b0);
       const uint16_t* Xc = X + (int64_t)b0 * ldx;
       float* Yc = Y + (int64_t)b0 * ldy;
+      const bool stream = stream_layout && (tiles >= (int64_t)kStreamMinTiles ||
+                                            (tiles >= (int64_t)kStreamMinTiles * 3 / 4 && cb > 8));
+      if constexpr (BITS != 3) {
+        if (stream) {
+          launch_stream<BITS>(st, packed, m, n, ldp, scales, zeros, G, Xc, cb, ldx, Yc, ldy, tiles);
+          continue;
+        }
+      }
       if (m <= 16384)
         launch_mfma<BITS, 1, 1>(st, packed, m, n, ldp, scales, zeros, G, group_size, Xc, cb, ldx, Yc, ldy, vec_w,
                                 vec_x);
