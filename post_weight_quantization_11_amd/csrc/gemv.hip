@@ -581,15 +581,16 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_kernel(
 constexpr int kStreamChunks = 4;  // chunks (128 columns each) per X panel
 constexpr int kStreamMaxTpw = 3;   // tiles of 16 rows per wave at most
 constexpr int kStreamMinTiles = 1024;  // 16-row tiles a layer needs for this kernel (a wave per SIMD)
+constexpr int kStreamGroupMinTiles = 768;  // the same for contiguous groups
 
 template <int BITS> struct SegWords;
 template <> struct SegWords<4> { typedef u32x4 type; };
 template <> struct SegWords<2> { typedef unsigned int type __attribute__((ext_vector_type(2))); };
 
-template <int BITS, int NB, int TPW>
+template <int BITS, int NB, int TPW, bool GROUPED>
 __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
     const uint32_t* __restrict__ packed, int m, int n, int64_t ldp, const float* __restrict__ scales,
-    const uint8_t* __restrict__ zeros, int G, const uint16_t* __restrict__ X, int batch, int64_t ldx,
+    const uint8_t* __restrict__ zeros, int G, int gchunks, const uint16_t* __restrict__ X, int batch, int64_t ldx,
     float* __restrict__ Y, int64_t ldy) {
   static_assert(BITS == 2 || BITS == 4, "whole-word segments");
   static_assert(NB == 4 || NB == 8 || NB == 16, "X rows staged");
@@ -600,6 +601,9 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
   static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "whole waves stage");
   __shared__ u32x4 xs[2][PC][4][4][NB];
   __shared__ floatx4 xsum[2][PC][NB];
+  // Groups (GROUPED): (s, z) of the workgroup's rows for each chunk's group.
+  constexpr int kWgRows = kWaves * TPW * 16;
+  __shared__ float2 gsz[GROUPED ? 2 : 1][GROUPED ? PC : 1][GROUPED ? kWgRows : 1];
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nseg = n / kSeg;
@@ -643,6 +647,26 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
       s = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, xn[j]), __builtin_bit_cast(half2_t, ones), s, false);
     xsum[buf][c][sb][qs] = s;
   };
+  // Grid values of a panel (GROUPED): thread t < kWgRows stages its row's
+  // (s, z) for the panel's chunks (neighbouring groups of one row share a
+  // cache line); the loads have no branch (threads past kWgRows and rows
+  // past m read a clamped row, groups past G the last one).
+  static_assert(kWgRows <= kThreads, "one thread per workgroup row");
+  const int wg_row0 = (int)blockIdx.x * kWgRows;
+  const int sz_row = min(wg_row0 + min((int)threadIdx.x, kWgRows - 1), m - 1);
+  auto sz_load = [&](float2 (&v)[PC], int p) {
+#pragma unroll
+    for (int c = 0; c < PC; ++c) {
+      const int gi = min((p * PC + c) / gchunks, G - 1);
+      v[c] = float2{scales[(int64_t)sz_row * G + gi], (float)zeros[(int64_t)sz_row * G + gi]};
+    }
+  };
+  auto sz_store = [&](const float2 (&v)[PC], int buf) {
+    if ((int)threadIdx.x < kWgRows) {
+#pragma unroll
+      for (int c = 0; c < PC; ++c) gsz[buf][c][threadIdx.x] = v[c];
+    }
+  };
   // A panel's words for the wave's tiles: segment 4 (p PC + c) + q of each
   // tile row, clamped to the last segment (its X is staged as zeros).
   struct Words {
@@ -657,13 +681,39 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
         o.w[i][c] = __builtin_nontemporal_load(reinterpret_cast<const WordT*>(wrow[i] + (int64_t)seg * BITS));
     }
   };
-  floatx4 acc[TPW];
+  // Per-row grids: one accumulator per tile over all of n and sum x over
+  // the row.  Groups: every chunk is folded into y on its own (the fold is
+  // linear, so a group of several chunks is the sum of its chunks' folds),
+  // one chunk late: chunk c accumulates into accs[c & 1] and its fold waits
+  // until chunk c + 1's products are issued, so it never waits for the
+  // matrix core.
+  floatx4 accs[GROUPED ? 2 : 1][TPW];
 #pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < (GROUPED ? 2 : 1); ++k)
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) accs[k][i] = floatx4{0.f, 0.f, 0.f, 0.f};
   float sx = 0.f;
-  auto compute = [&](const Words& o, int buf) {
+  float sxc[2] = {0.f, 0.f};
+  floatx4 yacc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) yacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // y += s (2^24 acc - z sum x) for the chunk held in accs[par] (chunk fc of
+  // the panel in LDS buffer fbuf), then that accumulator starts afresh.
+  auto fold = [&](int par, int fbuf, int fc) {
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float2 v = gsz[fbuf][fc][(wave + kWaves * i) * 16 + 4 * q + e];
+        yacc[i][e] = __builtin_fmaf(v.x, __builtin_fmaf(accs[par][i][e], kTwo24, -v.y * sxc[par]), yacc[i][e]);
+      }
+      accs[par][i] = floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto compute = [&](const Words& o, int buf, int p) {
 #pragma unroll
     for (int c = 0; c < PC; ++c) {
+      const int par = GROUPED ? (c & 1) : 0;
       half8_t bop[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) bop[j] = __builtin_bit_cast(half8_t, xs[buf][c][j][q][bb]);
@@ -677,13 +727,27 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
         D::pairs(w, pr);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]),
-                                                          bop[j], acc[i], 0, 0, 0);
+          accs[par][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+              as_half8(pr[4 * j], pr[4 * j + 1], pr[4 * j + 2], pr[4 * j + 3]), bop[j], accs[par][i], 0, 0, 0);
       }
-      sx += s4[0];
-      sx += s4[1];
-      sx += s4[2];
-      sx += s4[3];
+      if constexpr (GROUPED) {
+        float t = s4[0];
+        t += s4[1];
+        t += s4[2];
+        t += s4[3];
+        sxc[par] = t;
+        // the previous chunk: c - 1 of this panel, or the last chunk of the
+        // previous panel (its LDS buffer is rewritten only after this panel)
+        if (c > 0)
+          fold(par ^ 1, buf, c - 1);
+        else if (p > 0)
+          fold(par ^ 1, buf ^ 1, PC - 1);
+      } else {
+        sx += s4[0];
+        sx += s4[1];
+        sx += s4[2];
+        sx += s4[3];
+      }
     }
   };
   // Panel 0 staged before the loop; panel p + 1's X and words load while
@@ -691,9 +755,14 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
   // array of them would put them in scratch memory).
   Words wa, wb;
   u32x4 xr[4];
+  float2 szr[PC];
   if (su < kUnits) {
     stage_load(xr, 0);
     stage_store(xr, 0);
+  }
+  if constexpr (GROUPED) {
+    sz_load(szr, 0);
+    sz_store(szr, 0);
   }
   load_words(wa, 0);
   __syncthreads();
@@ -701,22 +770,32 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
     const bool more1 = p + 1 < npanel;
     if (more1) {
       if (su < kUnits) stage_load(xr, p + 1);
+      if constexpr (GROUPED) sz_load(szr, p + 1);
       load_words(wb, p + 1);
     }
-    compute(wa, 0);
+    compute(wa, 0, p);
     if (more1 && su < kUnits) stage_store(xr, 1);
+    if constexpr (GROUPED) {
+      if (more1) sz_store(szr, 1);
+    }
     __syncthreads();
     if (!more1) break;
     const bool more2 = p + 2 < npanel;
     if (more2) {
       if (su < kUnits) stage_load(xr, p + 2);
+      if constexpr (GROUPED) sz_load(szr, p + 2);
       load_words(wa, p + 2);
     }
-    compute(wb, 1);
+    compute(wb, 1, p + 1);
     if (more2 && su < kUnits) stage_store(xr, 0);
+    if constexpr (GROUPED) {
+      if (more2) sz_store(szr, 0);
+    }
     __syncthreads();
   }
-  // y = s (2^24 acc - z sum x); rows past m and X rows past the batch are not stored.
+  if constexpr (GROUPED) fold((PC - 1) & 1, (npanel - 1) & 1, PC - 1);
+  // Per-row grids: y = s (2^24 acc - z sum x); groups: the folded sums.
+  // Rows past m and X rows past the batch are not stored.
   if (c16 >= batch) return;
 #pragma unroll
   for (int i = 0; i < TPW; ++i)
@@ -724,9 +803,13 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
     for (int e = 0; e < 4; ++e) {
       const int row = (tile0 + kWaves * i) * 16 + 4 * q + e;
       if (row < m) {
-        const float sc = scales[(int64_t)row * G];
-        const float z = (float)zeros[(int64_t)row * G];
-        Y[(int64_t)c16 * ldy + row] = sc * __builtin_fmaf(acc[i][e], kTwo24, -z * sx);
+        if constexpr (GROUPED) {
+          Y[(int64_t)c16 * ldy + row] = yacc[i][e];
+        } else {
+          const float sc = scales[(int64_t)row * G];
+          const float z = (float)zeros[(int64_t)row * G];
+          Y[(int64_t)c16 * ldy + row] = sc * __builtin_fmaf(accs[0][i][e], kTwo24, -z * sx);
+        }
       }
     }
 }
@@ -912,6 +995,22 @@ void launch_mfma(hipStream_t st, const uint32_t* packed, int m, int n, int64_t l
                                                                batch, ldx, Y, ldy, vec_w, vec_x);
 }
 
+// The streaming kernel with `tpw` tiles of 16 rows per wave.
+template <int BITS, int NB, bool GROUPED>
+void launch_stream_grouped(hipStream_t st, unsigned grid, int tpw, const uint32_t* packed, int m, int n,
+                           int64_t ldp, const float* scales, const uint8_t* zeros, int G, int gchunks,
+                           const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy) {
+  if (tpw >= 3)
+    dequant_mfma_stream_kernel<BITS, NB, 3, GROUPED><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G,
+                                                                               gchunks, X, batch, ldx, Y, ldy);
+  else if (tpw == 2)
+    dequant_mfma_stream_kernel<BITS, NB, 2, GROUPED><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G,
+                                                                               gchunks, X, batch, ldx, Y, ldy);
+  else
+    dequant_mfma_stream_kernel<BITS, NB, 1, GROUPED><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G,
+                                                                               gchunks, X, batch, ldx, Y, ldy);
+}
+
 // Tiles per wave of the streaming kernel: the most (up to kStreamMaxTpw) that
 // still give every CU a workgroup.  With four staged rows of X, one tile per
 // wave (three times the workgroups, each staging X again) keeps more loads in
@@ -919,32 +1018,29 @@ void launch_mfma(hipStream_t st, const uint32_t* packed, int m, int n, int64_t l
 // that gains (49152 x 12288 4-bit: batch 3 73 vs 82 us, batch 16 92 vs 86 us).
 template <int BITS, int NB>
 void launch_stream_nb(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
-                      const uint8_t* zeros, int G, const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy,
-                      int64_t tiles) {
+                      const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx,
+                      float* Y, int64_t ldy, int64_t tiles) {
   int tpw = NB == 4 ? 1 : kStreamMaxTpw;
   while (tpw > 1 && ceil_div(tiles, (int64_t)kWaves * tpw) < kStreamMinTiles / kWaves) --tpw;
   const unsigned grid = (unsigned)ceil_div(tiles, (int64_t)kWaves * tpw);
-  if (tpw >= 3)
-    dequant_mfma_stream_kernel<BITS, NB, 3><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
-                                                                      ldx, Y, ldy);
-  else if (tpw == 2)
-    dequant_mfma_stream_kernel<BITS, NB, 2><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
-                                                                      ldx, Y, ldy);
+  if (group_size > 0)
+    launch_stream_grouped<BITS, NB, true>(st, grid, tpw, packed, m, n, ldp, scales, zeros, G, group_size / 128, X,
+                                          batch, ldx, Y, ldy);
   else
-    dequant_mfma_stream_kernel<BITS, NB, 1><<<grid, kThreads, 0, st>>>(packed, m, n, ldp, scales, zeros, G, X, batch,
-                                                                      ldx, Y, ldy);
+    launch_stream_grouped<BITS, NB, false>(st, grid, tpw, packed, m, n, ldp, scales, zeros, G, 1, X, batch, ldx, Y,
+                                           ldy);
 }
 
 template <int BITS>
 void launch_stream(hipStream_t st, const uint32_t* packed, int m, int n, int64_t ldp, const float* scales,
-                   const uint8_t* zeros, int G, const uint16_t* X, int batch, int64_t ldx, float* Y, int64_t ldy,
-                   int64_t tiles) {
+                   const uint8_t* zeros, int G, int group_size, const uint16_t* X, int batch, int64_t ldx, float* Y,
+                   int64_t ldy, int64_t tiles) {
   if (batch <= 4)
-    launch_stream_nb<BITS, 4>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+    launch_stream_nb<BITS, 4>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, tiles);
   else if (batch <= 8)
-    launch_stream_nb<BITS, 8>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+    launch_stream_nb<BITS, 8>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, tiles);
   else
-    launch_stream_nb<BITS, 16>(st, packed, m, n, ldp, scales, zeros, G, X, batch, ldx, Y, ldy, tiles);
+    launch_stream_nb<BITS, 16>(st, packed, m, n, ldp, scales, zeros, G, group_size, X, batch, ldx, Y, ldy, tiles);
 }
 
 template <int BITS>
@@ -962,16 +1058,17 @@ void launch_mfma_shape(hipStream_t st, const uint32_t* packed, int m, int n, int
     // 49152: batch 3-8 102-123 us on the kernel below against 142-152 us,
     // batch 12-16 160-203 us against 149 us).
     const int64_t tiles = ceil_div(m, (int64_t)16);
-    const bool stream_layout = BITS != 3 && group_size == 0 && n >= kSeg && n % kSeg == 0 && vec_w && vec_x;
+    const bool stream_layout = BITS != 3 && n >= kSeg && n % kSeg == 0 && vec_w && vec_x;
     for (int b0 = 0; b0 < batch; b0 += 16) {
       const int cb = std::min(16, batch - b0);
       const uint16_t* Xc = X + (int64_t)b0 * ldx;
       float* Yc = Y + (int64_t)b0 * ldy;
       const bool stream = stream_layout && (tiles >= (int64_t)kStreamMinTiles ||
-                                            (tiles >= (int64_t)kStreamMinTiles * 3 / 4 && cb > 8));
+                                            (tiles >= (int64_t)kStreamMinTiles * 3 / 4 && cb > 8) ||
+                                            (group_size > 0 && tiles >= (int64_t)kStreamGroupMinTiles));
       if constexpr (BITS != 3) {
         if (stream) {
-          launch_stream<BITS>(st, packed, m, n, ldp, scales, zeros, G, Xc, cb, ldx, Yc, ldy, tiles);
+          launch_stream<BITS>(st, packed, m, n, ldp, scales, zeros, G, group_size, Xc, cb, ldx, Yc, ldy, tiles);
           continue;
         }
       }

@@ -115,29 +115,36 @@ def test_dequant_gemv_decode_kernel_matches_row_group_kernel(g, m, n, bits, grou
 
 
 # Decode batches of 3 to 16 rows of X on layers of at least 1024 tiles of 16
-# rows, or 768 with more than eight rows of X (per-row grids, 2- or 4-bit, n
-# a multiple of 32, aligned rows) run on the streaming kernel that stages X
-# in LDS panels of 512 columns; the cases cover one, two and three tiles per
-# wave, a ragged last tile, panels of fewer than four chunks, an odd panel
-# count and every staged X width.
+# rows, or 768 with more than eight rows of X (per-row grids or contiguous
+# groups of a multiple of 128 columns, 2- or 4-bit, n a multiple of 32,
+# aligned rows) run on the streaming kernel that stages X (and, for groups,
+# the rows' scales and zeros) in LDS panels of 512 columns; the cases cover
+# one, two and three tiles per wave, a ragged last tile, panels of fewer than
+# four chunks, an odd panel count, every staged X width, groups of one, two
+# and three chunks and a partial last group.
 STREAM_CASES = [
-    # m, n, bits, batch, entry
-    (16390, 1024, 4, 3, "gemv"),     # one tile per wave, ragged last tile, two panels, 4 staged rows
-    (32768, 1376, 4, 8, "gemv"),     # two tiles per wave, 43 segments: partial last chunk, three panels
-    (24576, 2080, 2, 16, "gemv"),    # 2-bit, 16 rows of X, five panels
-    (49152, 640, 4, 12, "gemv"),     # three tiles per wave, 16 staged rows, 12 used
-    (20000, 384, 4, 2, "gemm"),      # one panel of three chunks through the matrix-core entry at batch 2
-    (16384, 512, 2, 21, "gemm"),     # batch past one 16-row pass: 16 + 5
-    (12288, 1056, 4, 12, "gemv"),    # 768 tiles: taken for more than eight rows of X only
+    # m, n, bits, group, batch, entry
+    (16390, 1024, 4, 0, 3, "gemv"),      # one tile per wave, ragged last tile, two panels, 4 staged rows
+    (32768, 1376, 4, 0, 8, "gemv"),      # two tiles per wave, 43 segments: partial last chunk, three panels
+    (24576, 2080, 2, 0, 16, "gemv"),     # 2-bit, 16 rows of X, five panels
+    (49152, 640, 4, 0, 12, "gemv"),      # three tiles per wave, 16 staged rows, 12 used
+    (20000, 384, 4, 0, 2, "gemm"),       # one panel of three chunks through the matrix-core entry at batch 2
+    (16384, 512, 2, 0, 21, "gemm"),      # batch past one 16-row pass: 16 + 5
+    (12288, 1056, 4, 0, 12, "gemv"),     # 768 tiles: taken for more than eight rows of X only
+    (16390, 1024, 4, 128, 3, "gemv"),    # groups of one chunk, one tile per wave
+    (32768, 1376, 4, 256, 8, "gemv"),    # groups of two chunks, partial last group, two tiles per wave
+    (49152, 640, 4, 128, 12, "gemv"),    # groups, three tiles per wave
+    (24576, 2080, 2, 384, 16, "gemv"),   # 2-bit, groups of three chunks, partial last group
+    (12288, 1056, 4, 128, 9, "gemv"),    # groups on a 768-tile layer
 ]
 
 
-@pytest.mark.parametrize("m,n,bits,batch,entry", STREAM_CASES)
-def test_dequant_streaming_kernel(g, m, n, bits, batch, entry):
-    log(f"dequant streaming kernel m={m} n={n} bits={bits} batch={batch} entry={entry}")
-    L = _layer(m, n, bits, 0, False, seed=m + n + batch)
+@pytest.mark.parametrize("m,n,bits,group,batch,entry", STREAM_CASES)
+def test_dequant_streaming_kernel(g, m, n, bits, group, batch, entry):
+    log(f"dequant streaming kernel m={m} n={n} bits={bits} group={group} batch={batch} entry={entry}")
+    L = _layer(m, n, bits, group, False, seed=m + n + batch + group)
     X16, Xbuf = _x(batch, n, seed=5 * n + batch)
-    Y = _run(g, L, X16, Xbuf, n, bits, 0, False) if entry == "gemv" else _run_gemm(g, L, Xbuf, n, bits, 0)
+    Y = _run(g, L, X16, Xbuf, n, bits, group, False) if entry == "gemv" else _run_gemm(g, L, Xbuf, n, bits, group)
     rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([m, n, 41])))
     rows = np.unique(np.concatenate([rng.choice(m, size=256, replace=False), [0, 15, 16, m - 16, m - 1]]))
     words = L["packed"][rows, :L["nw"]]
