@@ -542,6 +542,93 @@ __device__ inline void upd_tile(const UpdPlan& u, int t, int& bi, int& bj, bool&
   }
 }
 
+// Full-mode tiles in band order: bands of kBand block columns, and within a
+// band the block rows in order, each row's tiles left to right -- first the
+// SYRK triangle (band b: columns next + b kBand .., rows from the band's
+// first column down), then the inverse rectangle (band b: columns
+// b kBand .., rows next .. nbk-1).  Work is handed out in contiguous ranges
+// of this order, one range of it per XCD, so an XCD's L2 keeps its bands' B
+// blocks (kBand x 128 KB at K = 256) while the A rows stream through once
+// per band, instead of every row of a row band streaming the whole panel's
+// B.  Tile 0 is still the diagonal block.  The walk starts with a loop over
+// the bands and then steps one tile at a time.
+constexpr int kBand = 8;
+struct BandWalk {
+  int t;          // tile index of the current position
+  int b, r, c;    // band, row within the band's rows, column within the band
+  bool syrk;
+};
+
+__device__ inline int band_width(int b, int cols) { return min(kBand, cols - b * kBand); }
+
+// SYRK band b of a T x T lower triangle: rows R = T - b kBand, row r holds
+// min(wb, r + 1) tiles.
+__device__ inline int syrk_band_tiles(int T, int b) {
+  const int R = T - b * kBand, wb = min(kBand, R);
+  return wb * (wb + 1) / 2 + (R - wb) * wb;
+}
+
+__device__ inline void band_start(const UpdPlan& u, int t, BandWalk& w) {
+  w.t = t;
+  if (t < u.S) {
+    w.syrk = true;
+    int b = 0, e = t;
+    while (e >= syrk_band_tiles(u.T, b)) e -= syrk_band_tiles(u.T, b++);
+    const int wb = band_width(b, u.T), tri = wb * (wb + 1) / 2;
+    int r, c;
+    if (e < tri) {
+      r = 0;
+      while ((r + 1) * (r + 2) / 2 <= e) ++r;
+      c = e - r * (r + 1) / 2;
+    } else {
+      r = wb + (e - tri) / wb;
+      c = (e - tri) % wb;
+    }
+    w.b = b;
+    w.r = r;
+    w.c = c;
+  } else {
+    w.syrk = false;
+    int e = t - u.S, b = 0;
+    while (e >= u.T * band_width(b, u.next)) e -= u.T * band_width(b++, u.next);
+    const int wb = band_width(b, u.next);
+    w.b = b;
+    w.r = e / wb;
+    w.c = e % wb;
+  }
+}
+
+__device__ inline void band_step(const UpdPlan& u, BandWalk& w) {
+  ++w.t;
+  if (w.syrk) {
+    const int wb = band_width(w.b, u.T);
+    if (++w.c < min(wb, w.r + 1)) return;
+    w.c = 0;
+    if (++w.r < u.T - w.b * kBand) return;
+    w.r = 0;
+    if (++w.b * kBand < u.T) return;
+    w.syrk = false;   // on to the inverse rectangle
+    w.b = 0;
+    return;
+  }
+  if (++w.c < band_width(w.b, u.next)) return;
+  w.c = 0;
+  if (++w.r < u.T) return;
+  w.r = 0;
+  ++w.b;
+}
+
+__device__ inline void band_tile(const UpdPlan& u, const BandWalk& w, int& bi, int& bj, bool& syrk) {
+  syrk = w.syrk;
+  if (w.syrk) {
+    bi = u.next + w.b * kBand + w.r;
+    bj = u.next + w.b * kBand + w.c;
+  } else {
+    bi = u.next + w.r;
+    bj = w.b * kBand + w.c;
+  }
+}
+
 // Half tiles per workgroup of the trailing update (one per wave at a time).
 constexpr int kUpdWaves = kThreads / 64;
 
@@ -626,10 +713,18 @@ __global__ __launch_bounds__(kThreads) void chol_update_kernel(double* __restric
   // Unit u's operands from its first usable panel on: A rows of the half
   // tile, the B block (row-major over k, leading dimension np), the C rows,
   // the number of 16-deep chunks, and whether C starts from zero.
+  // Full mode walks the band order from the first tile of the range.
+  BandWalk walk;
+  if (!up.narrow) band_start(up, u_lo >> 1, walk);
   auto unit_ref = [&](int u, const double*& ua, const double*& ub, double*& uc, int& nch, bool& first) {
     int bi, bj;
     bool syrk;
-    upd_tile(up, u >> 1, bi, bj, syrk);
+    if (up.narrow) {
+      upd_tile(up, u >> 1, bi, bj, syrk);
+    } else {
+      while (walk.t < (u >> 1)) band_step(up, walk);
+      band_tile(up, walk, bi, bj, syrk);
+    }
     const int pstart = syrk ? 0 : max(0, bj - p0);   // X[p, bj] = 0 for panels p < bj
     if (syrk) {
       ub = Lt + (int64_t)pstart * kB * np + (int64_t)bj * kB;

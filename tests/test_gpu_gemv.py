@@ -196,21 +196,24 @@ def test_dequant_gemv_edges(g):
     assert np.all(host(Y) == 0)
 
 
-def test_dequant_gemv_full_size_layer(g):
-    # The 175B-class fc1 layer (49152 x 12288, 4-bit per-row) at batch 1, the
-    # shape the decode measurement times; sampled rows against the oracle.
+@pytest.mark.parametrize("batch,group", [(1, 0), (2, 0), (4, 0), (16, 0), (4, 128), (16, 128)])
+def test_dequant_gemv_full_size_layer(g, batch, group):
+    # The 175B-class fc1 layer (49152 x 12288, 4-bit) at the batches the
+    # decode measurements time (1 and 16 in the bench line's next rows, 4 in
+    # its profile) and with groups of 128; sampled rows against the oracle.
     import torch
     m, n, bits = 49152, 12288, 4
-    log("dequant_gemv full size 49152 x 12288")
-    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([11, 33])))
+    log(f"dequant_gemv full size 49152 x 12288 batch {batch} group {group}")
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([11, 33, batch, group])))
     nw = oracle.packed_words_per_row(n, bits)
+    G = 1 if group == 0 else n // group
     words = rng.integers(0, 1 << 32, size=(m, nw), dtype=np.uint64).astype(np.uint32)
-    scales = (rng.uniform(0.5, 2.0, size=(m, 1)) * 1e-2).astype(np.float32)
-    zeros = rng.integers(0, 16, size=(m, 1)).astype(np.uint8)
-    g_idx = np.zeros(n, dtype=np.int32)
-    X16 = rng.standard_normal((1, n)).astype(np.float16)
+    scales = (rng.uniform(0.5, 2.0, size=(m, G)) * 1e-2).astype(np.float32)
+    zeros = rng.integers(0, 16, size=(m, G)).astype(np.uint8)
+    g_idx = (np.arange(n) // group if group else np.zeros(n)).astype(np.int32)
+    X16 = rng.standard_normal((batch, n)).astype(np.float16)
     Y = g.gptq_dequant_gemv(torch.from_numpy(words.view(np.int32)).cuda(), dev(scales), dev(zeros, "u8"),
-                            torch.from_numpy(X16).cuda(), n, bits)
+                            torch.from_numpy(X16).cuda(), n, bits, group_size=group)
     torch.cuda.synchronize()
     Yg = host(Y).astype(np.float64)
     rows = np.sort(rng.choice(m, size=64, replace=False))
