@@ -601,9 +601,12 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
   static_assert(kUnits % 64 == 0 && kUnits <= kThreads, "whole waves stage");
   __shared__ u32x4 xs[2][PC][4][4][NB];
   __shared__ floatx4 xsum[2][PC][NB];
-  // Groups (GROUPED): (s, z) of the workgroup's rows for each chunk's group.
+  // Groups (GROUPED): (s, z) of the workgroup's rows for each chunk's group,
+  // panel p in buffer p mod 3: while panel p multiplies, a wave still folds
+  // panel p - 1's last chunk and a faster wave may already store panel p + 1,
+  // so three panels are live at once.
   constexpr int kWgRows = kWaves * TPW * 16;
-  __shared__ float2 gsz[GROUPED ? 2 : 1][GROUPED ? PC : 1][GROUPED ? kWgRows : 1];
+  __shared__ float2 gsz[GROUPED ? 3 : 1][GROUPED ? PC : 1][GROUPED ? kWgRows : 1];
   const int lane = threadIdx.x & 63, q = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int nseg = n / kSeg;
@@ -698,7 +701,8 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
 #pragma unroll
   for (int i = 0; i < TPW; ++i) yacc[i] = floatx4{0.f, 0.f, 0.f, 0.f};
   // y += s (2^24 acc - z sum x) for the chunk held in accs[par] (chunk fc of
-  // the panel in LDS buffer fbuf), then that accumulator starts afresh.
+  // the panel whose (s, z) are in gsz[fbuf]), then that accumulator starts
+  // afresh.
   auto fold = [&](int par, int fbuf, int fc) {
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -737,11 +741,11 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
         t += s4[3];
         sxc[par] = t;
         // the previous chunk: c - 1 of this panel, or the last chunk of the
-        // previous panel (its LDS buffer is rewritten only after this panel)
+        // previous panel
         if (c > 0)
-          fold(par ^ 1, buf, c - 1);
+          fold(par ^ 1, p % 3, c - 1);
         else if (p > 0)
-          fold(par ^ 1, buf ^ 1, PC - 1);
+          fold(par ^ 1, (p + 2) % 3, PC - 1);
       } else {
         sx += s4[0];
         sx += s4[1];
@@ -776,7 +780,7 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
     compute(wa, 0, p);
     if (more1 && su < kUnits) stage_store(xr, 1);
     if constexpr (GROUPED) {
-      if (more1) sz_store(szr, 1);
+      if (more1) sz_store(szr, (p + 1) % 3);
     }
     __syncthreads();
     if (!more1) break;
@@ -789,11 +793,11 @@ __global__ __launch_bounds__(kThreads) void dequant_mfma_stream_kernel(
     compute(wb, 1, p + 1);
     if (more2 && su < kUnits) stage_store(xr, 0);
     if constexpr (GROUPED) {
-      if (more2) sz_store(szr, 0);
+      if (more2) sz_store(szr, (p + 2) % 3);
     }
     __syncthreads();
   }
-  if constexpr (GROUPED) fold((PC - 1) & 1, (npanel - 1) & 1, PC - 1);
+  if constexpr (GROUPED) fold((PC - 1) & 1, (npanel - 1) % 3, PC - 1);
   // Per-row grids: y = s (2^24 acc - z sum x); groups: the folded sums.
   // Rows past m and X rows past the batch are not stored.
   if (c16 >= batch) return;
