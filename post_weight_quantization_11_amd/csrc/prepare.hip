@@ -543,29 +543,30 @@ __device__ inline void upd_tile(const UpdPlan& u, int t, int& bi, int& bj, bool&
 }
 
 // Full-mode tiles in band order: bands of kBand block columns, and within a
-// band the block rows in order, each row's tiles left to right -- first the
-// SYRK triangle (band b: columns next + b kBand .., rows from the band's
-// first column down), then the inverse rectangle (band b: columns
-// b kBand .., rows next .. nbk-1).  Work is handed out in contiguous ranges
-// of this order, one range of it per XCD, so an XCD's L2 keeps its bands' B
-// blocks (kBand x 128 KB at K = 256) while the A rows stream through once
-// per band, instead of every row of a row band streaming the whole panel's
-// B.  Tile 0 is still the diagonal block.  The walk starts with a loop over
-// the bands and then steps one tile at a time.
+// band the columns in order, each column's tiles top to bottom -- first the
+// SYRK triangle (band b: columns next + b kBand .., each from its diagonal
+// tile down), then the inverse rectangle (band b: columns b kBand .., rows
+// next .. nbk-1).  Work is handed out in contiguous ranges of this order,
+// one range of it per XCD: the waves of an XCD then work on the columns of
+// one band at once, each a short run down one column, so a column's B block
+// is read by the waves on that column and a row's A half by the waves on the
+// band's columns at about the same time, and both stay in that XCD's L2
+// between those uses.  Tile 0 is still the diagonal block.  The walk starts
+// with a loop over the bands and then steps one tile at a time.
 constexpr int kBand = 8;
 struct BandWalk {
   int t;          // tile index of the current position
-  int b, r, c;    // band, row within the band's rows, column within the band
+  int b, c, r;    // band, column within the band, row within the band's rows
   bool syrk;
 };
 
 __device__ inline int band_width(int b, int cols) { return min(kBand, cols - b * kBand); }
 
-// SYRK band b of a T x T lower triangle: rows R = T - b kBand, row r holds
-// min(wb, r + 1) tiles.
+// SYRK band b of a T x T lower triangle: R = T - b kBand rows, column c
+// (c < wb) holds rows c .. R-1.
 __device__ inline int syrk_band_tiles(int T, int b) {
   const int R = T - b * kBand, wb = min(kBand, R);
-  return wb * (wb + 1) / 2 + (R - wb) * wb;
+  return wb * R - wb * (wb - 1) / 2;
 }
 
 __device__ inline void band_start(const UpdPlan& u, int t, BandWalk& w) {
@@ -574,47 +575,41 @@ __device__ inline void band_start(const UpdPlan& u, int t, BandWalk& w) {
     w.syrk = true;
     int b = 0, e = t;
     while (e >= syrk_band_tiles(u.T, b)) e -= syrk_band_tiles(u.T, b++);
-    const int wb = band_width(b, u.T), tri = wb * (wb + 1) / 2;
-    int r, c;
-    if (e < tri) {
-      r = 0;
-      while ((r + 1) * (r + 2) / 2 <= e) ++r;
-      c = e - r * (r + 1) / 2;
-    } else {
-      r = wb + (e - tri) / wb;
-      c = (e - tri) % wb;
-    }
+    const int R = u.T - b * kBand;
+    int c = 0;
+    while (e >= R - c) e -= R - c++;
     w.b = b;
-    w.r = r;
     w.c = c;
+    w.r = c + e;
   } else {
     w.syrk = false;
     int e = t - u.S, b = 0;
     while (e >= u.T * band_width(b, u.next)) e -= u.T * band_width(b++, u.next);
-    const int wb = band_width(b, u.next);
     w.b = b;
-    w.r = e / wb;
-    w.c = e % wb;
+    w.c = e / u.T;
+    w.r = e % u.T;
   }
 }
 
 __device__ inline void band_step(const UpdPlan& u, BandWalk& w) {
   ++w.t;
   if (w.syrk) {
-    const int wb = band_width(w.b, u.T);
-    if (++w.c < min(wb, w.r + 1)) return;
-    w.c = 0;
-    if (++w.r < u.T - w.b * kBand) return;
-    w.r = 0;
+    const int R = u.T - w.b * kBand;
+    if (++w.r < R) return;
+    if (++w.c < band_width(w.b, u.T)) {
+      w.r = w.c;
+      return;
+    }
+    w.c = w.r = 0;
     if (++w.b * kBand < u.T) return;
     w.syrk = false;   // on to the inverse rectangle
     w.b = 0;
     return;
   }
-  if (++w.c < band_width(w.b, u.next)) return;
-  w.c = 0;
   if (++w.r < u.T) return;
   w.r = 0;
+  if (++w.c < band_width(w.b, u.next)) return;
+  w.c = 0;
   ++w.b;
 }
 
