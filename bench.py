@@ -15,11 +15,14 @@ takes the 12288 x 12288 layer of the same model, `--config 2` the Llama-7B
 
 Prints one JSON line: columns/s of the whole step, per-stage times and
 roofline fractions, the dominant kernel's roofline record, the CPU
-oracle's time on a bounded sample of the same workload, and under
-"next_rows" short measurements (3 steps each) of the rows built on top of
-the path: the packed decode product, asymmetric calibration, the low-rank
-correction with one refinement round, and a two-block decoder pass
-(`--no-next-rows` skips them).
+oracle's time on a bounded sample of the same workload, under
+"other_layers" short runs (3 steps each) of the other named layer
+workloads (the 256 x 256 fp32 layer, the Llama-7B attention projection and
+MLP pair, the 12288 x 12288 layer), and under "next_rows" short
+measurements of the rows built on top of the path: the packed decode
+product, asymmetric calibration, the low-rank correction with one
+refinement round, and a two-block decoder pass (`--no-next-rows` skips
+both).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 4]
                        [--layer L] [--no-cpu] [--copy-calibration]
@@ -519,6 +522,135 @@ def bench_gemv(args):
     return rec
 
 
+def hessian_flops(n, tokens):
+    return float(n) * (n + 1) * tokens          # upper triangle incl. the diagonal
+
+
+def update_flops(m, n, block):
+    return float(m) * n * (n - block)
+
+
+def stage_record(cfg, m, n, N, G, bits, st_ms):
+    """Per-stage times with their roofline fractions and time budgets: the
+    Hessian against the matrix-core peak of X's type, prepare against float64,
+    the deferred update against the float32 matrix cores, the sweep and pack
+    bytes against HBM."""
+    flops_h = hessian_flops(n, N)
+    flops_p = 2.0 / 3.0 * float(n) ** 3
+    flops_u = update_flops(m, n, cfg.block_size)
+    in_bytes = {"bf16": 2, "f16": 2, "f32": 4}[cfg.dtype]
+    peak_h = PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS
+    bytes_sweep = float(m) * n * (in_bytes + 4 + 1) + m * G * 5 + n * cfg.block_size * 4
+    bytes_pack = float(m) * n * (1 + bits / 8) + 8 * n
+    return {
+        "hessian": {"ms": st_ms["hessian"], "tflops": flops_h / st_ms["hessian"] / 1e9,
+                    "frac_peak": flops_h / st_ms["hessian"] / 1e9 / peak_h,
+                    "peak": f"{'bf16' if cfg.dtype == 'bf16' else 'fp16' if cfg.dtype == 'f16' else 'fp32'} MFMA"},
+        "prepare": {"ms": st_ms["prepare"], "tflops": flops_p / st_ms["prepare"] / 1e9,
+                    "frac_peak": flops_p / st_ms["prepare"] / 1e9 / PEAK_F64_TFLOPS, "peak": "f64 78.6 TF"},
+        "quantize": {"ms": st_ms["quantize"], "launches": -(-n // cfg.block_size),
+                     "update_tflops": flops_u / st_ms["quantize"] / 1e9,
+                     "update_frac_f32_peak": flops_u / st_ms["quantize"] / 1e9 / PEAK_F32_TFLOPS,
+                     "update_budget_ms_at_60pct": flops_u / (0.6 * PEAK_F32_TFLOPS * 1e9),
+                     "sweep_GBps": bytes_sweep / st_ms["quantize"] / 1e6,
+                     "sweep_frac_hbm": bytes_sweep / st_ms["quantize"] / 1e6 / PEAK_HBM_GBS,
+                     "sweep_budget_ms_at_50pct": bytes_sweep / (0.5 * PEAK_HBM_GBS * 1e6)},
+        "pack": {"ms": st_ms["pack"], "GBps": bytes_pack / st_ms["pack"] / 1e6,
+                 "frac_hbm": bytes_pack / st_ms["pack"] / 1e6 / PEAK_HBM_GBS,
+                 "budget_ms_at_50pct": bytes_pack / (0.5 * PEAK_HBM_GBS * 1e6)},
+    }
+
+
+def measure_layer(config, li, steps, warmup, keep_inputs=False):
+    """Whole-path steps on one named layer, inputs resident in HBM: `warmup`
+    untimed steps, then `steps` timed ones with HIP events between the four
+    calls.  Returns the per-stage mean times, the wall time per step and the
+    result's sanity flags (with keep_inputs also the host inputs and the
+    outputs, for the caller's CPU baseline)."""
+    import torch
+    import post_weight_quantization_11_amd as g
+    from post_weight_quantization_11_amd import _lib
+    lib = g.load()
+    cfg = wl.WORKLOADS[config]
+    layer = cfg.layers[li]
+    m, n, N = layer.m, layer.n, cfg.tokens
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    L = wl.workload_layer(config, li)
+    X = L.x_all()
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s: W {m}x{n} {cfg.dtype}, X {N}x{n}")
+    Wd = to_device(L.W)
+    Xd = to_device(X)
+    torch.cuda.synchronize()
+
+    # Outputs and workspaces allocated once, outside the timed region.
+    dev = Wd.device
+    H = torch.empty((n, n), dtype=torch.float32, device=dev)
+    U = torch.empty((n, n), dtype=torch.float32, device=dev)
+    perm = torch.empty((n,), dtype=torch.int32, device=dev)
+    G = 1 if cfg.group_size == 0 else -(-n // cfg.group_size)
+    out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=dev),
+               scales=torch.empty((m, G), dtype=torch.float32, device=dev),
+               zeros=torch.empty((m, G), dtype=torch.uint8, device=dev),
+               g_idx=torch.empty((n,), dtype=torch.int32, device=dev),
+               row_loss=torch.empty((m,), dtype=torch.float32, device=dev), Wq=None)
+    bits = bits_of(cfg.levels)
+    packed = torch.empty((m, g.packed_words(n, bits)), dtype=torch.int32, device=dev)
+    xdt = _lib._dtype_code(Xd)
+    ws_h = torch.empty(max(1, lib.gptq_hessian_ws_bytes(n, N, xdt)), dtype=torch.uint8, device=dev)
+    ws_p = torch.empty(max(1, lib.gptq_prepare_ws_bytes(n)), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(max(1, lib.gptq_quantize_ws_bytes(m, n, cfg.block_size)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        g.gptq_hessian_accumulate(H, Xd, 2.0, True, ws=ws_h)
+        if ev:
+            ev[1].record(stream)
+        g.gptq_prepare_hinv(H, cfg.damp_rel, cfg.act_order, U=U, perm=perm, ws=ws_p)
+        if ev:
+            ev[2].record(stream)
+        g.gptq_quantize_layer(Wd, U, perm if cfg.act_order else None, cfg.levels, cfg.group_size,
+                              cfg.block_size, out=out, ws=ws_q)
+        if ev:
+            ev[3].record(stream)
+        g.gptq_pack(out["codes"], bits, packed=packed)
+        if ev:
+            ev[4].record(stream)
+
+    for i in range(warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"warmup step {i + 1}/{warmup} done")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log(f"{steps} timed steps done in {wall:.2f}s")
+    stage_names = ["hessian", "prepare", "quantize", "pack"]
+    st_ms = {k: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)]))
+             for i, k in enumerate(stage_names)}
+    ms_per_step = wall * 1e3 / steps
+
+    # Sanity of the result (not a parity check; the tests do that).
+    codes_ok = bool(int(out["codes"].max().item()) <= cfg.levels - 1)
+    finite = bool(torch.isfinite(out["scales"]).all().item() and torch.isfinite(out["row_loss"]).all().item())
+    res = dict(layer=layer, m=m, n=n, N=N, st_ms=st_ms, ms_per_step=ms_per_step, G=G, bits=bits,
+               codes_ok=codes_ok, finite=finite, dev=dev)
+    del Xd, Wd, H, U, perm, packed, ws_h, ws_p, ws_q
+    if keep_inputs:
+        res.update(L=L, X=X, out=out)
+    else:
+        del out, L, X
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -572,70 +704,10 @@ def main():
         return
     cfg = wl.WORKLOADS[args.config]
     li = (len(cfg.layers) - 1 if args.config == 4 else 0) if args.layer is None else args.layer
-    layer = cfg.layers[li]
-    m, n, N = layer.m, layer.n, cfg.tokens
-    torch.cuda.set_device(0)
-    t0 = time.perf_counter()
-    L = wl.workload_layer(args.config, li)
-    X = L.x_all()
-    log(f"inputs generated in {time.perf_counter() - t0:.1f}s: W {m}x{n} {cfg.dtype}, X {N}x{n}")
-    Wd = to_device(L.W)
-    Xd = to_device(X)
-    torch.cuda.synchronize()
-
-    # Outputs and workspaces allocated once, outside the timed region.
-    dev = Wd.device
-    H = torch.empty((n, n), dtype=torch.float32, device=dev)
-    U = torch.empty((n, n), dtype=torch.float32, device=dev)
-    perm = torch.empty((n,), dtype=torch.int32, device=dev)
-    G = 1 if cfg.group_size == 0 else -(-n // cfg.group_size)
-    out = dict(codes=torch.empty((m, n), dtype=torch.uint8, device=dev),
-               scales=torch.empty((m, G), dtype=torch.float32, device=dev),
-               zeros=torch.empty((m, G), dtype=torch.uint8, device=dev),
-               g_idx=torch.empty((n,), dtype=torch.int32, device=dev),
-               row_loss=torch.empty((m,), dtype=torch.float32, device=dev), Wq=None)
-    bits = bits_of(cfg.levels)
-    packed = torch.empty((m, g.packed_words(n, bits)), dtype=torch.int32, device=dev)
-    xdt = _lib._dtype_code(Xd)
-    ws_h = torch.empty(max(1, lib.gptq_hessian_ws_bytes(n, N, xdt)), dtype=torch.uint8, device=dev)
-    ws_p = torch.empty(max(1, lib.gptq_prepare_ws_bytes(n)), dtype=torch.uint8, device=dev)
-    ws_q = torch.empty(max(1, lib.gptq_quantize_ws_bytes(m, n, cfg.block_size)), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step(ev=None):
-        if ev:
-            ev[0].record(stream)
-        g.gptq_hessian_accumulate(H, Xd, 2.0, True, ws=ws_h)
-        if ev:
-            ev[1].record(stream)
-        g.gptq_prepare_hinv(H, cfg.damp_rel, cfg.act_order, U=U, perm=perm, ws=ws_p)
-        if ev:
-            ev[2].record(stream)
-        g.gptq_quantize_layer(Wd, U, perm if cfg.act_order else None, cfg.levels, cfg.group_size,
-                              cfg.block_size, out=out, ws=ws_q)
-        if ev:
-            ev[3].record(stream)
-        g.gptq_pack(out["codes"], bits, packed=packed)
-        if ev:
-            ev[4].record(stream)
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"warmup step {i + 1}/{args.warmup} done")
-
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(events[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    log(f"{args.steps} timed steps done in {wall:.2f}s")
-    stage_names = ["hessian", "prepare", "quantize", "pack"]
-    st_ms = {k: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]))
-             for i, k in enumerate(stage_names)}
-    ms_per_step = wall * 1e3 / args.steps
+    meas = measure_layer(args.config, li, args.steps, args.warmup, keep_inputs=True)
+    layer, m, n, N = meas["layer"], meas["m"], meas["n"], meas["N"]
+    st_ms, ms_per_step, G, bits = meas["st_ms"], meas["ms_per_step"], meas["G"], meas["bits"]
+    L, X, out, dev = meas["L"], meas["X"], meas["out"], meas["dev"]
 
     if args.copy_calibration:
         a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
@@ -645,34 +717,11 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # Sanity of the result (not a parity check; the tests do that).
-    codes_ok = bool(int(out["codes"].max().item()) <= cfg.levels - 1)
-    finite = bool(torch.isfinite(out["scales"]).all().item() and torch.isfinite(out["row_loss"]).all().item())
+    codes_ok, finite = meas["codes_ok"], meas["finite"]
 
     nblocks = -(-n // cfg.block_size)
-    flops_h = float(n) * (n + 1) * N
-    flops_p = 2.0 / 3.0 * float(n) ** 3
-    flops_u = float(m) * n * (n - cfg.block_size)
-    in_bytes = {"bf16": 2, "f16": 2, "f32": 4}[cfg.dtype]
-    bytes_sweep = float(m) * n * (in_bytes + 4 + 1) + m * G * 5 + n * cfg.block_size * 4
-    bytes_pack = float(m) * n * (1 + bits / 8) + 8 * n
-    stages = {
-        "hessian": {"ms": st_ms["hessian"], "tflops": flops_h / st_ms["hessian"] / 1e9,
-                    "frac_peak": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
-                    "peak": f"{'bf16' if cfg.dtype == 'bf16' else 'fp16' if cfg.dtype == 'f16' else 'fp32'} MFMA"},
-        "prepare": {"ms": st_ms["prepare"], "tflops": flops_p / st_ms["prepare"] / 1e9,
-                    "frac_peak": flops_p / st_ms["prepare"] / 1e9 / PEAK_F64_TFLOPS, "peak": "f64 78.6 TF"},
-        "quantize": {"ms": st_ms["quantize"], "launches": nblocks,
-                     "update_tflops": flops_u / st_ms["quantize"] / 1e9,
-                     "update_frac_f32_peak": flops_u / st_ms["quantize"] / 1e9 / PEAK_F32_TFLOPS,
-                     "update_budget_ms_at_60pct": flops_u / (0.6 * PEAK_F32_TFLOPS * 1e9),
-                     "sweep_GBps": bytes_sweep / st_ms["quantize"] / 1e6,
-                     "sweep_frac_hbm": bytes_sweep / st_ms["quantize"] / 1e6 / PEAK_HBM_GBS,
-                     "sweep_budget_ms_at_50pct": bytes_sweep / (0.5 * PEAK_HBM_GBS * 1e6)},
-        "pack": {"ms": st_ms["pack"], "GBps": bytes_pack / st_ms["pack"] / 1e6,
-                 "frac_hbm": bytes_pack / st_ms["pack"] / 1e6 / PEAK_HBM_GBS,
-                 "budget_ms_at_50pct": bytes_pack / (0.5 * PEAK_HBM_GBS * 1e6)},
-    }
+    flops_h, flops_u = hessian_flops(n, N), update_flops(m, n, cfg.block_size)
+    stages = stage_record(cfg, m, n, N, G, bits, st_ms)
     # Dominant kernel's roofline record.  The quantize call is one launch of
     # quant_block_kernel per 128-column block (plus a per-row grid kernel of a
     # few microseconds), so its per-launch figures are the call's divided by
@@ -696,9 +745,9 @@ def main():
             "kernel": "gptq_hessian_accumulate (syrk16 MFMA + split reduce), HIP events around the call",
             "bound": "mfma",
             "achieved": flops_h / st_ms["hessian"] / 1e9,
-            "peak": PEAK_BF16_TFLOPS,
+            "peak": PEAK_F32_TFLOPS if cfg.dtype == "f32" else PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
-            "frac": flops_h / st_ms["hessian"] / 1e9 / PEAK_BF16_TFLOPS,
+            "frac": stages["hessian"]["frac_peak"],
             "traffic": measured_traffic("hessian", args.config, li),
             "algorithmic": f"n(n+1)N = {flops_h:.4g} flop per launch",
         }
@@ -727,15 +776,46 @@ def main():
         "roofline": roof,
         "sanity": {"codes_in_range": codes_ok, "finite": finite},
     }
-    del Xd, Wd, H, U, perm, out, packed, ws_h, ws_p, ws_q
+    del meas, out
     torch.cuda.empty_cache()
     if not args.no_cpu:
         log("timing the CPU oracle on a bounded sample ...")
         rec["cpu_baseline"] = cpu_baseline(L, X, cfg, n, m, N)
     del L, X
     if not args.no_next_rows:
+        rec["other_layers"] = other_layers(args.config, li)
         rec["next_rows"] = next_rows(args)
     print(json.dumps(rec), flush=True)
+
+
+# The named layer workloads other than the headline one, timed in the same
+# run (3 steps each after one warm-up step): the 256 x 256 fp32 layer, the
+# Llama-7B attention projection (4-bit g128), the Llama-7B MLP pair (3-bit
+# g128 with act-order) and the 12288 x 12288 layer of the 175B-class model.
+OTHER_LAYERS = ((1, 0), (2, 0), (3, 0), (3, 1), (4, 0), (4, 1))
+
+
+def other_layers(config, li):
+    import torch
+    out = {}
+    for c, l in OTHER_LAYERS:
+        if (c, l) == (config, li):
+            continue
+        t0 = time.perf_counter()
+        cfg = wl.WORKLOADS[c]
+        r = measure_layer(c, l, 3, 1)
+        torch.cuda.synchronize()
+        name = f"{cfg.layers[l].name} {r['m']}x{r['n']}"
+        out[f"config{c}_{cfg.layers[l].name}"] = {
+            "workload": f"{cfg.name}: {name}",
+            "ms_per_step": r["ms_per_step"],
+            "columns_per_s": r["n"] / (r["ms_per_step"] / 1e3),
+            "stages": stage_record(cfg, r["m"], r["n"], r["N"], r["G"], r["bits"], r["st_ms"]),
+            "sanity": {"codes_in_range": r["codes_ok"], "finite": r["finite"]},
+        }
+        log(f"other layer config {c} {name}: {r['ms_per_step']:.3f} ms per step "
+            f"({time.perf_counter() - t0:.1f}s)")
+    return out
 
 
 def next_rows(args):
