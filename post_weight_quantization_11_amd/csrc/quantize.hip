@@ -91,6 +91,11 @@ template <> __device__ inline void store_from_f32<GPTQ_F32>(void* p, int64_t i, 
   static_cast<float*>(p)[i] = v;
 }
 template <> __device__ inline void store_from_f32<GPTQ_F16>(void* p, int64_t i, float v) {
+  // v is already rounded to float32; the empty asm keeps it so: without it
+  // the compiler fuses a product feeding this conversion into one
+  // v_fma_mixlo_f16, which rounds the exact product to float16 once and
+  // differs from fl16(fl32(.)) where the float32 value lies on a float16 tie.
+  asm volatile("" : "+v"(v));
   static_cast<_Float16*>(p)[i] = (_Float16)v;
 }
 template <> __device__ inline void store_from_f32<GPTQ_BF16>(void* p, int64_t i, float v) {
