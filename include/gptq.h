@@ -169,7 +169,8 @@ gptq_status gptq_prepare_hinv(const float* H, int64_t n, float damp_rel, int act
  *   perm       device, n int32 processing order (a permutation of 0..n-1),
  *              or NULL for the identity.
  *   levels     3 (ternary), 4 (2-bit), 8 (3-bit) or 16 (4-bit).
- *   group_size 0 (one grid per row), 16, 32, 64, or a multiple of 128.
+ *   group_size 0 (one grid per row), a divisor of 128 (1, 2, 4, ..., 128)
+ *              or a multiple of 128; others return GPTQ_ERR_UNSUPPORTED.
  *   block_size 128.
  * Outputs (original column order unless noted):
  *   codes      device, m x n uint8 (leading dimension n): codes[r*n + k] is the

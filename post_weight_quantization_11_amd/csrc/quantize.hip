@@ -400,7 +400,7 @@ struct SweepLds {
 // block's sweep left for these rows.  When make_next, the rows' errors of
 // this block are kept in the tile as its columns are finished and
 // E[:, block kb] U[block kb, block kb+1] is written to Plast at the end.
-template <int DT>
+template <int DT, bool SMALLG>
 __device__ __forceinline__ void sweep_body(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
     const float* __restrict__ P, int nsplit, float* __restrict__ Plast, int use_last, int make_next, float maxq,
@@ -536,7 +536,12 @@ __device__ __forceinline__ void sweep_body(
   // A group that starts at this block and spans it (g a multiple of 128, or
   // reaching past n): its range is the slab's, reduced across the 32 lanes
   // that hold a row; lanes 0 and 32 of slot q publish rows 2q and 2q + 1.
-  const bool block_group = g > 0 && (c0 % g) == 0 && (g % kBS == 0 || c0 + g >= n);
+  const bool block_group = g >= kSB && (c0 % g) == 0 && (g % kBS == 0 || c0 + g >= n);
+  // Groups narrower than a register sub-block (1, 2, 4 or 8 columns) start
+  // inside the column chain: their range is taken there, over the current
+  // values of their columns in registers.
+  // (SMALLG: g is 1, 2, 4 or 8; the kernel is instantiated apart so that
+  // the other group sizes run code without these starts.)
   if (block_group) {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
@@ -634,6 +639,28 @@ __device__ __forceinline__ void sweep_body(
     }
   };
 
+  // A group of g < 16 columns starts at processing column col, sub-block
+  // column jj: its range is
+  // over the current values w[jj .. jj+g) of this row (columns from `lim` on
+  // lie past the layer), then its grid is stored.  Called with a
+  // compile-time jj from the unrolled chains, so w stays in registers.
+  auto small_group_start = [&](int col, int jj, const float (&wv)[kSB], int lim) {
+    float mn = wv[jj], mx = wv[jj];
+#pragma unroll
+    for (int kk = 1; kk < kSB; ++kk) {
+      if (jj + kk < kSB && kk < g && jj + kk < lim) {
+        mn = fminf(mn, wv[jj + kk]);
+        mx = fmaxf(mx, wv[jj + kk]);
+      }
+    }
+    grid_from_range(mn, mx, maxq, s, z, inv_s);
+    if (active) {
+      const int gi = col / g;
+      scales[row * G + gi] = s;
+      zeros[row * G + gi] = (uint8_t)z;
+    }
+  };
+
   auto sub_block = [&](auto sbc, auto fullc) {
     constexpr bool FULL = decltype(fullc)::value;
     const int sb = sbc;
@@ -656,7 +683,7 @@ __device__ __forceinline__ void sweep_body(
         scales[row * G + gi] = s;
         zeros[row * G + gi] = (uint8_t)z;
       }
-    } else if (g > 0 && ((c0 + j0) % g) == 0) {
+    } else if (g >= kSB && ((c0 + j0) % g) == 0) {
       // group range over the current values; g is a multiple of 16 and the
       // group lies inside the block (tail columns beyond bw are excluded)
       const int gl = min(g, bw - j0);
@@ -720,6 +747,9 @@ __device__ __forceinline__ void sweep_body(
 #pragma unroll
           for (int kk = jj + 2; kk < kSB; ++kk) un[kk] = Ud[ud_index(j0 + jj + 1, j0 + kk)];
         }
+        if constexpr (SMALLG) {
+          if (((c0 + j0 + jj) & (g - 1)) == 0) small_group_start(c0 + j0 + jj, jj, w, kSB);
+        }
         const float c = quant_code(w[jj], s, inv_s, z, maxq);
         const float what = s * (c - z);
         const float e = (w[jj] - what) * idc;
@@ -733,6 +763,9 @@ __device__ __forceinline__ void sweep_body(
 #pragma unroll
       for (int jj = 0; jj < kSB; ++jj) {
         if (j0 + jj < bw) {
+          if constexpr (SMALLG) {
+            if (((c0 + j0 + jj) & (g - 1)) == 0) small_group_start(c0 + j0 + jj, jj, w, bw - j0);
+          }
           const float c = quant_code(w[jj], s, inv_s, z, maxq);
           const float what = s * (c - z);
           const float e = (w[jj] - what) * invd[j0 + jj];
@@ -838,7 +871,7 @@ __device__ __forceinline__ void sweep_body(
 // each); workgroups nsw .. compute the partial products of block kb+1's
 // deferred update over the columns before block kb (the last block's share
 // comes from the sweep itself), split over K in ranges of sps stages.
-template <int DT>
+template <int DT, bool SMALLG>
 __global__ __launch_bounds__(kThreads, 2) void quant_block_kernel(
     const void* __restrict__ Wsrc, int64_t ldw, int m, int n, int kb, const float* __restrict__ U,
     const float* __restrict__ Pcur, int nsplit, float* __restrict__ Plast, int use_last, int make_next,
@@ -851,8 +884,8 @@ __global__ __launch_bounds__(kThreads, 2) void quant_block_kernel(
   } lds;
   const int wg = (int)blockIdx.x;
   if (wg < nsw) {
-    sweep_body<DT>(Wsrc, ldw, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales,
-                   zeros, row_loss, codes_aligned, perm, grange, wg, lds.s);
+    sweep_body<DT, SMALLG>(Wsrc, ldw, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E,
+                           scales, zeros, row_loss, codes_aligned, perm, grange, wg, lds.s);
   } else {
     const int gid = wg - nsw;
     update_gemm_body(E, U, m, n, kb + 1, kb * kBS, sps, Pnext, gid % mtiles, gid / mtiles, lds.g);
@@ -934,9 +967,10 @@ gptq_status launch_block(const void* src, int64_t ld, int m, int n, int kb, cons
                          const int32_t* perm, const float* grange, int nsw, int mtiles, int ngemm, int sps,
                          float* Pnext, hipStream_t st) {
   const int codes_aligned = (reinterpret_cast<uintptr_t>(codes) & 15) == 0;
-  quant_block_kernel<DT><<<(unsigned)(nsw + ngemm), kThreads, 0, st>>>(
-      src, ld, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next, maxq, g, G, codes, E, scales, zeros,
-      row_loss, codes_aligned, perm, grange, nsw, mtiles, sps, Pnext);
+  auto kern = g > 0 && g < kSB ? quant_block_kernel<DT, true> : quant_block_kernel<DT, false>;
+  kern<<<(unsigned)(nsw + ngemm), kThreads, 0, st>>>(src, ld, m, n, kb, U, Pcur, nsplit, Plast, use_last, make_next,
+                                                      maxq, g, G, codes, E, scales, zeros, row_loss, codes_aligned,
+                                                      perm, grange, nsw, mtiles, sps, Pnext);
   GPTQ_TRY_LAUNCH();
   return GPTQ_OK;
 }
@@ -1052,8 +1086,9 @@ extern "C" gptq_status gptq_quantize_layer(const void* W, int w_dtype, int64_t m
   if (!(levels == 3 || levels == 4 || levels == 8 || levels == 16)) return GPTQ_ERR_INVALID_ARG;
   if (group_size < 0 || block_size <= 0) return GPTQ_ERR_INVALID_ARG;
   if (block_size != kBS) return GPTQ_ERR_UNSUPPORTED;
-  if (!(group_size == 0 || group_size == 16 || group_size == 32 || group_size == 64 || group_size % kBS == 0))
-    return GPTQ_ERR_UNSUPPORTED;
+  // groups that divide the block (the 16-column register sub-block included)
+  // or are whole multiples of it
+  if (!(group_size == 0 || kBS % group_size == 0 || group_size % kBS == 0)) return GPTQ_ERR_UNSUPPORTED;
   if (n > (int64_t)1 << 16 || m > ((int64_t)1 << 31) - 1) return GPTQ_ERR_UNSUPPORTED;
   if (n == 0) return GPTQ_OK;
   hipStream_t st = static_cast<hipStream_t>(stream);

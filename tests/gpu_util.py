@@ -130,6 +130,23 @@ def sweep_sigma(W64, U64, perm, res):
     return np.sqrt(np.maximum(var.T, 0.0))
 
 
+def small_group_scale_bound(W64, U64, perm, rec):
+    """Allowed absolute scale error per (row, group) for groups of 1-8
+    columns, from an oracle result recorded with record_inputs=True: such a
+    group's range comes from one or a few error-updated values, each off by
+    at most K_SIGMA sigma_k + u |w_k| in a float32 sweep, so the scale
+    (range / maxq) is off by at most twice the largest of those over maxq,
+    plus three float32 roundings of its own; never below the 1e-5 relative
+    bar."""
+    g = int(rec["group_size"])
+    so = np.asarray(rec["scales"], dtype=np.float64)
+    ew = K_SIGMA * sweep_sigma(W64, U64, perm, rec) + U_F32 * np.abs(np.asarray(rec["qin"], dtype=np.float64))
+    ewg = np.zeros_like(so)
+    for gi in range(so.shape[1]):
+        ewg[:, gi] = np.max(ew[:, gi * g:(gi + 1) * g], axis=1)
+    return np.maximum(1e-5 * so, 2.0 * ewg / (int(rec["levels"]) - 1) + 3 * U_F32 * so)
+
+
 def certify_ties(W64, U64, perm, levels, group, block, codes_gpu, codes_oracle, max_rows=16, branches=None):
     """Returns (rows_checked, ties) for the rows where codes differ; raises
     AssertionError when a split is not at a near-tie, when the GPU's code is

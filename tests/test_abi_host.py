@@ -146,10 +146,12 @@ def test_quantize_argument_errors(lib):
         assert call(levels=lv) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(dt=5) == _lib.GPTQ_ERR_INVALID_ARG
     assert call(group=-1) == _lib.GPTQ_ERR_INVALID_ARG
-    for g in (8, 24, 48, 96, 200, 320):
+    # groups neither dividing the 128-column block nor a multiple of it
+    for g in (3, 6, 12, 24, 48, 96, 200, 320):
         assert call(group=g) == _lib.GPTQ_ERR_UNSUPPORTED
-    # groups that are multiples of the block pass validation (workspace checked next)
-    for g in (256, 384, 1024):
+    # groups that divide the block or are multiples of it pass validation
+    # (workspace checked next)
+    for g in (1, 2, 4, 8, 16, 32, 64, 128, 256, 384, 1024):
         assert call(group=g, wsb=16) == _lib.GPTQ_ERR_WORKSPACE
     assert call(block=64) == _lib.GPTQ_ERR_UNSUPPORTED
     assert call(ldw=255) == _lib.GPTQ_ERR_INVALID_ARG

@@ -74,9 +74,10 @@ def test_certify_rejects_a_code_not_adjacent_to_the_tie(monkeypatch):
         gu.certify_ties(W, U, None, 16, 8, 16, branch["codes"], res["codes"])
 
 
-def _fp32_sweep(W, U, levels, group):
+def _fp32_sweep(W, U, levels, group, scales_out=None):
     """The unblocked sweep with every operation rounded to float32 (values
-    recorded when quantized): a float32 computation of the same decisions."""
+    recorded when quantized): a float32 computation of the same decisions.
+    With scales_out (a list), each group's scales are appended to it."""
     f = np.float32
     W = np.asarray(W, dtype=f)
     U = np.asarray(U, dtype=f)
@@ -87,9 +88,13 @@ def _fp32_sweep(W, U, levels, group):
     codes = np.zeros((m, n), dtype=f)
     if group == 0:
         s, z = oracle.grid_params(V, maxq)
+        if scales_out is not None:
+            scales_out.append(s)
     for j in range(n):
         if group and j % group == 0:
             s, z = oracle.grid_params(V[:, j:j + group], maxq)
+            if scales_out is not None:
+                scales_out.append(s)
         v = V[:, j].copy()
         qin[:, j] = v
         c = oracle.quantize_values(v, s, z, maxq)
@@ -100,7 +105,7 @@ def _fp32_sweep(W, U, levels, group):
     return codes, qin
 
 
-@pytest.mark.parametrize("group", [0, 16])
+@pytest.mark.parametrize("group", [0, 16, 8, 2])
 def test_fp32_sweep_deviation_within_the_derived_sigma(group):
     # The tolerance model must not be optimistic: a float32 sweep's values
     # deviate from the float64 oracle's by less than K_SIGMA sigma_j at every
@@ -125,6 +130,31 @@ def test_fp32_sweep_deviation_within_the_derived_sigma(group):
         ratios.append(dev / np.maximum(sigma[r, :upto], 1e-300))
     ratios = np.concatenate(ratios)
     assert np.sqrt(np.mean(ratios ** 2)) < 1.0
+
+
+@pytest.mark.parametrize("group,levels", [(1, 4), (2, 16), (4, 8), (8, 3)])
+def test_small_group_scale_bound_holds_for_a_float32_sweep(group, levels):
+    # Scales of groups of 1-8 columns come from one or a few error-updated
+    # values; a float32 sweep's scales stay within small_group_scale_bound
+    # of the float64 oracle's on every row whose codes agree, and the bound
+    # is tight enough to mean something (well under the values' magnitude).
+    rng = np.random.default_rng(41 + group)
+    n, m = 256, 40
+    X = rng.standard_normal((4 * n, n)) @ (np.eye(n) + rng.standard_normal((n, n)) / np.sqrt(n))
+    X *= np.exp(rng.normal(0, 1, n))
+    Hd, _ = oracle.damp_and_permute(oracle.hessian(X), None, 0.01)
+    U = oracle.inverse_cholesky_upper(Hd).astype(np.float32).astype(np.float64)
+    W = (rng.standard_normal((m, n)) * 0.02).astype(np.float32).astype(np.float64)
+    rec = oracle.gptq_quantize(W, U, None, levels, group, block_size=1, record_inputs=True)
+    sc = []
+    c32, _ = _fp32_sweep(W, U, levels, group, scales_out=sc)
+    s32 = np.stack(sc, axis=1).astype(np.float64)
+    ok = np.all(c32 == rec["codes"], axis=1)
+    assert ok.sum() >= m // 2
+    tol = gu.small_group_scale_bound(W, U, None, rec)
+    so = np.asarray(rec["scales"], dtype=np.float64)
+    assert np.all(np.abs(s32[ok] - so[ok]) <= tol[ok])
+    assert np.median(tol[ok] / so[ok]) < 1e-3
 
 
 def test_certify_accepts_a_branch_at_admitted_ties(monkeypatch):
