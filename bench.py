@@ -825,7 +825,8 @@ def next_rows(args):
     launches each),
     then three steps each of asymmetric
     calibration and the rank-64 low-rank correction with one refinement
-    round on the 4096 x 4096 layer, and a two-block Llama-7B decoder pass."""
+    round on the 4096 x 4096 layer, and a two-block Llama-7B decoder pass
+    (2-bit g64, then ternary g64)."""
     import argparse as _ap
     import torch
     short = _ap.Namespace(**vars(args))
@@ -857,6 +858,9 @@ def next_rows(args):
                    "frac_f64": {k: v["frac"] for k, v in r["lowrank_roofline"]["stages"].items()}})
     short.decoder_blocks = 2
     run("f1_decoder_pass", bench_decoder,
+        lambda r: {"layers": r["layers"], "quantizer_s": r["quantizer_s"], "stage_s": r["stage_s"]})
+    short.levels = 3                                        # the ternary stress variant
+    run("f1_decoder_pass_ternary", bench_decoder,
         lambda r: {"layers": r["layers"], "quantizer_s": r["quantizer_s"], "stage_s": r["stage_s"]})
     return out
 
