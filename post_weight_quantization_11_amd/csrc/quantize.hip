@@ -537,11 +537,10 @@ __device__ __forceinline__ void sweep_body(
   // reaching past n): its range is the slab's, reduced across the 32 lanes
   // that hold a row; lanes 0 and 32 of slot q publish rows 2q and 2q + 1.
   const bool block_group = g >= kSB && (c0 % g) == 0 && (g % kBS == 0 || c0 + g >= n);
-  // Groups narrower than a register sub-block (1, 2, 4 or 8 columns) start
-  // inside the column chain: their range is taken there, over the current
-  // values of their columns in registers.
-  // (SMALLG: g is 1, 2, 4 or 8; the kernel is instantiated apart so that
-  // the other group sizes run code without these starts.)
+  // Groups narrower than a register sub-block (1, 2, 4 or 8 columns: SMALLG,
+  // a kernel instantiation of its own, so that the other group sizes run
+  // code without these starts) begin inside the column chain, which takes
+  // their range there from the current values of their columns.
   if (block_group) {
 #pragma unroll
     for (int q = 0; q < kSlots; ++q) {
@@ -639,11 +638,11 @@ __device__ __forceinline__ void sweep_body(
     }
   };
 
-  // A group of g < 16 columns starts at processing column col, sub-block
-  // column jj: its range is
-  // over the current values w[jj .. jj+g) of this row (columns from `lim` on
-  // lie past the layer), then its grid is stored.  Called with a
-  // compile-time jj from the unrolled chains, so w stays in registers.
+  // A group of g < 16 columns starts at processing column col (sub-block
+  // column jj): its range is over the current values w[jj .. jj+g) of this
+  // row (columns from `lim` on lie past the layer), then its grid is stored.
+  // Called with a compile-time jj from the unrolled chains, so w stays in
+  // registers.
   auto small_group_start = [&](int col, int jj, const float (&wv)[kSB], int lim) {
     float mn = wv[jj], mx = wv[jj];
 #pragma unroll
