@@ -18,7 +18,8 @@ roofline fractions, the dominant kernel's roofline record, the CPU
 oracle's time on a bounded sample of the same workload, under
 "other_layers" short runs (3 steps each) of the other named layer
 workloads (the 256 x 256 fp32 layer, the Llama-7B attention projection and
-MLP pair, the 12288 x 12288 layer), and under "next_rows" short
+MLP pair, the 12288 x 12288 layer) and one GPU's share of the fc1 layer
+split over eight GPUs, and under "next_rows" short
 measurements of the rows built on top of the path: the packed decode
 product, asymmetric calibration, the low-rank correction with one
 refinement round, and a two-block decoder pass (`--no-next-rows` skips
@@ -561,7 +562,7 @@ def stage_record(cfg, m, n, N, G, bits, st_ms):
     }
 
 
-def measure_layer(config, li, steps, warmup, keep_inputs=False):
+def measure_layer(config, li, steps, warmup, keep_inputs=False, m=None, tokens=None):
     """Whole-path steps on one named layer, inputs resident in HBM: `warmup`
     untimed steps, then `steps` timed ones with HIP events between the four
     calls.  Returns the per-stage mean times, the wall time per step and the
@@ -573,10 +574,10 @@ def measure_layer(config, li, steps, warmup, keep_inputs=False):
     lib = g.load()
     cfg = wl.WORKLOADS[config]
     layer = cfg.layers[li]
-    m, n, N = layer.m, layer.n, cfg.tokens
+    m, n, N = m or layer.m, layer.n, tokens or cfg.tokens
     torch.cuda.set_device(0)
     t0 = time.perf_counter()
-    L = wl.workload_layer(config, li)
+    L = wl.workload_layer(config, li, m=m, tokens=N)
     X = L.x_all()
     log(f"inputs generated in {time.perf_counter() - t0:.1f}s: W {m}x{n} {cfg.dtype}, X {N}x{n}")
     Wd = to_device(L.W)
@@ -633,7 +634,8 @@ def measure_layer(config, li, steps, warmup, keep_inputs=False):
     wall = time.perf_counter() - t0
     log(f"{steps} timed steps done in {wall:.2f}s")
     stage_names = ["hessian", "prepare", "quantize", "pack"]
-    st_ms = {k: float(np.mean([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)]))
+    # stage times: median over the timed steps
+    st_ms = {k: float(np.median([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)]))
              for i, k in enumerate(stage_names)}
     ms_per_step = wall * 1e3 / steps
 
@@ -815,6 +817,21 @@ def other_layers(config, li):
         }
         log(f"other layer config {c} {name}: {r['ms_per_step']:.3f} ms per step "
             f"({time.perf_counter() - t0:.1f}s)")
+    # One GPU's share of the fc1 layer split over eight GPUs: 1/8 of the rows
+    # (rows are independent given U) and 1/8 of the calibration tokens (each
+    # GPU's partial H is then summed by an all-reduce, not timed here); the
+    # prepare step is the full-width one every GPU would run.
+    t0 = time.perf_counter()
+    cfg = wl.WORKLOADS[4]
+    r = measure_layer(4, 1, 3, 1, m=cfg.layers[1].m // 8, tokens=cfg.tokens // 8)
+    out["config4_fc1_share_of_8"] = {
+        "workload": f"{cfg.name}: fc1 rows 6144 of 49152, tokens 32768 of 262144 (one GPU's share of eight)",
+        "ms_per_step": r["ms_per_step"],
+        "stages": stage_record(cfg, r["m"], r["n"], r["N"], r["G"], r["bits"], r["st_ms"]),
+        "sanity": {"codes_in_range": r["codes_ok"], "finite": r["finite"]},
+    }
+    log(f"one GPU's share of eight of the fc1 layer: {r['ms_per_step']:.3f} ms per step "
+        f"({time.perf_counter() - t0:.1f}s)")
     return out
 
 
