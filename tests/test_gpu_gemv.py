@@ -82,6 +82,9 @@ CASES = [
     (50, 640, 2, 0, False, False, 8),       # per-row, full batch: matrix-core kernel
     (3000, 1280, 4, 0, False, False, 1),    # decode kernel with X in LDS: lanes past the last segment
     (200, 8192, 2, 64, False, False, 1),    # decode kernel with X in LDS: 2-bit, groups of 64
+    (48, 520, 4, 8, False, False, 1),       # groups of 8 columns
+    (30, 264, 3, 2, True, True, 4),         # act-order groups of 2 through g_idx
+    (25, 300, 2, 1, False, False, 6),       # one column per group
 ]
 
 
@@ -252,6 +255,7 @@ GEMM_CASES = [
     (96, 640, 4, 128, 100),     # prefill-sized batch (128 x 128 tiles, X staged in LDS)
     (300, 1000, 3, 0, 257),     # prefill, ragged rows, columns and batch, 3-bit
     (130, 512, 2, 256, 130),    # prefill, 2-bit groups of 256
+    (60, 520, 4, 8, 24),        # groups of 8 columns (per-code path)
 ]
 
 
