@@ -233,6 +233,19 @@ QUANT_CASES = [
 ]
 
 
+def test_quantize_zero_rows_still_writes_g_idx(g):
+    """A layer with no rows quantizes nothing but still reports g_idx, the
+    group of every original column (processing order from perm)."""
+    n, group = 300, 8
+    X = wl.correlated_x(3 * n, n, 5, "f32")
+    H = oracle.hessian(X.f32).astype(F32)
+    U, perm = g.gptq_prepare_hinv(dev(H), 0.01, True)
+    W = wl.gaussian_w(1, n, 5, 0.02, "bf16")
+    q = g.gptq_quantize_layer(stored_to_dev(W)[:0], U, perm, 16, group)
+    assert tuple(q["codes"].shape) == (0, n)
+    np.testing.assert_array_equal(host(q["g_idx"]), oracle.group_index(host(perm), group))
+
+
 @pytest.mark.parametrize("m,n,dtype,levels,group,act", QUANT_CASES)
 def test_quantize_parity(g, m, n, dtype, levels, group, act):
     log(f"quantize m={m} n={n} {dtype} levels={levels} g={group} act={act}")
