@@ -562,7 +562,7 @@ def stage_record(cfg, m, n, N, G, bits, st_ms):
     }
 
 
-def measure_layer(config, li, steps, warmup, keep_inputs=False, m=None, tokens=None):
+def measure_layer(config, li, steps, warmup, keep_inputs=False, m=None, tokens=None, first_block=False):
     """Whole-path steps on one named layer, inputs resident in HBM: `warmup`
     untimed steps, then `steps` timed ones with HIP events between the four
     calls.  Returns the per-stage mean times, the wall time per step and the
@@ -639,11 +639,45 @@ def measure_layer(config, li, steps, warmup, keep_inputs=False, m=None, tokens=N
              for i, k in enumerate(stage_names)}
     ms_per_step = wall * 1e3 / steps
 
+    # One 128-column block of W (all rows, U's leading block) quantized
+    # alone: one sweep launch with no deferred update (plus, for per-row
+    # grids, the range kernel over those columns), so its time is the sweep
+    # role's own, the work each of the layer's launches does beside its
+    # update (median of 20 calls).
+    sweep1 = None
+    if first_block and n >= cfg.block_size:
+        B = cfg.block_size
+        U1 = U[:B, :B].contiguous()
+        o1 = dict(codes=torch.empty((m, B), dtype=torch.uint8, device=dev),
+                  scales=torch.empty((m, 1 if cfg.group_size == 0 else -(-B // cfg.group_size)), dtype=torch.float32,
+                                     device=dev),
+                  zeros=torch.empty((m, 1 if cfg.group_size == 0 else -(-B // cfg.group_size)), dtype=torch.uint8,
+                                    device=dev),
+                  g_idx=None, row_loss=None, Wq=None)
+        ws1 = torch.empty(max(1, lib.gptq_quantize_ws_bytes(m, B, B)), dtype=torch.uint8, device=dev)
+        ts = []
+        for i in range(22):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            g.gptq_quantize_layer(Wd[:, :B], U1, None, cfg.levels, cfg.group_size, B, want_row_loss=False,
+                                  want_g_idx=False, out=o1, ws=ws1)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= 2:
+                ts.append(e0.elapsed_time(e1))
+        in_bytes = {"bf16": 2, "f16": 2, "f32": 4}[cfg.dtype]
+        nbytes = float(m) * B * (in_bytes + 4 + 1) + m * 5 + B * B * 4
+        us = float(np.median(ts)) * 1e3
+        sweep1 = {"us": us, "GBps": nbytes / (us * 1e-6) / 1e9, "frac_hbm": nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS,
+                  "bytes": nbytes,
+                  "what": "one 128-column block of W quantized alone (all rows): a sweep launch with no deferred update"}
+        del U1, o1, ws1
+
     # Sanity of the result (not a parity check; the tests do that).
     codes_ok = bool(int(out["codes"].max().item()) <= cfg.levels - 1)
     finite = bool(torch.isfinite(out["scales"]).all().item() and torch.isfinite(out["row_loss"]).all().item())
     res = dict(layer=layer, m=m, n=n, N=N, st_ms=st_ms, ms_per_step=ms_per_step, G=G, bits=bits,
-               codes_ok=codes_ok, finite=finite, dev=dev)
+               codes_ok=codes_ok, finite=finite, dev=dev, sweep_first_block=sweep1)
     del Xd, Wd, H, U, perm, packed, ws_h, ws_p, ws_q
     if keep_inputs:
         res.update(L=L, X=X, out=out)
@@ -706,7 +740,7 @@ def main():
         return
     cfg = wl.WORKLOADS[args.config]
     li = (len(cfg.layers) - 1 if args.config == 4 else 0) if args.layer is None else args.layer
-    meas = measure_layer(args.config, li, args.steps, args.warmup, keep_inputs=True)
+    meas = measure_layer(args.config, li, args.steps, args.warmup, keep_inputs=True, first_block=True)
     layer, m, n, N = meas["layer"], meas["m"], meas["n"], meas["N"]
     st_ms, ms_per_step, G, bits = meas["st_ms"], meas["ms_per_step"], meas["G"], meas["bits"]
     L, X, out, dev = meas["L"], meas["X"], meas["out"], meas["dev"]
@@ -724,6 +758,8 @@ def main():
     nblocks = -(-n // cfg.block_size)
     flops_h, flops_u = hessian_flops(n, N), update_flops(m, n, cfg.block_size)
     stages = stage_record(cfg, m, n, N, G, bits, st_ms)
+    if meas["sweep_first_block"] is not None:
+        stages["quantize"]["sweep_first_block"] = meas["sweep_first_block"]
     # Dominant kernel's roofline record.  The quantize call is one launch of
     # quant_block_kernel per 128-column block (plus a per-row grid kernel of a
     # few microseconds), so its per-launch figures are the call's divided by
