@@ -42,7 +42,7 @@ extern "C" {
 typedef enum {
   GPTQ_OK = 0,
   GPTQ_ERR_INVALID_ARG = 1,  /* null pointer, bad size or leading dimension */
-  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request this build does not implement */
+  GPTQ_ERR_UNSUPPORTED = 2,  /* valid request the library does not implement */
   GPTQ_ERR_WORKSPACE = 3,    /* workspace missing or smaller than the query */
   GPTQ_ERR_NOT_PD = 4,       /* damped Hessian not positive definite */
   GPTQ_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed */

@@ -36,7 +36,7 @@ def read_golden(name):
 
 @pytest.fixture(scope="session")
 def gpu_lib():
-    """The loaded HIP library on a GPU machine; fails loudly if it is missing."""
+    """The loaded HIP library on a machine with a GPU; fails loudly if it is missing."""
     import torch
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
